@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Throughput of the KV-cache compression path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic KV:
+fused transform + quantize (K and V), lossless encode, scan, compaction,
+then lossless decode and fused reconstruction of the produced stream.  The
+default workload is the Llama-3.1-70B-shaped cache at 32768 tokens (80
+layers x 8 KV heads x 128, bf16, K int4 per-channel groups of 64 tokens, V
+int2 per-token groups of 32, lossless TUPL8_1 -> BIT_8 -> RZE_2), with all
+inputs resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is uncompressed K+V bytes per second of a
+whole step (encode + decode); encode and decode rates are reported too.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+for p in (ROOT, os.path.join(ROOT, "tests")):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E peak
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def fused_bytes_per_elem(pol):
+    # read 2 B, write bits/8 B of codes and 4 B of parameters per group
+    return 2.0 + pol.bits / 8.0 + 4.0 / pol.group
+
+
+def cpu_baseline(wl, layers: int):
+    """The oracle as it stands, single-threaded, on the first `layers` layers
+    of the workload (same value model, generated on the host)."""
+    import kvc_workloads as W
+    import oracle_api as O
+    k, v = W.dense_kv(wl, layers=layers, device="cpu")
+    ku, vu = W.as_u16(k), W.as_u16(v)
+    cfg = O.cfg_from_workload(wl, layers=layers)
+    t0 = time.perf_counter()
+    st, s = O.encode(cfg, ku, vu, wl.tokens)
+    t1 = time.perf_counter()
+    st2, _, _ = O.decode(s, layers * wl.tokens * wl.heads * wl.head_dim)
+    t2 = time.perf_counter()
+    assert st == O.OK and st2 == O.OK
+    U = wl.uncompressed_bytes() / wl.layers * layers
+    return {"value": round(U / (t2 - t0) / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layers 0..{layers - 1} of the workload ({U / 1e9:.3f} GB of K+V), encode + decode",
+            "encode_GBps": round(U / (t1 - t0) / 1e9, 6), "decode_GBps": round(U / (t2 - t1) / 1e9, 6),
+            "seconds": round(t2 - t0, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3_llama70b_32k")
+    ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the compression path runs on one device and this build "
+              "has no multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_compression_kvc_amd as K
+    import kvc_workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    L, T = wl.layers, wl.tokens
+    dev = torch.device("cuda:0")
+    log(f"generating {wl.name}: {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype} on {dev}")
+    k, v = W.dense_kv(wl, device=dev)
+    plan = K.Plan(K.config_from_workload(wl))
+    ms, wsb = plan.sizes(T)
+    out = torch.empty(ms, dtype=torch.uint8, device=dev)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    kd = torch.empty_like(k)
+    vd = torch.empty_like(v)
+    U = wl.uncompressed_bytes()
+    torch.cuda.synchronize()
+
+    n = plan.encode(k, v, T, out, ws)                       # synchronous: size and status
+    plan.decode(out, n, T, kd, vd, ws)
+    st = plan.query_status(ws)
+    assert st == K.OK, K.status_string(st)
+    log(f"stream {n} bytes, ratio {U / n:.4f}")
+
+    def step():
+        plan.encode(k, v, T, out, ws, sync=False)
+        plan.decode(out, ms, T, kd, vd, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    s = torch.cuda.current_stream()
+    K.profile_reset()
+    K.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(args.steps):
+        step()
+    e1.record(s)
+    torch.cuda.synchronize()
+    K.profile_enable(False)
+    step_ms = e0.elapsed_time(e1) / args.steps
+    prof = {name: K.profile_query(name) for name in K.KERNELS}
+    log(f"step {step_ms:.3f} ms; per-kernel ms/launch: " +
+        ", ".join(f"{k_}={t / max(c, 1):.3f}" for k_, (t, c) in prof.items() if c))
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(args.steps):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    enc_ms = timed(lambda: plan.encode(k, v, T, out, ws, sync=False))
+    dec_ms = timed(lambda: plan.decode(out, ms, T, kd, vd, ws))
+    st = plan.query_status(ws)
+    assert st == K.OK, K.status_string(st)
+    log(f"encode {enc_ms:.3f} ms ({U / enc_ms / 1e6:.1f} GB/s), decode {dec_ms:.3f} ms ({U / dec_ms / 1e6:.1f} GB/s)")
+
+    # roofline of the dominant fused kernel, algorithmic bytes per launch
+    elems = L * T * wl.heads * wl.head_dim
+    cand = {
+        "ENCODE_K": elems * fused_bytes_per_elem(wl.k), "ENCODE_V": elems * fused_bytes_per_elem(wl.v),
+        "DECODE_K": elems * fused_bytes_per_elem(wl.k), "DECODE_V": elems * fused_bytes_per_elem(wl.v),
+    }
+    avg = {k_: prof[k_][0] / max(prof[k_][1], 1) for k_ in cand}
+    dom = max(avg, key=avg.get)
+    achieved = cand[dom] / (avg[dom] * 1e-3) / 1e9
+    import ctypes as C
+    codes_params = 0
+    # quantized bytes (codes + parameters) from the closed form
+    for pol in (wl.k, wl.v):
+        codes_params += elems * (pol.bits / 8.0 + 4.0 / pol.group)
+    result = {
+        "metric": "KV encode / decode GB/s (uncompressed bytes) + % HBM peak, compression ratio",
+        "value": round(U / step_ms / 1e6, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama3.1-70b-kv-32k-tokens", "layers": L, "tokens": T, "kv_heads": wl.heads,
+                   "head_dim": wl.head_dim, "io_dtype": wl.dtype,
+                   "k_policy": f"int{wl.k.bits} per-{wl.k.axis} g{wl.k.group} hadamard",
+                   "v_policy": f"int{wl.v.bits} per-{wl.v.axis} g{wl.v.group} hadamard",
+                   "lossless": ">".join(wl.stages), "chunk_bytes": wl.chunk_bytes,
+                   "uncompressed_bytes": U},
+        "encode_GBps": round(U / enc_ms / 1e6, 3),
+        "decode_GBps": round(U / dec_ms / 1e6, 3),
+        "encode_frac_hbm_peak": round(U / enc_ms / 1e6 / HBM_PEAK_GBPS, 4),
+        "decode_frac_hbm_peak": round(U / dec_ms / 1e6 / HBM_PEAK_GBPS, 4),
+        "compression_ratio": round(U / n, 4),
+        "compression_ratio_quant": round(U / codes_params, 4),
+        "compression_ratio_lossless": round(codes_params / n, 4),
+        "stream_bytes": n,
+        "kernel_ms_per_launch": {k_: round(t / max(c, 1), 4) for k_, (t, c) in prof.items() if c},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    s_enc, s_dec = U / enc_ms / 1e6, U / dec_ms / 1e6
+    s_p = s_enc * s_dec / (s_enc + s_dec)
+    result["harmonic_s_p_GBps"] = round(s_p, 3)
+    result["break_even_bandwidth_GBps"] = round((1 - n / U) * s_p, 3)
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on {args.cpu_layers} layers on the host")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_layers)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

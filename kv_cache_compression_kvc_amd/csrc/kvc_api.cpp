@@ -1,0 +1,638 @@
+// Host side of libkvc: plan validation, stream and workspace layouts, launch
+// sequences for encode / decode (dense and paged), device status, profiling.
+//
+// FastKVComp ("Beyond Compression Ratio: High-Throughput KV Compression for
+// Disaggregated LLM Serving") Sec. 4.2: the runtime consumes device buffers,
+// keeps the compressed stream on the GPU, reuses persistent scratch and
+// returns only the compressed size to the host.  Sec. 4.1: signs and
+// precision assignments are computed once and reused (the plan).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+struct kvc_plan_s {
+  kvc_config cfg;
+  TensorPol pol[2];
+  uint32_t signs[4];
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvc_status fail(kvc_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kvc_status fail(kvc_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+kvc_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t a16(int64_t x) { return (x + 15) & ~int64_t(15); }
+int64_t a256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+// splitmix64 output stream (Steele, Lea, Flood, OOPSLA 2014): the i-th sign
+// is -1 when the top bit of the i-th output, state started at the seed, is set.
+uint64_t splitmix_next(uint64_t& st) {
+  st += 0x9E3779B97F4A7C15ull;
+  uint64_t z = st;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+int64_t codes_bytes_of(const TensorPol& p, int L, int T, int H) {
+  if (T == 0) return 0;
+  if (p.axis == 0) return (int64_t)L * T * H * kHeadDim * p.bits / 8;
+  const int64_t ng = cdiv(T, p.group);
+  const int64_t glast = T - (ng - 1) * p.group;
+  const int64_t per_layer = (ng - 1) * H * kHeadDim * (p.group * p.bits / 8) +
+                            (int64_t)H * kHeadDim * cdiv(glast * p.bits, 8);
+  return (int64_t)L * per_layer;
+}
+
+int64_t params_bytes_of(const TensorPol& p, int L, int T, int H) {
+  if (p.axis == 0) return (int64_t)L * T * H * (kHeadDim / p.group) * 4;
+  return (int64_t)L * cdiv(T, p.group) * H * kHeadDim * 4;
+}
+
+int64_t tiles_of(const TensorPol& p, int L, int T, int H) {
+  if (T == 0) return 0;
+  if (p.axis == 0) return (int64_t)L * cdiv((int64_t)T * H, 32);
+  return (int64_t)L * cdiv(T, 64) * H;
+}
+
+// Fill the stream layout of one request with T tokens (offsets inside its stream).
+void request_layout(const kvc_plan_s* p, int T, ReqDesc& rq) {
+  const kvc_config& c = p->cfg;
+  std::memset(&rq, 0, sizeof(rq));
+  rq.T = T;
+  int64_t nch = 0;
+  for (int w = 0; w < 2; ++w) {
+    rq.codes_bytes[w] = codes_bytes_of(p->pol[w], c.layers, T, c.kv_heads);
+    rq.params_bytes[w] = params_bytes_of(p->pol[w], c.layers, T, c.kv_heads);
+    rq.nchunks[w] = (int32_t)cdiv(rq.codes_bytes[w], c.chunk_bytes);
+    nch += rq.nchunks[w];
+    rq.params_ws_off[w] = -1;
+  }
+  rq.params_off[0] = a16(kHeaderBytes + 4 * nch);
+  rq.params_off[1] = a16(rq.params_off[0] + rq.params_bytes[0]);
+  rq.payload_off = a16(rq.params_off[1] + rq.params_bytes[1]);
+  int64_t pay = 0;
+  for (int w = 0; w < 2; ++w)
+    for (int64_t i = 0; i < rq.nchunks[w]; ++i)
+      pay += a16(std::min<int64_t>(c.chunk_bytes, rq.codes_bytes[w] - i * c.chunk_bytes));
+  rq.max_stream = rq.payload_off + pay;
+}
+
+// Workspace carving shared by all calls.
+struct WsLayout {
+  int64_t ctl, sizes, offs, worklist, codes, params, reqs, total;
+};
+
+WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int64_t R) {
+  WsLayout w;
+  w.ctl = 0;
+  w.sizes = 256;
+  w.offs = w.sizes + a256(4 * std::max<int64_t>(nchunks, 1));
+  // the worklist follows the offsets directly (kernels locate it there)
+  w.worklist = w.offs + 8 * (nchunks + 1);
+  w.codes = a256(w.worklist + 4 * std::max<int64_t>(nchunks, 1));
+  w.params = a256(w.codes + codes_area);
+  w.reqs = a256(w.params + params_area);
+  w.total = a256(w.reqs + (R > 1 ? R * (int64_t)sizeof(ReqDesc) : 0));
+  return w;
+}
+
+// ---------------------------------------------------------------- profiling
+
+struct ProfRec { int kind; hipEvent_t a, b; };
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_open;      // recorded, not yet harvested
+std::vector<hipEvent_t> g_prof_pool;
+double g_prof_ms[KVC_KERNEL_COUNT];
+int64_t g_prof_n[KVC_KERNEL_COUNT];
+thread_local hipEvent_t t_prof_start[KVC_KERNEL_COUNT];
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) { hipEvent_t e = g_prof_pool.back(); g_prof_pool.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void prof_harvest_locked() {
+  for (ProfRec& r : g_prof_open) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) { g_prof_ms[r.kind] += ms; g_prof_n[r.kind] += 1; }
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_open.clear();
+}
+
+}  // namespace
+
+namespace kvc {
+void prof_begin(int kind, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  hipEvent_t e = prof_event();
+  if (!e || hipEventRecord(e, s) != hipSuccess) return;
+  t_prof_start[kind] = e;
+}
+void prof_end(int kind, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || !t_prof_start[kind]) return;
+  hipEvent_t e = prof_event();
+  if (!e || hipEventRecord(e, s) != hipSuccess) { t_prof_start[kind] = nullptr; return; }
+  g_prof_open.push_back({kind, t_prof_start[kind], e});
+  t_prof_start[kind] = nullptr;
+  if (g_prof_open.size() > 4096) prof_harvest_locked();
+}
+}  // namespace kvc
+
+namespace {
+
+template <typename F>
+hipError_t timed(int kind, hipStream_t s, F&& f) {
+  prof_begin(kind, s);
+  hipError_t e = f();
+  prof_end(kind, s);
+  return e;
+}
+
+// ---------------------------------------------------------------- validation
+
+kvc_status check_policy(const kvc_tensor_policy& t, const char* name, int head_dim) {
+  if (!(t.bits == 2 || t.bits == 4 || t.bits == 8)) return fail(KVC_ERR_INVALID_ARG, "%s.bits must be 2, 4 or 8", name);
+  if (t.axis > 1) return fail(KVC_ERR_INVALID_ARG, "%s.axis must be 0 or 1", name);
+  if (t.hadamard > 1) return fail(KVC_ERR_INVALID_ARG, "%s.hadamard must be 0 or 1", name);
+  if (!pow2(t.group)) return fail(KVC_ERR_INVALID_ARG, "%s.group must be a power of two", name);
+  if (t.axis == 0 && (t.group < 8 || t.group > head_dim))
+    return fail(KVC_ERR_INVALID_ARG, "%s.group must be in [8, head_dim] for per-token groups", name);
+  if (t.axis == 1 && (t.group < 16 || t.group > 256))
+    return fail(KVC_ERR_INVALID_ARG, "%s.group must be in [16, 256] for per-channel groups", name);
+  return KVC_OK;
+}
+
+kvc_status check_gpu_support(const kvc_tensor_policy& t, const char* name) {
+  if (!t.hadamard)
+    return fail(KVC_ERR_UNSUPPORTED, "%s: the GPU kernels always apply the randomized Hadamard transform", name);
+  if (t.axis == 0 && t.group < 16)
+    return fail(KVC_ERR_UNSUPPORTED, "%s: per-token groups smaller than 16 are not implemented on the GPU", name);
+  if (t.axis == 1 && !(t.group == 32 || t.group == 64))
+    return fail(KVC_ERR_UNSUPPORTED, "%s: per-channel groups other than 32 or 64 are not implemented on the GPU", name);
+  return KVC_OK;
+}
+
+kvc_status check_ptr(const void* p, size_t align, const char* name) {
+  if (!p) return fail(KVC_ERR_INVALID_ARG, "%s is NULL", name);
+  if (((uintptr_t)p) % align) return fail(KVC_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, align);
+  return KVC_OK;
+}
+
+void fill_common(const kvc_plan_s* p, CallDesc& c) {
+  std::memset(&c, 0, sizeof(c));
+  c.layers = p->cfg.layers;
+  c.heads = p->cfg.kv_heads;
+  c.dtype = p->cfg.dtype;
+  c.pol[0] = p->pol[0];
+  c.pol[1] = p->pol[1];
+  std::memcpy(c.signs, p->signs, sizeof(c.signs));
+  std::memcpy(c.stages, p->cfg.lossless, 4);
+  c.chunk_bytes = p->cfg.chunk_bytes;
+  c.seed = p->cfg.sign_seed;
+}
+
+kvc_status device_status(uint32_t bits) {
+  if (bits & kStMismatch) return fail(KVC_ERR_PLAN_MISMATCH, "stream header does not match the plan or token count");
+  if (bits & kStCorrupt) return fail(KVC_ERR_CORRUPT_STREAM, "stream failed validation on the device");
+  if (bits & kStBadBlock) return fail(KVC_ERR_INVALID_ARG, "block table entry out of range");
+  if (bits & kStRange) return fail(KVC_ERR_RANGE, "a quantization parameter is not a finite fp16 value");
+  return KVC_OK;
+}
+
+kvc_status sync_and_read(Control* d_ctl, hipStream_t s, Control& h) {
+  hipError_t e = hipMemcpyAsync(&h, d_ctl, 16, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(status)");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  return KVC_OK;
+}
+
+// Requests of a paged call, laid out one after another.
+struct PagedJob {
+  std::vector<ReqDesc> reqs;
+  int64_t chunks = 0, pieces = 0, codes_area = 0, params_area = 0, max_total = 0;
+  int64_t tiles[2] = {0, 0};
+};
+
+PagedJob paged_job(const kvc_plan_s* p, const int32_t* lens, int R, bool encode) {
+  PagedJob j;
+  j.reqs.resize(R);
+  for (int r = 0; r < R; ++r) {
+    ReqDesc& rq = j.reqs[r];
+    request_layout(p, lens[r], rq);
+    rq.row = r;
+    rq.chunk_begin = j.chunks;
+    j.chunks += rq.nchunks[0] + rq.nchunks[1];
+    for (int w = 0; w < 2; ++w) {
+      rq.tile_begin[w] = j.tiles[w];
+      j.tiles[w] += tiles_of(p->pol[w], p->cfg.layers, lens[r], p->cfg.kv_heads);
+      rq.codes_off[w] = j.codes_area;
+      j.codes_area += a256(rq.codes_bytes[w]);
+      if (encode) {
+        rq.params_ws_off[w] = j.params_area;
+        j.params_area += a256(rq.params_bytes[w]);
+      }
+    }
+    rq.piece_begin = j.pieces;
+    if (encode) j.pieces += cdiv(rq.params_bytes[0], 65536) + cdiv(rq.params_bytes[1], 65536);
+    j.max_total += rq.max_stream;
+  }
+  return j;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" {
+
+const char* kvc_status_string(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARG: return "invalid argument";
+    case KVC_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVC_ERR_NO_MEMORY: return "out of host memory";
+    case KVC_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case KVC_ERR_CORRUPT_STREAM: return "corrupt stream";
+    case KVC_ERR_PLAN_MISMATCH: return "stream does not match the plan";
+    case KVC_ERR_RANGE: return "quantization parameter out of fp16 range";
+    case KVC_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+kvc_status kvc_plan(const kvc_config* cfg, kvc_plan_t* out) {
+  if (!cfg || !out) return fail(KVC_ERR_INVALID_ARG, "cfg and out must be non-NULL");
+  *out = nullptr;
+  if (cfg->struct_size != sizeof(kvc_config))
+    return fail(KVC_ERR_INVALID_ARG, "struct_size %u != sizeof(kvc_config) %zu", cfg->struct_size, sizeof(kvc_config));
+  if (cfg->layers < 1 || cfg->layers > 4096) return fail(KVC_ERR_INVALID_ARG, "layers must be in [1, 4096]");
+  if (cfg->max_tokens < 0 || cfg->max_tokens > (1 << 26)) return fail(KVC_ERR_INVALID_ARG, "max_tokens must be in [0, 2^26]");
+  if (cfg->kv_heads < 1 || cfg->kv_heads > 1024) return fail(KVC_ERR_INVALID_ARG, "kv_heads must be in [1, 1024]");
+  if (!pow2(cfg->head_dim) || cfg->head_dim < 16 || cfg->head_dim > 256)
+    return fail(KVC_ERR_INVALID_ARG, "head_dim must be a power of two in [16, 256]");
+  if (cfg->dtype != KVC_F16 && cfg->dtype != KVC_BF16) return fail(KVC_ERR_INVALID_ARG, "dtype must be KVC_F16 or KVC_BF16");
+  kvc_status st;
+  if ((st = check_policy(cfg->k, "k", cfg->head_dim)) != KVC_OK) return st;
+  if ((st = check_policy(cfg->v, "v", cfg->head_dim)) != KVC_OK) return st;
+  if (cfg->chunk_bytes < 4096 || cfg->chunk_bytes > 65536 || cfg->chunk_bytes % 4096)
+    return fail(KVC_ERR_INVALID_ARG, "chunk_bytes must be a multiple of 4096 in [4096, 65536]");
+  bool rze = false;
+  for (int i = 0; i < 4 && cfg->lossless[i]; ++i) {
+    const int s = cfg->lossless[i];
+    if (s < KVC_TUPL2_1 || s > KVC_RZE_8) return fail(KVC_ERR_INVALID_ARG, "lossless[%d] = %d is not a stage id", i, s);
+    if (rze) return fail(KVC_ERR_UNSUPPORTED, "zero elimination must be the last lossless stage");
+    if (s >= KVC_RZE_1) rze = true;
+  }
+  if (cfg->page_tokens < 0) return fail(KVC_ERR_INVALID_ARG, "page_tokens must be >= 0");
+  if (cfg->head_dim != kHeadDim) return fail(KVC_ERR_UNSUPPORTED, "the GPU kernels implement head_dim 128 only");
+  if ((st = check_gpu_support(cfg->k, "k")) != KVC_OK) return st;
+  if ((st = check_gpu_support(cfg->v, "v")) != KVC_OK) return st;
+
+  kvc_plan_s* p = new (std::nothrow) kvc_plan_s;
+  if (!p) return fail(KVC_ERR_NO_MEMORY, "plan allocation failed");
+  p->cfg = *cfg;
+  const kvc_tensor_policy* tp[2] = {&cfg->k, &cfg->v};
+  for (int w = 0; w < 2; ++w) {
+    p->pol[w].bits = tp[w]->bits;
+    p->pol[w].axis = tp[w]->axis;
+    p->pol[w].group = tp[w]->group;
+    p->pol[w].hadamard = tp[w]->hadamard;
+    p->pol[w].c = tp[w]->hadamard ? (float)(1.0 / std::sqrt((double)cfg->head_dim)) : 1.0f;
+  }
+  std::memset(p->signs, 0, sizeof(p->signs));
+  uint64_t st64 = cfg->sign_seed;
+  for (int i = 0; i < kHeadDim; ++i)
+    if (splitmix_next(st64) >> 63) p->signs[i >> 5] |= 1u << (i & 31);
+  *out = p;
+  return KVC_OK;
+}
+
+kvc_status kvc_plan_destroy(kvc_plan_t plan) {
+  delete plan;
+  return KVC_OK;
+}
+
+kvc_status kvc_plan_sizes(kvc_plan_t p, int64_t tokens, size_t* max_stream_bytes, size_t* workspace_bytes) {
+  if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
+  if (tokens < 0 || tokens > p->cfg.max_tokens) return fail(KVC_ERR_INVALID_ARG, "tokens must be in [0, max_tokens]");
+  ReqDesc rq;
+  request_layout(p, (int)tokens, rq);
+  const int64_t codes_area = a256(rq.codes_bytes[0]) + a256(rq.codes_bytes[1]);
+  const WsLayout w = ws_layout(rq.nchunks[0] + rq.nchunks[1], codes_area, 0, 1);
+  if (max_stream_bytes) *max_stream_bytes = (size_t)rq.max_stream;
+  if (workspace_bytes) *workspace_bytes = (size_t)w.total;
+  return KVC_OK;
+}
+
+kvc_status kvc_plan_sizes_paged(kvc_plan_t p, const int32_t* lens, int32_t R, size_t* max_total, size_t* ws_bytes) {
+  if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
+  if (R < 0 || (R > 0 && !lens)) return fail(KVC_ERR_INVALID_ARG, "bad request list");
+  for (int r = 0; r < R; ++r)
+    if (lens[r] < 0 || lens[r] > (1 << 26)) return fail(KVC_ERR_INVALID_ARG, "seq_lens[%d] out of range", r);
+  const PagedJob je = paged_job(p, lens, R, true);
+  const PagedJob jd = paged_job(p, lens, R, false);
+  const WsLayout we = ws_layout(je.chunks, je.codes_area, je.params_area, R);
+  const WsLayout wd = ws_layout(jd.chunks, jd.codes_area, jd.params_area, R);
+  if (max_total) *max_total = (size_t)je.max_total;
+  if (ws_bytes) *ws_bytes = (size_t)std::max(we.total, wd.total);
+  return KVC_OK;
+}
+
+kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t tokens, void* d_out,
+                      size_t out_capacity, void* d_ws, size_t ws_bytes, size_t* h_out_bytes, void* stream) {
+  if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
+  if (tokens < 0 || tokens > p->cfg.max_tokens) return fail(KVC_ERR_INVALID_ARG, "tokens must be in [0, max_tokens]");
+  kvc_status st;
+  if (tokens > 0) {
+    if ((st = check_ptr(d_k, 16, "d_k")) != KVC_OK) return st;
+    if ((st = check_ptr(d_v, 16, "d_v")) != KVC_OK) return st;
+  }
+  if ((st = check_ptr(d_out, 16, "d_out")) != KVC_OK) return st;
+  if ((st = check_ptr(d_ws, 256, "d_ws")) != KVC_OK) return st;
+  CallDesc c;
+  fill_common(p, c);
+  c.R = 1;
+  request_layout(p, tokens, c.one);
+  const int64_t codes_area = a256(c.one.codes_bytes[0]) + a256(c.one.codes_bytes[1]);
+  c.one.codes_off[1] = a256(c.one.codes_bytes[0]);
+  const WsLayout w = ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1);
+  if ((int64_t)out_capacity < c.one.max_stream)
+    return fail(KVC_ERR_BUFFER_TOO_SMALL, "out_capacity %zu < %lld", out_capacity, (long long)c.one.max_stream);
+  if ((int64_t)ws_bytes < w.total) return fail(KVC_ERR_BUFFER_TOO_SMALL, "ws_bytes %zu < %lld", ws_bytes, (long long)w.total);
+  uint8_t* ws = (uint8_t*)d_ws;
+  c.in_kv[0] = d_k;
+  c.in_kv[1] = d_v;
+  c.codes = ws + w.codes;
+  c.stream = (uint8_t*)d_out;
+  c.chunk_sizes = (uint32_t*)(ws + w.sizes);
+  c.chunk_offs = (uint64_t*)(ws + w.offs);
+  c.ctl = (Control*)(ws + w.ctl);
+  c.total_chunks = c.one.nchunks[0] + c.one.nchunks[1];
+  for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
+  if ((e = timed(KVC_KERNEL_ENCODE_K, s, [&] { return launch_encode_fused(c, 0, s); })) != hipSuccess) return hip_fail(e, "encode K");
+  if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return launch_encode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "encode V");
+  if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
+  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
+  if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_compact(c, s); })) != hipSuccess) return hip_fail(e, "compact");
+  if (h_out_bytes) {
+    Control h;
+    if ((st = sync_and_read(c.ctl, s, h)) != KVC_OK) return st;
+    *h_out_bytes = (size_t)h.total;
+    return device_status(h.status);
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t tokens, void* d_k, void* d_v,
+                      void* d_ws, size_t ws_bytes, void* stream) {
+  if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
+  if (tokens < 0 || tokens > p->cfg.max_tokens) return fail(KVC_ERR_INVALID_ARG, "tokens must be in [0, max_tokens]");
+  kvc_status st;
+  if ((st = check_ptr(d_in, 16, "d_in")) != KVC_OK) return st;
+  if (tokens > 0) {
+    if ((st = check_ptr(d_k, 16, "d_k")) != KVC_OK) return st;
+    if ((st = check_ptr(d_v, 16, "d_v")) != KVC_OK) return st;
+  }
+  if ((st = check_ptr(d_ws, 256, "d_ws")) != KVC_OK) return st;
+  CallDesc c;
+  fill_common(p, c);
+  c.R = 1;
+  request_layout(p, tokens, c.one);
+  if ((int64_t)in_bytes < c.one.payload_off)
+    return fail(KVC_ERR_CORRUPT_STREAM, "in_bytes %zu is shorter than the stream's fixed sections (%lld)", in_bytes,
+                (long long)c.one.payload_off);
+  const int64_t codes_area = a256(c.one.codes_bytes[0]) + a256(c.one.codes_bytes[1]);
+  c.one.codes_off[1] = a256(c.one.codes_bytes[0]);
+  const WsLayout w = ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1);
+  if ((int64_t)ws_bytes < w.total) return fail(KVC_ERR_BUFFER_TOO_SMALL, "ws_bytes %zu < %lld", ws_bytes, (long long)w.total);
+  uint8_t* ws = (uint8_t*)d_ws;
+  c.out_kv[0] = d_k;
+  c.out_kv[1] = d_v;
+  c.codes = ws + w.codes;
+  c.stream = (uint8_t*)const_cast<void*>(d_in);
+  c.stream_bytes = in_bytes;
+  c.chunk_sizes = (uint32_t*)(ws + w.sizes);
+  c.chunk_offs = (uint64_t*)(ws + w.offs);
+  c.ctl = (Control*)(ws + w.ctl);
+  c.total_chunks = c.one.nchunks[0] + c.one.nchunks[1];
+  for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
+  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_validate(c, s); })) != hipSuccess) return hip_fail(e, "validate");
+  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
+  if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
+  if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return launch_decode_fused(c, 0, s); })) != hipSuccess) return hip_fail(e, "decode K");
+  if ((e = timed(KVC_KERNEL_DECODE_V, s, [&] { return launch_decode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "decode V");
+  return KVC_OK;
+}
+
+static kvc_status paged_common(kvc_plan_t p, int64_t num_blocks, const int32_t* d_bt, int32_t maxb,
+                               const int32_t* lens, int32_t R) {
+  if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
+  if (p->cfg.page_tokens < 1) return fail(KVC_ERR_INVALID_ARG, "plan was built without page_tokens");
+  if (p->pol[0].axis != 0 || p->pol[1].axis != 0)
+    return fail(KVC_ERR_UNSUPPORTED, "paged calls implement per-token policies only");
+  if (((int64_t)p->cfg.page_tokens * p->cfg.kv_heads) % 32)
+    return fail(KVC_ERR_UNSUPPORTED, "page_tokens * kv_heads must be a multiple of 32");
+  if (R < 1 || !lens) return fail(KVC_ERR_INVALID_ARG, "need at least one request");
+  if (num_blocks < 0 || maxb < 1) return fail(KVC_ERR_INVALID_ARG, "bad pool or block table shape");
+  kvc_status st;
+  if ((st = check_ptr(d_bt, 4, "d_block_table")) != KVC_OK) return st;
+  for (int r = 0; r < R; ++r) {
+    if (lens[r] < 0 || lens[r] > (1 << 26)) return fail(KVC_ERR_INVALID_ARG, "seq_lens[%d] out of range", r);
+    if (cdiv(lens[r], p->cfg.page_tokens) > maxb)
+      return fail(KVC_ERR_INVALID_ARG, "seq_lens[%d] needs more than max_blocks_per_req pages", r);
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_pool, int64_t num_blocks,
+                            const int32_t* d_bt, int32_t maxb, const int32_t* lens, int32_t R, void* d_out,
+                            size_t out_capacity, uint64_t* d_req_offsets, void* d_ws, size_t ws_bytes,
+                            size_t* h_out_bytes, void* stream) {
+  kvc_status st = paged_common(p, num_blocks, d_bt, maxb, lens, R);
+  if (st != KVC_OK) return st;
+  if ((st = check_ptr(d_k_pool, 16, "d_k_pool")) != KVC_OK) return st;
+  if ((st = check_ptr(d_v_pool, 16, "d_v_pool")) != KVC_OK) return st;
+  if ((st = check_ptr(d_out, 16, "d_out")) != KVC_OK) return st;
+  if ((st = check_ptr(d_req_offsets, 8, "d_req_offsets")) != KVC_OK) return st;
+  if ((st = check_ptr(d_ws, 256, "d_ws")) != KVC_OK) return st;
+  PagedJob j = paged_job(p, lens, R, true);
+  const WsLayout w = ws_layout(j.chunks, j.codes_area, j.params_area, R);
+  if ((int64_t)out_capacity < j.max_total) return fail(KVC_ERR_BUFFER_TOO_SMALL, "out_capacity too small");
+  if ((int64_t)ws_bytes < w.total) return fail(KVC_ERR_BUFFER_TOO_SMALL, "ws_bytes too small");
+  CallDesc c;
+  fill_common(p, c);
+  uint8_t* ws = (uint8_t*)d_ws;
+  c.R = R;
+  c.one = j.reqs[0];
+  c.reqs = (const ReqDesc*)(ws + w.reqs);
+  c.page_tokens = p->cfg.page_tokens;
+  c.num_blocks = num_blocks;
+  c.block_table = d_bt;
+  c.max_blocks = maxb;
+  c.in_kv[0] = d_k_pool;
+  c.in_kv[1] = d_v_pool;
+  c.codes = ws + w.codes;
+  c.params_ws = ws + w.params;
+  c.stream = (uint8_t*)d_out;
+  c.req_offsets_out = d_req_offsets;
+  c.chunk_sizes = (uint32_t*)(ws + w.sizes);
+  c.chunk_offs = (uint64_t*)(ws + w.offs);
+  c.ctl = (Control*)(ws + w.ctl);
+  c.total_chunks = j.chunks;
+  c.total_pieces = j.pieces;
+  c.tiles[0] = j.tiles[0];
+  c.tiles[1] = j.tiles[1];
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (R > 1) {
+    e = hipMemcpyAsync(ws + w.reqs, j.reqs.data(), R * sizeof(ReqDesc), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(requests)");
+  }
+  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
+  if ((e = timed(KVC_KERNEL_ENCODE_K, s, [&] { return launch_encode_fused(c, 0, s); })) != hipSuccess) return hip_fail(e, "encode K");
+  if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return launch_encode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "encode V");
+  if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
+  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
+  if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_compact(c, s); })) != hipSuccess) return hip_fail(e, "compact");
+  if (h_out_bytes) {
+    Control h;
+    if ((st = sync_and_read(c.ctl, s, h)) != KVC_OK) return st;
+    *h_out_bytes = (size_t)h.total;
+    return device_status(h.status);
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_decode_paged(kvc_plan_t p, const void* d_in, size_t in_bytes, const uint64_t* d_req_offsets,
+                            const int32_t* lens, int32_t R, void* d_k_pool, void* d_v_pool, int64_t num_blocks,
+                            const int32_t* d_bt, int32_t maxb, void* d_ws, size_t ws_bytes, void* stream) {
+  kvc_status st = paged_common(p, num_blocks, d_bt, maxb, lens, R);
+  if (st != KVC_OK) return st;
+  if ((st = check_ptr(d_in, 16, "d_in")) != KVC_OK) return st;
+  if ((st = check_ptr(d_req_offsets, 8, "d_req_offsets")) != KVC_OK) return st;
+  if ((st = check_ptr(d_k_pool, 16, "d_k_pool")) != KVC_OK) return st;
+  if ((st = check_ptr(d_v_pool, 16, "d_v_pool")) != KVC_OK) return st;
+  if ((st = check_ptr(d_ws, 256, "d_ws")) != KVC_OK) return st;
+  PagedJob j = paged_job(p, lens, R, false);
+  const WsLayout w = ws_layout(j.chunks, j.codes_area, j.params_area, R);
+  if ((int64_t)ws_bytes < w.total) return fail(KVC_ERR_BUFFER_TOO_SMALL, "ws_bytes too small");
+  CallDesc c;
+  fill_common(p, c);
+  uint8_t* ws = (uint8_t*)d_ws;
+  c.R = R;
+  c.one = j.reqs[0];
+  c.reqs = (const ReqDesc*)(ws + w.reqs);
+  c.page_tokens = p->cfg.page_tokens;
+  c.num_blocks = num_blocks;
+  c.block_table = d_bt;
+  c.max_blocks = maxb;
+  c.out_kv[0] = d_k_pool;
+  c.out_kv[1] = d_v_pool;
+  c.codes = ws + w.codes;
+  c.stream = (uint8_t*)const_cast<void*>(d_in);
+  c.stream_bytes = in_bytes;
+  c.req_offsets = d_req_offsets;
+  c.chunk_sizes = (uint32_t*)(ws + w.sizes);
+  c.chunk_offs = (uint64_t*)(ws + w.offs);
+  c.ctl = (Control*)(ws + w.ctl);
+  c.total_chunks = j.chunks;
+  c.tiles[0] = j.tiles[0];
+  c.tiles[1] = j.tiles[1];
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (R > 1) {
+    e = hipMemcpyAsync(ws + w.reqs, j.reqs.data(), R * sizeof(ReqDesc), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(requests)");
+  }
+  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
+  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_validate(c, s); })) != hipSuccess) return hip_fail(e, "validate");
+  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
+  if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
+  if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return launch_decode_fused(c, 0, s); })) != hipSuccess) return hip_fail(e, "decode K");
+  if ((e = timed(KVC_KERNEL_DECODE_V, s, [&] { return launch_decode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "decode V");
+  return KVC_OK;
+}
+
+kvc_status kvc_query_status(kvc_plan_t p, const void* d_ws, void* stream) {
+  if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
+  kvc_status st = check_ptr(d_ws, 256, "d_ws");
+  if (st != KVC_OK) return st;
+  Control h;
+  Control* ctl = (Control*)const_cast<void*>(d_ws);
+  if ((st = sync_and_read(ctl, (hipStream_t)stream, h)) != KVC_OK) return st;
+  CallDesc c;
+  std::memset(&c, 0, sizeof(c));
+  c.ctl = ctl;
+  hipError_t e = launch_reset(c, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reset");
+  return device_status(h.status);
+}
+
+kvc_status kvc_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return KVC_OK;
+}
+
+kvc_status kvc_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_harvest_locked();
+  for (int k = 0; k < KVC_KERNEL_COUNT; ++k) { g_prof_ms[k] = 0; g_prof_n[k] = 0; }
+  return KVC_OK;
+}
+
+kvc_status kvc_profile_query(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= KVC_KERNEL_COUNT) return fail(KVC_ERR_INVALID_ARG, "bad kernel kind");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_harvest_locked();
+  if (total_ms) *total_ms = g_prof_ms[kind];
+  if (launches) *launches = g_prof_n[kind];
+  return KVC_OK;
+}
+
+}  // extern "C"

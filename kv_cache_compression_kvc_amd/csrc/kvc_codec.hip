@@ -1,0 +1,877 @@
+// Fused transform + quantize (encode) and fused reconstruct (decode) kernels
+// for gfx950.
+//
+// Method: "Beyond Compression Ratio: High-Throughput KV Compression for
+// Disaggregated LLM Serving" (FastKVComp), Sec. 4.1.  The encoder applies a
+// seeded sign flip and a Hadamard transform over head_dim, computes per-group
+// min/max, derives fp16 (scale, minimum) parameters and writes packed 2/4/8-bit
+// codes, all in one pass over the input; no transformed tensor is written to
+// HBM.  The decoder dequantizes, applies the inverse transform with the
+// normalization folded into the group parameters, restores the signs and
+// writes 16-bit values.
+//
+// Arithmetic (fixed so that results are reproducible bit for bit):
+//   z      = unnormalized Walsh-Hadamard transform of d*x in binary32, stages
+//            with pair distance 1, 2, 4, ..., 64 in that order;
+//   lo, hi = c*min z rounded down, c*max z rounded up (binary32);
+//   m      = lo rounded down to fp16;  s = ((hi - m) rounded up) / (2^b - 1)
+//            rounded up to binary32, then up to fp16;  inv = 1/s (0 if s = 0);
+//   q      = round-half-even( fma(z, c, -m) * inv ), product exact;
+//   decode = d * FWHT( fma(q, fl(s*c), fl(m*c)) ), rounded to nearest-even.
+// Directed roundings use error-free transforms (TwoProduct with fma, TwoSum).
+//
+// Work layout.  A head vector (128 channels) is held by two lanes, 64 values
+// each (lane L and L+32 of a wavefront of 64).  Inputs are read with
+// bounds-checked 16-byte buffer loads (out-of-range lanes read zero, so there
+// is no branch per load), sign-flipped in the 16-bit domain and transposed
+// through a wave-private LDS tile whose 272-byte row pitch keeps both the
+// row-major writes and the per-lane reads free of bank conflicts.  Six
+// butterfly stages run in registers; the seventh pairs the two lanes with
+// v_permlane32_swap, which also leaves each lane holding whole 32-channel
+// groups.  Per-channel groups (keys) are reduced through a second LDS
+// transpose so that one thread owns one channel of one token group.
+#include <algorithm>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+typedef int int2v __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over [p, p + bytes): loads past the end return zero and
+// stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const int4v x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4((uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void bstore16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  int4v x = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void bstore8(uint2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  int2v x = {(int)v.x, (int)v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void bstore4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32((int)v, r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ float next_up32(float f) {
+  uint32_t u = f2u(f);
+  if ((u & 0x7fffffffu) == 0) return u2f(1u);
+  return u2f((u >> 31) ? u - 1 : u + 1);
+}
+__device__ __forceinline__ float next_down32(float f) {
+  uint32_t u = f2u(f);
+  if ((u & 0x7fffffffu) == 0) return u2f(0x80000001u);
+  return u2f((u >> 31) ? u + 1 : u - 1);
+}
+
+// Largest binary32 <= a*b.  fma gives the exact error of the rounded product;
+// its sign bit is reliable even when it underflows to a signed zero.
+__device__ __forceinline__ float mul_rd(float a, float b) {
+  float p = a * b;
+  float e = __builtin_fmaf(a, b, -p);
+  return (f2u(e) >> 31) ? next_down32(p) : p;
+}
+__device__ __forceinline__ float mul_ru(float a, float b) { return -mul_rd(-a, b); }
+
+// Smallest binary32 >= a - b (TwoSum).
+__device__ __forceinline__ float sub_ru(float a, float b) {
+  float s = a - b;
+  float bb = s - a;
+  float e = (a - (s - bb)) + (-b - bb);
+  return (e > 0.0f) ? next_up32(s) : s;
+}
+
+// Smallest binary32 >= r / k for r >= 0 and a small positive integer k.
+__device__ __forceinline__ float div_ru(float r, float k) {
+  float q = r / k;
+  float e = __builtin_fmaf(q, k, -r);
+  return (f2u(e) >> 31) ? next_up32(q) : q;
+}
+
+__device__ __forceinline__ uint32_t h16_from(float f) {
+  _Float16 h = (_Float16)f;                     // v_cvt_f16_f32, round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f_from_h16(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ uint32_t h16_next_down(uint32_t h) {
+  if (h == 0xfc00u) return h;
+  if (h == 0x0000u) return 0x8001u;
+  return (h & 0x8000u) ? h + 1 : h - 1;
+}
+__device__ __forceinline__ uint32_t h16_next_up(uint32_t h) {
+  if (h == 0x7c00u) return h;
+  if (h == 0x8000u) return 0x0001u;
+  return (h & 0x8000u) ? h - 1 : h + 1;
+}
+__device__ __forceinline__ uint32_t h16_rd(float f) {
+  uint32_t h = h16_from(f);
+  return (f_from_h16(h) > f) ? h16_next_down(h) : h;
+}
+__device__ __forceinline__ uint32_t h16_ru(float f) {
+  uint32_t h = h16_from(f);
+  return (f_from_h16(h) < f) ? h16_next_up(h) : h;
+}
+
+struct GroupQ {
+  float neg_m;      // -m as binary32
+  float inv;        // 1/s or 0
+  uint32_t packed;  // s | m << 16 (stream parameter word)
+  bool bad;         // a parameter is not a finite fp16
+};
+
+__device__ __forceinline__ GroupQ group_params(float zmin, float zmax, float c, float levels) {
+  const float lo = mul_rd(zmin, c);
+  const float hi = mul_ru(zmax, c);
+  const uint32_t m16 = h16_rd(lo);
+  const float mf = f_from_h16(m16);
+  const float range = sub_ru(hi, mf);
+  const float s32 = div_ru(range, levels);
+  const uint32_t s16 = h16_ru(s32);
+  const float sf = f_from_h16(s16);
+  GroupQ g;
+  g.neg_m = -mf;
+  g.inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+  g.packed = s16 | (m16 << 16);
+  g.bad = ((s16 & 0x7c00u) == 0x7c00u) || ((m16 & 0x7c00u) == 0x7c00u) || (lo != lo) || (hi != hi);
+  return g;
+}
+
+// Code of one value: fl(fl(z*c - m) * inv + 2^23) carries round-half-even(t*inv)
+// in its low mantissa bits (exact product, one rounding); bits 8..23 are zero.
+__device__ __forceinline__ uint32_t quant_code(float z, float c, const GroupQ& g) {
+  const float t = __builtin_fmaf(z, c, g.neg_m);
+  return f2u(__builtin_fmaf(t, g.inv, 0x1p23f));
+}
+
+// Merge codes held in the low byte of each word (bits 8..23 zero) into packed
+// BITS-bit fields, LSB first: 32/BITS codes -> one dword.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_dword(const uint32_t* q) {
+  if constexpr (BITS == 8) {
+    const uint32_t a = (q[1] << 8) | q[0], b = (q[3] << 8) | q[2];
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+  } else if constexpr (BITS == 4) {
+    const uint32_t p0 = (q[1] << 4) | q[0], p1 = (q[3] << 4) | q[2];
+    const uint32_t p2 = (q[5] << 4) | q[4], p3 = (q[7] << 4) | q[6];
+    const uint32_t a = (p1 << 8) | p0, b = (p3 << 8) | p2;
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+  } else {
+    uint32_t by[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t p0 = (q[4 * k + 1] << 2) | q[4 * k];
+      const uint32_t p1 = (q[4 * k + 3] << 2) | q[4 * k + 2];
+      by[k] = (p1 << 4) | p0;
+    }
+    const uint32_t a = (by[1] << 8) | by[0], b = (by[3] << 8) | by[2];
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ float unpack_code(const uint32_t* w, int i) {
+  if constexpr (BITS == 4) return (float)((w[i >> 3] >> (4 * (i & 7))) & 15u);
+  else if constexpr (BITS == 2) return (float)((w[i >> 4] >> (2 * (i & 15))) & 3u);
+  else return (float)((w[i >> 2] >> (8 * (i & 3))) & 255u);
+}
+
+// 16-bit pair -> two binary32 values
+template <bool BF16>
+__device__ __forceinline__ void unpack16(uint32_t u, float& lo, float& hi) {
+  if constexpr (BF16) {
+    lo = u2f(u << 16);
+    hi = u2f(u & 0xffff0000u);
+  } else {
+    lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xffffu));
+    hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16));
+  }
+}
+
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
+
+// two binary32 values -> 16-bit pair, round to nearest even
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack16(float lo, float hi) {
+  float2v f = {lo, hi};
+  if constexpr (BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf162v));
+  else return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2v));
+}
+
+// Sign-flip masks for the 8 channels [8*slot, 8*slot + 8) of a 16-byte slot:
+// dword j flips channels 8*slot + 2j (bit 15) and 8*slot + 2j + 1 (bit 31).
+__device__ __forceinline__ void slot_sign_masks(const uint32_t* signs, int slot, uint32_t* m) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ch = 8 * slot + 2 * j;
+    const uint32_t b0 = (signs[ch >> 5] >> (ch & 31)) & 1u;
+    const uint32_t b1 = (signs[(ch + 1) >> 5] >> ((ch + 1) & 31)) & 1u;
+    m[j] = (b0 << 15) | (b1 << 31);
+  }
+}
+
+// One butterfly (a, b) -> (a + b, a - b), each result rounded once.  Written
+// as a fixed two-instruction sequence so that the register allocator updates
+// the pair in place (one temporary) instead of keeping every stage's inputs
+// and outputs alive; that halves the registers the transform needs.
+__device__ __forceinline__ void bfly(float& a, float& b) {
+  float t;
+  asm volatile("v_sub_f32 %0, %1, %2\n\tv_add_f32 %1, %1, %2" : "=&v"(t), "+v"(a) : "v"(b));
+  b = t;
+}
+
+// Butterfly stages 1..32 on a lane's 64 values (register r <-> local channel r).
+__device__ __forceinline__ void fwht64_inreg(float* v) {
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      if (!(r & h)) bfly(v[r], v[r + h]);
+    }
+  }
+}
+
+// Stage 64 across the lane pair (L, L+32).  Before: lane half hf holds
+// channels [64 hf, 64 hf + 64).  After: register r < 32 holds channel
+// 32 hf + r and register 32 + r holds channel 64 + 32 hf + r.
+__device__ __forceinline__ void fwht_cross(float* v) {
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    auto p = __builtin_amdgcn_permlane32_swap(f2u(v[r]), f2u(v[r + 32]), false, false);
+    float a = u2f(p[0]), b = u2f(p[1]);
+    bfly(a, b);
+    v[r] = a;
+    v[r + 32] = b;
+  }
+}
+
+// value of the partner lane (L xor 32)
+__device__ __forceinline__ float pair_xchg(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return u2f((__lane_id() < 32) ? p[1] : p[0]);
+}
+
+template <typename T>
+__device__ __forceinline__ T pick(int which, const T (&a)[2]) { return which ? a[1] : a[0]; }
+
+__device__ __forceinline__ void set_status(Control* ctl, uint32_t bit) {
+  __hip_atomic_fetch_or(&ctl->status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ ReqDesc load_req(const CallDesc& c, int r) {
+  return (c.R == 1) ? c.one : c.reqs[r];
+}
+
+__device__ __forceinline__ int find_req_by_tile(const CallDesc& c, int which, int64_t tile) {
+  if (c.R == 1) return 0;
+  int lo = 0, hi = c.R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int64_t b = which ? c.reqs[mid].tile_begin[1] : c.reqs[mid].tile_begin[0];
+    if (b <= tile) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Paged: base (in 16-bit elements) of vectors [vstart, vstart + 32) of layer l
+// of request rq, which lie inside one page.  ok = false flags a bad block id.
+__device__ __forceinline__ int64_t page_run_base(const CallDesc& c, const ReqDesc& rq, int l, int64_t vstart,
+                                                 bool& ok) {
+  const int64_t vpp = (int64_t)c.page_tokens * c.heads;     // vectors per page
+  const int64_t page = vstart / vpp;
+  const int64_t voff = vstart - page * vpp;
+  const int32_t blk = c.block_table[(int64_t)rq.row * c.max_blocks + page];
+  ok = blk >= 0 && blk < c.num_blocks;
+  if (!ok) return 0;
+  return (((int64_t)l * c.num_blocks + blk) * c.page_tokens * c.heads + voff) * kHeadDim;
+}
+
+constexpr int RP = 68;               // LDS row pitch in dwords (272 bytes)
+constexpr int kWaveLds = 32 * RP;    // dwords of one wave's staging tile
+
+// Stage 32 head vectors (256 bytes each, consecutive vectors vstride bytes
+// apart) through LDS and return this lane's 64 values: lane half hf gets
+// channels [64 hf, 64 hf + 64) of vector (lane & 31), sign-flipped.
+template <bool BF16>
+__device__ __forceinline__ void stage_in(__amdgpu_buffer_rsrc_t src, uint32_t vstride, uint32_t* wl,
+                                         const uint32_t* sm, float* f) {
+  const int lane = __lane_id();
+  const uint32_t voff = (uint32_t)(lane >> 4) * vstride + (uint32_t)(lane & 15) * 16;
+  uint4 d[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) d[k] = bload16(src, voff, (uint32_t)k * 4 * vstride);
+  uint32_t* wrow = wl + (lane >> 4) * RP + (lane & 15) * 4;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint4 x = d[k];
+    x.x ^= sm[0]; x.y ^= sm[1]; x.z ^= sm[2]; x.w ^= sm[3];
+    *(uint4*)(wrow + k * 4 * RP) = x;
+  }
+  wave_sync();
+  const uint32_t* rrow = wl + (lane & 31) * RP + (lane >> 5) * 32;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 x = *(const uint4*)(rrow + 4 * j);
+    unpack16<BF16>(x.x, f[8 * j + 0], f[8 * j + 1]);
+    unpack16<BF16>(x.y, f[8 * j + 2], f[8 * j + 3]);
+    unpack16<BF16>(x.z, f[8 * j + 4], f[8 * j + 5]);
+    unpack16<BF16>(x.w, f[8 * j + 6], f[8 * j + 7]);
+  }
+  wave_sync();
+}
+
+// Convert the lane's 64 reconstructed values (layout after fwht_cross) to
+// 16-bit, transpose through LDS and store 32 vectors (vstride bytes apart),
+// restoring signs; stores past the resource end are dropped.
+template <bool BF16>
+__device__ __forceinline__ void stage_out(const float* f, uint32_t* wl, const uint32_t* sm,
+                                          __amdgpu_buffer_rsrc_t dst, uint32_t vstride) {
+  const int lane = __lane_id();
+  const int hf = lane >> 5;
+  uint32_t* wrow = wl + (lane & 31) * RP + hf * 16;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int r0 = 32 * half + 8 * s4;
+      uint4 x;
+      x.x = pack16<BF16>(f[r0 + 0], f[r0 + 1]);
+      x.y = pack16<BF16>(f[r0 + 2], f[r0 + 3]);
+      x.z = pack16<BF16>(f[r0 + 4], f[r0 + 5]);
+      x.w = pack16<BF16>(f[r0 + 6], f[r0 + 7]);
+      *(uint4*)(wrow + half * 32 + s4 * 4) = x;
+    }
+  }
+  wave_sync();
+  const uint32_t* rrow = wl + (lane >> 4) * RP + (lane & 15) * 4;
+  const uint32_t voff = (uint32_t)(lane >> 4) * vstride + (uint32_t)(lane & 15) * 16;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    uint4 x = *(const uint4*)(rrow + k * 4 * RP);
+    x.x ^= sm[0]; x.y ^= sm[1]; x.z ^= sm[2]; x.w ^= sm[3];
+    bstore16(x, dst, voff, (uint32_t)k * 4 * vstride);
+  }
+  wave_sync();
+}
+
+// ===================================================================
+// Encode, per-token groups.  One wavefront encodes 32 consecutive head
+// vectors (a tile); 4 wavefronts per block.  Dense calls treat all L*T*H
+// vectors as one run (codes and parameters follow the same order); paged
+// calls decompose tiles by request, layer and page.
+// ===================================================================
+template <int BITS, int G, bool BF16, bool PAGED>
+__global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[4 * kWaveLds];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t* wl = lds + wave * kWaveLds;
+  const TensorPol pol = which ? c.pol[1] : c.pol[0];
+  const float cc = pol.c;
+  const float levels = (float)((1 << BITS) - 1);
+  uint32_t sm[4];
+  slot_sign_masks(c.signs, lane & 15, sm);
+  const uint16_t* in = (const uint16_t*)(which ? c.in_kv[1] : c.in_kv[0]);
+  const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
+  const int v = lane & 31, hf = lane >> 5;
+  constexpr int LG = (G < 32) ? G : 32;          // group size held in one lane
+  constexpr int NLG = 64 / LG;
+  constexpr int CB = kHeadDim * BITS / 8;        // code bytes per vector
+  constexpr int NGV = kHeadDim / G;              // groups per vector
+  const int64_t nvec_dense = (int64_t)c.layers * c.one.T * c.heads;
+
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += stride) {
+    int64_t vg0;          // index of the tile's first vector within its request
+    int nv;
+    const uint16_t* src;
+    uint8_t* codes_base;
+    uint8_t* params_base;
+    if constexpr (!PAGED) {
+      vg0 = tile * 32;
+      nv = (int)std::min<int64_t>(32, nvec_dense - vg0);
+      src = in + vg0 * kHeadDim;
+      codes_base = c.codes + pick(which, c.one.codes_off);
+      params_base = c.stream + pick(which, c.one.params_off);
+    } else {
+      const int r = find_req_by_tile(c, which, tile);
+      const ReqDesc rq = load_req(c, r);
+      const int64_t vpl = (int64_t)rq.T * c.heads;               // vectors per layer
+      const int64_t tpl = (vpl + 31) >> 5;                        // tiles per layer
+      const int64_t tr = tile - pick(which, rq.tile_begin);
+      const int l = (int)(tr / tpl);
+      const int64_t vstart = (tr - (int64_t)l * tpl) * 32;
+      nv = (int)std::min<int64_t>(32, vpl - vstart);
+      vg0 = (int64_t)l * vpl + vstart;
+      bool ok;
+      const int64_t base = page_run_base(c, rq, l, vstart, ok);
+      if (!ok) { if (lane == 0) set_status(c.ctl, kStBadBlock); nv = 0; }
+      src = in + base;
+      codes_base = c.codes + pick(which, rq.codes_off);
+      params_base = c.params_ws + pick(which, rq.params_ws_off);
+    }
+    float f[64];
+    stage_in<BF16>(make_rsrc(src, (uint32_t)nv * 256u), 256u, wl, sm, f);
+    fwht64_inreg(f);
+    fwht_cross(f);
+    // register r: channel (r < 32 ? 32 hf + r : 64 + 32 hf + r - 32)
+
+    float mn[NLG], mx[NLG];
+#pragma unroll
+    for (int j = 0; j < NLG; ++j) {
+      float a = f[j * LG], b = f[j * LG];
+#pragma unroll
+      for (int i = 1; i < LG; ++i) { a = fminf(a, f[j * LG + i]); b = fmaxf(b, f[j * LG + i]); }
+      mn[j] = a; mx[j] = b;
+    }
+    if constexpr (G == 128) {
+      mn[0] = fminf(mn[0], mn[1]); mx[0] = fmaxf(mx[0], mx[1]);
+      mn[0] = fminf(mn[0], pair_xchg(mn[0])); mx[0] = fmaxf(mx[0], pair_xchg(mx[0]));
+      mn[1] = mn[0]; mx[1] = mx[0];
+    } else if constexpr (G == 64) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) { mn[j] = fminf(mn[j], pair_xchg(mn[j])); mx[j] = fmaxf(mx[j], pair_xchg(mx[j])); }
+    }
+    GroupQ gq[NLG];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < NLG; ++j) { gq[j] = group_params(mn[j], mx[j], cc, levels); bad |= gq[j].bad; }
+    if (bad && v < nv) set_status(c.ctl, kStRange);
+
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes_base + vg0 * CB, (uint32_t)nv * CB);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t w[BITS];
+      constexpr int PER = 32 / BITS;                              // codes per dword
+#pragma unroll
+      for (int dw = 0; dw < BITS; ++dw) {
+        uint32_t q[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int r2 = 32 * half + dw * PER + i;
+          q[i] = quant_code(f[r2], cc, gq[r2 / LG]);
+        }
+        w[dw] = pack_dword<BITS>(q);
+      }
+      const uint32_t off = (uint32_t)v * CB + (64 * half + 32 * hf) * BITS / 8;
+      if constexpr (BITS == 2) bstore8(make_uint2(w[0], w[1]), crs, off, 0);
+      else if constexpr (BITS == 4) bstore16(make_uint4(w[0], w[1], w[2], w[3]), crs, off, 0);
+      else {
+        bstore16(make_uint4(w[0], w[1], w[2], w[3]), crs, off, 0);
+        bstore16(make_uint4(w[4], w[5], w[6], w[7]), crs, off + 16, 0);
+      }
+    }
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(params_base + vg0 * NGV * 4, (uint32_t)nv * NGV * 4);
+    const uint32_t prow = (uint32_t)v * NGV * 4;
+    if constexpr (G <= 32) {
+#pragma unroll
+      for (int j = 0; j < NLG; ++j) {
+        const int ch0 = (j * LG < 32) ? 32 * hf + j * LG : 64 + 32 * hf + (j * LG - 32);
+        bstore4(gq[j].packed, prs, prow + (ch0 / G) * 4, 0);
+      }
+    } else if constexpr (G == 64) {
+      bstore4(hf ? gq[1].packed : gq[0].packed, prs, prow + hf * 4, 0);
+    } else {
+      if (hf == 0) bstore4(gq[0].packed, prs, prow, 0);
+    }
+  }
+}
+
+// ===================================================================
+// Decode, per-token groups: the mirror image of k_encode_token.
+// ===================================================================
+template <int BITS, int G, bool BF16, bool PAGED>
+__global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[4 * kWaveLds];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t* wl = lds + wave * kWaveLds;
+  const TensorPol pol = which ? c.pol[1] : c.pol[0];
+  const float cc = pol.c;
+  uint32_t sm[4];
+  slot_sign_masks(c.signs, lane & 15, sm);
+  uint16_t* out = (uint16_t*)(which ? c.out_kv[1] : c.out_kv[0]);
+  const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
+  const int v = lane & 31, hf = lane >> 5;
+  constexpr int CB = kHeadDim * BITS / 8;
+  constexpr int NGV = kHeadDim / G;
+  constexpr int LG = (G < 64) ? G : 64;                  // group size within the lane's 64 inputs
+  constexpr int NLG = 64 / LG;
+  const int64_t nvec_dense = (int64_t)c.layers * c.one.T * c.heads;
+
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += stride) {
+    int64_t vg0;
+    int nv, nvo;
+    const uint8_t* codes_base;
+    const uint8_t* params_base;
+    uint16_t* dst;
+    if constexpr (!PAGED) {
+      vg0 = tile * 32;
+      nv = (int)std::min<int64_t>(32, nvec_dense - vg0);
+      nvo = nv;
+      codes_base = c.codes + pick(which, c.one.codes_off);
+      params_base = c.stream + pick(which, c.one.params_off);
+      dst = out + vg0 * kHeadDim;
+    } else {
+      const int r = find_req_by_tile(c, which, tile);
+      const ReqDesc rq = load_req(c, r);
+      const int64_t vpl = (int64_t)rq.T * c.heads;
+      const int64_t tpl = (vpl + 31) >> 5;
+      const int64_t tr = tile - pick(which, rq.tile_begin);
+      const int l = (int)(tr / tpl);
+      const int64_t vstart = (tr - (int64_t)l * tpl) * 32;
+      nv = (int)std::min<int64_t>(32, vpl - vstart);
+      vg0 = (int64_t)l * vpl + vstart;
+      // this request's parameters must lie inside the input
+      const uint64_t off = c.req_offsets[r];
+      const bool pok =
+          off + (uint64_t)pick(which, rq.params_off) + (uint64_t)pick(which, rq.params_bytes) <= c.stream_bytes;
+      if (!pok) { if (lane == 0) set_status(c.ctl, kStCorrupt); nv = 0; }
+      codes_base = c.codes + pick(which, rq.codes_off);
+      params_base = c.stream + (pok ? off : 0) + pick(which, rq.params_off);
+      bool ok;
+      const int64_t base = page_run_base(c, rq, l, vstart, ok);
+      if (!ok && lane == 0) set_status(c.ctl, kStBadBlock);
+      nvo = ok ? (int)std::min<int64_t>(32, vpl - vstart) : 0;
+      dst = out + base;
+    }
+
+    // codes of channels [64 hf, 64 hf + 64) and their group parameters
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes_base + vg0 * CB, (uint32_t)nv * CB);
+    const uint32_t coff = (uint32_t)v * CB + 64 * hf * BITS / 8;
+    uint32_t w[4 * ((2 * BITS + 3) / 4)];
+#pragma unroll
+    for (int i = 0; i < 2 * BITS; i += 4) {
+      const uint4 x = bload16(crs, coff + 4 * i, 0);
+      w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
+    }
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(params_base + vg0 * NGV * 4, (uint32_t)nv * NGV * 4);
+    float sg[NLG], mu[NLG];
+#pragma unroll
+    for (int j = 0; j < NLG; ++j) {
+      const uint32_t pw = bload4(prs, (uint32_t)v * NGV * 4 + ((64 * hf + j * LG) / G) * 4, 0);
+      sg[j] = f_from_h16(pw & 0xffffu) * cc;
+      mu[j] = f_from_h16(pw >> 16) * cc;
+    }
+    float f[64];
+#pragma unroll
+    for (int r2 = 0; r2 < 64; ++r2) f[r2] = __builtin_fmaf(unpack_code<BITS>(w, r2), sg[r2 / LG], mu[r2 / LG]);
+
+    fwht64_inreg(f);
+    fwht_cross(f);
+    stage_out<BF16>(f, wl, sm, make_rsrc(dst, (uint32_t)nvo * 256u), 256u);
+  }
+}
+
+// ===================================================================
+// Per-channel groups (keys), dense calls.  A block of two wavefronts handles
+// one tile of 64 tokens x 1 head of one layer (one group of 64 or two groups
+// of 32).  LDS tile z[64 tokens][64 channels] (pitch 68), channels of rows
+// 32..63 XOR-swizzled by 32 so that the two token halves read distinct banks;
+// each wave's staging tile aliases its own 32 rows.
+// ===================================================================
+__device__ __forceinline__ int64_t pc_layer_bytes(int T, int G, int H, int bits) {
+  const int ng = (T + G - 1) / G;
+  const int glast = T - (ng - 1) * G;
+  return (int64_t)(ng - 1) * H * kHeadDim * (G * bits / 8) + (int64_t)H * kHeadDim * ((glast * bits + 7) / 8);
+}
+// byte offset of the (l, g, h) block and the column bytes of that group
+__device__ __forceinline__ int64_t pc_block(int T, int G, int H, int bits, int l, int g, int h, int& colb) {
+  const int ng = (T + G - 1) / G;
+  const int gg = (g == ng - 1) ? T - g * G : G;
+  colb = (gg * bits + 7) / 8;
+  return (int64_t)l * pc_layer_bytes(T, G, H, bits) + (int64_t)g * H * kHeadDim * (G * bits / 8) +
+         (int64_t)h * kHeadDim * colb;
+}
+
+template <int BITS, int G, bool BF16>
+__global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which) {
+  __shared__ __attribute__((aligned(16))) float zb[64 * RP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const TensorPol pol = which ? c.pol[1] : c.pol[0];
+  const float cc = pol.c;
+  const float levels = (float)((1 << BITS) - 1);
+  uint32_t sm[4];
+  slot_sign_masks(c.signs, lane & 15, sm);
+  const uint16_t* in = (const uint16_t*)(which ? c.in_kv[1] : c.in_kv[0]);
+  const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
+  uint32_t* stg = (uint32_t*)(zb + 32 * wave * RP);          // this wave's staging (aliases its z rows)
+  const int v = lane & 31, hf = lane >> 5;
+  const int H = c.heads;
+  const int T = c.one.T;
+  const int n64 = (T + 63) / 64;
+  const int ngr = (T + G - 1) / G;
+  uint8_t* codes_sec = c.codes + pick(which, c.one.codes_off);
+  uint32_t* prm = (uint32_t*)(c.stream + pick(which, c.one.params_off));
+  const uint32_t vstride = (uint32_t)H * 256u;
+
+  for (int tile = blockIdx.x; tile < (int)ntiles; tile += gridDim.x) {
+    const int h = tile % H;
+    const int g64 = (tile / H) % n64;
+    const int l = tile / (H * n64);
+    const int t0 = g64 * 64;
+    const int gg = min(64, T - t0);                    // valid tokens in this tile
+    const int tw0 = 32 * wave;                         // this wave's first token in the tile
+    const int nvw = max(0, min(32, gg - tw0));
+
+    __syncthreads();                                    // previous tile's readers are done
+    float f[64];
+    const uint16_t* src = in + (((int64_t)l * T + t0 + tw0) * H + h) * kHeadDim;
+    stage_in<BF16>(make_rsrc(src, nvw ? (uint32_t)(nvw - 1) * vstride + 256u : 0u), vstride, stg, sm, f);
+    fwht64_inreg(f);
+    fwht_cross(f);
+
+    // two passes of 64 channels: pass p holds channels [64p, 64p + 64)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      float* wrow = zb + (tw0 + v) * RP + ((32 * hf) ^ (32 * wave));   // rows >= 32 swizzled by 32
+#pragma unroll
+      for (int s4 = 0; s4 < 8; ++s4)
+        *(float4*)(wrow + 4 * s4) = make_float4(f[32 * p + 4 * s4], f[32 * p + 4 * s4 + 1],
+                                                f[32 * p + 4 * s4 + 2], f[32 * p + 4 * s4 + 3]);
+      __syncthreads();
+      // channel phase: this thread owns channel chl of token half th
+      const int chl = 32 * wave + (lane & 31);
+      const int th = lane >> 5;
+      const int ch = 64 * p + chl;
+      const int nvt = max(0, min(32, gg - 32 * th));   // valid tokens of this half
+      float zc[32];
+      const float* rcol = zb + 32 * th * RP + (chl ^ (32 * th));
+#pragma unroll
+      for (int i = 0; i < 32; ++i) zc[i] = rcol[i * RP];
+      float a = __builtin_inff(), b = -__builtin_inff();
+      if (nvt == 32) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) { a = fminf(a, zc[i]); b = fmaxf(b, zc[i]); }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) if (i < nvt) { a = fminf(a, zc[i]); b = fmaxf(b, zc[i]); }
+      }
+      int grp, ntok;
+      if constexpr (G == 64) {
+        a = fminf(a, pair_xchg(a));
+        b = fmaxf(b, pair_xchg(b));
+        grp = g64; ntok = gg;
+      } else {
+        grp = 2 * g64 + th; ntok = nvt;
+      }
+      const GroupQ gq = group_params(a, b, cc, levels);
+      if (gq.bad && nvt > 0) set_status(c.ctl, kStRange);
+      uint32_t w[BITS];
+      constexpr int PER = 32 / BITS;
+#pragma unroll
+      for (int dw = 0; dw < BITS; ++dw) {
+        uint32_t q[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int t2 = dw * PER + i;
+          q[i] = (t2 < nvt) ? quant_code(zc[t2], cc, gq) : 0x4b000000u;
+        }
+        w[dw] = pack_dword<BITS>(q);
+      }
+      if (ntok > 0 && nvt > 0) {
+        int colb;
+        const int64_t boff = pc_block(T, G, H, BITS, l, grp, h, colb);
+        uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
+        const int tok0 = (G == 64) ? 32 * th : 0;        // first token of this thread in its group
+        uint8_t* dst = col + tok0 * BITS / 8;
+        if (nvt == 32 && colb == G * BITS / 8) {
+          if constexpr (BITS == 2) *(uint2*)dst = make_uint2(w[0], w[1]);
+          else if constexpr (BITS == 4) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+          else {
+            *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+            *(uint4*)(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+          }
+        } else {
+          // partial group: this thread's codes start at byte tok0 * BITS / 8
+          const int nbytes = (nvt * BITS + 7) / 8;
+#pragma unroll
+          for (int i = 0; i < 4 * BITS; ++i)
+            if (i < nbytes) dst[i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+        }
+      }
+      const bool writer = (G == 64) ? (th == 0) : true;
+      if (writer && ntok > 0) prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch] = gq.packed;
+      __syncthreads();                                   // before the next pass overwrites zb
+    }
+  }
+}
+
+template <int BITS, int G, bool BF16>
+__global__ __launch_bounds__(128, 4) void k_decode_channel(CallDesc c, int which) {
+  __shared__ __attribute__((aligned(16))) float zb[64 * RP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const TensorPol pol = which ? c.pol[1] : c.pol[0];
+  const float cc = pol.c;
+  uint32_t sm[4];
+  slot_sign_masks(c.signs, lane & 15, sm);
+  uint16_t* out = (uint16_t*)(which ? c.out_kv[1] : c.out_kv[0]);
+  const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
+  uint32_t* stg = (uint32_t*)(zb + 32 * wave * RP);
+  const int v = lane & 31, hf = lane >> 5;
+  const int H = c.heads;
+  const int T = c.one.T;
+  const int n64 = (T + 63) / 64;
+  const int ngr = (T + G - 1) / G;
+  const uint8_t* codes_sec = c.codes + pick(which, c.one.codes_off);
+  const uint32_t* prm = (const uint32_t*)(c.stream + pick(which, c.one.params_off));
+  const uint32_t vstride = (uint32_t)H * 256u;
+
+  for (int tile = blockIdx.x; tile < (int)ntiles; tile += gridDim.x) {
+    const int h = tile % H;
+    const int g64 = (tile / H) % n64;
+    const int l = tile / (H * n64);
+    const int t0 = g64 * 64;
+    const int gg = min(64, T - t0);
+    const int tw0 = 32 * wave;
+    const int nvw = max(0, min(32, gg - tw0));
+
+    float f[64];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      __syncthreads();
+      const int chl = 32 * wave + (lane & 31);
+      const int th = lane >> 5;
+      const int ch = 64 * p + chl;
+      const int nvt = max(0, min(32, gg - 32 * th));
+      const int grp = (G == 64) ? g64 : 2 * g64 + th;
+      uint32_t w[BITS];
+#pragma unroll
+      for (int i = 0; i < BITS; ++i) w[i] = 0;
+      float sg = 0.0f, mu = 0.0f;
+      if (nvt > 0) {
+        int colb;
+        const int64_t boff = pc_block(T, G, H, BITS, l, grp, h, colb);
+        const uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
+        const int tok0 = (G == 64) ? 32 * th : 0;
+        const uint8_t* s = col + tok0 * BITS / 8;
+        if (nvt == 32 && colb == G * BITS / 8) {
+          if constexpr (BITS == 2) { const uint2 x = *(const uint2*)s; w[0] = x.x; w[1] = x.y; }
+          else {
+#pragma unroll
+            for (int i = 0; i < BITS; i += 4) {
+              const uint4 x = *(const uint4*)(s + 4 * i);
+              w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
+            }
+          }
+        } else {
+          const int nbytes = (nvt * BITS + 7) / 8;
+#pragma unroll
+          for (int i = 0; i < 4 * BITS; ++i)
+            if (i < nbytes) w[i >> 2] |= (uint32_t)s[i] << (8 * (i & 3));
+        }
+        const uint32_t pw = prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch];
+        sg = f_from_h16(pw & 0xffffu) * cc;
+        mu = f_from_h16(pw >> 16) * cc;
+      }
+      // rows of tokens past the end hold finite filler that is never stored
+      float* wcol = zb + 32 * th * RP + (chl ^ (32 * th));
+#pragma unroll
+      for (int i = 0; i < 32; ++i) wcol[i * RP] = __builtin_fmaf(unpack_code<BITS>(w, i), sg, mu);
+      __syncthreads();
+      if (hf == p) {
+        const float* rrow = zb + (tw0 + v) * RP;
+        const int sw = 32 * wave;                         // rows >= 32 are swizzled by 32
+#pragma unroll
+        for (int s4 = 0; s4 < 16; ++s4) {
+          const float4 x = *(const float4*)(rrow + ((4 * s4) ^ sw));
+          f[4 * s4] = x.x; f[4 * s4 + 1] = x.y; f[4 * s4 + 2] = x.z; f[4 * s4 + 3] = x.w;
+        }
+      }
+    }
+    __syncthreads();                                      // all z reads done before staging reuse
+    fwht64_inreg(f);
+    fwht_cross(f);
+    uint16_t* dst = out + (((int64_t)l * T + t0 + tw0) * H + h) * kHeadDim;
+    stage_out<BF16>(f, stg, sm, make_rsrc(dst, nvw ? (uint32_t)(nvw - 1) * vstride + 256u : 0u), vstride);
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+static int grid_for(int64_t blocks_needed, int cap) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>(blocks_needed, (int64_t)cap));
+}
+
+#define KVC_TOKEN_CASES_P(KERNEL, BITS, BF, PG)                                    \
+  switch (pol.group) {                                                             \
+    case 16: KERNEL<BITS, 16, BF, PG><<<grid, block, 0, s>>>(c, which); break;    \
+    case 32: KERNEL<BITS, 32, BF, PG><<<grid, block, 0, s>>>(c, which); break;    \
+    case 64: KERNEL<BITS, 64, BF, PG><<<grid, block, 0, s>>>(c, which); break;    \
+    default: KERNEL<BITS, 128, BF, PG><<<grid, block, 0, s>>>(c, which); break;   \
+  }
+#define KVC_TOKEN_CASES(KERNEL, BITS, BF)                                          \
+  if (c.page_tokens) { KVC_TOKEN_CASES_P(KERNEL, BITS, BF, true) }                 \
+  else { KVC_TOKEN_CASES_P(KERNEL, BITS, BF, false) }
+#define KVC_CHANNEL_CASES(KERNEL, BITS, BF)                                        \
+  switch (pol.group) {                                                             \
+    case 32: KERNEL<BITS, 32, BF><<<grid, block, 0, s>>>(c, which); break;        \
+    default: KERNEL<BITS, 64, BF><<<grid, block, 0, s>>>(c, which); break;        \
+  }
+#define KVC_BITS_CASES(CASES, KERNEL, BF)                                          \
+  switch (pol.bits) {                                                              \
+    case 2: CASES(KERNEL, 2, BF) break;                                            \
+    case 4: CASES(KERNEL, 4, BF) break;                                            \
+    default: CASES(KERNEL, 8, BF) break;                                           \
+  }
+
+hipError_t launch_encode_fused(const CallDesc& c, int which, hipStream_t s) {
+  const TensorPol& pol = which ? c.pol[1] : c.pol[0];
+  const int64_t tiles = which ? c.tiles[1] : c.tiles[0];
+  if (tiles == 0) return hipSuccess;
+  if (pol.axis == 0) {
+    const dim3 block(256);
+    const int grid = grid_for((tiles + 3) / 4, 256 * 16);
+    if (c.dtype == 1) { KVC_BITS_CASES(KVC_TOKEN_CASES, k_encode_token, true) }
+    else { KVC_BITS_CASES(KVC_TOKEN_CASES, k_encode_token, false) }
+  } else {
+    const dim3 block(128);
+    const int grid = grid_for(tiles, 256 * 32);
+    if (c.dtype == 1) { KVC_BITS_CASES(KVC_CHANNEL_CASES, k_encode_channel, true) }
+    else { KVC_BITS_CASES(KVC_CHANNEL_CASES, k_encode_channel, false) }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fused(const CallDesc& c, int which, hipStream_t s) {
+  const TensorPol& pol = which ? c.pol[1] : c.pol[0];
+  const int64_t tiles = which ? c.tiles[1] : c.tiles[0];
+  if (tiles == 0) return hipSuccess;
+  if (pol.axis == 0) {
+    const dim3 block(256);
+    const int grid = grid_for((tiles + 3) / 4, 256 * 16);
+    if (c.dtype == 1) { KVC_BITS_CASES(KVC_TOKEN_CASES, k_decode_token, true) }
+    else { KVC_BITS_CASES(KVC_TOKEN_CASES, k_decode_token, false) }
+  } else {
+    const dim3 block(128);
+    const int grid = grid_for(tiles, 256 * 32);
+    if (c.dtype == 1) { KVC_BITS_CASES(KVC_CHANNEL_CASES, k_decode_channel, true) }
+    else { KVC_BITS_CASES(KVC_CHANNEL_CASES, k_decode_channel, false) }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,109 @@
+// Internal declarations shared by libkvc's translation units (host API and
+// kernels).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kHeadDim = 128;          // head_dim the kernels are written for
+constexpr uint32_t kMagic = 0x3143564Bu;
+constexpr int kHeaderBytes = 64;
+constexpr uint32_t kRawFlag = 0x80000000u;
+
+// Status word bits recorded by kernels in the workspace control block.
+enum : uint32_t {
+  kStCorrupt = 1u << 0,
+  kStMismatch = 1u << 1,
+  kStRange = 1u << 2,
+  kStBadBlock = 1u << 3,
+};
+
+// Workspace control block (first 256 bytes of every workspace).
+struct Control {
+  uint32_t status;
+  uint32_t pad0;
+  uint64_t total;        // dense encode: stream bytes
+  uint64_t pad[30];
+};
+static_assert(sizeof(Control) == 256, "control block is 256 bytes");
+
+// Quantization policy of one tensor as the kernels see it.
+struct TensorPol {
+  int bits;
+  int axis;              // 0 per-token, 1 per-channel
+  int group;
+  int hadamard;
+  float c;               // 1/sqrt(head_dim) rounded to binary32 (1 if no transform)
+};
+
+// One request of a call; a dense call is a single request.
+struct ReqDesc {
+  int32_t T;                 // tokens
+  int32_t row;               // block-table row (paged)
+  int32_t nchunks[2];        // code chunks of K and V
+  int64_t chunk_begin;       // global index of the first chunk (K chunks, then V chunks)
+  int64_t tile_begin[2];     // first fused-kernel tile of K and of V
+  int64_t codes_off[2];      // code sections in the workspace codes area
+  int64_t codes_bytes[2];
+  int64_t params_ws_off[2];  // parameter staging in the workspace (paged encode), -1 if direct
+  int64_t params_off[2];     // parameter sections inside this request's stream
+  int64_t params_bytes[2];
+  int64_t payload_off;       // payload offset inside this request's stream
+  int64_t max_stream;        // stream bytes with every chunk raw
+  int64_t piece_begin;       // first parameter-copy piece (paged encode)
+};
+
+// Where the requests live and where their data goes.
+struct CallDesc {
+  int R;                     // requests
+  const ReqDesc* reqs;       // device array [R] (R > 1)
+  ReqDesc one;               // the request when R == 1
+  int layers, heads;
+  int dtype;                 // 0 fp16, 1 bf16
+  TensorPol pol[2];
+  uint32_t signs[4];         // bit i set: sign of channel i is -1
+  uint8_t stages[4];
+  uint32_t chunk_bytes;
+  uint64_t seed;
+  // paged addressing (page_tokens == 0: dense)
+  int page_tokens;
+  int64_t num_blocks;
+  const int32_t* block_table;
+  int max_blocks;
+  // buffers
+  const void* in_kv[2];      // encode: K, V inputs (dense tensors or pools)
+  void* out_kv[2];           // decode: K, V outputs (dense tensors or pools)
+  uint8_t* codes;            // workspace codes area
+  uint8_t* params_ws;        // workspace parameter staging area (paged encode)
+  uint8_t* stream;           // dense: the stream; paged: base of all streams
+  const uint64_t* req_offsets;  // paged: stream offsets (device)
+  uint64_t* req_offsets_out;    // paged encode: written by the scan
+  uint64_t stream_bytes;     // decode: bytes available in the input
+  uint32_t* chunk_sizes;     // [total chunks] stored sizes | raw flag
+  uint64_t* chunk_offs;      // [total chunks + 1] exclusive scan of align16(stored)
+  Control* ctl;
+  int64_t total_chunks;
+  int64_t total_pieces;      // paged encode: parameter copy pieces
+  int64_t tiles[2];          // fused-kernel tiles of K and V over all requests
+};
+
+// Kernel launch wrappers (defined in the .hip files).  Each returns the HIP
+// error of its launch.
+hipError_t launch_reset(const CallDesc& c, hipStream_t s);
+hipError_t launch_encode_fused(const CallDesc& c, int which, hipStream_t s);
+hipError_t launch_decode_fused(const CallDesc& c, int which, hipStream_t s);
+hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s);
+hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s);
+hipError_t launch_compact(const CallDesc& c, hipStream_t s);
+hipError_t launch_validate(const CallDesc& c, hipStream_t s);
+hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s);
+
+// Per-kernel timing hooks (kvc_api.cpp).
+void prof_begin(int kind, hipStream_t s);
+void prof_end(int kind, hipStream_t s);
+
+}  // namespace kvc

@@ -1,0 +1,684 @@
+// Chunked lossless backend over the packed codes, its scan and compaction,
+// stream headers and validation, for gfx950.
+//
+// FastKVComp ("Beyond Compression Ratio: High-Throughput KV Compression for
+// Disaggregated LLM Serving") Sec. 4.2 composes reordering of byte tuples,
+// shuffling of bits and elimination of zero words into one pipeline
+// (TUPL8_1 -> BIT_8 -> RZE_2).  Stage definitions used here:
+//   TUPLk_1  m = n/k tuples: out[j*m + i] = in[i*k + j]; tail copied;
+//   DIFFw    w-byte words: out[i] = in[i] - in[i-1] mod 2^(8w); tail copied;
+//   BITw     8w words of w bytes form a square bit matrix that is transposed;
+//            incomplete trailing group copied;
+//   RZEw     bitmap (bit i set iff word i != 0, LSB first), the non-zero
+//            words, then the tail bytes.
+// A chunk whose result is not smaller than its input is stored raw.
+//
+// Encode runs in two kernels.  The first computes every chunk's exact
+// compressed size without materializing the transform: for the two standard
+// pipelines a 2-byte RZE word of the output is zero exactly when a fixed set
+// of input bits is zero, so the count of non-zero output words is a popcount
+// of OR-reductions of the input words.  Chunks that stay raw are done; the
+// rest (and chunks of other pipelines or partial chunks) go on a worklist
+// for the second kernel, which runs the stages in LDS (two 64 KiB buffers)
+// and writes the result in place into the chunk's slot.  A single-block scan
+// turns stored sizes into 16-byte aligned offsets; the compaction kernel
+// copies chunks and parameter pieces to their final places and writes the
+// headers and the chunk tables.
+#include <algorithm>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+__device__ __forceinline__ void set_status2(Control* ctl, uint32_t bit) {
+  __hip_atomic_fetch_or(&ctl->status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ ReqDesc req_at(const CallDesc& c, int r) { return (c.R == 1) ? c.one : c.reqs[r]; }
+
+__device__ __forceinline__ int find_req_by_chunk(const CallDesc& c, int64_t chunk) {
+  if (c.R == 1) return 0;
+  int lo = 0, hi = c.R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (c.reqs[mid].chunk_begin <= chunk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+struct ChunkLoc {
+  int r, w;
+  int64_t index;    // within its section
+  int64_t n;        // raw bytes
+  int64_t src;      // byte offset in the codes area
+};
+
+__device__ __forceinline__ ChunkLoc locate_chunk(const CallDesc& c, const ReqDesc& rq, int r, int64_t chunk) {
+  ChunkLoc L;
+  L.r = r;
+  const int64_t k = chunk - rq.chunk_begin;
+  L.w = (k < rq.nchunks[0]) ? 0 : 1;
+  L.index = (L.w == 0) ? k : k - rq.nchunks[0];
+  const int64_t rem = rq.codes_bytes[L.w] - L.index * (int64_t)c.chunk_bytes;
+  L.n = rem < (int64_t)c.chunk_bytes ? rem : (int64_t)c.chunk_bytes;
+  L.src = rq.codes_off[L.w] + L.index * (int64_t)c.chunk_bytes;
+  return L;
+}
+
+__device__ __forceinline__ int64_t align16(int64_t x) { return (x + 15) & ~(int64_t)15; }
+
+__device__ __forceinline__ uint64_t stream_base(const CallDesc& c, int r, bool encode) {
+  if (c.R == 1 && c.req_offsets == nullptr && c.req_offsets_out == nullptr) return 0;
+  return encode ? c.req_offsets_out[r] : c.req_offsets[r];
+}
+
+// ------------------------------------------------------------------ reset
+
+__global__ void k_reset(Control* ctl) {
+  if (threadIdx.x == 0) {
+    ctl->status = 0;
+    ctl->pad0 = 0;     // worklist count
+    ctl->total = 0;
+  }
+}
+
+hipError_t launch_reset(const CallDesc& c, hipStream_t s) {
+  k_reset<<<1, 64, 0, s>>>(c.ctl);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ block helpers
+
+template <typename T>
+__device__ __forceinline__ T block_exclusive_scan(T x, T* sh, T& total) {
+  // sh: blockDim.x entries
+  const int t = threadIdx.x, nt = blockDim.x;
+  sh[t] = x;
+  __syncthreads();
+  for (int off = 1; off < nt; off <<= 1) {
+    T y = (t >= off) ? sh[t - off] : (T)0;
+    __syncthreads();
+    sh[t] += y;
+    __syncthreads();
+  }
+  total = sh[nt - 1];
+  const T incl = sh[t];
+  __syncthreads();
+  return incl - x;
+}
+
+__device__ __forceinline__ uint64_t ld_word(const uint8_t* p, int w) {
+  uint64_t v = 0;
+  for (int b = 0; b < w; ++b) v |= (uint64_t)p[b] << (8 * b);
+  return v;
+}
+__device__ __forceinline__ void st_word(uint8_t* p, int w, uint64_t v) {
+  for (int b = 0; b < w; ++b) p[b] = (uint8_t)(v >> (8 * b));
+}
+
+__device__ __forceinline__ int stage_kind(int s) {
+  if (s >= KVC_TUPL2_1 && s <= KVC_TUPL8_1) return 0;
+  if (s >= KVC_DIFF1 && s <= KVC_DIFF8) return 1;
+  if (s >= KVC_BIT_1 && s <= KVC_BIT_8) return 2;
+  return 3;
+}
+__device__ __forceinline__ int stage_width(int s) {
+  const int k = stage_kind(s);
+  if (k == 0) return 2 << (s - KVC_TUPL2_1);
+  if (k == 1) return 1 << (s - KVC_DIFF1);
+  if (k == 2) return 1 << (s - KVC_BIT_1);
+  return 1 << (s - KVC_RZE_1);
+}
+
+// One forward stage, block-cooperative, LDS in -> LDS out.  Returns the output size.
+__device__ int stage_forward(int stage, const uint8_t* in, uint8_t* out, int n, uint32_t* sh32) {
+  const int kind = stage_kind(stage), w = stage_width(stage);
+  const int t = threadIdx.x, nt = blockDim.x;
+  if (kind == 0) {
+    const int m = n / w;
+    for (int p = t; p < n; p += nt) {
+      if (p < m * w) { const int j = p / m, i = p - j * m; out[p] = in[i * w + j]; }
+      else out[p] = in[p];
+    }
+    __syncthreads();
+    return n;
+  }
+  if (kind == 1) {
+    const int nw = n / w;
+    const uint64_t mask = (w == 8) ? ~0ull : ((1ull << (8 * w)) - 1);
+    for (int i = t; i < nw; i += nt) {
+      const uint64_t cur = ld_word(in + i * w, w);
+      const uint64_t prev = i ? ld_word(in + (i - 1) * w, w) : 0ull;
+      st_word(out + i * w, w, (cur - prev) & mask);
+    }
+    for (int p = nw * w + t; p < n; p += nt) out[p] = in[p];
+    __syncthreads();
+    return n;
+  }
+  if (kind == 2) {
+    const int B = 8 * w, gb = w * B, ng = n / gb;
+    for (int o = t; o < ng * B; o += nt) {
+      const int g = o / B, j = o - g * B;
+      const uint8_t* src = in + g * gb;
+      uint64_t acc = 0;
+      for (int i = 0; i < B; ++i) acc |= ((ld_word(src + i * w, w) >> j) & 1ull) << i;
+      st_word(out + g * gb + j * w, w, acc);
+    }
+    for (int p = ng * gb + t; p < n; p += nt) out[p] = in[p];
+    __syncthreads();
+    return n;
+  }
+  // RZE: each thread owns a contiguous range of words
+  const int nw = n / w, bm = (nw + 7) / 8, tail = n - nw * w;
+  const int per = (nw + nt - 1) / nt;
+  const int i0 = min(nw, t * per), i1 = min(nw, i0 + per);
+  uint32_t cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += ld_word(in + i * w, w) != 0ull;
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan<uint32_t>(cnt, sh32, total);
+  // zero elimination is the last stage: a result that does not shrink the
+  // chunk means the chunk is stored raw, so nothing is written (and the
+  // output buffer cannot overflow)
+  if ((int64_t)bm + (int64_t)total * w + tail >= n) return n;
+  for (int b = t; b < bm; b += nt) {
+    uint32_t byte = 0;
+    for (int k = 0; k < 8; ++k) {
+      const int i = 8 * b + k;
+      if (i < nw && ld_word(in + i * w, w) != 0ull) byte |= 1u << k;
+    }
+    out[b] = (uint8_t)byte;
+  }
+  int pos = bm + (int)before * w;
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t v = ld_word(in + i * w, w);
+    if (v) { st_word(out + pos, w, v); pos += w; }
+  }
+  const int tpos = bm + (int)total * w;
+  for (int p = t; p < tail; p += nt) out[tpos + p] = in[nw * w + p];
+  __syncthreads();
+  return tpos + tail;
+}
+
+// Inverse of one stage; n is the decoded length.  Returns false on a corrupt input.
+__device__ bool stage_inverse(int stage, const uint8_t* in, int in_n, uint8_t* out, int n,
+                              uint32_t* sh32, uint64_t* sh64) {
+  const int kind = stage_kind(stage), w = stage_width(stage);
+  const int t = threadIdx.x, nt = blockDim.x;
+  if (kind != 3 && in_n != n) return false;
+  if (kind == 0) {
+    const int m = n / w;
+    for (int p = t; p < n; p += nt) {
+      if (p < m * w) { const int i = p / w, j = p - i * w; out[p] = in[j * m + i]; }
+      else out[p] = in[p];
+    }
+    __syncthreads();
+    return true;
+  }
+  if (kind == 1) {
+    const int nw = n / w;
+    const uint64_t mask = (w == 8) ? ~0ull : ((1ull << (8 * w)) - 1);
+    const int per = (nw + nt - 1) / nt;
+    const int i0 = min(nw, t * per), i1 = min(nw, i0 + per);
+    uint64_t sum = 0;
+    for (int i = i0; i < i1; ++i) sum += ld_word(in + i * w, w);
+    uint64_t total;
+    uint64_t acc = block_exclusive_scan<uint64_t>(sum, sh64, total);
+    for (int i = i0; i < i1; ++i) {
+      acc += ld_word(in + i * w, w);
+      st_word(out + i * w, w, acc & mask);
+    }
+    for (int p = nw * w + t; p < n; p += nt) out[p] = in[p];
+    __syncthreads();
+    return true;
+  }
+  if (kind == 2) {
+    stage_forward(stage, in, out, n, sh32);
+    return true;
+  }
+  const int nw = n / w, bm = (nw + 7) / 8, tail = n - nw * w;
+  if (in_n < bm + tail) return false;
+  const int per = (nw + nt - 1) / nt;
+  const int i0 = min(nw, t * per), i1 = min(nw, i0 + per);
+  uint32_t cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += (in[i >> 3] >> (i & 7)) & 1u;
+  uint32_t total;
+  const uint32_t before = block_exclusive_scan<uint32_t>(cnt, sh32, total);
+  // stray bitmap bits past the last word, or a size mismatch, mean corruption
+  bool okk = (int)(bm + total * w + tail) == in_n;
+  if (bm * 8 > nw) {
+    const uint32_t last = in[bm - 1];
+    if (last >> (nw - (bm - 1) * 8)) okk = false;
+  }
+  if (!okk) return false;
+  int pos = bm + (int)before * w;
+  uint32_t zero_flag = 0;
+  for (int i = i0; i < i1; ++i) {
+    if ((in[i >> 3] >> (i & 7)) & 1u) {
+      const uint64_t v = ld_word(in + pos, w);
+      zero_flag |= (v == 0ull);
+      st_word(out + i * w, w, v);
+      pos += w;
+    } else {
+      st_word(out + i * w, w, 0ull);
+    }
+  }
+  for (int p = t; p < tail; p += nt) out[nw * w + p] = in[bm + total * w + p];
+  const int any_zero = __syncthreads_or((int)zero_flag);
+  return any_zero == 0;
+}
+
+// ------------------------------------------------------------------ encode: sizes
+
+// Non-zero 2-byte words after TUPL8_1 -> BIT_8 -> RZE_2, for a full chunk of
+// n bytes (n a multiple of 4096).  Word (stream j, block gi, byte kk, bit b,
+// quarter u) is zero iff bit b of byte j of the input words
+// gi*512 + i*8 + kk, i in [16u, 16u+16), are all zero.
+__device__ uint32_t nnz_tupl8_bit8_rze2(const uint64_t* src, int n, uint32_t* sh32) {
+  const int nr = (n / 4096) * 32;                 // (gi, u, kk) triples
+  uint32_t cnt = 0;
+  for (int e = threadIdx.x; e < nr; e += blockDim.x) {
+    const int kk = e & 7, u = (e >> 3) & 3, gi = e >> 5;
+    uint64_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc |= src[gi * 512 + (16 * u + i) * 8 + kk];
+    cnt += __popcll(acc);
+  }
+  uint32_t total;
+  block_exclusive_scan<uint32_t>(cnt, sh32, total);
+  return total;
+}
+
+// Non-zero 2-byte words after TUPL8_1 -> RZE_2: word (stream j, pair p) is
+// byte j of input words 2p and 2p+1.
+__device__ uint32_t nnz_tupl8_rze2(const uint64_t* src, int n, uint32_t* sh32) {
+  const int np = n / 16;
+  uint32_t cnt = 0;
+  for (int p = threadIdx.x; p < np; p += blockDim.x) {
+    const uint64_t x = src[2 * p] | src[2 * p + 1];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cnt += ((x >> (8 * j)) & 0xffull) != 0ull;
+  }
+  uint32_t total;
+  block_exclusive_scan<uint32_t>(cnt, sh32, total);
+  return total;
+}
+
+__global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, uint32_t* worklist) {
+  __shared__ uint32_t sh32[256];
+  const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
+  const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
+  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const int n = (int)L.n;
+    bool generic = true;
+    if ((p1 || p2) && n == (int)c.chunk_bytes && (n % 4096) == 0) {
+      const uint64_t* src = (const uint64_t*)(c.codes + L.src);
+      const uint32_t nnz = p1 ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
+      const int64_t size = n / 16 + 2 * (int64_t)nnz;
+      if (size >= n) {
+        if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
+        generic = false;
+      }
+    } else if (c.stages[0] == 0) {
+      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
+      generic = false;
+    }
+    if (generic && threadIdx.x == 0) {
+      const uint32_t slot = __hip_atomic_fetch_add(&c.ctl->pad0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      worklist[slot] = (uint32_t)ch;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uint32_t* worklist) {
+  __shared__ __attribute__((aligned(16))) uint8_t bufA[65536];
+  __shared__ __attribute__((aligned(16))) uint8_t bufB[65536];
+  __shared__ uint32_t sh32[256];
+  const uint32_t count = c.ctl->pad0;
+  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+    const int64_t ch = worklist[item];
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const int n = (int)L.n;
+    uint8_t* slot = c.codes + L.src;
+    for (int p = threadIdx.x; p < n; p += blockDim.x) bufA[p] = slot[p];
+    __syncthreads();
+    uint8_t* cur = bufA;
+    uint8_t* alt = bufB;
+    int size = n;
+    for (int s = 0; s < 4 && c.stages[s]; ++s) {
+      size = stage_forward(c.stages[s], cur, alt, size, sh32);
+      uint8_t* tmp = cur; cur = alt; alt = tmp;
+    }
+    if (size >= n) {
+      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
+    } else {
+      for (int p = threadIdx.x; p < size; p += blockDim.x) slot[p] = cur[p];
+      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
+  if (c.total_chunks == 0) return hipSuccess;
+  uint32_t* worklist = (uint32_t*)(c.chunk_offs + c.total_chunks + 1);
+  const int grid = (int)std::min<int64_t>(c.total_chunks, 256 * 8);
+  k_ll_sizes<<<grid, 256, 0, s>>>(c, worklist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_ll_encode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ scan
+
+// One block: exclusive scan of align16(stored size) over all chunks.  For
+// decode the stored sizes come from the streams' chunk tables (bounds
+// checked) and are copied to chunk_sizes.  For a paged encode it also scans
+// the per-request stream sizes into req_offsets_out.
+__global__ __launch_bounds__(1024) void k_scan(CallDesc c, int from_table) {
+  __shared__ uint64_t sh[1024];
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int64_t N = c.total_chunks;
+  const int64_t per = (N + nt - 1) / nt;
+  const int64_t i0 = min(N, (int64_t)t * per), i1 = min(N, i0 + per);
+  if (from_table) {
+    for (int64_t i = i0; i < i1; ++i) {
+      const int r = find_req_by_chunk(c, i);
+      const ReqDesc rq = req_at(c, r);
+      const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+      const uint64_t pos = base + 64 + 4 * (uint64_t)(i - rq.chunk_begin);
+      uint32_t e = 0;
+      if (pos + 4 <= c.stream_bytes && pos + 4 <= base + (uint64_t)rq.payload_off) e = *(const uint32_t*)(c.stream + pos);
+      else set_status2(c.ctl, kStCorrupt);
+      c.chunk_sizes[i] = e;
+    }
+    __syncthreads();
+  }
+  uint64_t sum = 0;
+  for (int64_t i = i0; i < i1; ++i) sum += (uint64_t)align16(c.chunk_sizes[i] & 0x7fffffffu);
+  uint64_t total;
+  uint64_t acc = block_exclusive_scan<uint64_t>(sum, sh, total);
+  for (int64_t i = i0; i < i1; ++i) {
+    c.chunk_offs[i] = acc;
+    acc += (uint64_t)align16(c.chunk_sizes[i] & 0x7fffffffu);
+  }
+  if (t == 0) c.chunk_offs[N] = total;
+  __syncthreads();
+  if (from_table) return;
+  if (c.req_offsets_out == nullptr) {
+    if (t == 0) c.ctl->total = (uint64_t)c.one.payload_off + total;
+    return;
+  }
+  // per-request stream sizes -> offsets
+  const int R = c.R;
+  const int rper = (R + nt - 1) / nt;
+  const int r0 = min(R, t * rper), r1 = min(R, r0 + rper);
+  __threadfence_block();
+  uint64_t rs = 0;
+  for (int r = r0; r < r1; ++r) {
+    const ReqDesc rq = req_at(c, r);
+    const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
+    rs += (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
+  }
+  uint64_t rtotal;
+  uint64_t racc = block_exclusive_scan<uint64_t>(rs, sh, rtotal);
+  for (int r = r0; r < r1; ++r) {
+    const ReqDesc rq = req_at(c, r);
+    const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
+    c.req_offsets_out[r] = racc;
+    racc += (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
+  }
+  if (t == 0) { c.req_offsets_out[R] = rtotal; c.ctl->total = rtotal; }
+}
+
+hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s) {
+  k_scan<<<1, 1024, 0, s>>>(c, from_table ? 1 : 0);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ compaction
+
+__device__ void write_header(const CallDesc& c, const ReqDesc& rq, uint8_t* o, uint64_t total) {
+  // threads 0..63 of the block each write one byte
+  const int t = threadIdx.x;
+  if (t >= 64) return;
+  uint8_t b = 0;
+  auto byte_of = [](uint64_t v, int k) { return (uint8_t)(v >> (8 * k)); };
+  if (t < 4) b = byte_of(kMagic, t);
+  else if (t < 6) b = byte_of(1, t - 4);
+  else if (t == 6) b = (uint8_t)c.dtype;
+  else if (t == 7) b = 0;
+  else if (t < 12) b = byte_of((uint32_t)c.layers, t - 8);
+  else if (t < 16) b = byte_of((uint32_t)rq.T, t - 12);
+  else if (t < 20) b = byte_of((uint32_t)c.heads, t - 16);
+  else if (t < 24) b = byte_of((uint32_t)kHeadDim, t - 20);
+  else if (t < 40) {
+    const int w = (t - 24) / 8, k = (t - 24) % 8;
+    const TensorPol& p = c.pol[w];
+    if (k == 0) b = (uint8_t)p.bits;
+    else if (k == 1) b = (uint8_t)p.axis;
+    else if (k == 2) b = (uint8_t)p.hadamard;
+    else if (k == 4) b = byte_of((uint32_t)p.group, 0);
+    else if (k == 5) b = byte_of((uint32_t)p.group, 1);
+  } else if (t < 48) b = byte_of(c.seed, t - 40);
+  else if (t < 52) b = c.stages[t - 48];
+  else if (t < 56) b = byte_of(c.chunk_bytes, t - 52);
+  else b = byte_of(total, t - 56);
+  o[t] = b;
+}
+
+// zero the alignment gaps between table, parameter sections and payload
+__device__ void zero_gaps(const ReqDesc& rq, uint8_t* o) {
+  const int64_t tend = 64 + 4 * (int64_t)(rq.nchunks[0] + rq.nchunks[1]);
+  const int64_t g0[3] = {tend, rq.params_off[0] + rq.params_bytes[0], rq.params_off[1] + rq.params_bytes[1]};
+  const int64_t g1[3] = {rq.params_off[0], rq.params_off[1], rq.payload_off};
+  for (int k = 0; k < 3; ++k)
+    for (int64_t p = g0[k] + threadIdx.x; p < g1[k]; p += blockDim.x) o[p] = 0;
+}
+
+__device__ __forceinline__ int find_req_by_piece(const CallDesc& c, int64_t piece) {
+  int lo = 0, hi = c.R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (c.reqs[mid].piece_begin <= piece) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void k_compact(CallDesc c) {
+  const int64_t items = c.total_chunks + c.R + c.total_pieces;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    if (it < c.total_chunks) {
+      const int64_t ch = it;
+      const int r = find_req_by_chunk(c, ch);
+      const ReqDesc rq = req_at(c, r);
+      const ChunkLoc L = locate_chunk(c, rq, r, ch);
+      const uint32_t e = c.chunk_sizes[ch];
+      const int64_t stored = e & 0x7fffffffu;
+      const uint64_t base = stream_base(c, r, true);
+      uint8_t* out = c.stream + base;
+      uint8_t* dst = out + rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+      const uint8_t* src = c.codes + L.src;
+      const int64_t nv = align16(stored) / 16;
+      for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) {
+        uint4 x = ((const uint4*)src)[k];
+        const int64_t lim = stored - 16 * k;
+        if (lim < 16) {
+          uint8_t* xb = (uint8_t*)&x;
+          for (int b = 0; b < 16; ++b) if (b >= lim) xb[b] = 0;
+        }
+        ((uint4*)dst)[k] = x;
+      }
+      if (threadIdx.x == 0) *(uint32_t*)(out + 64 + 4 * (ch - rq.chunk_begin)) = e;
+    } else if (it < c.total_chunks + c.R) {
+      const int r = (int)(it - c.total_chunks);
+      const ReqDesc rq = req_at(c, r);
+      const uint64_t base = stream_base(c, r, true);
+      const uint64_t total = (c.req_offsets_out != nullptr) ? c.req_offsets_out[r + 1] - c.req_offsets_out[r]
+                                                            : c.ctl->total;
+      write_header(c, rq, c.stream + base, total);
+      zero_gaps(rq, c.stream + base);
+    } else {
+      const int64_t piece = it - c.total_chunks - c.R;
+      const int r = find_req_by_piece(c, piece);
+      const ReqDesc rq = req_at(c, r);
+      int64_t k = piece - rq.piece_begin;
+      const int64_t p0 = (rq.params_bytes[0] + 65535) / 65536;
+      const int w = (k < p0) ? 0 : 1;
+      if (w == 1) k -= p0;
+      const int64_t off = k * 65536;
+      const int64_t len = min<int64_t>(65536, rq.params_bytes[w] - off);
+      const uint32_t* src = (const uint32_t*)(c.params_ws + rq.params_ws_off[w] + off);
+      uint32_t* dst = (uint32_t*)(c.stream + stream_base(c, r, true) + rq.params_off[w] + off);
+      for (int64_t i = threadIdx.x; i < len / 4; i += blockDim.x) dst[i] = src[i];
+    }
+  }
+}
+
+hipError_t launch_compact(const CallDesc& c, hipStream_t s) {
+  const int64_t items = c.total_chunks + c.R + c.total_pieces;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, 256 * 16));
+  k_compact<<<grid, 256, 0, s>>>(c);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ decode
+
+// Check each request's header against the plan and the bytes available.
+__global__ __launch_bounds__(64) void k_validate(CallDesc c) {
+  for (int r = blockIdx.x; r < c.R; r += gridDim.x) {
+    const ReqDesc rq = req_at(c, r);
+    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+    const int t = threadIdx.x;
+    uint32_t bad = 0;
+    if (base + (uint64_t)rq.payload_off > c.stream_bytes) {
+      bad = kStCorrupt;
+    } else {
+      const uint8_t* h = c.stream + base;
+      if (t == 0) {
+        if (*(const uint32_t*)h != kMagic || *(const uint16_t*)(h + 4) != 1) bad |= kStCorrupt;
+        else {
+          if (h[6] != (uint8_t)c.dtype || *(const int32_t*)(h + 8) != c.layers ||
+              *(const int32_t*)(h + 12) != rq.T || *(const int32_t*)(h + 16) != c.heads ||
+              *(const int32_t*)(h + 20) != kHeadDim || *(const uint64_t*)(h + 40) != c.seed ||
+              *(const uint32_t*)(h + 52) != c.chunk_bytes)
+            bad |= kStMismatch;
+          for (int w = 0; w < 2; ++w) {
+            const uint8_t* p = h + 24 + 8 * w;
+            if (p[0] != c.pol[w].bits || p[1] != c.pol[w].axis || p[2] != c.pol[w].hadamard ||
+                *(const uint16_t*)(p + 4) != c.pol[w].group)
+              bad |= kStMismatch;
+          }
+          for (int k = 0; k < 4; ++k) if (h[48 + k] != c.stages[k]) bad |= kStMismatch;
+          const uint64_t total = *(const uint64_t*)(h + 56);
+          if (total < (uint64_t)rq.payload_off || total > (uint64_t)rq.max_stream || base + total > c.stream_bytes)
+            bad |= kStCorrupt;
+        }
+      }
+    }
+    if (bad && t == 0) set_status2(c.ctl, bad);
+  }
+}
+
+hipError_t launch_validate(const CallDesc& c, hipStream_t s) {
+  k_validate<<<(int)std::min(c.R, 1024), 64, 0, s>>>(c);
+  return hipGetLastError();
+}
+
+// Raw chunks are copied to their code slot; compressed chunks go to a worklist.
+// Block 0 also checks that each stream's chunk sizes add up to its header total.
+__global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* worklist) {
+  if (blockIdx.x == 0) {
+    for (int r = threadIdx.x; r < c.R; r += blockDim.x) {
+      const ReqDesc rq = req_at(c, r);
+      const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+      const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
+      const uint64_t want = (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
+      if (base + 64 > c.stream_bytes || *(const uint64_t*)(c.stream + base + 56) != want)
+        set_status2(c.ctl, kStCorrupt);
+    }
+  }
+  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const uint32_t e = c.chunk_sizes[ch];
+    const int64_t stored = e & 0x7fffffffu;
+    const bool raw = (e >> 31) != 0;
+    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+    const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+    const bool ok = (raw ? stored == L.n : (stored < L.n && stored > 0)) && pos + (uint64_t)stored <= c.stream_bytes &&
+                    (pos & 15) == 0;
+    if (!ok) {
+      if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+      continue;
+    }
+    if (raw) {
+      const uint4* src = (const uint4*)(c.stream + pos);
+      uint4* dst = (uint4*)(c.codes + L.src);
+      const int64_t nv = L.n / 16;
+      for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) dst[k] = src[k];
+      for (int64_t p = nv * 16 + threadIdx.x; p < L.n; p += blockDim.x) c.codes[L.src + p] = c.stream[pos + p];
+    } else if (threadIdx.x == 0) {
+      const uint32_t slot = __hip_atomic_fetch_add(&c.ctl->pad0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      worklist[slot] = (uint32_t)ch;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_ll_decode_generic(CallDesc c, const uint32_t* worklist) {
+  __shared__ __attribute__((aligned(16))) uint8_t bufA[65536];
+  __shared__ __attribute__((aligned(16))) uint8_t bufB[65536];
+  __shared__ uint32_t sh32[256];
+  __shared__ uint64_t sh64[256];
+  const uint32_t count = c.ctl->pad0;
+  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+    const int64_t ch = worklist[item];
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const uint32_t e = c.chunk_sizes[ch];
+    const int stored = (int)(e & 0x7fffffffu);
+    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+    const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+    const int n = (int)L.n;
+    for (int p = threadIdx.x; p < stored; p += blockDim.x) bufA[p] = c.stream[pos + p];
+    __syncthreads();
+    int ns = 0;
+    while (ns < 4 && c.stages[ns]) ++ns;
+    uint8_t* cur = bufA;
+    uint8_t* alt = bufB;
+    int size = stored;
+    bool ok = true;
+    for (int s = ns - 1; s >= 0 && ok; --s) {
+      ok = stage_inverse(c.stages[s], cur, size, alt, n, sh32, sh64);
+      uint8_t* tmp = cur; cur = alt; alt = tmp;
+      size = n;
+    }
+    if (!ok) {
+      if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+    } else {
+      for (int p = threadIdx.x; p < n; p += blockDim.x) c.codes[L.src + p] = cur[p];
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s) {
+  if (c.total_chunks == 0) return hipSuccess;
+  uint32_t* worklist = (uint32_t*)(c.chunk_offs + c.total_chunks + 1);
+  const int grid = (int)std::min<int64_t>(c.total_chunks, 256 * 8);
+  k_ll_decode_raw<<<grid, 256, 0, s>>>(c, worklist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_ll_decode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
+  return hipGetLastError();
+}
+
+}  // namespace kvc
