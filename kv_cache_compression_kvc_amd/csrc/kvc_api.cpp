@@ -77,9 +77,12 @@ int64_t params_bytes_of(const TensorPol& p, int L, int T, int H) {
   return (int64_t)L * cdiv(T, p.group) * H * kHeadDim * 4;
 }
 
-int64_t tiles_of(const TensorPol& p, int L, int T, int H) {
+// Fused-kernel tiles.  Per-token tiles are 32 head vectors: a dense call maps
+// them over all L*T*H vectors as one run; a paged request maps them per layer
+// so that no tile crosses a page.  Per-channel tiles are 64 tokens x 1 head.
+int64_t tiles_of(const TensorPol& p, int L, int T, int H, bool paged) {
   if (T == 0) return 0;
-  if (p.axis == 0) return (int64_t)L * cdiv((int64_t)T * H, 32);
+  if (p.axis == 0) return paged ? (int64_t)L * cdiv((int64_t)T * H, 32) : cdiv((int64_t)L * T * H, 32);
   return (int64_t)L * cdiv(T, 64) * H;
 }
 
@@ -261,7 +264,7 @@ PagedJob paged_job(const kvc_plan_s* p, const int32_t* lens, int R, bool encode)
     j.chunks += rq.nchunks[0] + rq.nchunks[1];
     for (int w = 0; w < 2; ++w) {
       rq.tile_begin[w] = j.tiles[w];
-      j.tiles[w] += tiles_of(p->pol[w], p->cfg.layers, lens[r], p->cfg.kv_heads);
+      j.tiles[w] += tiles_of(p->pol[w], p->cfg.layers, lens[r], p->cfg.kv_heads, true);
       rq.codes_off[w] = j.codes_area;
       j.codes_area += a256(rq.codes_bytes[w]);
       if (encode) {
@@ -407,7 +410,7 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   c.chunk_offs = (uint64_t*)(ws + w.offs);
   c.ctl = (Control*)(ws + w.ctl);
   c.total_chunks = c.one.nchunks[0] + c.one.nchunks[1];
-  for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads);
+  for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads, false);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
@@ -457,7 +460,7 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
   c.chunk_offs = (uint64_t*)(ws + w.offs);
   c.ctl = (Control*)(ws + w.ctl);
   c.total_chunks = c.one.nchunks[0] + c.one.nchunks[1];
-  for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads);
+  for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads, false);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");

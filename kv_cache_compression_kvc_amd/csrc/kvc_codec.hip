@@ -51,7 +51,10 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
 
 // Raw buffer resource over [p, p + bytes): loads past the end return zero and
-// stores past the end are dropped.
+// stores past the end are dropped.  The range check covers the VGPR offset
+// (and the instruction's immediate) but not the SGPR offset, so every
+// position that must be checked goes in the VGPR offset; callers pass 0 as
+// the SGPR offset.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
@@ -143,6 +146,9 @@ struct GroupQ {
 };
 
 __device__ __forceinline__ GroupQ group_params(float zmin, float zmax, float c, float levels) {
+  // -0 and +0 are one real value; the group extremes use +0 for it
+  zmin = zmin + 0.0f;
+  zmax = zmax + 0.0f;
   const float lo = mul_rd(zmin, c);
   const float hi = mul_ru(zmax, c);
   const uint32_t m16 = h16_rd(lo);
@@ -323,7 +329,7 @@ __device__ __forceinline__ void stage_in(__amdgpu_buffer_rsrc_t src, uint32_t vs
   const uint32_t voff = (uint32_t)(lane >> 4) * vstride + (uint32_t)(lane & 15) * 16;
   uint4 d[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) d[k] = bload16(src, voff, (uint32_t)k * 4 * vstride);
+  for (int k = 0; k < 8; ++k) d[k] = bload16(src, voff + (uint32_t)k * 4 * vstride, 0);
   uint32_t* wrow = wl + (lane >> 4) * RP + (lane & 15) * 4;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -373,7 +379,7 @@ __device__ __forceinline__ void stage_out(const float* f, uint32_t* wl, const ui
   for (int k = 0; k < 8; ++k) {
     uint4 x = *(const uint4*)(rrow + k * 4 * RP);
     x.x ^= sm[0]; x.y ^= sm[1]; x.z ^= sm[2]; x.w ^= sm[3];
-    bstore16(x, dst, voff, (uint32_t)k * 4 * vstride);
+    bstore16(x, dst, voff + (uint32_t)k * 4 * vstride, 0);
   }
   wave_sync();
 }
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
     uint8_t* params_base;
     if constexpr (!PAGED) {
       vg0 = tile * 32;
-      nv = (int)std::min<int64_t>(32, nvec_dense - vg0);
+      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec_dense - vg0));
       src = in + vg0 * kHeadDim;
       codes_base = c.codes + pick(which, c.one.codes_off);
       params_base = c.stream + pick(which, c.one.params_off);
@@ -424,7 +430,7 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
       const int64_t tr = tile - pick(which, rq.tile_begin);
       const int l = (int)(tr / tpl);
       const int64_t vstart = (tr - (int64_t)l * tpl) * 32;
-      nv = (int)std::min<int64_t>(32, vpl - vstart);
+      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart));
       vg0 = (int64_t)l * vpl + vstart;
       bool ok;
       const int64_t base = page_run_base(c, rq, l, vstart, ok);
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
     uint16_t* dst;
     if constexpr (!PAGED) {
       vg0 = tile * 32;
-      nv = (int)std::min<int64_t>(32, nvec_dense - vg0);
+      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec_dense - vg0));
       nvo = nv;
       codes_base = c.codes + pick(which, c.one.codes_off);
       params_base = c.stream + pick(which, c.one.params_off);
@@ -543,7 +549,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
       const int64_t tr = tile - pick(which, rq.tile_begin);
       const int l = (int)(tr / tpl);
       const int64_t vstart = (tr - (int64_t)l * tpl) * 32;
-      nv = (int)std::min<int64_t>(32, vpl - vstart);
+      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart));
       vg0 = (int64_t)l * vpl + vstart;
       // this request's parameters must lie inside the input
       const uint64_t off = c.req_offsets[r];
@@ -555,7 +561,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
       bool ok;
       const int64_t base = page_run_base(c, rq, l, vstart, ok);
       if (!ok && lane == 0) set_status(c.ctl, kStBadBlock);
-      nvo = ok ? (int)std::min<int64_t>(32, vpl - vstart) : 0;
+      nvo = ok ? (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart)) : 0;
       dst = out + base;
     }
 

@@ -79,6 +79,7 @@ __global__ void k_reset(Control* ctl) {
     ctl->status = 0;
     ctl->pad0 = 0;     // worklist count
     ctl->total = 0;
+    ctl->pad[0] = 0;   // header-field diagnosis bits
   }
 }
 
@@ -564,18 +565,25 @@ __global__ __launch_bounds__(64) void k_validate(CallDesc c) {
       if (t == 0) {
         if (*(const uint32_t*)h != kMagic || *(const uint16_t*)(h + 4) != 1) bad |= kStCorrupt;
         else {
-          if (h[6] != (uint8_t)c.dtype || *(const int32_t*)(h + 8) != c.layers ||
-              *(const int32_t*)(h + 12) != rq.T || *(const int32_t*)(h + 16) != c.heads ||
-              *(const int32_t*)(h + 20) != kHeadDim || *(const uint64_t*)(h + 40) != c.seed ||
-              *(const uint32_t*)(h + 52) != c.chunk_bytes)
-            bad |= kStMismatch;
+          uint32_t diag = 0;
+          diag |= (h[6] != (uint8_t)c.dtype) << 0;
+          diag |= (*(const int32_t*)(h + 8) != c.layers) << 1;
+          diag |= (*(const int32_t*)(h + 12) != rq.T) << 2;
+          diag |= (*(const int32_t*)(h + 16) != c.heads) << 3;
+          diag |= (*(const int32_t*)(h + 20) != kHeadDim) << 4;
+          diag |= (*(const uint64_t*)(h + 40) != c.seed) << 5;
+          diag |= (*(const uint32_t*)(h + 52) != c.chunk_bytes) << 6;
           for (int w = 0; w < 2; ++w) {
             const uint8_t* p = h + 24 + 8 * w;
-            if (p[0] != c.pol[w].bits || p[1] != c.pol[w].axis || p[2] != c.pol[w].hadamard ||
-                *(const uint16_t*)(p + 4) != c.pol[w].group)
-              bad |= kStMismatch;
+            diag |= (p[0] != c.pol[w].bits || p[1] != c.pol[w].axis || p[2] != c.pol[w].hadamard ||
+                     *(const uint16_t*)(p + 4) != c.pol[w].group) << (7 + w);
           }
-          for (int k = 0; k < 4; ++k) if (h[48 + k] != c.stages[k]) bad |= kStMismatch;
+          for (int k = 0; k < 4; ++k) diag |= (h[48 + k] != c.stages[k]) << (9 + k);
+          if (diag) {
+            bad |= kStMismatch;
+            // which header fields differ (bit per field), kept for diagnosis
+            __hip_atomic_fetch_or((uint32_t*)&c.ctl->pad[0], diag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
           const uint64_t total = *(const uint64_t*)(h + 56);
           if (total < (uint64_t)rq.payload_off || total > (uint64_t)rq.max_stream || base + total > c.stream_bytes)
             bad |= kStCorrupt;

@@ -241,6 +241,9 @@ extern "C" int kvco_group_params(const float* z, int count, int bits, float c,
     if (z[i] < zmin) zmin = z[i];
     if (z[i] > zmax) zmax = z[i];
   }
+  /* -0 and +0 are one real value; the group extremes use +0 for it */
+  if (zmin == 0.0f) zmin = 0.0f;
+  if (zmax == 0.0f) zmax = 0.0f;
   const int levels = (1 << bits) - 1;
   float lo = rd32_mul(zmin, c);
   float hi = ru32_mul(zmax, c);

@@ -53,7 +53,12 @@ def gpu_decode(plan, stream_np: np.ndarray, wl, T, layers, ws=None):
         _, wsb = plan.sizes(T)
         ws = torch.full((wsb,), 0x33, dtype=torch.uint8, device=DEV)
     plan.decode(s, stream_np.size, T, k, v, ws)
+    torch.cuda.synchronize()
+    ctl = ws[:32].cpu().numpy()
     st = plan.query_status(ws)
+    if st != K.OK:
+        log(f"  decode status {st}: control words {ctl.view(np.uint32)[:2].tolist()} "
+            f"header-diag {ctl.view(np.uint64)[2]:#x}")
     torch.cuda.synchronize()
     return st, k, v
 

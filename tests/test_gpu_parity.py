@@ -188,3 +188,45 @@ def test_encode_is_deterministic_and_async_size_matches():
     torch.cuda.synchronize()
     total = int(np.frombuffer(out[56:64].cpu().numpy().tobytes(), np.uint64)[0])
     assert total == a.size and np.array_equal(out[:total].cpu().numpy(), a)
+
+
+GUARD = 1 << 16
+
+
+def _guarded(nbytes, fill=0x33):
+    t = torch.full((nbytes + 2 * GUARD,), fill, dtype=torch.uint8, device=DEV)
+    return t, t[GUARD:GUARD + nbytes]
+
+
+def _canaries_intact(big, fill=0x33):
+    a = big.cpu().numpy()
+    return bool((a[:GUARD] == fill).all() and (a[-GUARD:] == fill).all())
+
+
+@pytest.mark.parametrize("name,T", [("c3_llama70b_32k", 1), ("c3_llama70b_32k", 37), ("c2_llama8b_4k", 150),
+                                    ("c5_llama70b_128k", 65), ("c1_single_layer_512", 3)])
+def test_no_writes_outside_the_given_buffers(name, T):
+    """Encode and decode touch only their own buffers (regression: tile counts
+    that overran a ragged tail wrote past the output)."""
+    wl = W.WORKLOADS[name].with_(chunk_bytes=8192)
+    L = 2
+    log(f"guard case {name} T={T}")
+    k, v = W.dense_kv(wl, layers=L, tokens=T, seed=3)
+    n_el = L * T * wl.heads * wl.head_dim
+    plan = K.Plan(K.config_from_workload(wl, max_tokens=T, layers=L))
+    ms, wsb = plan.sizes(T)
+    kb, kin = _guarded(2 * n_el); vb, vin = _guarded(2 * n_el)
+    kin.copy_(k.reshape(-1).view(torch.uint8).to(DEV)); vin.copy_(v.reshape(-1).view(torch.uint8).to(DEV))
+    ob, out = _guarded(ms)
+    wb, ws = _guarded(wsb)
+    n = plan.encode(kin.view(wl.torch_dtype), vin.view(wl.torch_dtype), T, out, ws)
+    for big in (kb, vb, ob, wb):
+        assert _canaries_intact(big)
+    kdb, kd = _guarded(2 * n_el); vdb, vd = _guarded(2 * n_el)
+    wb2, ws2 = _guarded(wsb)
+    plan.decode(out, n, T, kd.view(wl.torch_dtype), vd.view(wl.torch_dtype), ws2)
+    assert plan.query_status(ws2) == K.OK
+    for big in (ob, kdb, vdb, wb2):
+        assert _canaries_intact(big)
+    st, ref = oracle_encode(wl, to_u16(k), to_u16(v), T, L)
+    assert np.array_equal(out[:n].cpu().numpy(), ref)
