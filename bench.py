@@ -66,6 +66,8 @@ def main():
     ap.add_argument("--workload", default="c3_llama70b_32k")
     ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30,
+                    help="size of the plain device copy timed as the practical bandwidth reference")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -76,6 +78,22 @@ def main():
     import torch
     import kv_cache_compression_kvc_amd as K
     import kvc_workloads as W
+
+    # plain device copy of known size: practical bandwidth reference, and the
+    # kernel whose counters scale the HBM byte counts of the profile runs
+    ca = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda:0")
+    cb = torch.empty_like(ca)
+    cb.copy_(ca)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        cb.copy_(ca)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * args.copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    log(f"device copy of {args.copy_bytes} bytes: {copy_gbps:.1f} GB/s (read + write)")
+    del ca, cb
 
     wl = W.WORKLOADS[args.workload]
     L, T = wl.layers, wl.tokens
@@ -181,6 +199,7 @@ def main():
         "compression_ratio_lossless": round(codes_params / n, 4),
         "stream_bytes": n,
         "kernel_ms_per_launch": {k_: round(t / max(c, 1), 4) for k_, (t, c) in prof.items() if c},
+        "device_copy_GBps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
     }
