@@ -15,7 +15,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
-    # packed fp32 arithmetic stays off
+    # no packed fp32 instructions: the kernels are written for scalar fp32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     "-I" + os.path.join(ROOT, "include"), "-I" + SRC,

@@ -31,6 +31,7 @@
 // groups.  Per-channel groups (keys) are reduced through a second LDS
 // transpose so that one thread owns one channel of one token group.
 #include <algorithm>
+#include <type_traits>
 
 #include "kvc_internal.h"
 
@@ -55,61 +56,49 @@ typedef int int2v __attribute__((ext_vector_type(2)));
 // (and the instruction's immediate) but not the SGPR offset, so every
 // position that must be checked goes in the VGPR offset; callers pass 0 as
 // the SGPR offset.
+// Cache policy bits of the streaming buffer accesses (2 = non-temporal).
+// Every input and output byte of these kernels is touched once.
+#ifndef KVC_LOAD_POLICY
+#define KVC_LOAD_POLICY 2
+#endif
+#ifndef KVC_STORE_POLICY
+#define KVC_STORE_POLICY 2
+#endif
+#ifndef KVC_NARROW_STORE_POLICY
+#define KVC_NARROW_STORE_POLICY 2
+#endif
+constexpr int kLoadPol = KVC_LOAD_POLICY;
+constexpr int kStorePol = KVC_STORE_POLICY;          // 16-byte stores
+constexpr int kNarrowStorePol = KVC_NARROW_STORE_POLICY;   // 4- and 8-byte stores
+
+// Every resource here describes a per-wave (or per-block) range, so its base
+// and size are wave-uniform; reading them through readfirstlane puts the
+// descriptor in scalar registers, which buffer instructions require (a
+// descriptor in vector registers makes the compiler loop over lanes).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* q = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(q, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const int4v x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  const int4v x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kLoadPol);
   return make_uint4((uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w);
 }
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kLoadPol);
 }
 __device__ __forceinline__ void bstore16(uint4 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   int4v x = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)voff, (int)soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)voff, (int)soff, kStorePol);
 }
 __device__ __forceinline__ void bstore8(uint2 v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   int2v x = {(int)v.x, (int)v.y};
-  __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)voff, (int)soff, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, (int)voff, (int)soff, kNarrowStorePol);
 }
 __device__ __forceinline__ void bstore4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b32((int)v, r, (int)voff, (int)soff, 0);
-}
-
-__device__ __forceinline__ float next_up32(float f) {
-  uint32_t u = f2u(f);
-  if ((u & 0x7fffffffu) == 0) return u2f(1u);
-  return u2f((u >> 31) ? u - 1 : u + 1);
-}
-__device__ __forceinline__ float next_down32(float f) {
-  uint32_t u = f2u(f);
-  if ((u & 0x7fffffffu) == 0) return u2f(0x80000001u);
-  return u2f((u >> 31) ? u + 1 : u - 1);
-}
-
-// Largest binary32 <= a*b.  fma gives the exact error of the rounded product;
-// its sign bit is reliable even when it underflows to a signed zero.
-__device__ __forceinline__ float mul_rd(float a, float b) {
-  float p = a * b;
-  float e = __builtin_fmaf(a, b, -p);
-  return (f2u(e) >> 31) ? next_down32(p) : p;
-}
-__device__ __forceinline__ float mul_ru(float a, float b) { return -mul_rd(-a, b); }
-
-// Smallest binary32 >= a - b (TwoSum).
-__device__ __forceinline__ float sub_ru(float a, float b) {
-  float s = a - b;
-  float bb = s - a;
-  float e = (a - (s - bb)) + (-b - bb);
-  return (e > 0.0f) ? next_up32(s) : s;
-}
-
-// Smallest binary32 >= r / k for r >= 0 and a small positive integer k.
-__device__ __forceinline__ float div_ru(float r, float k) {
-  float q = r / k;
-  float e = __builtin_fmaf(q, k, -r);
-  return (f2u(e) >> 31) ? next_up32(q) : q;
+  __builtin_amdgcn_raw_buffer_store_b32((int)v, r, (int)voff, (int)soff, kNarrowStorePol);
 }
 
 __device__ __forceinline__ uint32_t h16_from(float f) {
@@ -119,23 +108,77 @@ __device__ __forceinline__ uint32_t h16_from(float f) {
 __device__ __forceinline__ float f_from_h16(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
-__device__ __forceinline__ uint32_t h16_next_down(uint32_t h) {
-  if (h == 0xfc00u) return h;
-  if (h == 0x0000u) return 0x8001u;
-  return (h & 0x8000u) ? h + 1 : h - 1;
+
+// Directed rounding through the MODE register: bits [1:0] hold the binary32
+// rounding mode and bits [3:2] the fp16/fp64 one (0 nearest-even, 1 toward
+// +inf, 2 toward -inf).  Each statement sets both fields, runs its
+// instructions and restores nearest-even; being one asm statement, nothing
+// else is scheduled while the mode differs.  The wait state before the
+// restore keeps it from overtaking the last arithmetic instruction.
+// lo = RD32(a*b), h = RD16(lo) (in the low 16 bits; the high bits are zero)
+__device__ __forceinline__ void mul_cvt_rd(float a, float b, float& lo, uint32_t& h) {
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 10\n\t"
+      "v_mul_f32 %0, %2, %3\n\t"
+      "v_cvt_f16_f32 %1, %0\n\t"
+      "s_nop 0\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 0"
+      : "=&v"(lo), "=&v"(h)
+      : "v"(a), "v"(b));
 }
-__device__ __forceinline__ uint32_t h16_next_up(uint32_t h) {
-  if (h == 0x7c00u) return h;
-  if (h == 0x8000u) return 0x0001u;
-  return (h & 0x8000u) ? h - 1 : h + 1;
+// hi = RU32(a*b), r = RU32(hi - m)
+__device__ __forceinline__ void mul_sub_ru(float a, float b, float m, float& hi, float& r) {
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 5\n\t"
+      "v_mul_f32 %0, %2, %3\n\t"
+      "v_sub_f32 %1, %0, %4\n\t"
+      "s_nop 0\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 0"
+      : "=&v"(hi), "=&v"(r)
+      : "v"(a), "v"(b), "v"(m));
 }
-__device__ __forceinline__ uint32_t h16_rd(float f) {
-  uint32_t h = h16_from(f);
-  return (f_from_h16(h) > f) ? h16_next_down(h) : h;
+// RU16(x) in the low 16 bits
+__device__ __forceinline__ uint32_t cvt_f16_ru(float x) {
+  uint32_t h;
+  asm volatile(
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 5\n\t"
+      "v_cvt_f16_f32 %0, %1\n\t"
+      "s_nop 0\n\t"
+      "s_setreg_imm32_b32 hwreg(HW_REG_MODE, 0, 4), 0"
+      : "=v"(h)
+      : "v"(x));
+  return h;
 }
-__device__ __forceinline__ uint32_t h16_ru(float f) {
-  uint32_t h = h16_from(f);
-  return (f_from_h16(h) < f) ? h16_next_up(h) : h;
+
+// RN32(1 / (2^b - 1))
+template <int BITS>
+__device__ __forceinline__ constexpr float rcp_levels() {
+  return BITS == 2 ? 0x1.555556p-2f : BITS == 4 ? 0x1.111112p-4f : 0x1.010102p-8f;
+}
+
+// Smallest binary32 >= r / k for finite r >= 0 and k = 2^b - 1: q1 is the
+// correctly rounded quotient (one Markstein correction of r * RN(1/k), with
+// exact fma residuals), then the residual's sign decides one step up.  The
+// sequence was checked against the exact result for every binary32 r >= 0
+// and k in {3, 15, 255}.
+template <int BITS>
+__device__ __forceinline__ float div_levels_ru(float r) {
+  constexpr float k = (float)((1 << BITS) - 1);
+  constexpr float rk = rcp_levels<BITS>();
+  const float q0 = r * rk;
+  const float e1 = __builtin_fmaf(-q0, k, r);
+  const float q1 = __builtin_fmaf(e1, rk, q0);
+  const float e2 = __builtin_fmaf(-q1, k, r);
+  return (e2 > 0.0f) ? u2f(f2u(q1) + 1u) : q1;
+}
+
+// RN32(1 / s) for a positive fp16 value s: hardware reciprocal refined by one
+// Newton step with an exact fma residual (equal to the IEEE quotient for every
+// positive finite fp16 value, checked exhaustively).
+__device__ __forceinline__ float rcp_rn_f16val(float s) {
+  const float y0 = __builtin_amdgcn_rcpf(s);
+  const float e = __builtin_fmaf(-s, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
 }
 
 struct GroupQ {
@@ -145,24 +188,58 @@ struct GroupQ {
   bool bad;         // a parameter is not a finite fp16
 };
 
-__device__ __forceinline__ GroupQ group_params(float zmin, float zmax, float c, float levels) {
+template <int BITS>
+__device__ __forceinline__ GroupQ group_params(float zmin, float zmax, float c) {
   // -0 and +0 are one real value; the group extremes use +0 for it
   zmin = zmin + 0.0f;
   zmax = zmax + 0.0f;
-  const float lo = mul_rd(zmin, c);
-  const float hi = mul_ru(zmax, c);
-  const uint32_t m16 = h16_rd(lo);
+  float lo, hi, range;
+  uint32_t m16;
+  mul_cvt_rd(zmin, c, lo, m16);
   const float mf = f_from_h16(m16);
-  const float range = sub_ru(hi, mf);
-  const float s32 = div_ru(range, levels);
-  const uint32_t s16 = h16_ru(s32);
+  mul_sub_ru(zmax, c, mf, hi, range);
+  const uint32_t s16 = cvt_f16_ru(div_levels_ru<BITS>(range));
   const float sf = f_from_h16(s16);
   GroupQ g;
   g.neg_m = -mf;
-  g.inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+  g.inv = (sf == 0.0f) ? 0.0f : rcp_rn_f16val(sf);
   g.packed = s16 | (m16 << 16);
-  g.bad = ((s16 & 0x7c00u) == 0x7c00u) || ((m16 & 0x7c00u) == 0x7c00u) || (lo != lo) || (hi != hi);
+  // a NaN or infinite extreme makes m or s NaN or infinite
+  g.bad = ((s16 & 0x7c00u) == 0x7c00u) || ((m16 & 0x7c00u) == 0x7c00u);
   return g;
+}
+
+// min / max without NaN canonicalization of the operands: every value reduced
+// here is the result of arithmetic (never a signaling NaN)
+__device__ __forceinline__ float vmin3(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmin(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// min and max of n >= 1 values
+template <int N>
+__device__ __forceinline__ void minmax_n(const float* x, float& mn, float& mx) {
+  mn = x[0];
+  mx = x[0];
+  int i = 1;
+#pragma unroll
+  for (; i + 1 < N; i += 2) { mn = vmin3(mn, x[i], x[i + 1]); mx = vmax3(mx, x[i], x[i + 1]); }
+  if (i < N) { mn = vmin(mn, x[i]); mx = vmax(mx, x[i]); }
 }
 
 // Code of one value: fl(fl(z*c - m) * inv + 2^23) carries round-half-even(t*inv)
@@ -384,22 +461,148 @@ __device__ __forceinline__ void stage_out(const float* f, uint32_t* wl, const ui
   wave_sync();
 }
 
+// ------------------------------------------------------------------
+// Tile loads straight into LDS.  A wavefront's tile is 32 head vectors of 256
+// bytes; the 16-byte loads of one instruction land in LDS at consecutive
+// lanes (lane i at base + 16 i), so four rows per instruction.  Lanes fetch
+// the global chunk that makes the LDS tile XOR-swizzled: row r's chunk j sits
+// in slot j ^ (r & 15).  Rows then start on the same bank but the per-lane
+// reads of (row, chunk) pairs spread over all banks.
+// ------------------------------------------------------------------
+constexpr int kTileBytes = 32 * 256;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;     // low half of a shared-aperture address is the LDS offset
+}
+
+// One 16-byte load per lane into LDS at m0 + 16 * lane.  Issued from asm so
+// that the compiler's wait insertion does not add a wait for all outstanding
+// memory operations before every LDS read; the caller waits explicitly.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds)
+               : "memory");
+}
+
+// Wait until at most N vector memory operations are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+// Loads of 32 rows (vstride bytes apart) of one tile into a wave's LDS tile.
+__device__ __forceinline__ void tile_dma(__amdgpu_buffer_rsrc_t src, uint32_t vstride, uint32_t lds) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t r = 4 * k + (lane >> 4);
+    const uint32_t j = (uint32_t)(lane & 15) ^ (r & 15);
+    dma16(src, r * vstride + j * 16, lds + 1024 * k);
+  }
+}
+
+// This lane's 64 values of its vector from a loaded LDS tile: lane half hf
+// gets channels [64 hf, 64 hf + 64) of row (lane & 31), sign-flipped with the
+// table of per-chunk masks (16 chunks x 4 dwords).
+template <bool BF16>
+__device__ __forceinline__ void tile_read(const uint32_t* tile, const uint32_t* masks, float* f) {
+  const int lane = __lane_id();
+  const int v = lane & 31, hf = lane >> 5;
+  const uint32_t x = (uint32_t)(8 * hf) ^ (uint32_t)(v & 15);
+  const uint32_t base = (uint32_t)v * 256u + x * 16u;             // byte offset of chunk 8 hf
+  const uint4* mk = (const uint4*)(masks + 32 * hf);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    uint4 d = *(const uint4*)((const char*)tile + (base ^ (uint32_t)(16 * jj)));
+    const uint4 m = mk[jj];
+    d.x ^= m.x; d.y ^= m.y; d.z ^= m.z; d.w ^= m.w;
+    unpack16<BF16>(d.x, f[8 * jj + 0], f[8 * jj + 1]);
+    unpack16<BF16>(d.y, f[8 * jj + 2], f[8 * jj + 3]);
+    unpack16<BF16>(d.z, f[8 * jj + 4], f[8 * jj + 5]);
+    unpack16<BF16>(d.w, f[8 * jj + 6], f[8 * jj + 7]);
+  }
+}
+
+// Sign-mask table: dword 4 g + j flips channels 8 g + 2 j (bit 15) and
+// 8 g + 2 j + 1 (bit 31).
+__device__ __forceinline__ void fill_mask_table(const uint32_t* signs, uint32_t* table) {
+  if (threadIdx.x < 64) {
+    const int g = threadIdx.x >> 2, j = threadIdx.x & 3;
+    const int ch = 8 * g + 2 * j;
+    const uint32_t b0 = (signs[ch >> 5] >> (ch & 31)) & 1u;
+    const uint32_t b1 = (signs[(ch + 1) >> 5] >> ((ch + 1) & 31)) & 1u;
+    table[threadIdx.x] = (b0 << 15) | (b1 << 31);
+  }
+}
+
+// Where a per-token tile's vectors and outputs live.
+struct TokTile {
+  const uint16_t* src;     // first input vector
+  int nv;                  // vectors present (0..32)
+  int64_t vg0;             // index of the first vector within its request
+  uint8_t* codes_base;
+  uint8_t* params_base;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ TokTile enc_token_tile(const CallDesc& c, int which, int64_t tile, const uint16_t* in) {
+  TokTile t;
+  if constexpr (!PAGED) {
+    const int64_t nvec = (int64_t)c.layers * c.one.T * c.heads;
+    t.vg0 = tile * 32;
+    t.nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec - t.vg0));
+    t.src = in + t.vg0 * kHeadDim;
+    t.codes_base = c.codes + pick(which, c.one.codes_off);
+    t.params_base = c.stream + pick(which, c.one.params_off);
+  } else {
+    const int r = find_req_by_tile(c, which, tile);
+    const ReqDesc rq = load_req(c, r);
+    const int64_t vpl = (int64_t)rq.T * c.heads;               // vectors per layer
+    const int64_t tpl = (vpl + 31) >> 5;                        // tiles per layer
+    const int64_t tr = tile - pick(which, rq.tile_begin);
+    const int l = (int)(tr / tpl);
+    const int64_t vstart = (tr - (int64_t)l * tpl) * 32;
+    t.nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart));
+    t.vg0 = (int64_t)l * vpl + vstart;
+    bool ok;
+    const int64_t base = page_run_base(c, rq, l, vstart, ok);
+    if (!ok) {
+      if (__lane_id() == 0) set_status(c.ctl, kStBadBlock);
+      t.nv = 0;
+    }
+    t.src = in + base;
+    t.codes_base = c.codes + pick(which, rq.codes_off);
+    t.params_base = c.params_ws + pick(which, rq.params_ws_off);
+  }
+  return t;
+}
+
 // ===================================================================
 // Encode, per-token groups.  One wavefront encodes 32 consecutive head
 // vectors (a tile); 4 wavefronts per block.  Dense calls treat all L*T*H
 // vectors as one run (codes and parameters follow the same order); paged
-// calls decompose tiles by request, layer and page.
+// calls decompose tiles by request, layer and page.  The loads of a wave's
+// next tile are issued as soon as the current tile has been read out of LDS,
+// so they are in flight while the current tile is transformed, quantized and
+// stored.
 // ===================================================================
 template <int BITS, int G, bool BF16, bool PAGED>
 __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) {
-  __shared__ __attribute__((aligned(16))) uint32_t lds[4 * kWaveLds];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint32_t* wl = lds + wave * kWaveLds;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[4 * kTileBytes / 4 + 64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint32_t* wl = lds + wave * (kTileBytes / 4);
+  uint32_t* masks = lds + 4 * (kTileBytes / 4);
+  const uint32_t wl_lds = lds_addr(wl);
   const TensorPol pol = which ? c.pol[1] : c.pol[0];
   const float cc = pol.c;
-  const float levels = (float)((1 << BITS) - 1);
-  uint32_t sm[4];
-  slot_sign_masks(c.signs, lane & 15, sm);
+  fill_mask_table(c.signs, masks);
+  __syncthreads();
   const uint16_t* in = (const uint16_t*)(which ? c.in_kv[1] : c.in_kv[0]);
   const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
   const int v = lane & 31, hf = lane >> 5;
@@ -407,67 +610,57 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
   constexpr int NLG = 64 / LG;
   constexpr int CB = kHeadDim * BITS / 8;        // code bytes per vector
   constexpr int NGV = kHeadDim / G;              // groups per vector
-  const int64_t nvec_dense = (int64_t)c.layers * c.one.T * c.heads;
+  // vector memory operations issued after a tile's loads: the code stores
+  // (one per half, two for 8-bit codes) and the parameter stores; all are
+  // unconditional so the count is exact
+  constexpr int NPST = (G <= 32) ? NLG : 1;
+  constexpr int NST = 2 * ((BITS == 8) ? 2 : 1) + NPST;
 
   const int64_t stride = (int64_t)gridDim.x * 4;
-  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += stride) {
-    int64_t vg0;          // index of the tile's first vector within its request
-    int nv;
-    const uint16_t* src;
-    uint8_t* codes_base;
-    uint8_t* params_base;
-    if constexpr (!PAGED) {
-      vg0 = tile * 32;
-      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec_dense - vg0));
-      src = in + vg0 * kHeadDim;
-      codes_base = c.codes + pick(which, c.one.codes_off);
-      params_base = c.stream + pick(which, c.one.params_off);
-    } else {
-      const int r = find_req_by_tile(c, which, tile);
-      const ReqDesc rq = load_req(c, r);
-      const int64_t vpl = (int64_t)rq.T * c.heads;               // vectors per layer
-      const int64_t tpl = (vpl + 31) >> 5;                        // tiles per layer
-      const int64_t tr = tile - pick(which, rq.tile_begin);
-      const int l = (int)(tr / tpl);
-      const int64_t vstart = (tr - (int64_t)l * tpl) * 32;
-      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart));
-      vg0 = (int64_t)l * vpl + vstart;
-      bool ok;
-      const int64_t base = page_run_base(c, rq, l, vstart, ok);
-      if (!ok) { if (lane == 0) set_status(c.ctl, kStBadBlock); nv = 0; }
-      src = in + base;
-      codes_base = c.codes + pick(which, rq.codes_off);
-      params_base = c.params_ws + pick(which, rq.params_ws_off);
-    }
+  int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+  if (tile >= ntiles) return;
+  TokTile cur = enc_token_tile<PAGED>(c, which, tile, in);
+  tile_dma(make_rsrc(cur.src, (uint32_t)cur.nv * 256u), 256u, wl_lds);
+  bool first = true;
+  for (; tile < ntiles; tile += stride) {
+    if (first) wait_vmcnt<0>();
+    else wait_vmcnt<NST>();
+    first = false;
     float f[64];
-    stage_in<BF16>(make_rsrc(src, (uint32_t)nv * 256u), 256u, wl, sm, f);
+    tile_read<BF16>(wl, masks, f);
+    wait_lgkm0();                                  // reads done before the tile is reloaded
+    const TokTile t = cur;
+    if (tile + stride < ntiles) {
+      cur = enc_token_tile<PAGED>(c, which, tile + stride, in);
+      tile_dma(make_rsrc(cur.src, (uint32_t)cur.nv * 256u), 256u, wl_lds);
+    }
     fwht64_inreg(f);
     fwht_cross(f);
     // register r: channel (r < 32 ? 32 hf + r : 64 + 32 hf + r - 32)
 
     float mn[NLG], mx[NLG];
 #pragma unroll
-    for (int j = 0; j < NLG; ++j) {
-      float a = f[j * LG], b = f[j * LG];
-#pragma unroll
-      for (int i = 1; i < LG; ++i) { a = fminf(a, f[j * LG + i]); b = fmaxf(b, f[j * LG + i]); }
-      mn[j] = a; mx[j] = b;
-    }
+    for (int j = 0; j < NLG; ++j) minmax_n<LG>(f + j * LG, mn[j], mx[j]);
     if constexpr (G == 128) {
-      mn[0] = fminf(mn[0], mn[1]); mx[0] = fmaxf(mx[0], mx[1]);
-      mn[0] = fminf(mn[0], pair_xchg(mn[0])); mx[0] = fmaxf(mx[0], pair_xchg(mx[0]));
+      mn[0] = vmin(mn[0], mn[1]); mx[0] = vmax(mx[0], mx[1]);
+      mn[0] = vmin(mn[0], pair_xchg(mn[0])); mx[0] = vmax(mx[0], pair_xchg(mx[0]));
       mn[1] = mn[0]; mx[1] = mx[0];
     } else if constexpr (G == 64) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) { mn[j] = fminf(mn[j], pair_xchg(mn[j])); mx[j] = fmaxf(mx[j], pair_xchg(mx[j])); }
+      for (int j = 0; j < 2; ++j) { mn[j] = vmin(mn[j], pair_xchg(mn[j])); mx[j] = vmax(mx[j], pair_xchg(mx[j])); }
     }
     GroupQ gq[NLG];
     bool bad = false;
+    if constexpr (G == 128) {
+      gq[0] = group_params<BITS>(mn[0], mx[0], cc);
+      gq[1] = gq[0];
+      bad = gq[0].bad;
+    } else {
 #pragma unroll
-    for (int j = 0; j < NLG; ++j) { gq[j] = group_params(mn[j], mx[j], cc, levels); bad |= gq[j].bad; }
-    if (bad && v < nv) set_status(c.ctl, kStRange);
+      for (int j = 0; j < NLG; ++j) { gq[j] = group_params<BITS>(mn[j], mx[j], cc); bad |= gq[j].bad; }
+    }
 
-    const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes_base + vg0 * CB, (uint32_t)nv * CB);
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(t.codes_base + t.vg0 * CB, (uint32_t)t.nv * CB);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint32_t w[BITS];
@@ -490,7 +683,7 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
         bstore16(make_uint4(w[4], w[5], w[6], w[7]), crs, off + 16, 0);
       }
     }
-    const __amdgpu_buffer_rsrc_t prs = make_rsrc(params_base + vg0 * NGV * 4, (uint32_t)nv * NGV * 4);
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(t.params_base + t.vg0 * NGV * 4, (uint32_t)t.nv * NGV * 4);
     const uint32_t prow = (uint32_t)v * NGV * 4;
     if constexpr (G <= 32) {
 #pragma unroll
@@ -501,8 +694,10 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
     } else if constexpr (G == 64) {
       bstore4(hf ? gq[1].packed : gq[0].packed, prs, prow + hf * 4, 0);
     } else {
-      if (hf == 0) bstore4(gq[0].packed, prs, prow, 0);
+      // one parameter word per vector: the upper lane's store is pushed out of range
+      bstore4(gq[0].packed, prs, hf ? 0x7ffffff0u : prow, 0);
     }
+    if (bad && v < t.nv) set_status(c.ctl, kStRange);
   }
 }
 
@@ -512,7 +707,7 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
 template <int BITS, int G, bool BF16, bool PAGED>
 __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[4 * kWaveLds];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint32_t* wl = lds + wave * kWaveLds;
   const TensorPol pol = which ? c.pol[1] : c.pol[0];
   const float cc = pol.c;
@@ -616,10 +811,9 @@ __device__ __forceinline__ int64_t pc_block(int T, int G, int H, int bits, int l
 template <int BITS, int G, bool BF16>
 __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which) {
   __shared__ __attribute__((aligned(16))) float zb[64 * RP];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const TensorPol pol = which ? c.pol[1] : c.pol[0];
   const float cc = pol.c;
-  const float levels = (float)((1 << BITS) - 1);
   uint32_t sm[4];
   slot_sign_masks(c.signs, lane & 15, sm);
   const uint16_t* in = (const uint16_t*)(which ? c.in_kv[1] : c.in_kv[0]);
@@ -663,64 +857,68 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
       const int chl = 32 * wave + (lane & 31);
       const int th = lane >> 5;
       const int ch = 64 * p + chl;
-      const int nvt = max(0, min(32, gg - 32 * th));   // valid tokens of this half
       float zc[32];
       const float* rcol = zb + 32 * th * RP + (chl ^ (32 * th));
 #pragma unroll
       for (int i = 0; i < 32; ++i) zc[i] = rcol[i * RP];
-      float a = __builtin_inff(), b = -__builtin_inff();
-      if (nvt == 32) {
+      // FULL: all 64 tokens of the tile exist (every group is complete)
+      auto pass = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        const int nvt = FULL ? 32 : max(0, min(32, gg - 32 * th));   // valid tokens of this half
+        float a, b;
+        if constexpr (FULL) {
+          minmax_n<32>(zc, a, b);
+        } else {
+          a = __builtin_inff(); b = -__builtin_inff();
 #pragma unroll
-        for (int i = 0; i < 32; ++i) { a = fminf(a, zc[i]); b = fmaxf(b, zc[i]); }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) if (i < nvt) { a = fminf(a, zc[i]); b = fmaxf(b, zc[i]); }
-      }
-      int grp, ntok;
-      if constexpr (G == 64) {
-        a = fminf(a, pair_xchg(a));
-        b = fmaxf(b, pair_xchg(b));
-        grp = g64; ntok = gg;
-      } else {
-        grp = 2 * g64 + th; ntok = nvt;
-      }
-      const GroupQ gq = group_params(a, b, cc, levels);
-      if (gq.bad && nvt > 0) set_status(c.ctl, kStRange);
-      uint32_t w[BITS];
-      constexpr int PER = 32 / BITS;
-#pragma unroll
-      for (int dw = 0; dw < BITS; ++dw) {
-        uint32_t q[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int t2 = dw * PER + i;
-          q[i] = (t2 < nvt) ? quant_code(zc[t2], cc, gq) : 0x4b000000u;
+          for (int i = 0; i < 32; ++i) if (i < nvt) { a = vmin(a, zc[i]); b = vmax(b, zc[i]); }
         }
-        w[dw] = pack_dword<BITS>(q);
-      }
-      if (ntok > 0 && nvt > 0) {
+        int grp, ntok;
+        if constexpr (G == 64) {
+          a = vmin(a, pair_xchg(a));
+          b = vmax(b, pair_xchg(b));
+          grp = g64; ntok = gg;
+        } else {
+          grp = 2 * g64 + th; ntok = nvt;
+        }
+        const GroupQ gq = group_params<BITS>(a, b, cc);
+        if (gq.bad && nvt > 0) set_status(c.ctl, kStRange);
+        uint32_t w[BITS];
+        constexpr int PER = 32 / BITS;
+#pragma unroll
+        for (int dw = 0; dw < BITS; ++dw) {
+          uint32_t q[PER];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) {
+            const int t2 = dw * PER + i;
+            q[i] = (FULL || t2 < nvt) ? quant_code(zc[t2], cc, gq) : 0x4b000000u;
+          }
+          w[dw] = pack_dword<BITS>(q);
+        }
         int colb;
         const int64_t boff = pc_block(T, G, H, BITS, l, grp, h, colb);
         uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
         const int tok0 = (G == 64) ? 32 * th : 0;        // first token of this thread in its group
         uint8_t* dst = col + tok0 * BITS / 8;
-        if (nvt == 32 && colb == G * BITS / 8) {
+        if (FULL || (nvt == 32 && colb == G * BITS / 8)) {
           if constexpr (BITS == 2) *(uint2*)dst = make_uint2(w[0], w[1]);
           else if constexpr (BITS == 4) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
           else {
             *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
             *(uint4*)(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
           }
-        } else {
+        } else if (ntok > 0 && nvt > 0) {
           // partial group: this thread's codes start at byte tok0 * BITS / 8
           const int nbytes = (nvt * BITS + 7) / 8;
 #pragma unroll
           for (int i = 0; i < 4 * BITS; ++i)
             if (i < nbytes) dst[i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
         }
-      }
-      const bool writer = (G == 64) ? (th == 0) : true;
-      if (writer && ntok > 0) prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch] = gq.packed;
+        const bool writer = (G == 64) ? (th == 0) : true;
+        if (writer && ntok > 0) prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch] = gq.packed;
+      };
+      if (gg == 64) pass(std::true_type{});
+      else pass(std::false_type{});
       __syncthreads();                                   // before the next pass overwrites zb
     }
   }
@@ -729,7 +927,7 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
 template <int BITS, int G, bool BF16>
 __global__ __launch_bounds__(128, 4) void k_decode_channel(CallDesc c, int which) {
   __shared__ __attribute__((aligned(16))) float zb[64 * RP];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const TensorPol pol = which ? c.pol[1] : c.pol[0];
   const float cc = pol.c;
   uint32_t sm[4];

@@ -19,8 +19,8 @@
  * fp16 or bf16 according to the config; every function returns a status code
  * (KVCO_OK = 0) and never reads or writes outside the sizes it is given.
  *
- * Parity status of each function is stated in tests/ and the design doc; every
- * arithmetic function here is pinned by a test that does not re-use it.
+ * Every arithmetic function here is pinned by a test under tests/ that does
+ * not re-use it (test_oracle_*.py).
  */
 #ifndef KVC_ORACLE_H
 #define KVC_ORACLE_H
