@@ -66,6 +66,10 @@ def main():
     ap.add_argument("--workload", default="c3_llama70b_32k")
     ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--values", choices=["gaussian", "zero_rich"], default="gaussian",
+                    help="value model: the workload's Gaussian KV (headline), or KV whose 64-token blocks "
+                         "are zero with probability --zero-frac (exercises compressing chunks)")
+    ap.add_argument("--zero-frac", type=float, default=0.5)
     ap.add_argument("--copy-bytes", type=int, default=1 << 30,
                     help="size of the plain device copy timed as the practical bandwidth reference")
     args = ap.parse_args()
@@ -99,7 +103,10 @@ def main():
     L, T = wl.layers, wl.tokens
     dev = torch.device("cuda:0")
     log(f"generating {wl.name}: {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype} on {dev}")
-    k, v = W.dense_kv(wl, device=dev)
+    if args.values == "gaussian":
+        k, v = W.dense_kv(wl, device=dev)
+    else:
+        k, v = W.zero_rich_kv(wl, L, T, seed=W.SEED_BASE + 7, device=dev, zero_frac=args.zero_frac)
     plan = K.Plan(K.config_from_workload(wl))
     ms, wsb = plan.sizes(T)
     out = torch.empty(ms, dtype=torch.uint8, device=dev)
@@ -183,7 +190,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic",
+        "data": "synthetic" if args.values == "gaussian" else f"synthetic-zero-rich-{args.zero_frac}",
         "config": {"workload": "llama3.1-70b-kv-32k-tokens", "layers": L, "tokens": T, "kv_heads": wl.heads,
                    "head_dim": wl.head_dim, "io_dtype": wl.dtype,
                    "k_policy": f"int{wl.k.bits} per-{wl.k.axis} g{wl.k.group} hadamard",

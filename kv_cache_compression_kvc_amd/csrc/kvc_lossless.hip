@@ -77,9 +77,10 @@ __device__ __forceinline__ uint64_t stream_base(const CallDesc& c, int r, bool e
 __global__ void k_reset(Control* ctl) {
   if (threadIdx.x == 0) {
     ctl->status = 0;
-    ctl->pad0 = 0;     // worklist count
+    ctl->pad0 = 0;     // worklist entries for the word-parallel kernels (from the front)
     ctl->total = 0;
     ctl->pad[0] = 0;   // header-field diagnosis bits
+    ctl->pad[1] = 0;   // worklist entries for the general stage engine (from the back)
   }
 }
 
@@ -268,6 +269,32 @@ __device__ bool stage_inverse(int stage, const uint8_t* in, int in_n, uint8_t* o
   return any_zero == 0;
 }
 
+// ------------------------------------------------------------------ worklist
+
+// Chunks that need the stage engines.  Chunks of the two standard pipelines
+// whose size is a multiple of the kernels' block go to the word-parallel
+// kernels (entries from the front of the list); all others go to the general
+// engine (entries from the back).  The list has one entry per chunk.
+__device__ __forceinline__ uint32_t* generic_count(const CallDesc& c) { return (uint32_t*)&c.ctl->pad[1]; }
+
+__device__ __forceinline__ int fast_pipeline(const CallDesc& c) {
+  if (c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0) return 1;
+  if (c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0) return 2;
+  return 0;
+}
+__device__ __forceinline__ bool fast_eligible(int pipe, int64_t n) {
+  return (pipe == 1 && n % 4096 == 0) || (pipe == 2 && n % 1024 == 0);
+}
+__device__ __forceinline__ void push_work(const CallDesc& c, uint32_t* worklist, int64_t ch, bool fast) {
+  if (fast) {
+    const uint32_t slot = __hip_atomic_fetch_add(&c.ctl->pad0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    worklist[slot] = (uint32_t)ch;
+  } else {
+    const uint32_t k = __hip_atomic_fetch_add(generic_count(c), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    worklist[c.total_chunks - 1 - k] = (uint32_t)ch;
+  }
+}
+
 // ------------------------------------------------------------------ encode: sizes
 
 // Non-zero 2-byte words after TUPL8_1 -> BIT_8 -> RZE_2, for a full chunk of
@@ -306,30 +333,28 @@ __device__ uint32_t nnz_tupl8_rze2(const uint64_t* src, int n, uint32_t* sh32) {
 
 __global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, uint32_t* worklist) {
   __shared__ uint32_t sh32[256];
-  const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
-  const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
+  const int pipe = fast_pipeline(c);
   for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
     const int r = find_req_by_chunk(c, ch);
     const ReqDesc rq = req_at(c, r);
     const ChunkLoc L = locate_chunk(c, rq, r, ch);
     const int n = (int)L.n;
-    bool generic = true;
-    if ((p1 || p2) && n == (int)c.chunk_bytes && (n % 4096) == 0) {
+    bool work = true;
+    const bool fast = fast_eligible(pipe, n);
+    if (fast) {
+      // exact size without the transform; raw chunks are done here
       const uint64_t* src = (const uint64_t*)(c.codes + L.src);
-      const uint32_t nnz = p1 ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
+      const uint32_t nnz = (pipe == 1) ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
       const int64_t size = n / 16 + 2 * (int64_t)nnz;
       if (size >= n) {
         if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
-        generic = false;
+        work = false;
       }
     } else if (c.stages[0] == 0) {
       if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
-      generic = false;
+      work = false;
     }
-    if (generic && threadIdx.x == 0) {
-      const uint32_t slot = __hip_atomic_fetch_add(&c.ctl->pad0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      worklist[slot] = (uint32_t)ch;
-    }
+    if (work && threadIdx.x == 0) push_work(c, worklist, ch, fast);
     __syncthreads();
   }
 }
@@ -338,9 +363,9 @@ __global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uin
   __shared__ __attribute__((aligned(16))) uint8_t bufA[65536];
   __shared__ __attribute__((aligned(16))) uint8_t bufB[65536];
   __shared__ uint32_t sh32[256];
-  const uint32_t count = c.ctl->pad0;
+  const uint32_t count = *generic_count(c);
   for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
-    const int64_t ch = worklist[item];
+    const int64_t ch = worklist[c.total_chunks - 1 - item];
     const int r = find_req_by_chunk(c, ch);
     const ReqDesc rq = req_at(c, r);
     const ChunkLoc L = locate_chunk(c, rq, r, ch);
@@ -365,6 +390,370 @@ __global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uin
   }
 }
 
+
+// ------------------------------------------------------------------ word-parallel kernels
+
+// For the two standard pipelines on chunks of n bytes (P1: TUPL8_1 -> BIT_8 ->
+// RZE_2, n a multiple of 4096; P2: TUPL8_1 -> RZE_2, n a multiple of 1024)
+// the stages reduce to word operations.  With input words w[0 .. n/8) and
+// m = n/8:
+//  P1: the BIT_8 output is, for every gi < n/4096 and kk < 8, the transpose
+//      of the 64x64 bit matrix whose row i is w[512 gi + 8 i + kk]; its row c
+//      is the 8-byte word at byte offset (c/8) m + 512 gi + 64 kk + 8 (c%8).
+//      The RZE_2 words are the four 16-bit quarters of those rows.
+//  P2: the RZE_2 word (j, p), index j m/2 + p, is byte j of w[2p] followed
+//      by byte j of w[2p+1].
+// Every 32 consecutive RZE words share one bitmap dword.  Both kernels build
+// the bitmap, scan its popcounts for the word offsets and write the words.
+
+__device__ __forceinline__ uint32_t rotr32(uint32_t x, uint32_t s) { return __builtin_amdgcn_alignbit(x, x, s); }
+__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
+
+// Lane constants of the 64x64 bit transpose: for the rounds exchanging with
+// lane ^ 16, ^ 8, ^ 4, ^ 2, ^ 1, the bits this lane keeps and the rotation
+// that aligns the partner's bits.
+struct XposeLane {
+  uint32_t mk[5];
+  uint32_t sh[5];
+};
+__device__ __forceinline__ XposeLane xpose_lane() {
+  XposeLane x;
+  const int lane = __lane_id();
+  const uint32_t m[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+#pragma unroll
+  for (int r = 0; r < 5; ++r) {
+    const int j = 16 >> r;
+    const bool lower = (lane & j) == 0;
+    x.mk[r] = lower ? m[r] : ~m[r];
+    x.sh[r] = lower ? (uint32_t)(32 - j) : (uint32_t)j;
+  }
+  return x;
+}
+// partner values: lane ^ 16 and lane ^ 4 through the swizzle unit, lane ^ 8
+// (rotate a 16-lane row by 8), lane ^ 2 and lane ^ 1 (quad permutes) by DPP
+__device__ __forceinline__ uint32_t xchg16(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); }
+__device__ __forceinline__ uint32_t xchg8(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t xchg4(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); }
+__device__ __forceinline__ uint32_t xchg2(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t xchg1(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false); }
+
+// Lane i holds row i of a 64x64 bit matrix (lo: bits 0..31, hi: 32..63);
+// afterwards lane c holds column c.  Each round swaps the off-diagonal
+// blocks of one bit of the row and column index.
+__device__ __forceinline__ void xpose64(uint32_t& lo, uint32_t& hi, const XposeLane& X) {
+  {
+    auto p = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+    lo = p[0];
+    hi = p[1];
+  }
+  uint32_t a, b;
+  a = xchg16(lo); b = xchg16(hi);
+  lo = bfi32(X.mk[0], lo, rotr32(a, X.sh[0])); hi = bfi32(X.mk[0], hi, rotr32(b, X.sh[0]));
+  a = xchg8(lo); b = xchg8(hi);
+  lo = bfi32(X.mk[1], lo, rotr32(a, X.sh[1])); hi = bfi32(X.mk[1], hi, rotr32(b, X.sh[1]));
+  a = xchg4(lo); b = xchg4(hi);
+  lo = bfi32(X.mk[2], lo, rotr32(a, X.sh[2])); hi = bfi32(X.mk[2], hi, rotr32(b, X.sh[2]));
+  a = xchg2(lo); b = xchg2(hi);
+  lo = bfi32(X.mk[3], lo, rotr32(a, X.sh[3])); hi = bfi32(X.mk[3], hi, rotr32(b, X.sh[3]));
+  a = xchg1(lo); b = xchg1(hi);
+  lo = bfi32(X.mk[4], lo, rotr32(a, X.sh[4])); hi = bfi32(X.mk[4], hi, rotr32(b, X.sh[4]));
+}
+
+// bits 0..3: which 16-bit quarters of (lo, hi) are non-zero
+__device__ __forceinline__ uint32_t nz_quarters(uint32_t lo, uint32_t hi) {
+  const uint32_t a = ((lo & 0xFFFFu) != 0u) | ((uint32_t)((lo >> 16) != 0u) << 1);
+  const uint32_t b = ((hi & 0xFFFFu) != 0u) | ((uint32_t)((hi >> 16) != 0u) << 1);
+  return a | (b << 2);
+}
+
+// OR over the 8 lanes of each aligned group of 8
+__device__ __forceinline__ uint32_t or8(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);    // lane ^ 1
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);    // lane ^ 2
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);   // mirror within 8
+  return x;
+}
+
+// Block scan of the popcounts of nd <= 1024 bitmap dwords: offs[d] = number
+// of set bits before dword d; returns the total.  256 threads.
+__device__ __forceinline__ uint32_t scan_bitmap(const uint32_t* bm, uint32_t* offs, int nd, uint32_t* sh32) {
+  const int t = threadIdx.x;
+  uint32_t cnt[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = 4 * t + i;
+    cnt[i] = (d < nd) ? (uint32_t)__builtin_popcount(bm[d]) : 0u;
+    sum += cnt[i];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_scan<uint32_t>(sum, sh32, total);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = 4 * t + i;
+    if (d < nd) offs[d] = run;
+    run += cnt[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// 16-bit store to global memory
+__device__ __forceinline__ void st16(uint8_t* p, uint32_t v) { *(uint16_t*)p = (uint16_t)v; }
+
+__global__ __launch_bounds__(256) void k_ll_encode_p1(CallDesc c, const uint32_t* worklist) {
+  __shared__ __attribute__((aligned(16))) uint64_t pre[8192];   // BIT_8 rows, [gi][kk][c] order
+  __shared__ uint32_t bm[1024];
+  __shared__ uint32_t offs[1024];
+  __shared__ uint32_t sh32[256];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const XposeLane X = xpose_lane();
+  const uint32_t count = c.ctl->pad0;
+  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+    const int64_t ch = worklist[item];
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const int n = (int)L.n;                 // multiple of 4096
+    const int ngi = n / 4096, nd = n / 64, dpj = n / 512;     // bitmap dwords per plane
+    uint8_t* slot = c.codes + L.src;
+    for (int gi = wave; gi < ngi; gi += 4) {
+      const uint4* src = (const uint4*)(slot + (int64_t)gi * 4096 + 64 * lane);
+      uint32_t w[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 x = src[k];
+        w[4 * k] = x.x; w[4 * k + 1] = x.y; w[4 * k + 2] = x.z; w[4 * k + 3] = x.w;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        uint32_t lo = w[2 * kk], hi = w[2 * kk + 1];
+        xpose64(lo, hi, X);
+        pre[(gi * 8 + kk) * 64 + lane] = ((uint64_t)hi << 32) | lo;
+        const uint32_t dw = or8(nz_quarters(lo, hi) << (4 * (lane & 7)));
+        if ((lane & 7) == 0) bm[(lane >> 3) * dpj + 8 * gi + kk] = dw;
+      }
+    }
+    __syncthreads();
+    const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
+    const int size = n / 16 + 2 * (int)nnz;
+    if (size >= n) {
+      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
+    } else {
+      for (int d = threadIdx.x; d < nd; d += blockDim.x) ((uint32_t*)slot)[d] = bm[d];
+      uint8_t* words = slot + n / 16;
+      const uint16_t* pre16 = (const uint16_t*)pre;
+      const int rr = lane & 31;
+      for (int d0 = 2 * wave; d0 < nd; d0 += 8) {
+        const int d = d0 + (lane >> 5);
+        if (d < nd) {
+          const int j = d / dpj, rem = d - j * dpj;
+          const int gi = rem >> 3, kk = rem & 7;
+          const uint32_t bits = bm[d];
+          const uint32_t v = pre16[((gi * 8 + kk) * 64 + 8 * j) * 4 + rr];
+          if ((bits >> rr) & 1u) {
+            const uint32_t pos = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u));
+            st16(words + 2 * pos, v);
+          }
+        }
+      }
+      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_ll_encode_p2(CallDesc c, const uint32_t* worklist) {
+  __shared__ __attribute__((aligned(16))) uint4 buf[4096];     // the chunk, one input word pair per entry
+  __shared__ uint32_t bm[1024];
+  __shared__ uint32_t offs[1024];
+  __shared__ uint32_t sh32[256];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint32_t count = c.ctl->pad0;
+  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+    const int64_t ch = worklist[item];
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const int n = (int)L.n;                 // multiple of 1024
+    const int np = n / 16, nblk = np / 64, nd = n / 64, dpj = n / 512;
+    uint8_t* slot = c.codes + L.src;
+    for (int blk = wave; blk < nblk; blk += 4) {
+      const int p = 64 * blk + lane;
+      const uint4 x = ((const uint4*)slot)[p];
+      buf[p] = x;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t a = (j < 4) ? x.x : x.y, b = (j < 4) ? x.z : x.w;
+        const uint32_t jj = (uint32_t)(j & 3);
+        const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
+        const uint64_t m = __ballot(word != 0u);
+        if (lane == 0) {
+          bm[j * dpj + 2 * blk] = (uint32_t)m;
+          bm[j * dpj + 2 * blk + 1] = (uint32_t)(m >> 32);
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
+    const int size = n / 16 + 2 * (int)nnz;
+    if (size >= n) {
+      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
+    } else {
+      for (int d = threadIdx.x; d < nd; d += blockDim.x) ((uint32_t*)slot)[d] = bm[d];
+      uint8_t* words = slot + n / 16;
+      const int rr = lane & 31;
+      for (int blk = wave; blk < nblk; blk += 4) {
+        const int p = 64 * blk + lane;
+        const uint4 x = buf[p];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t a = (j < 4) ? x.x : x.y, b = (j < 4) ? x.z : x.w;
+          const uint32_t jj = (uint32_t)(j & 3);
+          const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
+          const int d = j * dpj + 2 * blk + (lane >> 5);
+          const uint32_t bits = bm[d];
+          if ((bits >> rr) & 1u) {
+            const uint32_t pos = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u));
+            st16(words + 2 * pos, word);
+          }
+        }
+      }
+      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
+    }
+    __syncthreads();
+  }
+}
+
+// Stage a compressed chunk into LDS and check that its bitmap accounts for
+// its length.  Returns false (and flags the stream) if not.
+__device__ __forceinline__ bool load_compressed(const CallDesc& c, uint64_t pos, int stored, int n, uint4* buf,
+                                                uint32_t* offs, uint32_t* sh32, uint32_t& nnz) {
+  const uint64_t avail = (c.stream_bytes > pos) ? c.stream_bytes - pos : 0;
+  const int nv = (stored + 15) / 16;
+  const uint4* src = (const uint4*)(c.stream + pos);
+  for (int k = threadIdx.x; k < nv; k += blockDim.x) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if ((uint64_t)(16 * k + 16) <= avail) x = src[k];
+    buf[k] = x;
+  }
+  __syncthreads();
+  // bytes of the last 16-byte line past the stored length are ignored
+  if (stored < n / 16) return false;
+  nnz = scan_bitmap((const uint32_t*)buf, offs, n / 64, sh32);
+  return n / 16 + 2 * (int)nnz == stored && (uint64_t)(16 * nv) <= avail + 15;
+}
+
+__global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
+  __shared__ __attribute__((aligned(16))) uint4 buf[4096];
+  __shared__ uint32_t offs[1024];
+  __shared__ uint32_t sh32[256];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const XposeLane X = xpose_lane();
+  const uint32_t count = c.ctl->pad0;
+  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+    const int64_t ch = worklist[item];
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const int n = (int)L.n;
+    const int stored = (int)(c.chunk_sizes[ch] & 0x7fffffffu);
+    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+    const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+    uint32_t nnz = 0;
+    const bool ok = load_compressed(c, pos, stored, n, buf, offs, sh32, nnz);
+    if (!ok) {
+      if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+      __syncthreads();
+      continue;
+    }
+    const uint32_t* bm = (const uint32_t*)buf;
+    const uint16_t* words = (const uint16_t*)buf + n / 32;
+    const int ngi = n / 4096, dpj = n / 512;
+    const int j = lane >> 3, bb = lane & 7;
+    uint32_t bad = 0;
+    for (int gi = wave; gi < ngi; gi += 4) {
+      uint32_t w[16];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int d = j * dpj + 8 * gi + kk;
+        const uint32_t bits = bm[d];
+        const uint32_t nib = (bits >> (4 * bb)) & 15u;
+        const uint32_t r0 = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << (4 * bb)) - 1u));
+        uint32_t q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t rk = r0 + (uint32_t)__builtin_popcount(nib & ((1u << u) - 1u));
+          const uint32_t v = ((nib >> u) & 1u) ? (uint32_t)words[min(rk, nnz - 1u)] : 0u;
+          bad |= ((nib >> u) & 1u) & (uint32_t)(v == 0u);
+          q[u] = v;
+        }
+        uint32_t lo = q[0] | (q[1] << 16), hi = q[2] | (q[3] << 16);
+        xpose64(lo, hi, X);
+        w[2 * kk] = lo;
+        w[2 * kk + 1] = hi;
+      }
+      uint4* dst = (uint4*)(c.codes + L.src + (int64_t)gi * 4096 + 64 * lane);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+    }
+    // a set bitmap bit must mark a non-zero word
+    if (__syncthreads_or((int)bad) && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t* worklist) {
+  __shared__ __attribute__((aligned(16))) uint4 buf[4096];
+  __shared__ uint32_t offs[1024];
+  __shared__ uint32_t sh32[256];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const uint32_t count = c.ctl->pad0;
+  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+    const int64_t ch = worklist[item];
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const int n = (int)L.n;
+    const int stored = (int)(c.chunk_sizes[ch] & 0x7fffffffu);
+    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+    const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+    uint32_t nnz = 0;
+    const bool ok = load_compressed(c, pos, stored, n, buf, offs, sh32, nnz);
+    if (!ok) {
+      if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+      __syncthreads();
+      continue;
+    }
+    const uint32_t* bm = (const uint32_t*)buf;
+    const uint16_t* words = (const uint16_t*)buf + n / 32;
+    const int nblk = n / 1024, dpj = n / 512;
+    const int rr = lane & 31;
+    uint32_t bad = 0;
+    for (int blk = wave; blk < nblk; blk += 4) {
+      uint32_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = j * dpj + 2 * blk + (lane >> 5);
+        const uint32_t bits = bm[d];
+        const uint32_t set = (bits >> rr) & 1u;
+        const uint32_t rk = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u));
+        const uint32_t x = set ? (uint32_t)words[min(rk, nnz - 1u)] : 0u;
+        bad |= set & (uint32_t)(x == 0u);
+        v[j] = x;
+      }
+      // byte j of w[2p] is the low byte of word j, byte j of w[2p+1] its high byte
+      const uint32_t p01 = v[0] | (v[1] << 16), p23 = v[2] | (v[3] << 16);
+      const uint32_t p45 = v[4] | (v[5] << 16), p67 = v[6] | (v[7] << 16);
+      uint4 x;
+      x.x = __builtin_amdgcn_perm(p23, p01, 0x06040200u);
+      x.y = __builtin_amdgcn_perm(p67, p45, 0x06040200u);
+      x.z = __builtin_amdgcn_perm(p23, p01, 0x07050301u);
+      x.w = __builtin_amdgcn_perm(p67, p45, 0x07050301u);
+      ((uint4*)(c.codes + L.src))[64 * blk + lane] = x;
+    }
+    if (__syncthreads_or((int)bad) && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+  }
+}
+
 hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
   if (c.total_chunks == 0) return hipSuccess;
   uint32_t* worklist = (uint32_t*)(c.chunk_offs + c.total_chunks + 1);
@@ -372,6 +761,12 @@ hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
   k_ll_sizes<<<grid, 256, 0, s>>>(c, worklist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
+  const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
+  const int fgrid = (int)std::min<int64_t>(c.total_chunks, 512);
+  if (p1) k_ll_encode_p1<<<fgrid, 256, 0, s>>>(c, worklist);
+  else if (p2) k_ll_encode_p2<<<fgrid, 256, 0, s>>>(c, worklist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   k_ll_encode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
   return hipGetLastError();
 }
@@ -634,8 +1029,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
       for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) dst[k] = src[k];
       for (int64_t p = nv * 16 + threadIdx.x; p < L.n; p += blockDim.x) c.codes[L.src + p] = c.stream[pos + p];
     } else if (threadIdx.x == 0) {
-      const uint32_t slot = __hip_atomic_fetch_add(&c.ctl->pad0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      worklist[slot] = (uint32_t)ch;
+      push_work(c, worklist, ch, fast_eligible(fast_pipeline(c), L.n));
     }
   }
 }
@@ -645,9 +1039,9 @@ __global__ __launch_bounds__(256) void k_ll_decode_generic(CallDesc c, const uin
   __shared__ __attribute__((aligned(16))) uint8_t bufB[65536];
   __shared__ uint32_t sh32[256];
   __shared__ uint64_t sh64[256];
-  const uint32_t count = c.ctl->pad0;
+  const uint32_t count = *generic_count(c);
   for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
-    const int64_t ch = worklist[item];
+    const int64_t ch = worklist[c.total_chunks - 1 - item];
     const int r = find_req_by_chunk(c, ch);
     const ReqDesc rq = req_at(c, r);
     const ChunkLoc L = locate_chunk(c, rq, r, ch);
@@ -685,6 +1079,12 @@ hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s) {
   k_ll_decode_raw<<<grid, 256, 0, s>>>(c, worklist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
+  const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
+  const int fgrid = (int)std::min<int64_t>(c.total_chunks, 512);
+  if (p1) k_ll_decode_p1<<<fgrid, 256, 0, s>>>(c, worklist);
+  else if (p2) k_ll_decode_p2<<<fgrid, 256, 0, s>>>(c, worklist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   k_ll_decode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
   return hipGetLastError();
 }

@@ -100,6 +100,17 @@ def split_stream(stream: np.ndarray, wl, L, T):
     return codes, params
 
 
+def chunk_kinds(stream: np.ndarray, wl, L, T):
+    """(raw, compressed) chunk counts of a stream, from its chunk table."""
+    cfg = O.cfg_from_workload(wl, layers=L)
+    import ctypes as C
+    codes_b = [O.lib().kvco_codes_bytes(C.byref(cfg), w, T) for w in range(2)]
+    nch = sum(-(-c // wl.chunk_bytes) for c in codes_b)
+    table = np.frombuffer(stream.tobytes(), np.uint32, nch, 64)
+    raw = int((table >> 31).sum())
+    return raw, nch - raw
+
+
 def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
     per = 8 // bits
     sh = np.arange(per, dtype=np.uint8) * bits

@@ -13,7 +13,7 @@ import torch
 
 import kvc_workloads as W
 import oracle_api as O
-from gpu_helpers import (DEV, assert_encode_parity, assert_values_close, compare_encode, gpu_decode, gpu_encode,
+from gpu_helpers import (DEV, assert_encode_parity, assert_values_close, chunk_kinds, compare_encode, gpu_decode, gpu_encode,
                          log, oracle_encode, to_u16)
 import kv_cache_compression_kvc_amd as K
 
@@ -22,10 +22,10 @@ pytestmark = pytest.mark.gpu
 TP = W.TensorPolicy
 
 
-def run_case(wl, L, T, seed=1, zero_rich=False, check_decode=True):
+def run_case(wl, L, T, seed=1, zero_rich=False, check_decode=True, zero_frac=0.9):
     log(f"case {wl.name} L={L} T={T} k={wl.k} v={wl.v} stages={wl.stages} cb={wl.chunk_bytes} zero_rich={zero_rich}")
     if zero_rich:
-        k, v = W.zero_rich_kv(wl, L, T, seed=seed)
+        k, v = W.zero_rich_kv(wl, L, T, seed=seed, zero_frac=zero_frac)
     else:
         k, v = W.dense_kv(wl, layers=L, tokens=T, seed=seed)
     ku, vu = to_u16(k), to_u16(v)
@@ -33,6 +33,7 @@ def run_case(wl, L, T, seed=1, zero_rich=False, check_decode=True):
     assert st == O.OK
     plan, got, ws = gpu_encode(wl, k.to(DEV), v.to(DEV), T, L)
     stats = compare_encode(got, ref, wl, L, T)
+    stats["chunks_raw"], stats["chunks_compressed"] = chunk_kinds(ref, wl, L, T)
     log(f"  encode: {stats}")
     assert_encode_parity(stats)
     if check_decode:
@@ -100,6 +101,18 @@ def test_zero_rich_inputs_compress(stages):
     wl = C3.with_(stages=stages, chunk_bytes=8192, name="zero_rich")
     s = run_case(wl, 2, 512, zero_rich=True)
     assert s["identical"]
+
+
+@pytest.mark.parametrize("stages", [("TUPL8_1", "BIT_8", "RZE_2"), ("TUPL8_1", "RZE_2")])
+@pytest.mark.parametrize("T", [528, 516])
+def test_word_parallel_lossless_full_chunks(stages, T):
+    # 64 KiB chunks, half of the 64-token blocks zero: most chunks compress and
+    # go through the word-parallel kernels; T = 528 leaves partial last chunks
+    # whose size is a multiple of 4096 bytes, T = 516 one that is not
+    wl = C3.with_(stages=stages, chunk_bytes=65536, name="word_parallel")
+    s = run_case(wl, 2, T, zero_rich=True, zero_frac=0.5, seed=3)
+    assert s["identical"]
+    assert s["chunks_compressed"] >= 8, s
 
 
 def test_range_error_is_reported():
