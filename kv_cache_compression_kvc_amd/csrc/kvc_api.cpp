@@ -86,6 +86,33 @@ int64_t tiles_of(const TensorPol& p, int L, int T, int H, bool paged) {
   return (int64_t)L * cdiv(T, 64) * H;
 }
 
+// Whether every reconstruct tile's codes of a dense call lie inside one chunk
+// (then raw chunks can be read straight from the stream): per-token tiles
+// are 32 vectors at multiples of their size; per-channel tiles read blocks of
+// 128 columns of one token group, uniform in size only when no group is partial.
+bool tiles_within_chunks(const TensorPol& p, int T, uint32_t chunk_bytes) {
+  if (p.axis == 0) return chunk_bytes % (32 * kHeadDim * p.bits / 8) == 0;
+  if (T % p.group) return false;
+  return chunk_bytes % (kHeadDim * p.group * p.bits / 8) == 0;
+}
+
+// The two lossless pipelines with word-parallel kernels: 1 = TUPL8_1 -> BIT_8 ->
+// RZE_2, 2 = TUPL8_1 -> RZE_2, 0 = other.
+int lossless_pipe(const uint8_t* st) {
+  if (st[0] == KVC_TUPL8_1 && st[1] == KVC_BIT_8 && st[2] == KVC_RZE_2 && st[3] == 0) return 1;
+  if (st[0] == KVC_TUPL8_1 && st[1] == KVC_RZE_2 && st[2] == 0) return 2;
+  return 0;
+}
+
+// Whether the fused encoders of a dense call can count a section's non-zero
+// RZE words: every wave's codes must cover whole aligned 1 KiB regions of one
+// chunk.  Per-token tiles always do; per-channel kernels count groups of 64
+// tokens of 4 or 8 bits when no group is partial.
+bool fused_count_ok(const TensorPol& p, int T, uint32_t chunk_bytes) {
+  if (p.axis == 0) return true;
+  return p.group == 64 && p.bits >= 4 && T % 64 == 0 && chunk_bytes % (kHeadDim * 64 * p.bits / 8) == 0;
+}
+
 // Fill the stream layout of one request with T tokens (offsets inside its stream).
 void request_layout(const kvc_plan_s* p, int T, ReqDesc& rq) {
   const kvc_config& c = p->cfg;
@@ -396,7 +423,11 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   c.R = 1;
   request_layout(p, tokens, c.one);
   const int64_t codes_area = a256(c.one.codes_bytes[0]) + a256(c.one.codes_bytes[1]);
-  c.one.codes_off[1] = a256(c.one.codes_bytes[0]);
+  // The fused kernels write the codes where a stream whose chunks are all raw
+  // keeps them (K codes at the payload start, V codes 16-byte aligned after
+  // them); compressed chunks and raw chunks that must move go through the
+  // workspace codes area, which uses the same offsets.
+  c.one.codes_off[1] = a16(c.one.codes_bytes[0]);
   const WsLayout w = ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1);
   if ((int64_t)out_capacity < c.one.max_stream)
     return fail(KVC_ERR_BUFFER_TOO_SMALL, "out_capacity %zu < %lld", out_capacity, (long long)c.one.max_stream);
@@ -404,13 +435,16 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   uint8_t* ws = (uint8_t*)d_ws;
   c.in_kv[0] = d_k;
   c.in_kv[1] = d_v;
-  c.codes = ws + w.codes;
+  c.codes = (uint8_t*)d_out + c.one.payload_off;
+  c.codes_out = ws + w.codes;
   c.stream = (uint8_t*)d_out;
   c.chunk_sizes = (uint32_t*)(ws + w.sizes);
   c.chunk_offs = (uint64_t*)(ws + w.offs);
   c.ctl = (Control*)(ws + w.ctl);
   c.total_chunks = c.one.nchunks[0] + c.one.nchunks[1];
   for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads, false);
+  c.nnz_pipe = lossless_pipe(p->cfg.lossless);
+  for (int k = 0; k < 2; ++k) c.nnz_sec[k] = (c.nnz_pipe && fused_count_ok(p->pol[k], tokens, p->cfg.chunk_bytes)) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
@@ -418,6 +452,7 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return launch_encode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "encode V");
   if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
+  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_stash(c, s); })) != hipSuccess) return hip_fail(e, "stash");
   if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_compact(c, s); })) != hipSuccess) return hip_fail(e, "compact");
   if (h_out_bytes) {
     Control h;
@@ -454,6 +489,8 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
   c.out_kv[0] = d_k;
   c.out_kv[1] = d_v;
   c.codes = ws + w.codes;
+  c.codes_out = c.codes;
+  for (int k = 0; k < 2; ++k) c.direct[k] = tiles_within_chunks(p->pol[k], tokens, p->cfg.chunk_bytes) ? 1 : 0;
   c.stream = (uint8_t*)const_cast<void*>(d_in);
   c.stream_bytes = in_bytes;
   c.chunk_sizes = (uint32_t*)(ws + w.sizes);
@@ -520,6 +557,7 @@ kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_
   c.in_kv[0] = d_k_pool;
   c.in_kv[1] = d_v_pool;
   c.codes = ws + w.codes;
+  c.codes_out = c.codes;
   c.params_ws = ws + w.params;
   c.stream = (uint8_t*)d_out;
   c.req_offsets_out = d_req_offsets;
@@ -577,6 +615,7 @@ kvc_status kvc_decode_paged(kvc_plan_t p, const void* d_in, size_t in_bytes, con
   c.out_kv[0] = d_k_pool;
   c.out_kv[1] = d_v_pool;
   c.codes = ws + w.codes;
+  c.codes_out = c.codes;
   c.stream = (uint8_t*)const_cast<void*>(d_in);
   c.stream_bytes = in_bytes;
   c.req_offsets = d_req_offsets;

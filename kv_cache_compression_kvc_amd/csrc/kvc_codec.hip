@@ -59,13 +59,13 @@ typedef int int2v __attribute__((ext_vector_type(2)));
 // Cache policy bits of the streaming buffer accesses (2 = non-temporal).
 // Every input and output byte of these kernels is touched once.
 #ifndef KVC_LOAD_POLICY
-#define KVC_LOAD_POLICY 2
+#define KVC_LOAD_POLICY 0
 #endif
 #ifndef KVC_STORE_POLICY
 #define KVC_STORE_POLICY 2
 #endif
 #ifndef KVC_NARROW_STORE_POLICY
-#define KVC_NARROW_STORE_POLICY 2
+#define KVC_NARROW_STORE_POLICY 0
 #endif
 constexpr int kLoadPol = KVC_LOAD_POLICY;
 constexpr int kStorePol = KVC_STORE_POLICY;          // 16-byte stores
@@ -461,6 +461,58 @@ __device__ __forceinline__ void stage_out(const float* f, uint32_t* wl, const ui
   wave_sync();
 }
 
+
+// ------------------------------------------------------------------
+// Lossless size contribution of freshly packed codes.  For TUPL8_1 -> BIT_8
+// -> RZE_2 the non-zero RZE words of a chunk number, over its aligned
+// 1 KiB regions (128 words) and the 8 residues kk of the word index mod 8,
+// the sum of popcount(OR of the region's 16 words of residue kk); for
+// TUPL8_1 -> RZE_2, the non-zero bytes of the OR of the two words of each
+// aligned 16-byte unit.  Both are sums of terms local to aligned pieces, so
+// a wave adds the terms of the codes it wrote to the chunk's counter.
+// ------------------------------------------------------------------
+// value of lane ^ K (K < 32)
+template <int K>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (K == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (K == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (K == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);
+  else return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (K << 10));
+}
+template <int K>
+__device__ __forceinline__ uint64_t or_lane_xor(uint64_t x) {
+  const uint32_t lo = lane_xor<K>((uint32_t)x), hi = lane_xor<K>((uint32_t)(x >> 32));
+  return x | (((uint64_t)hi << 32) | lo);
+}
+// OR over the lanes that differ only in lane-index bits LO .. HI-1 (HI <= 5)
+template <int LO, int HI>
+__device__ __forceinline__ uint64_t or_lane_bits(uint64_t x) {
+  if constexpr (LO <= 0 && 0 < HI) x = or_lane_xor<1>(x);
+  if constexpr (LO <= 1 && 1 < HI) x = or_lane_xor<2>(x);
+  if constexpr (LO <= 2 && 2 < HI) x = or_lane_xor<4>(x);
+  if constexpr (LO <= 3 && 3 < HI) x = or_lane_xor<8>(x);
+  if constexpr (LO <= 4 && 4 < HI) x = or_lane_xor<16>(x);
+  return x;
+}
+__device__ __forceinline__ uint32_t popc64(uint64_t x) { return (uint32_t)__builtin_popcountll(x); }
+// non-zero bytes of a 64-bit word
+__device__ __forceinline__ uint32_t nz_bytes64(uint64_t x) {
+  const uint32_t a = (uint32_t)x, b = (uint32_t)(x >> 32);
+  const uint32_t za = ~(((a & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | a | 0x7F7F7F7Fu);   // 0x80 in each zero byte
+  const uint32_t zb = ~(((b & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | b | 0x7F7F7F7Fu);
+  return 8u - (uint32_t)__builtin_popcount(za) - (uint32_t)__builtin_popcount(zb);
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
+  return v;
+}
+__device__ __forceinline__ void add_chunk_nnz(const CallDesc& c, int64_t gci, uint32_t v) {
+  const uint32_t t = wave_sum(v);
+  if (__lane_id() == 0 && t) __hip_atomic_fetch_add(&c.chunk_sizes[gci], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t u64of(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
+
 // ------------------------------------------------------------------
 // Tile loads straight into LDS.  A wavefront's tile is 32 head vectors of 256
 // bytes; the 16-byte loads of one instruction land in LDS at consecutive
@@ -613,8 +665,8 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
   // vector memory operations issued after a tile's loads: the code stores
   // (one per half, two for 8-bit codes) and the parameter stores; all are
   // unconditional so the count is exact
-  constexpr int NPST = (G <= 32) ? NLG : 1;
-  constexpr int NST = 2 * ((BITS == 8) ? 2 : 1) + NPST;
+  constexpr int NPST = 1;
+  constexpr int NST = ((BITS == 2) ? 1 : (BITS == 4) ? 2 : 4) + NPST;
 
   const int64_t stride = (int64_t)gridDim.x * 4;
   int64_t tile = (int64_t)blockIdx.x * 4 + wave;
@@ -661,9 +713,9 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
     }
 
     const __amdgpu_buffer_rsrc_t crs = make_rsrc(t.codes_base + t.vg0 * CB, (uint32_t)t.nv * CB);
+    uint32_t wv[2][BITS];                                         // packed codes of register halves 0, 1
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      uint32_t w[BITS];
       constexpr int PER = 32 / BITS;                              // codes per dword
 #pragma unroll
       for (int dw = 0; dw < BITS; ++dw) {
@@ -673,24 +725,97 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
           const int r2 = 32 * half + dw * PER + i;
           q[i] = quant_code(f[r2], cc, gq[r2 / LG]);
         }
-        w[dw] = pack_dword<BITS>(q);
+        wv[half][dw] = pack_dword<BITS>(q);
       }
-      const uint32_t off = (uint32_t)v * CB + (64 * half + 32 * hf) * BITS / 8;
-      if constexpr (BITS == 2) bstore8(make_uint2(w[0], w[1]), crs, off, 0);
-      else if constexpr (BITS == 4) bstore16(make_uint4(w[0], w[1], w[2], w[3]), crs, off, 0);
-      else {
-        bstore16(make_uint4(w[0], w[1], w[2], w[3]), crs, off, 0);
-        bstore16(make_uint4(w[4], w[5], w[6], w[7]), crs, off + 16, 0);
+    }
+    if constexpr (BITS == 2) {
+      // lane half hf holds the 8-byte code runs of channels [32 hf, 32 hf + 32)
+      // and [64 + 32 hf, ...); swapping the second run of the lower lane with the
+      // first run of the upper lane gives each lane 16 contiguous bytes
+#pragma unroll
+      for (int dw = 0; dw < 2; ++dw) {
+        auto p = __builtin_amdgcn_permlane32_swap(wv[0][dw], wv[1][dw], false, false);
+        wv[0][dw] = p[0];
+        wv[1][dw] = p[1];
       }
+      bstore16(make_uint4(wv[0][0], wv[0][1], wv[1][0], wv[1][1]), crs, (uint32_t)v * CB + 16 * hf, 0);
+    } else {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t off = (uint32_t)v * CB + (64 * half + 32 * hf) * BITS / 8;
+        if constexpr (BITS == 4) bstore16(make_uint4(wv[half][0], wv[half][1], wv[half][2], wv[half][3]), crs, off, 0);
+        else {
+          bstore16(make_uint4(wv[half][0], wv[half][1], wv[half][2], wv[half][3]), crs, off, 0);
+          bstore16(make_uint4(wv[half][4], wv[half][5], wv[half][6], wv[half][7]), crs, off + 16, 0);
+        }
+      }
+    }
+    if (c.nnz_pipe && c.nnz_sec[which]) {
+      // wv[h][*]: this lane's codes of register half h (for 2 bits, after the
+      // swap, the lane's 16 contiguous bytes are wv[0][0..1], wv[1][0..1])
+      uint32_t cnt = 0;
+      const bool live = v < t.nv;
+      if (c.nnz_pipe == 1) {
+        if constexpr (BITS == 2) {
+          // words 4v + 2hf, +1 of a 1 KiB region: residues 4 (v & 1) + 2 hf, +1;
+          // the same residue recurs in lanes differing in v bits 1..4
+          uint64_t x0 = live ? u64of(wv[0][0], wv[0][1]) : 0ull, x1 = live ? u64of(wv[1][0], wv[1][1]) : 0ull;
+          x0 = or_lane_bits<1, 5>(x0); x1 = or_lane_bits<1, 5>(x1);
+          cnt = ((v >> 1) == 0) ? popc64(x0) + popc64(x1) : 0u;
+        } else if constexpr (BITS == 4) {
+          // words 8v + 4h + 2hf, +1: residues 4h + 2hf, +1; regions of 16 vectors
+          uint64_t x[4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            x[2 * h] = live ? u64of(wv[h][0], wv[h][1]) : 0ull;
+            x[2 * h + 1] = live ? u64of(wv[h][2], wv[h][3]) : 0ull;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = or_lane_bits<0, 4>(x[i]);
+          cnt = ((v & 15) == 0) ? popc64(x[0]) + popc64(x[1]) + popc64(x[2]) + popc64(x[3]) : 0u;
+        } else {
+          // words 16v + 8h + 4hf + m: residues 4hf + m (both halves); regions of 8 vectors
+          uint64_t x[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            x[m] = live ? (u64of(wv[0][2 * m], wv[0][2 * m + 1]) | u64of(wv[1][2 * m], wv[1][2 * m + 1])) : 0ull;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) x[m] = or_lane_bits<0, 3>(x[m]);
+          cnt = ((v & 7) == 0) ? popc64(x[0]) + popc64(x[1]) + popc64(x[2]) + popc64(x[3]) : 0u;
+        }
+      } else if (live) {
+        if constexpr (BITS == 2) {
+          cnt = nz_bytes64(u64of(wv[0][0], wv[0][1]) | u64of(wv[1][0], wv[1][1]));
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int u = 0; u < BITS / 4; ++u)
+              cnt += nz_bytes64(u64of(wv[h][4 * u], wv[h][4 * u + 1]) | u64of(wv[h][4 * u + 2], wv[h][4 * u + 3]));
+        }
+      }
+      int64_t cbase;
+      if constexpr (PAGED) {
+        const int r = find_req_by_tile(c, which, tile);
+        const ReqDesc rq = load_req(c, r);
+        cbase = rq.chunk_begin + (which ? rq.nchunks[0] : 0);
+      } else {
+        cbase = which ? c.one.nchunks[0] : 0;
+      }
+      add_chunk_nnz(c, cbase + (t.vg0 * CB) / c.chunk_bytes, cnt);
     }
     const __amdgpu_buffer_rsrc_t prs = make_rsrc(t.params_base + t.vg0 * NGV * 4, (uint32_t)t.nv * NGV * 4);
     const uint32_t prow = (uint32_t)v * NGV * 4;
-    if constexpr (G <= 32) {
-#pragma unroll
-      for (int j = 0; j < NLG; ++j) {
-        const int ch0 = (j * LG < 32) ? 32 * hf + j * LG : 64 + 32 * hf + (j * LG - 32);
-        bstore4(gq[j].packed, prs, prow + (ch0 / G) * 4, 0);
-      }
+    if constexpr (G == 32) {
+      // groups 2 hf and 2 + hf; after the swap the lower lane holds groups 0, 1
+      // and the upper lane groups 2, 3
+      auto p = __builtin_amdgcn_permlane32_swap(gq[0].packed, gq[1].packed, false, false);
+      bstore8(make_uint2(p[0], p[1]), prs, prow + 8 * hf, 0);
+    } else if constexpr (G == 16) {
+      // groups {2 hf, 2 hf + 1} and {4 + 2 hf, 5 + 2 hf}, swapped the same way
+      auto p0 = __builtin_amdgcn_permlane32_swap(gq[0].packed, gq[2].packed, false, false);
+      auto p1 = __builtin_amdgcn_permlane32_swap(gq[1].packed, gq[3].packed, false, false);
+      bstore16(make_uint4(p0[0], p1[0], p0[1], p1[1]), prs, prow + 16 * hf, 0);
     } else if constexpr (G == 64) {
       bstore4(hf ? gq[1].packed : gq[0].packed, prs, prow + hf * 4, 0);
     } else {
@@ -726,14 +851,28 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
   for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += stride) {
     int64_t vg0;
     int nv, nvo;
-    const uint8_t* codes_base;
+    const uint8_t* csrc;       // the tile's codes
+    uint32_t cbytes;           // bytes readable there
     const uint8_t* params_base;
     uint16_t* dst;
     if constexpr (!PAGED) {
       vg0 = tile * 32;
       nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec_dense - vg0));
       nvo = nv;
-      codes_base = c.codes + pick(which, c.one.codes_off);
+      const int64_t coff = vg0 * CB;
+      csrc = c.codes + pick(which, c.one.codes_off) + coff;
+      cbytes = (uint32_t)nv * CB;
+      if (c.direct[which]) {
+        // a tile never straddles chunks here; a raw chunk is read in place
+        const int64_t ci = coff / c.chunk_bytes;
+        const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
+        const uint32_t e = c.chunk_sizes[gci];
+        if (e >> 31) {
+          const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] + (uint64_t)(coff - ci * c.chunk_bytes);
+          csrc = c.stream + pos;
+          cbytes = (pos >= c.stream_bytes) ? 0u : (uint32_t)std::min<uint64_t>(cbytes, c.stream_bytes - pos);
+        }
+      }
       params_base = c.stream + pick(which, c.one.params_off);
       dst = out + vg0 * kHeadDim;
     } else {
@@ -751,7 +890,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
       const bool pok =
           off + (uint64_t)pick(which, rq.params_off) + (uint64_t)pick(which, rq.params_bytes) <= c.stream_bytes;
       if (!pok) { if (lane == 0) set_status(c.ctl, kStCorrupt); nv = 0; }
-      codes_base = c.codes + pick(which, rq.codes_off);
+      csrc = c.codes + pick(which, rq.codes_off) + vg0 * CB;
+      cbytes = (uint32_t)nv * CB;
       params_base = c.stream + (pok ? off : 0) + pick(which, rq.params_off);
       bool ok;
       const int64_t base = page_run_base(c, rq, l, vstart, ok);
@@ -761,7 +901,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
     }
 
     // codes of channels [64 hf, 64 hf + 64) and their group parameters
-    const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes_base + vg0 * CB, (uint32_t)nv * CB);
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(csrc, cbytes);
     const uint32_t coff = (uint32_t)v * CB + 64 * hf * BITS / 8;
     uint32_t w[4 * ((2 * BITS + 3) / 4)];
 #pragma unroll
@@ -916,6 +1056,33 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
         }
         const bool writer = (G == 64) ? (th == 0) : true;
         if (writer && ntok > 0) prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch] = gq.packed;
+        if constexpr (G == 64 && FULL && BITS >= 4) {
+          if (c.nnz_pipe && c.nnz_sec[which]) {
+            // this thread's codes: 4 * BITS bytes at ch * 8 BITS + th * 4 BITS of
+            // the group block, i.e. words (4 BITS ch + 2 BITS th) / 4 + m
+            const int cl = lane & 31;
+            uint32_t cnt = 0;
+            if (c.nnz_pipe == 1) {
+              if constexpr (BITS == 4) {
+                // residues 4 (ch & 1) + 2 th, +1; a 1 KiB region is this wave's 32 channels
+                uint64_t x0 = u64of(w[0], w[1]), x1 = u64of(w[2], w[3]);
+                x0 = or_lane_bits<1, 5>(x0); x1 = or_lane_bits<1, 5>(x1);
+                cnt = ((cl >> 1) == 0) ? popc64(x0) + popc64(x1) : 0u;
+              } else {
+                // residues 4 th + m; regions of 16 channels
+                uint64_t x[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) x[m] = or_lane_bits<0, 4>(u64of(w[2 * m], w[2 * m + 1]));
+                cnt = ((cl & 15) == 0) ? popc64(x[0]) + popc64(x[1]) + popc64(x[2]) + popc64(x[3]) : 0u;
+              }
+            } else {
+#pragma unroll
+              for (int u = 0; u < BITS / 4; ++u)
+                cnt += nz_bytes64(u64of(w[4 * u], w[4 * u + 1]) | u64of(w[4 * u + 2], w[4 * u + 3]));
+            }
+            add_chunk_nnz(c, (which ? (int64_t)c.one.nchunks[0] : 0) + boff / c.chunk_bytes, cnt);
+          }
+        }
       };
       if (gg == 64) pass(std::true_type{});
       else pass(std::false_type{});
@@ -970,9 +1137,24 @@ __global__ __launch_bounds__(128, 4) void k_decode_channel(CallDesc c, int which
         int colb;
         const int64_t boff = pc_block(T, G, H, BITS, l, grp, h, colb);
         const uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
+        bool have = true;
+        if (c.direct[which]) {
+          // a group block never straddles chunks here; a raw chunk is read in place
+          const int64_t ci = boff / c.chunk_bytes;
+          const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
+          const uint32_t e = c.chunk_sizes[gci];
+          if (e >> 31) {
+            const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] +
+                                 (uint64_t)(boff - ci * c.chunk_bytes) + (uint64_t)ch * colb;
+            have = pos + (uint64_t)colb <= c.stream_bytes;
+            col = c.stream + pos;
+          }
+        }
         const int tok0 = (G == 64) ? 32 * th : 0;
         const uint8_t* s = col + tok0 * BITS / 8;
-        if (nvt == 32 && colb == G * BITS / 8) {
+        if (!have) {
+          // past the end of a damaged stream (already flagged): zero codes
+        } else if (nvt == 32 && colb == G * BITS / 8) {
           if constexpr (BITS == 2) { const uint2 x = *(const uint2*)s; w[0] = x.x; w[1] = x.y; }
           else {
 #pragma unroll

@@ -77,7 +77,12 @@ struct CallDesc {
   // buffers
   const void* in_kv[2];      // encode: K, V inputs (dense tensors or pools)
   void* out_kv[2];           // decode: K, V outputs (dense tensors or pools)
-  uint8_t* codes;            // workspace codes area
+  uint8_t* codes;            // packed codes: the workspace codes area, or (dense encode) the
+                             // stream's payload laid out as if every chunk were raw
+  uint8_t* codes_out;        // encode: where compressed chunk bytes go (== codes: in place)
+  int direct[2];             // decode: reconstruct kernels read raw chunks of K / V from the stream
+  int nnz_pipe;              // encode: 1 or 2 when the fused kernels count the non-zero RZE
+  int nnz_sec[2];            //   words of pipeline P1 / P2 per chunk (into chunk_sizes), per section
   uint8_t* params_ws;        // workspace parameter staging area (paged encode)
   uint8_t* stream;           // dense: the stream; paged: base of all streams
   const uint64_t* req_offsets;  // paged: stream offsets (device)
@@ -99,6 +104,7 @@ hipError_t launch_decode_fused(const CallDesc& c, int which, hipStream_t s);
 hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s);
 hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s);
 hipError_t launch_compact(const CallDesc& c, hipStream_t s);
+hipError_t launch_stash(const CallDesc& c, hipStream_t s);
 hipError_t launch_validate(const CallDesc& c, hipStream_t s);
 hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s);
 

@@ -74,18 +74,24 @@ __device__ __forceinline__ uint64_t stream_base(const CallDesc& c, int r, bool e
 
 // ------------------------------------------------------------------ reset
 
-__global__ void k_reset(Control* ctl) {
-  if (threadIdx.x == 0) {
+__global__ void k_reset(CallDesc c) {
+  Control* ctl = c.ctl;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     ctl->status = 0;
     ctl->pad0 = 0;     // worklist entries for the word-parallel kernels (from the front)
     ctl->total = 0;
     ctl->pad[0] = 0;   // header-field diagnosis bits
     ctl->pad[1] = 0;   // worklist entries for the general stage engine (from the back)
   }
+  // the fused encoders accumulate per-chunk non-zero word counts here
+  if (c.nnz_pipe)
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < c.total_chunks; i += (int64_t)gridDim.x * blockDim.x)
+      c.chunk_sizes[i] = 0;
 }
 
 hipError_t launch_reset(const CallDesc& c, hipStream_t s) {
-  k_reset<<<1, 64, 0, s>>>(c.ctl);
+  const int grid = c.nnz_pipe ? (int)std::max<int64_t>(1, std::min<int64_t>((c.total_chunks + 255) / 256, 1024)) : 1;
+  k_reset<<<grid, 256, 0, s>>>(c);
   return hipGetLastError();
 }
 
@@ -342,9 +348,16 @@ __global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, uint32_t* worklist
     bool work = true;
     const bool fast = fast_eligible(pipe, n);
     if (fast) {
-      // exact size without the transform; raw chunks are done here
+      // exact size without the transform; raw chunks are done here.  The
+      // fused encoders may already have counted the non-zero words.
       const uint64_t* src = (const uint64_t*)(c.codes + L.src);
-      const uint32_t nnz = (pipe == 1) ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
+      uint32_t nnz;
+      if (c.nnz_pipe == pipe && c.nnz_sec[L.w]) {
+        nnz = c.chunk_sizes[ch];
+        __syncthreads();                  // every thread read it before thread 0 overwrites it
+      } else {
+        nnz = (pipe == 1) ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
+      }
       const int64_t size = n / 16 + 2 * (int64_t)nnz;
       if (size >= n) {
         if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
@@ -383,7 +396,8 @@ __global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uin
     if (size >= n) {
       if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
     } else {
-      for (int p = threadIdx.x; p < size; p += blockDim.x) slot[p] = cur[p];
+      uint8_t* oslot = c.codes_out + L.src;
+      for (int p = threadIdx.x; p < size; p += blockDim.x) oslot[p] = cur[p];
       if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
     }
     __syncthreads();
@@ -515,7 +529,8 @@ __global__ __launch_bounds__(256) void k_ll_encode_p1(CallDesc c, const uint32_t
     const ChunkLoc L = locate_chunk(c, rq, r, ch);
     const int n = (int)L.n;                 // multiple of 4096
     const int ngi = n / 4096, nd = n / 64, dpj = n / 512;     // bitmap dwords per plane
-    uint8_t* slot = c.codes + L.src;
+    const uint8_t* slot = c.codes + L.src;
+    uint8_t* oslot = c.codes_out + L.src;
     for (int gi = wave; gi < ngi; gi += 4) {
       const uint4* src = (const uint4*)(slot + (int64_t)gi * 4096 + 64 * lane);
       uint32_t w[16];
@@ -539,8 +554,8 @@ __global__ __launch_bounds__(256) void k_ll_encode_p1(CallDesc c, const uint32_t
     if (size >= n) {
       if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
     } else {
-      for (int d = threadIdx.x; d < nd; d += blockDim.x) ((uint32_t*)slot)[d] = bm[d];
-      uint8_t* words = slot + n / 16;
+      for (int d = threadIdx.x; d < nd; d += blockDim.x) ((uint32_t*)oslot)[d] = bm[d];
+      uint8_t* words = oslot + n / 16;
       const uint16_t* pre16 = (const uint16_t*)pre;
       const int rr = lane & 31;
       for (int d0 = 2 * wave; d0 < nd; d0 += 8) {
@@ -576,7 +591,8 @@ __global__ __launch_bounds__(256) void k_ll_encode_p2(CallDesc c, const uint32_t
     const ChunkLoc L = locate_chunk(c, rq, r, ch);
     const int n = (int)L.n;                 // multiple of 1024
     const int np = n / 16, nblk = np / 64, nd = n / 64, dpj = n / 512;
-    uint8_t* slot = c.codes + L.src;
+    const uint8_t* slot = c.codes + L.src;
+    uint8_t* oslot = c.codes_out + L.src;
     for (int blk = wave; blk < nblk; blk += 4) {
       const int p = 64 * blk + lane;
       const uint4 x = ((const uint4*)slot)[p];
@@ -599,8 +615,8 @@ __global__ __launch_bounds__(256) void k_ll_encode_p2(CallDesc c, const uint32_t
     if (size >= n) {
       if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
     } else {
-      for (int d = threadIdx.x; d < nd; d += blockDim.x) ((uint32_t*)slot)[d] = bm[d];
-      uint8_t* words = slot + n / 16;
+      for (int d = threadIdx.x; d < nd; d += blockDim.x) ((uint32_t*)oslot)[d] = bm[d];
+      uint8_t* words = oslot + n / 16;
       const int rr = lane & 31;
       for (int blk = wave; blk < nblk; blk += 4) {
         const int p = 64 * blk + lane;
@@ -899,8 +915,21 @@ __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
       const int64_t stored = e & 0x7fffffffu;
       const uint64_t base = stream_base(c, r, true);
       uint8_t* out = c.stream + base;
-      uint8_t* dst = out + rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+      const uint64_t fin = c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin];
+      uint8_t* dst = out + rq.payload_off + fin;
       const uint8_t* src = c.codes + L.src;
+      if (c.codes_out != c.codes) {
+        // codes were written where an all-raw stream keeps them: a raw chunk
+        // whose offset did not change is in place (only its alignment padding
+        // is written); every other chunk comes from the staging area
+        if ((e >> 31) && fin == (uint64_t)L.src) {
+          const int64_t pad = align16(stored) - stored;
+          if (threadIdx.x < pad) dst[stored + threadIdx.x] = 0;
+          if (threadIdx.x == 0) *(uint32_t*)(out + 64 + 4 * (ch - rq.chunk_begin)) = e;
+          continue;
+        }
+        src = c.codes_out + L.src;
+      }
       const int64_t nv = align16(stored) / 16;
       for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) {
         uint4 x = ((const uint4*)src)[k];
@@ -935,6 +964,30 @@ __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
       for (int64_t i = threadIdx.x; i < len / 4; i += blockDim.x) dst[i] = src[i];
     }
   }
+}
+
+// Before compaction of a stream whose codes sit at their all-raw places: raw
+// chunks that move (some earlier chunk compressed) are copied to the staging
+// area first, so that no compaction write lands on bytes still to be read.
+__global__ __launch_bounds__(256) void k_stash(CallDesc c) {
+  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+    const uint32_t e = c.chunk_sizes[ch];
+    if (!(e >> 31)) continue;
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    if (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin] == (uint64_t)L.src) continue;
+    const uint4* src = (const uint4*)(c.codes + L.src);
+    uint4* dst = (uint4*)(c.codes_out + L.src);
+    const int64_t nv = align16(L.n) / 16;
+    for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) dst[k] = src[k];
+  }
+}
+
+hipError_t launch_stash(const CallDesc& c, hipStream_t s) {
+  if (c.codes_out == c.codes || c.total_chunks == 0) return hipSuccess;
+  k_stash<<<(int)std::min<int64_t>(c.total_chunks, 256 * 16), 256, 0, s>>>(c);
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const CallDesc& c, hipStream_t s) {
@@ -1022,7 +1075,9 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
       if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
       continue;
     }
-    if (raw) {
+    if (raw && c.direct[L.w]) {
+      // the reconstruct kernels read this chunk from the stream
+    } else if (raw) {
       const uint4* src = (const uint4*)(c.stream + pos);
       uint4* dst = (uint4*)(c.codes + L.src);
       const int64_t nv = L.n / 16;

@@ -115,6 +115,19 @@ def test_word_parallel_lossless_full_chunks(stages, T):
     assert s["chunks_compressed"] >= 8, s
 
 
+@pytest.mark.parametrize("stages", [("TUPL8_1", "BIT_8", "RZE_2"), ("TUPL8_1", "RZE_2")])
+@pytest.mark.parametrize("k,v", [(TP(8, "channel", 64), TP(4, "token", 64)),
+                                 (TP(4, "channel", 64), TP(8, "token", 16)),
+                                 (TP(2, "channel", 64), TP(2, "token", 128))])
+def test_fused_size_counts(stages, k, v):
+    # the fused encoders count the non-zero RZE words of the chunks they write
+    # (all code widths); compressed-chunk sizes must equal the oracle's
+    wl = C3.with_(stages=stages, k=k, v=v, chunk_bytes=16384, name="fused_counts")
+    s = run_case(wl, 2, 256, zero_rich=True, zero_frac=0.5, seed=11)
+    assert s["identical"]
+    assert s["chunks_compressed"] >= 4, s
+
+
 def test_range_error_is_reported():
     wl = C1
     k = torch.full((1, 64, 8, 128), 60000.0, dtype=torch.float16)
