@@ -827,8 +827,105 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
 }
 
 // ===================================================================
-// Decode, per-token groups: the mirror image of k_encode_token.
+// Decode, per-token groups: the mirror image of k_encode_token.  A wave's
+// next tile's codes and parameters (a few registers per lane) are loaded
+// before the current tile is transformed and stored.
 // ===================================================================
+struct DecTok {
+  const uint8_t* csrc;    // the tile's codes
+  uint32_t cbytes;        // bytes readable there
+  const uint8_t* psrc;    // the tile's parameter words
+  uint32_t pbytes;
+  uint16_t* dst;          // first output vector
+  int nvo;                // output vectors to store
+};
+
+template <int BITS, int G, bool PAGED>
+__device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, int64_t tile, uint16_t* out) {
+  constexpr int CB = kHeadDim * BITS / 8;
+  constexpr int NGV = kHeadDim / G;
+  DecTok d;
+  int64_t vg0;
+  int nv;
+  const uint8_t* params_base;
+  if constexpr (!PAGED) {
+    const int64_t nvec = (int64_t)c.layers * c.one.T * c.heads;
+    vg0 = tile * 32;
+    nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec - vg0));
+    d.nvo = nv;
+    const int64_t coff = vg0 * CB;
+    d.csrc = c.codes + pick(which, c.one.codes_off) + coff;
+    d.cbytes = (uint32_t)nv * CB;
+    if (c.direct[which]) {
+      // a tile never straddles chunks here; a raw chunk is read in place
+      const int64_t ci = coff / c.chunk_bytes;
+      const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
+      const uint32_t e = c.chunk_sizes[gci];
+      if (e >> 31) {
+        const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] + (uint64_t)(coff - ci * c.chunk_bytes);
+        d.csrc = c.stream + pos;
+        d.cbytes = (pos >= c.stream_bytes) ? 0u : (uint32_t)std::min<uint64_t>(d.cbytes, c.stream_bytes - pos);
+      }
+    }
+    params_base = c.stream + pick(which, c.one.params_off);
+    d.dst = out + vg0 * kHeadDim;
+  } else {
+    const int r = find_req_by_tile(c, which, tile);
+    const ReqDesc rq = load_req(c, r);
+    const int64_t vpl = (int64_t)rq.T * c.heads;
+    const int64_t tpl = (vpl + 31) >> 5;
+    const int64_t tr = tile - pick(which, rq.tile_begin);
+    const int l = (int)(tr / tpl);
+    const int64_t vstart = (tr - (int64_t)l * tpl) * 32;
+    nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart));
+    vg0 = (int64_t)l * vpl + vstart;
+    // this request's parameters must lie inside the input
+    const uint64_t off = c.req_offsets[r];
+    const bool pok =
+        off + (uint64_t)pick(which, rq.params_off) + (uint64_t)pick(which, rq.params_bytes) <= c.stream_bytes;
+    if (!pok) { if (__lane_id() == 0) set_status(c.ctl, kStCorrupt); nv = 0; }
+    d.csrc = c.codes + pick(which, rq.codes_off) + vg0 * CB;
+    d.cbytes = (uint32_t)nv * CB;
+    params_base = c.stream + (pok ? off : 0) + pick(which, rq.params_off);
+    bool ok;
+    const int64_t base = page_run_base(c, rq, l, vstart, ok);
+    if (!ok && __lane_id() == 0) set_status(c.ctl, kStBadBlock);
+    d.nvo = ok ? (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart)) : 0;
+    d.dst = out + base;
+  }
+  d.psrc = params_base + vg0 * NGV * 4;
+  d.pbytes = (uint32_t)nv * NGV * 4;
+  return d;
+}
+
+// a lane's codes of channels [64 hf, 64 hf + 64) and its group parameter words
+template <int BITS, int G>
+struct DecRegs {
+  static constexpr int LG = (G < 64) ? G : 64;
+  static constexpr int NLG = 64 / LG;
+  uint32_t w[4 * ((2 * BITS + 3) / 4)];
+  uint32_t pw[NLG];
+};
+
+template <int BITS, int G>
+__device__ __forceinline__ void dec_token_load(const DecTok& t, DecRegs<BITS, G>& R) {
+  constexpr int CB = kHeadDim * BITS / 8;
+  constexpr int NGV = kHeadDim / G;
+  const int lane = __lane_id();
+  const int v = lane & 31, hf = lane >> 5;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(t.csrc, t.cbytes);
+  const uint32_t coff = (uint32_t)v * CB + 64 * hf * BITS / 8;
+#pragma unroll
+  for (int i = 0; i < 2 * BITS; i += 4) {
+    const uint4 x = bload16(crs, coff + 4 * i, 0);
+    R.w[i] = x.x; R.w[i + 1] = x.y; R.w[i + 2] = x.z; R.w[i + 3] = x.w;
+  }
+  const __amdgpu_buffer_rsrc_t prs = make_rsrc(t.psrc, t.pbytes);
+#pragma unroll
+  for (int j = 0; j < DecRegs<BITS, G>::NLG; ++j)
+    R.pw[j] = bload4(prs, (uint32_t)v * NGV * 4 + ((64 * hf + j * DecRegs<BITS, G>::LG) / G) * 4, 0);
+}
+
 template <int BITS, int G, bool BF16, bool PAGED>
 __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[4 * kWaveLds];
@@ -840,90 +937,35 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
   slot_sign_masks(c.signs, lane & 15, sm);
   uint16_t* out = (uint16_t*)(which ? c.out_kv[1] : c.out_kv[0]);
   const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
-  const int v = lane & 31, hf = lane >> 5;
-  constexpr int CB = kHeadDim * BITS / 8;
-  constexpr int NGV = kHeadDim / G;
-  constexpr int LG = (G < 64) ? G : 64;                  // group size within the lane's 64 inputs
-  constexpr int NLG = 64 / LG;
-  const int64_t nvec_dense = (int64_t)c.layers * c.one.T * c.heads;
+  constexpr int LG = DecRegs<BITS, G>::LG;
+  constexpr int NLG = DecRegs<BITS, G>::NLG;
 
   const int64_t stride = (int64_t)gridDim.x * 4;
-  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntiles; tile += stride) {
-    int64_t vg0;
-    int nv, nvo;
-    const uint8_t* csrc;       // the tile's codes
-    uint32_t cbytes;           // bytes readable there
-    const uint8_t* params_base;
-    uint16_t* dst;
-    if constexpr (!PAGED) {
-      vg0 = tile * 32;
-      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec_dense - vg0));
-      nvo = nv;
-      const int64_t coff = vg0 * CB;
-      csrc = c.codes + pick(which, c.one.codes_off) + coff;
-      cbytes = (uint32_t)nv * CB;
-      if (c.direct[which]) {
-        // a tile never straddles chunks here; a raw chunk is read in place
-        const int64_t ci = coff / c.chunk_bytes;
-        const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
-        const uint32_t e = c.chunk_sizes[gci];
-        if (e >> 31) {
-          const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] + (uint64_t)(coff - ci * c.chunk_bytes);
-          csrc = c.stream + pos;
-          cbytes = (pos >= c.stream_bytes) ? 0u : (uint32_t)std::min<uint64_t>(cbytes, c.stream_bytes - pos);
-        }
-      }
-      params_base = c.stream + pick(which, c.one.params_off);
-      dst = out + vg0 * kHeadDim;
-    } else {
-      const int r = find_req_by_tile(c, which, tile);
-      const ReqDesc rq = load_req(c, r);
-      const int64_t vpl = (int64_t)rq.T * c.heads;
-      const int64_t tpl = (vpl + 31) >> 5;
-      const int64_t tr = tile - pick(which, rq.tile_begin);
-      const int l = (int)(tr / tpl);
-      const int64_t vstart = (tr - (int64_t)l * tpl) * 32;
-      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart));
-      vg0 = (int64_t)l * vpl + vstart;
-      // this request's parameters must lie inside the input
-      const uint64_t off = c.req_offsets[r];
-      const bool pok =
-          off + (uint64_t)pick(which, rq.params_off) + (uint64_t)pick(which, rq.params_bytes) <= c.stream_bytes;
-      if (!pok) { if (lane == 0) set_status(c.ctl, kStCorrupt); nv = 0; }
-      csrc = c.codes + pick(which, rq.codes_off) + vg0 * CB;
-      cbytes = (uint32_t)nv * CB;
-      params_base = c.stream + (pok ? off : 0) + pick(which, rq.params_off);
-      bool ok;
-      const int64_t base = page_run_base(c, rq, l, vstart, ok);
-      if (!ok && lane == 0) set_status(c.ctl, kStBadBlock);
-      nvo = ok ? (int)std::max<int64_t>(0, std::min<int64_t>(32, vpl - vstart)) : 0;
-      dst = out + base;
+  int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+  if (tile >= ntiles) return;
+  DecTok cur = dec_token_tile<BITS, G, PAGED>(c, which, tile, out);
+  DecRegs<BITS, G> R;
+  dec_token_load(cur, R);
+  for (; tile < ntiles; tile += stride) {
+    const DecTok t = cur;
+    const DecRegs<BITS, G> q = R;
+    if (tile + stride < ntiles) {
+      cur = dec_token_tile<BITS, G, PAGED>(c, which, tile + stride, out);
+      dec_token_load(cur, R);
     }
-
-    // codes of channels [64 hf, 64 hf + 64) and their group parameters
-    const __amdgpu_buffer_rsrc_t crs = make_rsrc(csrc, cbytes);
-    const uint32_t coff = (uint32_t)v * CB + 64 * hf * BITS / 8;
-    uint32_t w[4 * ((2 * BITS + 3) / 4)];
-#pragma unroll
-    for (int i = 0; i < 2 * BITS; i += 4) {
-      const uint4 x = bload16(crs, coff + 4 * i, 0);
-      w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
-    }
-    const __amdgpu_buffer_rsrc_t prs = make_rsrc(params_base + vg0 * NGV * 4, (uint32_t)nv * NGV * 4);
     float sg[NLG], mu[NLG];
 #pragma unroll
     for (int j = 0; j < NLG; ++j) {
-      const uint32_t pw = bload4(prs, (uint32_t)v * NGV * 4 + ((64 * hf + j * LG) / G) * 4, 0);
-      sg[j] = f_from_h16(pw & 0xffffu) * cc;
-      mu[j] = f_from_h16(pw >> 16) * cc;
+      sg[j] = f_from_h16(q.pw[j] & 0xffffu) * cc;
+      mu[j] = f_from_h16(q.pw[j] >> 16) * cc;
     }
     float f[64];
 #pragma unroll
-    for (int r2 = 0; r2 < 64; ++r2) f[r2] = __builtin_fmaf(unpack_code<BITS>(w, r2), sg[r2 / LG], mu[r2 / LG]);
+    for (int r2 = 0; r2 < 64; ++r2) f[r2] = __builtin_fmaf(unpack_code<BITS>(q.w, r2), sg[r2 / LG], mu[r2 / LG]);
 
     fwht64_inreg(f);
     fwht_cross(f);
-    stage_out<BF16>(f, wl, sm, make_rsrc(dst, (uint32_t)nvo * 256u), 256u);
+    stage_out<BF16>(f, wl, sm, make_rsrc(t.dst, (uint32_t)t.nvo * 256u), 256u);
   }
 }
 
@@ -1091,107 +1133,129 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
   }
 }
 
+// Per-channel decode.  A wave reconstructs 32 tokens x 1 head (half of a
+// 64-token tile) on its own LDS region, with no block barriers: in pass p
+// lane c dequantizes channel 64 p + c of its 32 tokens into column c of a
+// 32 x 64 tile, and the lanes of half p read their rows back.  The next
+// wave-tile's codes and parameters are loaded before the current one is
+// transformed and stored.
+template <int BITS>
+struct ChRegs {
+  uint32_t w[2][BITS];   // codes of channel 64 p + lane for the wave's 32 tokens
+  uint32_t pw[2];        // its group parameter word
+};
+
+template <int BITS, int G>
+__device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, int64_t wt, ChRegs<BITS>& R) {
+  const int lane = __lane_id();
+  const int H = c.heads, T = c.one.T;
+  const int n64 = (T + 63) / 64, ngr = (T + G - 1) / G;
+  const int tile = (int)(wt >> 1), half = (int)(wt & 1);
+  const int h = tile % H, g64 = (tile / H) % n64, l = tile / (H * n64);
+  const int gg = min(64, T - g64 * 64);
+  const int nvw = max(0, min(32, gg - 32 * half));            // tokens of this wave-tile
+  const int grp = (G == 64) ? g64 : 2 * g64 + half;
+  const int tok0 = (G == 64) ? 32 * half : 0;                 // first token of the wave in its group
+  const uint8_t* codes_sec = c.codes + pick(which, c.one.codes_off);
+  const uint32_t* prm = (const uint32_t*)(c.stream + pick(which, c.one.params_off));
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int ch = 64 * p + lane;
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) R.w[p][i] = 0;
+    R.pw[p] = 0;
+    if (nvw > 0) {
+      int colb;
+      const int64_t boff = pc_block(T, G, H, BITS, l, grp, h, colb);
+      const uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
+      bool have = true;
+      if (c.direct[which]) {
+        // a group block never straddles chunks here; a raw chunk is read in place
+        const int64_t ci = boff / c.chunk_bytes;
+        const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
+        const uint32_t e = c.chunk_sizes[gci];
+        if (e >> 31) {
+          const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] +
+                               (uint64_t)(boff - ci * c.chunk_bytes) + (uint64_t)ch * colb;
+          have = pos + (uint64_t)colb <= c.stream_bytes;
+          col = c.stream + pos;
+        }
+      }
+      const uint8_t* s = col + tok0 * BITS / 8;
+      if (!have) {
+        // past the end of a damaged stream (already flagged): zero codes
+      } else if (nvw == 32 && colb == G * BITS / 8) {
+        if constexpr (BITS == 2) { const uint2 x = *(const uint2*)s; R.w[p][0] = x.x; R.w[p][1] = x.y; }
+        else {
+#pragma unroll
+          for (int i = 0; i < BITS; i += 4) {
+            const uint4 x = *(const uint4*)(s + 4 * i);
+            R.w[p][i] = x.x; R.w[p][i + 1] = x.y; R.w[p][i + 2] = x.z; R.w[p][i + 3] = x.w;
+          }
+        }
+      } else {
+        const int nbytes = (nvw * BITS + 7) / 8;
+#pragma unroll
+        for (int i = 0; i < 4 * BITS; ++i)
+          if (i < nbytes) R.w[p][i >> 2] |= (uint32_t)s[i] << (8 * (i & 3));
+      }
+      R.pw[p] = prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch];
+    }
+  }
+}
+
 template <int BITS, int G, bool BF16>
-__global__ __launch_bounds__(128, 4) void k_decode_channel(CallDesc c, int which) {
-  __shared__ __attribute__((aligned(16))) float zb[64 * RP];
+__global__ __launch_bounds__(256, 4) void k_decode_channel(CallDesc c, int which) {
+  __shared__ __attribute__((aligned(16))) float lds[4 * 32 * RP];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  float* zw = lds + wave * 32 * RP;
+  uint32_t* stg = (uint32_t*)zw;                                  // output staging aliases it
   const TensorPol pol = which ? c.pol[1] : c.pol[0];
   const float cc = pol.c;
   uint32_t sm[4];
   slot_sign_masks(c.signs, lane & 15, sm);
   uint16_t* out = (uint16_t*)(which ? c.out_kv[1] : c.out_kv[0]);
-  const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
-  uint32_t* stg = (uint32_t*)(zb + 32 * wave * RP);
+  const int64_t nwt = 2 * (which ? c.tiles[1] : c.tiles[0]);
   const int v = lane & 31, hf = lane >> 5;
-  const int H = c.heads;
-  const int T = c.one.T;
+  const int H = c.heads, T = c.one.T;
   const int n64 = (T + 63) / 64;
-  const int ngr = (T + G - 1) / G;
-  const uint8_t* codes_sec = c.codes + pick(which, c.one.codes_off);
-  const uint32_t* prm = (const uint32_t*)(c.stream + pick(which, c.one.params_off));
   const uint32_t vstride = (uint32_t)H * 256u;
 
-  for (int tile = blockIdx.x; tile < (int)ntiles; tile += gridDim.x) {
-    const int h = tile % H;
-    const int g64 = (tile / H) % n64;
-    const int l = tile / (H * n64);
-    const int t0 = g64 * 64;
-    const int gg = min(64, T - t0);
-    const int tw0 = 32 * wave;
-    const int nvw = max(0, min(32, gg - tw0));
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  int64_t wt = (int64_t)blockIdx.x * 4 + wave;
+  if (wt >= nwt) return;
+  ChRegs<BITS> R;
+  ch_dec_load<BITS, G>(c, which, wt, R);
+  for (; wt < nwt; wt += stride) {
+    const ChRegs<BITS> q = R;
+    const int tile = (int)(wt >> 1), half = (int)(wt & 1);
+    if (wt + stride < nwt) ch_dec_load<BITS, G>(c, which, wt + stride, R);
+    const int h = tile % H, g64 = (tile / H) % n64, l = tile / (H * n64);
+    const int t0 = g64 * 64 + 32 * half;
+    const int nvw = max(0, min(32, T - t0));
 
     float f[64];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      __syncthreads();
-      const int chl = 32 * wave + (lane & 31);
-      const int th = lane >> 5;
-      const int ch = 64 * p + chl;
-      const int nvt = max(0, min(32, gg - 32 * th));
-      const int grp = (G == 64) ? g64 : 2 * g64 + th;
-      uint32_t w[BITS];
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) w[i] = 0;
-      float sg = 0.0f, mu = 0.0f;
-      if (nvt > 0) {
-        int colb;
-        const int64_t boff = pc_block(T, G, H, BITS, l, grp, h, colb);
-        const uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
-        bool have = true;
-        if (c.direct[which]) {
-          // a group block never straddles chunks here; a raw chunk is read in place
-          const int64_t ci = boff / c.chunk_bytes;
-          const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
-          const uint32_t e = c.chunk_sizes[gci];
-          if (e >> 31) {
-            const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] +
-                                 (uint64_t)(boff - ci * c.chunk_bytes) + (uint64_t)ch * colb;
-            have = pos + (uint64_t)colb <= c.stream_bytes;
-            col = c.stream + pos;
-          }
-        }
-        const int tok0 = (G == 64) ? 32 * th : 0;
-        const uint8_t* s = col + tok0 * BITS / 8;
-        if (!have) {
-          // past the end of a damaged stream (already flagged): zero codes
-        } else if (nvt == 32 && colb == G * BITS / 8) {
-          if constexpr (BITS == 2) { const uint2 x = *(const uint2*)s; w[0] = x.x; w[1] = x.y; }
-          else {
-#pragma unroll
-            for (int i = 0; i < BITS; i += 4) {
-              const uint4 x = *(const uint4*)(s + 4 * i);
-              w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
-            }
-          }
-        } else {
-          const int nbytes = (nvt * BITS + 7) / 8;
-#pragma unroll
-          for (int i = 0; i < 4 * BITS; ++i)
-            if (i < nbytes) w[i >> 2] |= (uint32_t)s[i] << (8 * (i & 3));
-        }
-        const uint32_t pw = prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch];
-        sg = f_from_h16(pw & 0xffffu) * cc;
-        mu = f_from_h16(pw >> 16) * cc;
-      }
+      const float sg = f_from_h16(q.pw[p] & 0xffffu) * cc;
+      const float mu = f_from_h16(q.pw[p] >> 16) * cc;
       // rows of tokens past the end hold finite filler that is never stored
-      float* wcol = zb + 32 * th * RP + (chl ^ (32 * th));
 #pragma unroll
-      for (int i = 0; i < 32; ++i) wcol[i * RP] = __builtin_fmaf(unpack_code<BITS>(w, i), sg, mu);
-      __syncthreads();
+      for (int i = 0; i < 32; ++i) zw[i * RP + lane] = __builtin_fmaf(unpack_code<BITS>(q.w[p], i), sg, mu);
+      wave_sync();
       if (hf == p) {
-        const float* rrow = zb + (tw0 + v) * RP;
-        const int sw = 32 * wave;                         // rows >= 32 are swizzled by 32
+        const float* rrow = zw + v * RP;
 #pragma unroll
         for (int s4 = 0; s4 < 16; ++s4) {
-          const float4 x = *(const float4*)(rrow + ((4 * s4) ^ sw));
+          const float4 x = *(const float4*)(rrow + 4 * s4);
           f[4 * s4] = x.x; f[4 * s4 + 1] = x.y; f[4 * s4 + 2] = x.z; f[4 * s4 + 3] = x.w;
         }
       }
+      wave_sync();
     }
-    __syncthreads();                                      // all z reads done before staging reuse
     fwht64_inreg(f);
     fwht_cross(f);
-    uint16_t* dst = out + (((int64_t)l * T + t0 + tw0) * H + h) * kHeadDim;
+    uint16_t* dst = out + (((int64_t)l * T + t0) * H + h) * kHeadDim;
     stage_out<BF16>(f, stg, sm, make_rsrc(dst, nvw ? (uint32_t)(nvw - 1) * vstride + 256u : 0u), vstride);
   }
 }
@@ -1252,8 +1316,8 @@ hipError_t launch_decode_fused(const CallDesc& c, int which, hipStream_t s) {
     if (c.dtype == 1) { KVC_BITS_CASES(KVC_TOKEN_CASES, k_decode_token, true) }
     else { KVC_BITS_CASES(KVC_TOKEN_CASES, k_decode_token, false) }
   } else {
-    const dim3 block(128);
-    const int grid = grid_for(tiles, 256 * 32);
+    const dim3 block(256);
+    const int grid = grid_for((2 * tiles + 3) / 4, 256 * 16);
     if (c.dtype == 1) { KVC_BITS_CASES(KVC_CHANNEL_CASES, k_decode_channel, true) }
     else { KVC_BITS_CASES(KVC_CHANNEL_CASES, k_decode_channel, false) }
   }
