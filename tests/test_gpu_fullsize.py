@@ -1,0 +1,175 @@
+"""Parity at full workload sizes, in the launch configuration bench.py times.
+
+The GPU encodes and decodes a whole workload; sampled layers (dense) or
+requests (paged) are checked against the oracle, which encodes and decodes
+just those samples: codes, parameters and chunk bytes of the GPU stream
+must equal the oracle's for the sampled layer, and the reconstruction must
+equal the oracle's bit for bit.  Inputs are generated on the GPU and the
+sampled slices are copied to the host for the oracle.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import gc
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_kvc_amd as K
+import kvc_workloads as W
+import oracle_api as O
+from gpu_helpers import DEV, log, split_stream, to_u16
+
+pytestmark = pytest.mark.gpu
+
+
+def a16(x):
+    return (x + 15) & ~15
+
+
+def free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def layer_slices(out: torch.Tensor, wl, L, T, layer, Tp):
+    """(codes[2], params[2]) of the first Tp tokens of one layer of a dense GPU
+    stream, chunks decoded with the oracle's chunk decoder.  Both code layouts
+    and both parameter layouts keep a layer's tokens in order, so its first Tp
+    tokens are a prefix of the layer's bytes equal to a (1 layer, Tp tokens)
+    stream's sections."""
+    cfg = O.cfg_from_workload(wl, layers=L)
+    cfg1 = O.cfg_from_workload(wl, layers=1)
+    lib = O.lib()
+    cb = wl.chunk_bytes
+    codes_b = [lib.kvco_codes_bytes(C.byref(cfg), w, T) for w in range(2)]
+    params_b = [lib.kvco_params_bytes(C.byref(cfg), w, T) for w in range(2)]
+    layer_codes = [lib.kvco_codes_bytes(C.byref(cfg1), w, T) for w in range(2)]
+    layer_params = [lib.kvco_params_bytes(C.byref(cfg1), w, T) for w in range(2)]
+    lcodes = [lib.kvco_codes_bytes(C.byref(cfg1), w, Tp) for w in range(2)]
+    lparams = [lib.kvco_params_bytes(C.byref(cfg1), w, Tp) for w in range(2)]
+    nch = [-(-c // cb) for c in codes_b]
+    table = out[64:64 + 4 * sum(nch)].cpu().numpy().view(np.uint32)
+    stored = (table & 0x7FFFFFFF).astype(np.int64)
+    offs = np.concatenate([[0], np.cumsum((stored + 15) & ~15)])
+    p0 = a16(64 + 4 * sum(nch))
+    p1 = a16(p0 + params_b[0])
+    pay = a16(p1 + params_b[1])
+    stages = [O.STAGE_IDS[s] for s in wl.stages]
+    codes, params = [], []
+    for w in range(2):
+        assert lcodes[w] % cb == 0 and layer_codes[w] % cb == 0
+        first = layer * layer_codes[w] // cb
+        g0 = (nch[0] if w else 0) + first
+        g1 = g0 + lcodes[w] // cb
+        span = out[pay + int(offs[g0]):pay + int(offs[g1])].cpu().numpy()      # one copy per section
+        parts = []
+        for gi in range(g0, g1):
+            pos = int(offs[gi] - offs[g0])
+            raw = bool(table[gi] >> 31)
+            st, dec = O.chunk_decode(stages, span[pos:pos + int(stored[gi])], raw, cb)
+            assert st == O.OK
+            parts.append(dec)
+        codes.append(np.concatenate(parts))
+        base = (p0, p1)[w]
+        params.append(out[base + layer * layer_params[w]:base + layer * layer_params[w] + lparams[w]].cpu().numpy())
+    return codes, params
+
+
+def check_dense_full(name, layers_to_check, Tp=None):
+    wl = W.WORKLOADS[name]
+    L, T = wl.layers, wl.tokens
+    log(f"{name}: generating {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype} on the GPU")
+    k, v = W.dense_kv(wl, device=DEV)
+    plan = K.Plan(K.config_from_workload(wl))
+    ms, wsb = plan.sizes(T)
+    out = torch.empty(ms, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    n = plan.encode(k, v, T, out, ws)
+    log(f"{name}: GPU stream {n} bytes")
+    kd = torch.empty_like(k)
+    vd = torch.empty_like(v)
+    plan.decode(out, n, T, kd, vd, ws)
+    assert plan.query_status(ws) == K.OK
+    Tp = T if Tp is None else Tp
+    for l in layers_to_check:
+        t0 = time.time()
+        log(f"{name}: layer {l}: oracle encode + decode of its first {Tp} tokens")
+        ku, vu = to_u16(k[l:l + 1, :Tp]), to_u16(v[l:l + 1, :Tp])
+        cfg1 = O.cfg_from_workload(wl, layers=1)
+        st, ref = O.encode(cfg1, ku, vu, Tp)
+        assert st == O.OK
+        rc, rp = split_stream(ref, wl, 1, Tp)
+        gc_, gp = layer_slices(out, wl, L, T, l, Tp)
+        for w in range(2):
+            assert np.array_equal(gc_[w], rc[w]), f"layer {l} section {w}: codes differ"
+            assert np.array_equal(gp[w], rp[w]), f"layer {l} section {w}: parameters differ"
+        st, kr, vr = O.decode(ref, Tp * wl.heads * wl.head_dim)
+        assert st == O.OK
+        assert np.array_equal(to_u16(kd[l:l + 1, :Tp]).reshape(-1), kr), f"layer {l}: K reconstruction differs"
+        assert np.array_equal(to_u16(vd[l:l + 1, :Tp]).reshape(-1), vr), f"layer {l}: V reconstruction differs"
+        log(f"{name}: layer {l} identical ({time.time() - t0:.1f} s)")
+    del k, v, kd, vd, out, ws
+    free()
+
+
+def test_llama70b_32k_full_size_sampled_layers():
+    check_dense_full("c3_llama70b_32k", [0, 79])
+
+
+def test_llama70b_128k_full_size_sampled_layer():
+    # fp16 outputs: the oracle's plain fp16 rounding is slow, so a token prefix
+    check_dense_full("c5_llama70b_128k", [37], Tp=8192)
+
+
+def test_paged_llama8b_full_size_sampled_requests():
+    wl = W.WORKLOADS["c4_paged_llama8b"]
+    batch = W.paged_layout(wl)
+    R = len(batch.seq_lens)
+    t0 = time.time()
+    log(f"c4: {R} requests, {batch.num_blocks} pages, generating pools on the GPU")
+    kp, vp = W.paged_pools(wl, batch, device=DEV)
+    torch.cuda.synchronize()
+    log(f"c4: pools ready ({time.time() - t0:.1f} s)")
+    plan = K.Plan(K.config_from_workload(wl, max_tokens=0))
+    ms, wsb = plan.sizes_paged(batch.seq_lens)
+    out = torch.empty(ms, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    offs = torch.zeros(R + 1, dtype=torch.int64, device=DEV)
+    bt = torch.from_numpy(batch.block_table).to(DEV)
+    n = plan.encode_paged(kp, vp, batch.num_blocks, bt, batch.seq_lens, out, offs, ws)
+    log(f"c4: GPU streams {n} bytes ({time.time() - t0:.1f} s)")
+    dst = W.paged_layout(wl, stream=1)
+    kq = torch.zeros_like(kp)
+    vq = torch.zeros_like(vp)
+    btd = torch.from_numpy(dst.block_table).to(DEV)
+    plan.decode_paged(out, n, offs, dst.seq_lens, kq, vq, dst.num_blocks, btd, ws)
+    assert plan.query_status(ws) == K.OK
+    offs_h = offs.cpu().numpy()
+    P = wl.page_tokens
+    order = np.argsort(batch.seq_lens)
+    sample = [int(order[0]), int(order[1])]            # the oracle's fp16 rounding is slow
+    cfg = O.cfg_from_workload(wl)
+    for r in sample:
+        T = int(batch.seq_lens[r])
+        npg = (T + P - 1) // P
+        log(f"c4: request {r} ({T} tokens): oracle encode + decode")
+        blocks = bt[r, :npg].long()
+        kr_in = kp[:, blocks].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T]
+        vr_in = vp[:, blocks].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T]
+        st, ref = O.encode(cfg, to_u16(kr_in), to_u16(vr_in), T)
+        assert st == O.OK
+        got = out[int(offs_h[r]):int(offs_h[r + 1])].cpu().numpy()
+        assert np.array_equal(got, ref), f"request {r}: stream differs"
+        st, kr, vr = O.decode(ref, wl.layers * T * wl.heads * wl.head_dim)
+        assert st == O.OK
+        bd = btd[r, :npg].long()
+        kg = kq[:, bd].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T]
+        vg = vq[:, bd].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T]
+        assert np.array_equal(to_u16(kg).reshape(-1), kr), f"request {r}: K reconstruction differs"
+        assert np.array_equal(to_u16(vg).reshape(-1), vr), f"request {r}: V reconstruction differs"
+        log(f"c4: request {r} identical ({time.time() - t0:.1f} s)")
+    del kp, vp, kq, vq, out, ws
+    free()
