@@ -254,6 +254,7 @@ void fill_common(const kvc_plan_s* p, CallDesc& c) {
   std::memcpy(c.signs, p->signs, sizeof(c.signs));
   std::memcpy(c.stages, p->cfg.lossless, 4);
   c.chunk_bytes = p->cfg.chunk_bytes;
+  c.chunk_shift = (c.chunk_bytes & (c.chunk_bytes - 1)) ? -1 : __builtin_ctz(c.chunk_bytes);
   c.seed = p->cfg.sign_seed;
 }
 

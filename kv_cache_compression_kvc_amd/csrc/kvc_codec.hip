@@ -257,10 +257,12 @@ __device__ __forceinline__ uint32_t pack_dword(const uint32_t* q) {
     const uint32_t a = (q[1] << 8) | q[0], b = (q[3] << 8) | q[2];
     return __builtin_amdgcn_perm(b, a, 0x05040100u);
   } else if constexpr (BITS == 4) {
-    const uint32_t p0 = (q[1] << 4) | q[0], p1 = (q[3] << 4) | q[2];
-    const uint32_t p2 = (q[5] << 4) | q[4], p3 = (q[7] << 4) | q[6];
-    const uint32_t a = (p1 << 8) | p0, b = (p3 << 8) | p2;
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+    // even codes to the low nibbles of four bytes, odd codes to the high ones
+    const uint32_t e = __builtin_amdgcn_perm(__builtin_amdgcn_perm(q[6], q[4], 0x0c0c0400u),
+                                             __builtin_amdgcn_perm(q[2], q[0], 0x0c0c0400u), 0x05040100u);
+    const uint32_t o = __builtin_amdgcn_perm(__builtin_amdgcn_perm(q[7], q[5], 0x0c0c0400u),
+                                             __builtin_amdgcn_perm(q[3], q[1], 0x0c0c0400u), 0x05040100u);
+    return (o << 4) | e;
   } else {
     uint32_t by[4];
 #pragma unroll
@@ -361,6 +363,12 @@ __device__ __forceinline__ float pair_xchg(float x) {
 template <typename T>
 __device__ __forceinline__ T pick(int which, const T (&a)[2]) { return which ? a[1] : a[0]; }
 
+// chunk holding byte off of a codes section (chunk sizes are multiples of 4 KiB)
+__device__ __forceinline__ int64_t chunk_of(const CallDesc& c, int64_t off) {
+  if (c.chunk_shift >= 0) return off >> c.chunk_shift;
+  return (int64_t)((uint64_t)(off >> 12) / (c.chunk_bytes >> 12));
+}
+
 __device__ __forceinline__ void set_status(Control* ctl, uint32_t bit) {
   __hip_atomic_fetch_or(&ctl->status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -396,33 +404,47 @@ __device__ __forceinline__ int64_t page_run_base(const CallDesc& c, const ReqDes
 constexpr int RP = 68;               // LDS row pitch in dwords (272 bytes)
 constexpr int kWaveLds = 32 * RP;    // dwords of one wave's staging tile
 
+// 16-bit pair -> two binary32 values with the sign bits set in m (bits 15
+// and 31) flipped.  For bfloat16 the flip rides on the unpacking: adding
+// bit 15 toggles it modulo 2^16 (the carry leaves with the shift), and the
+// high half takes an exclusive or before its mask.
+template <bool BF16>
+__device__ __forceinline__ void unpack16_signed(uint32_t u, uint32_t m, float& lo, float& hi) {
+  if constexpr (BF16) {
+    lo = u2f((u + m) << 16);
+    hi = u2f((u ^ m) & 0xffff0000u);
+  } else {
+    unpack16<false>(u ^ m, lo, hi);
+  }
+}
+
 // Stage 32 head vectors (256 bytes each, consecutive vectors vstride bytes
 // apart) through LDS and return this lane's 64 values: lane half hf gets
-// channels [64 hf, 64 hf + 64) of vector (lane & 31), sign-flipped.
+// channels [64 hf, 64 hf + 64) of vector (lane & 31), sign-flipped with the
+// table smt (32 words per lane half, word j covering channels 64 hf + 2 j, +1).
 template <bool BF16>
 __device__ __forceinline__ void stage_in(__amdgpu_buffer_rsrc_t src, uint32_t vstride, uint32_t* wl,
-                                         const uint32_t* sm, float* f) {
+                                         const uint32_t* smt, float* f) {
   const int lane = __lane_id();
-  const uint32_t voff = (uint32_t)(lane >> 4) * vstride + (uint32_t)(lane & 15) * 16;
+  uint32_t voff = (uint32_t)(lane >> 4) * vstride + (uint32_t)(lane & 15) * 16;
+  asm volatile("" : "+v"(voff));   // one offset register: the per-load offsets are added here, not kept
   uint4 d[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) d[k] = bload16(src, voff + (uint32_t)k * 4 * vstride, 0);
   uint32_t* wrow = wl + (lane >> 4) * RP + (lane & 15) * 4;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    uint4 x = d[k];
-    x.x ^= sm[0]; x.y ^= sm[1]; x.z ^= sm[2]; x.w ^= sm[3];
-    *(uint4*)(wrow + k * 4 * RP) = x;
-  }
+  for (int k = 0; k < 8; ++k) *(uint4*)(wrow + k * 4 * RP) = d[k];
   wave_sync();
   const uint32_t* rrow = wl + (lane & 31) * RP + (lane >> 5) * 32;
+  const uint32_t* mrow = smt + (lane >> 5) * 32;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint4 x = *(const uint4*)(rrow + 4 * j);
-    unpack16<BF16>(x.x, f[8 * j + 0], f[8 * j + 1]);
-    unpack16<BF16>(x.y, f[8 * j + 2], f[8 * j + 3]);
-    unpack16<BF16>(x.z, f[8 * j + 4], f[8 * j + 5]);
-    unpack16<BF16>(x.w, f[8 * j + 6], f[8 * j + 7]);
+    const uint4 m = *(const uint4*)(mrow + 4 * j);
+    unpack16_signed<BF16>(x.x, m.x, f[8 * j + 0], f[8 * j + 1]);
+    unpack16_signed<BF16>(x.y, m.y, f[8 * j + 2], f[8 * j + 3]);
+    unpack16_signed<BF16>(x.z, m.z, f[8 * j + 4], f[8 * j + 5]);
+    unpack16_signed<BF16>(x.w, m.w, f[8 * j + 6], f[8 * j + 7]);
   }
   wave_sync();
 }
@@ -502,13 +524,24 @@ __device__ __forceinline__ uint32_t nz_bytes64(uint64_t x) {
   const uint32_t zb = ~(((b & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | b | 0x7F7F7F7Fu);
   return 8u - (uint32_t)__builtin_popcount(za) - (uint32_t)__builtin_popcount(zb);
 }
+// sum over the wavefront (all lanes active): row sums by DPP, then the four rows
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
-  return v;
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false);    // lane ^ 1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false);    // lane ^ 2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false);   // row_ror:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);   // row_ror:8
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 __device__ __forceinline__ void add_chunk_nnz(const CallDesc& c, int64_t gci, uint32_t v) {
   const uint32_t t = wave_sum(v);
+  if (__lane_id() == 0 && t) __hip_atomic_fetch_add(&c.chunk_sizes[gci], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// as add_chunk_nnz when only lanes L0..L3 hold non-zero counts
+template <int L0, int L1, int L2, int L3>
+__device__ __forceinline__ void add_chunk_nnz4(const CallDesc& c, int64_t gci, uint32_t v) {
+  const uint32_t t = __builtin_amdgcn_readlane(v, L0) + __builtin_amdgcn_readlane(v, L1) +
+                     __builtin_amdgcn_readlane(v, L2) + __builtin_amdgcn_readlane(v, L3);
   if (__lane_id() == 0 && t) __hip_atomic_fetch_add(&c.chunk_sizes[gci], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t u64of(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
@@ -809,7 +842,7 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
       } else {
         cbase = which ? c.one.nchunks[0] : 0;
       }
-      add_chunk_nnz(c, cbase + (t.vg0 * CB) / c.chunk_bytes, cnt);
+      add_chunk_nnz(c, cbase + chunk_of(c, t.vg0 * CB), cnt);
     }
     const __amdgpu_buffer_rsrc_t prs = make_rsrc(t.params_base + t.vg0 * NGV * 4, (uint32_t)t.nv * NGV * 4);
     const uint32_t prow = (uint32_t)v * NGV * 4;
@@ -865,7 +898,7 @@ __device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, i
     d.cbytes = (uint32_t)nv * CB;
     if (c.direct[which]) {
       // a tile never straddles chunks here; a raw chunk is read in place
-      const int64_t ci = coff / c.chunk_bytes;
+      const int64_t ci = chunk_of(c, coff);
       const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
       const uint32_t e = c.chunk_sizes[gci];
       if (e >> 31) {
@@ -1000,11 +1033,15 @@ __device__ __forceinline__ int64_t pc_block(int T, int G, int H, int bits, int l
 template <int BITS, int G, bool BF16>
 __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which) {
   __shared__ __attribute__((aligned(16))) float zb[64 * RP];
+  __shared__ __attribute__((aligned(16))) uint32_t smt[64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const TensorPol pol = which ? c.pol[1] : c.pol[0];
   const float cc = pol.c;
-  uint32_t sm[4];
-  slot_sign_masks(c.signs, lane & 15, sm);
+  if (threadIdx.x < 64) {
+    // sign words of channel pairs (2 t, 2 t + 1) at bits 15 and 31
+    const int ch = 2 * threadIdx.x;
+    smt[threadIdx.x] = (((c.signs[ch >> 5] >> (ch & 31)) & 1u) << 15) | (((c.signs[ch >> 5] >> ((ch & 31) + 1)) & 1u) << 31);
+  }
   const uint16_t* in = (const uint16_t*)(which ? c.in_kv[1] : c.in_kv[0]);
   const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
   uint32_t* stg = (uint32_t*)(zb + 32 * wave * RP);          // this wave's staging (aliases its z rows)
@@ -1017,19 +1054,46 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
   uint32_t* prm = (uint32_t*)(c.stream + pick(which, c.one.params_off));
   const uint32_t vstride = (uint32_t)H * 256u;
 
-  for (int tile = blockIdx.x; tile < (int)ntiles; tile += gridDim.x) {
-    const int h = tile % H;
-    const int g64 = (tile / H) % n64;
-    const int l = tile / (H * n64);
+  // Tile order.  Workgroups are handed to the eight XCDs in turn, so the
+  // blocks one XCD receives are those with the same blockIdx mod 8.  Virtual
+  // tile v = 8 r + x (v below `full`) is head r mod H of 64-token group
+  // 8 (r / H) + x: an XCD takes all heads of a group one after another and
+  // reads whole token rows of the layer.  The last ngroups mod 8 groups
+  // (v >= full) go in plain order.  Group index = l * n64 + g64.
+  const int tw0 = 32 * wave;                           // this wave's first token in a tile
+  const int ngroups = (int)(ntiles / H);
+  const int full = (ngroups / 8) * 8 * H;
+  auto decode_tile = [&](int vt, int& l_, int& g_, int& h_) {
+    int gidx;
+    if (vt < full) {
+      const int r = vt >> 3;
+      h_ = r % H;
+      gidx = (r / H) * 8 + (vt & 7);
+    } else {
+      h_ = (vt - full) % H;
+      gidx = full / H + (vt - full) / H;
+    }
+    l_ = gidx / n64;
+    g_ = gidx % n64;
+  };
+  // advancing v by a grid size that is a multiple of 8 keeps x: r grows by
+  // step / 8 = dq H + dh, the group index by 8 dq (+ 8 when the head wraps)
+  const int step = (int)gridDim.x;
+  const bool stepwise = (step & 7) == 0;
+  const int dh = (step >> 3) % H, dq = (step >> 3) / H;
+  const int dgA = (8 * dq) % n64, dlA = (8 * dq) / n64;
+  const int dgB = (8 * dq + 8) % n64, dlB = (8 * dq + 8) / n64;
+  int l, g64, h;
+  decode_tile((int)blockIdx.x, l, g64, h);
+  for (int tile = blockIdx.x; tile < (int)ntiles; tile += step) {
     const int t0 = g64 * 64;
     const int gg = min(64, T - t0);                    // valid tokens in this tile
-    const int tw0 = 32 * wave;                         // this wave's first token in the tile
     const int nvw = max(0, min(32, gg - tw0));
 
     __syncthreads();                                    // previous tile's readers are done
     float f[64];
     const uint16_t* src = in + (((int64_t)l * T + t0 + tw0) * H + h) * kHeadDim;
-    stage_in<BF16>(make_rsrc(src, nvw ? (uint32_t)(nvw - 1) * vstride + 256u : 0u), vstride, stg, sm, f);
+    stage_in<BF16>(make_rsrc(src, nvw ? (uint32_t)(nvw - 1) * vstride + 256u : 0u), vstride, stg, smt, f);
     fwht64_inreg(f);
     fwht_cross(f);
 
@@ -1109,33 +1173,49 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
           if (c.nnz_pipe && c.nnz_sec[which]) {
             // this thread's codes: 4 * BITS bytes at ch * 8 BITS + th * 4 BITS of
             // the group block, i.e. words (4 BITS ch + 2 BITS th) / 4 + m
-            const int cl = lane & 31;
             uint32_t cnt = 0;
             if (c.nnz_pipe == 1) {
               if constexpr (BITS == 4) {
                 // residues 4 (ch & 1) + 2 th, +1; a 1 KiB region is this wave's 32 channels
                 uint64_t x0 = u64of(w[0], w[1]), x1 = u64of(w[2], w[3]);
                 x0 = or_lane_bits<1, 5>(x0); x1 = or_lane_bits<1, 5>(x1);
-                cnt = ((cl >> 1) == 0) ? popc64(x0) + popc64(x1) : 0u;
+                cnt = popc64(x0) + popc64(x1);               // the sum of lanes 0, 1, 32 and 33
               } else {
                 // residues 4 th + m; regions of 16 channels
                 uint64_t x[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) x[m] = or_lane_bits<0, 4>(u64of(w[2 * m], w[2 * m + 1]));
-                cnt = ((cl & 15) == 0) ? popc64(x[0]) + popc64(x[1]) + popc64(x[2]) + popc64(x[3]) : 0u;
+                cnt = popc64(x[0]) + popc64(x[1]) + popc64(x[2]) + popc64(x[3]);   // lanes 0, 16, 32, 48
               }
             } else {
 #pragma unroll
               for (int u = 0; u < BITS / 4; ++u)
                 cnt += nz_bytes64(u64of(w[4 * u], w[4 * u + 1]) | u64of(w[4 * u + 2], w[4 * u + 3]));
             }
-            add_chunk_nnz(c, (which ? (int64_t)c.one.nchunks[0] : 0) + boff / c.chunk_bytes, cnt);
+            const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + chunk_of(c, boff);
+            if (c.nnz_pipe == 1) {
+              if constexpr (BITS == 4) add_chunk_nnz4<0, 1, 32, 33>(c, gci, cnt);
+              else add_chunk_nnz4<0, 16, 32, 48>(c, gci, cnt);
+            } else {
+              add_chunk_nnz(c, gci, cnt);
+            }
           }
         }
       };
       if (gg == 64) pass(std::true_type{});
       else pass(std::false_type{});
       __syncthreads();                                   // before the next pass overwrites zb
+    }
+    const int nt = tile + step;
+    if (stepwise && nt < full) {
+      h += dh;
+      const bool cy = h >= H;
+      if (cy) h -= H;
+      g64 += cy ? dgB : dgA;
+      l += cy ? dlB : dlA;
+      if (g64 >= n64) { g64 -= n64; ++l; }
+    } else {
+      decode_tile(nt, l, g64, h);
     }
   }
 }
@@ -1178,7 +1258,7 @@ __device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, int64_
       bool have = true;
       if (c.direct[which]) {
         // a group block never straddles chunks here; a raw chunk is read in place
-        const int64_t ci = boff / c.chunk_bytes;
+        const int64_t ci = chunk_of(c, boff);
         const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
         const uint32_t e = c.chunk_sizes[gci];
         if (e >> 31) {

@@ -68,6 +68,7 @@ struct CallDesc {
   uint32_t signs[4];         // bit i set: sign of channel i is -1
   uint8_t stages[4];
   uint32_t chunk_bytes;
+  int chunk_shift;           // log2(chunk_bytes) when it is a power of two, else -1
   uint64_t seed;
   // paged addressing (page_tokens == 0: dense)
   int page_tokens;
