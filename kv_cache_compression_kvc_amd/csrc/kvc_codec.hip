@@ -1232,13 +1232,71 @@ struct ChRegs {
   uint32_t pw[2];        // its group parameter word
 };
 
+// A wave-tile: 32 tokens (half `half` of 64-token group g64 of layer l) of head h.
+struct WaveTile {
+  int l, g64, h, half;
+  int k;                 // 2 h + half
+};
+
+// Wave-tile order of the per-channel decoder.  Workgroups go to the eight
+// XCDs in turn (blockIdx mod 8), four wave-tiles per block.  Wave-tile
+// u = 4 b + w with b = 8 r + x (u below `full`) is entry k = s mod 2H,
+// s = 4 r + w, of 64-token group 8 (s / 2H) + x: the blocks of one XCD walk
+// all heads and halves of a group before the next.  The rest goes in plain
+// order.  Group index = l * n64 + g64.
+struct ChDecOrder {
+  int H, n64, full;
+  int dk, dgA, dlA, dgB, dlB;
+  bool stepwise;
+  __device__ ChDecOrder(int H_, int n64_, int64_t ntiles, int grid) : H(H_), n64(n64_) {
+    const int ngroups = (int)(ntiles / H);
+    full = (H % 2 == 0) ? (ngroups / 8) * 8 * 2 * H : 0;
+    stepwise = (grid & 7) == 0;
+    const int ds = grid / 2;                         // s advance per grid stride of wave-tiles
+    dk = ds % (2 * H);
+    const int dq = ds / (2 * H);
+    dgA = (8 * dq) % n64; dlA = (8 * dq) / n64;
+    dgB = (8 * dq + 8) % n64; dlB = (8 * dq + 8) / n64;
+  }
+  __device__ WaveTile decode(int64_t u) const {
+    WaveTile o;
+    int grp;
+    if (u < full) {
+      const int b = (int)(u >> 2);
+      const int sidx = 4 * (b >> 3) + (int)(u & 3);
+      o.k = sidx % (2 * H);
+      grp = 8 * (sidx / (2 * H)) + (b & 7);
+    } else {
+      const int64_t w = u - full;
+      o.k = (int)(w % (2 * H));
+      grp = full / (2 * H) + (int)(w / (2 * H));
+    }
+    o.h = o.k >> 1; o.half = o.k & 1;
+    o.l = grp / n64; o.g64 = grp % n64;
+    return o;
+  }
+  // wave-tile u, given o = wave-tile u - stride
+  __device__ WaveTile advance(int64_t u, WaveTile o) const {
+    if (stepwise && u < full) {
+      o.k += dk;
+      const bool cy = o.k >= 2 * H;
+      if (cy) o.k -= 2 * H;
+      o.g64 += cy ? dgB : dgA;
+      o.l += cy ? dlB : dlA;
+      if (o.g64 >= n64) { o.g64 -= n64; ++o.l; }
+      o.h = o.k >> 1; o.half = o.k & 1;
+      return o;
+    }
+    return decode(u);
+  }
+};
+
 template <int BITS, int G>
-__device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, int64_t wt, ChRegs<BITS>& R) {
+__device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, WaveTile wt, ChRegs<BITS>& R) {
   const int lane = __lane_id();
   const int H = c.heads, T = c.one.T;
-  const int n64 = (T + 63) / 64, ngr = (T + G - 1) / G;
-  const int tile = (int)(wt >> 1), half = (int)(wt & 1);
-  const int h = tile % H, g64 = (tile / H) % n64, l = tile / (H * n64);
+  const int ngr = (T + G - 1) / G;
+  const int half = wt.half, h = wt.h, g64 = wt.g64, l = wt.l;
   const int gg = min(64, T - g64 * 64);
   const int nvw = max(0, min(32, gg - 32 * half));            // tokens of this wave-tile
   const int grp = (G == 64) ? g64 : 2 * g64 + half;
@@ -1311,14 +1369,17 @@ __global__ __launch_bounds__(256, 4) void k_decode_channel(CallDesc c, int which
   const int64_t stride = (int64_t)gridDim.x * 4;
   int64_t wt = (int64_t)blockIdx.x * 4 + wave;
   if (wt >= nwt) return;
+  const ChDecOrder order(H, n64, nwt / 2, (int)gridDim.x);
+  WaveTile nxt = order.decode(wt);
   ChRegs<BITS> R;
-  ch_dec_load<BITS, G>(c, which, wt, R);
+  ch_dec_load<BITS, G>(c, which, nxt, R);
   for (; wt < nwt; wt += stride) {
     const ChRegs<BITS> q = R;
-    const int tile = (int)(wt >> 1), half = (int)(wt & 1);
-    if (wt + stride < nwt) ch_dec_load<BITS, G>(c, which, wt + stride, R);
-    const int h = tile % H, g64 = (tile / H) % n64, l = tile / (H * n64);
-    const int t0 = g64 * 64 + 32 * half;
+    const WaveTile cur = nxt;
+    nxt = order.advance(wt + stride, nxt);
+    if (wt + stride < nwt) ch_dec_load<BITS, G>(c, which, nxt, R);
+    const int h = cur.h, g64 = cur.g64, l = cur.l;
+    const int t0 = g64 * 64 + 32 * cur.half;
     const int nvw = max(0, min(32, T - t0));
 
     float f[64];
