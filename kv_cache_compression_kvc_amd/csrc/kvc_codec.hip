@@ -68,6 +68,9 @@ typedef int int2v __attribute__((ext_vector_type(2)));
 #define KVC_NARROW_STORE_POLICY 0
 #endif
 constexpr int kLoadPol = KVC_LOAD_POLICY;
+#ifndef KVC_EC_WAVES
+#define KVC_EC_WAVES 4   // waves per SIMD the complete-tile channel encoder is built for
+#endif
 constexpr int kStorePol = KVC_STORE_POLICY;          // 16-byte stores
 constexpr int kNarrowStorePol = KVC_NARROW_STORE_POLICY;   // 4- and 8-byte stores
 
@@ -1030,8 +1033,10 @@ __device__ __forceinline__ int64_t pc_block(int T, int G, int H, int bits, int l
          (int64_t)h * kHeadDim * colb;
 }
 
-template <int BITS, int G, bool BF16>
-__global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which) {
+// TAIL = false: the complete 64-token groups; TAIL = true: the last,
+// incomplete group of every (layer, head) when T is not a multiple of 64.
+template <int BITS, int G, bool BF16, bool TAIL>
+__global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel(CallDesc c, int which) {
   __shared__ __attribute__((aligned(16))) float zb[64 * RP];
   __shared__ __attribute__((aligned(16))) uint32_t smt[64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -1043,12 +1048,12 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
     smt[threadIdx.x] = (((c.signs[ch >> 5] >> (ch & 31)) & 1u) << 15) | (((c.signs[ch >> 5] >> ((ch & 31) + 1)) & 1u) << 31);
   }
   const uint16_t* in = (const uint16_t*)(which ? c.in_kv[1] : c.in_kv[0]);
-  const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
   uint32_t* stg = (uint32_t*)(zb + 32 * wave * RP);          // this wave's staging (aliases its z rows)
   const int v = lane & 31, hf = lane >> 5;
   const int H = c.heads;
   const int T = c.one.T;
-  const int n64 = (T + 63) / 64;
+  const int n64 = TAIL ? 1 : T / 64;                   // groups this kernel walks per layer
+  const int64_t ntiles = (int64_t)c.layers * n64 * H;
   const int ngr = (T + G - 1) / G;
   uint8_t* codes_sec = c.codes + pick(which, c.one.codes_off);
   uint32_t* prm = (uint32_t*)(c.stream + pick(which, c.one.params_off));
@@ -1085,10 +1090,11 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
   const int dgB = (8 * dq + 8) % n64, dlB = (8 * dq + 8) / n64;
   int l, g64, h;
   decode_tile((int)blockIdx.x, l, g64, h);
+  if constexpr (TAIL) g64 = T / 64;
   for (int tile = blockIdx.x; tile < (int)ntiles; tile += step) {
     const int t0 = g64 * 64;
-    const int gg = min(64, T - t0);                    // valid tokens in this tile
-    const int nvw = max(0, min(32, gg - tw0));
+    const int gg = TAIL ? T - t0 : 64;                 // valid tokens in this tile
+    const int nvw = TAIL ? max(0, min(32, gg - tw0)) : 32;
 
     __syncthreads();                                    // previous tile's readers are done
     float f[64];
@@ -1149,11 +1155,22 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
           w[dw] = pack_dword<BITS>(q);
         }
         int colb;
-        const int64_t boff = pc_block(T, G, H, BITS, l, grp, h, colb);
-        uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
+        // complete tiles: the block of the tile's first group (both halves of a
+        // G = 32 tile are complete groups, the second one block further on)
+        const int64_t boff = pc_block(T, G, H, BITS, l, FULL ? ((G == 64) ? g64 : 2 * g64) : grp, h, colb);
         const int tok0 = (G == 64) ? 32 * th : 0;        // first token of this thread in its group
-        uint8_t* dst = col + tok0 * BITS / 8;
-        if (FULL || (nvt == 32 && colb == G * BITS / 8)) {
+        if constexpr (FULL) {
+          const uint32_t gstride = (G == 64) ? 0u : (uint32_t)H * kHeadDim * colb;
+          const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes_sec + boff, gstride + (uint32_t)kHeadDim * colb);
+          const uint32_t co = (uint32_t)th * gstride + (uint32_t)ch * colb + (uint32_t)(tok0 * BITS / 8);
+          if constexpr (BITS == 2) bstore8(make_uint2(w[0], w[1]), crs, co, 0);
+          else if constexpr (BITS == 4) bstore16(make_uint4(w[0], w[1], w[2], w[3]), crs, co, 0);
+          else {
+            bstore16(make_uint4(w[0], w[1], w[2], w[3]), crs, co, 0);
+            bstore16(make_uint4(w[4], w[5], w[6], w[7]), crs, co + 16, 0);
+          }
+        } else if (nvt == 32 && colb == G * BITS / 8) {
+          uint8_t* dst = codes_sec + boff + (int64_t)ch * colb + tok0 * BITS / 8;
           if constexpr (BITS == 2) *(uint2*)dst = make_uint2(w[0], w[1]);
           else if constexpr (BITS == 4) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
           else {
@@ -1161,6 +1178,7 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
             *(uint4*)(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
           }
         } else if (ntok > 0 && nvt > 0) {
+          uint8_t* dst = codes_sec + boff + (int64_t)ch * colb + tok0 * BITS / 8;
           // partial group: this thread's codes start at byte tok0 * BITS / 8
           const int nbytes = (nvt * BITS + 7) / 8;
 #pragma unroll
@@ -1168,7 +1186,15 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
             if (i < nbytes) dst[i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
         }
         const bool writer = (G == 64) ? (th == 0) : true;
-        if (writer && ntok > 0) prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch] = gq.packed;
+        if constexpr (FULL) {
+          const int grp0 = (G == 64) ? g64 : 2 * g64;
+          const uint32_t pstride = (G == 64) ? 0u : (uint32_t)H * kHeadDim;   // next group, in words
+          const __amdgpu_buffer_rsrc_t prs =
+              make_rsrc(prm + (((int64_t)l * ngr + grp0) * H + h) * kHeadDim, 4u * (pstride + kHeadDim));
+          if (writer) bstore4(gq.packed, prs, 4u * ((uint32_t)th * pstride + (uint32_t)ch), 0);
+        } else if (writer && ntok > 0) {
+          prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch] = gq.packed;
+        }
         if constexpr (G == 64 && FULL && BITS >= 4) {
           if (c.nnz_pipe && c.nnz_sec[which]) {
             // this thread's codes: 4 * BITS bytes at ch * 8 BITS + th * 4 BITS of
@@ -1202,8 +1228,8 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
           }
         }
       };
-      if (gg == 64) pass(std::true_type{});
-      else pass(std::false_type{});
+      if constexpr (TAIL) pass(std::false_type{});
+      else pass(std::true_type{});
       __syncthreads();                                   // before the next pass overwrites zb
     }
     const int nt = tile + step;
@@ -1217,6 +1243,7 @@ __global__ __launch_bounds__(128, 4) void k_encode_channel(CallDesc c, int which
     } else {
       decode_tile(nt, l, g64, h);
     }
+    if constexpr (TAIL) g64 = T / 64;
   }
 }
 
@@ -1424,6 +1451,11 @@ static int grid_for(int64_t blocks_needed, int cap) {
 #define KVC_TOKEN_CASES(KERNEL, BITS, BF)                                          \
   if (c.page_tokens) { KVC_TOKEN_CASES_P(KERNEL, BITS, BF, true) }                 \
   else { KVC_TOKEN_CASES_P(KERNEL, BITS, BF, false) }
+#define KVC_ENC_CHANNEL_CASES(BF, BITS, TAIL)                                      \
+  switch (pol.group) {                                                             \
+    case 32: k_encode_channel<BITS, 32, BF, TAIL><<<grid, block, 0, s>>>(c, which); break; \
+    default: k_encode_channel<BITS, 64, BF, TAIL><<<grid, block, 0, s>>>(c, which); break; \
+  }
 #define KVC_CHANNEL_CASES(KERNEL, BITS, BF)                                        \
   switch (pol.group) {                                                             \
     case 32: KERNEL<BITS, 32, BF><<<grid, block, 0, s>>>(c, which); break;        \
@@ -1447,9 +1479,17 @@ hipError_t launch_encode_fused(const CallDesc& c, int which, hipStream_t s) {
     else { KVC_BITS_CASES(KVC_TOKEN_CASES, k_encode_token, false) }
   } else {
     const dim3 block(128);
-    const int grid = grid_for(tiles, 256 * 32);
-    if (c.dtype == 1) { KVC_BITS_CASES(KVC_CHANNEL_CASES, k_encode_channel, true) }
-    else { KVC_BITS_CASES(KVC_CHANNEL_CASES, k_encode_channel, false) }
+    const int T = c.one.T;
+    if (T >= 64) {
+      const int grid = grid_for((int64_t)c.layers * (T / 64) * c.heads, 256 * 32);
+      if (c.dtype == 1) { KVC_BITS_CASES(KVC_ENC_CHANNEL_CASES, true, false) }
+      else { KVC_BITS_CASES(KVC_ENC_CHANNEL_CASES, false, false) }
+    }
+    if (T % 64) {
+      const int grid = grid_for((int64_t)c.layers * c.heads, 256 * 32);
+      if (c.dtype == 1) { KVC_BITS_CASES(KVC_ENC_CHANNEL_CASES, true, true) }
+      else { KVC_BITS_CASES(KVC_ENC_CHANNEL_CASES, false, true) }
+    }
   }
   return hipGetLastError();
 }
