@@ -77,7 +77,32 @@ def cpu_baseline(wl, layers: int):
     return {"value": round(U / (t2 - t0) / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"layers 0..{layers - 1} of the workload ({U / 1e9:.3f} GB of K+V), encode + decode",
             "encode_GBps": round(U / (t1 - t0) / 1e9, 6), "decode_GBps": round(U / (t2 - t1) / 1e9, 6),
-            "seconds": round(t2 - t0, 2)}
+            "seconds": round(t2 - t0, 2), "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count()}
+
+
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Figures the pages report for their own implementation, with the hardware
+# they name (other machines: context, not a target for this metric).
+PAGES_FIGURES = {
+    "fused_transform_quantize_speedup": {
+        "value": "up to 5.9x", "over": "separate transform and quantize kernels",
+        "hardware": "NVIDIA RTX 5090 (local setup) and RTX PRO 6000 / H100 (remote setup); the figure is not tied to one"},
+    "lossless_backend_GBps": {"before": "< 90 (nvCOMP integration)", "after": "> 500 (searched LC pipeline)",
+                              "hardware": "as above"},
+    "complete_path_table1": {
+        "RTX PRO 6000, fused + LC": {"compression_ratio": 6.276, "comp_GBps": 139.218, "decomp_GBps": 155.841},
+        "H100, fused + LC": {"compression_ratio": 6.280, "comp_GBps": 91.606, "decomp_GBps": 103.104}},
+}
 
 
 def main():
@@ -233,6 +258,17 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "algorithmic_bytes": round(cand[dom]), "traffic": None},
     }
+    # each fused kernel, and the K and V kernels of one direction together
+    fk = {}
+    for k_ in cand:
+        gbps = cand[k_] / (avg[k_] * 1e-3) / 1e9
+        fk[k_] = {"ms": round(avg[k_], 4), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    for name, a_, b_ in (("ENCODE", "ENCODE_K", "ENCODE_V"), ("DECODE", "DECODE_K", "DECODE_V")):
+        ms_ = avg[a_] + avg[b_]
+        gbps = (cand[a_] + cand[b_]) / (ms_ * 1e-3) / 1e9
+        fk[name + "_K+V"] = {"ms": round(ms_, 4), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    result["fused_kernels"] = fk
+    result["pages_figures"] = PAGES_FIGURES
     t = counted_traffic(dom) if (args.workload == "c3_llama70b_32k" and args.values == "gaussian") else None
     if t is not None:
         result["roofline"]["traffic"] = t["bytes"]

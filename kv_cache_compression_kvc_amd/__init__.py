@@ -1,4 +1,5 @@
-"""Python binding of libkvc (the C ABI declared in include/kvc.h).
+"""Python binding of libkvc (the C ABI declared in include/kvc.h and
+include/kvc_select.h).
 
 Argument marshalling only: every step of the compression path runs in the
 library's HIP kernels.  PyTorch supplies device memory and streams.  The
@@ -36,6 +37,25 @@ class Config(C.Structure):
                 ("lossless", C.c_uint8 * 4), ("chunk_bytes", C.c_uint32), ("page_tokens", C.c_int32)]
 
 
+class Profile(C.Structure):
+    _fields_ = [("id", C.c_int32), ("bucket", C.c_int32), ("cr", C.c_double), ("s_enc", C.c_double),
+                ("s_dec", C.c_double)]
+
+
+class SelectorConfig(C.Structure):
+    _fields_ = [("struct_size", C.c_uint32), ("fallback_id", C.c_int32), ("alpha", C.c_double),
+                ("epsilon", C.c_double), ("cooldown_k", C.c_int32), ("cooldown_m", C.c_int32),
+                ("cooldown_len", C.c_int32), ("reserved", C.c_int32), ("seed", C.c_uint64)]
+
+
+class RequestContext(C.Structure):
+    _fields_ = [("bucket", C.c_int32), ("reserved", C.c_int32), ("bandwidth", C.c_double),
+                ("volume", C.c_double), ("t_model", C.c_double), ("t_slo", C.c_double)]
+
+
+PROFILE_RAW = -1
+
+
 class KvcError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -66,6 +86,15 @@ def lib():
             "kvc_profile_enable": [C.c_int],
             "kvc_profile_reset": [],
             "kvc_profile_query": [C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_int64)],
+            "kvc_predicted_jct": [C.POINTER(Profile), C.POINTER(RequestContext), C.POINTER(C.c_double)],
+            "kvc_selector_create": [C.POINTER(Profile), I32, C.POINTER(SelectorConfig), C.POINTER(C.c_void_p)],
+            "kvc_selector_destroy": [P],
+            "kvc_selector_envelope": [P, I32, I32, C.POINTER(I32), C.POINTER(C.c_double), C.POINTER(I32)],
+            "kvc_selector_model_choice": [P, I32, C.c_double, C.POINTER(I32)],
+            "kvc_selector_choose": [P, C.POINTER(RequestContext), C.POINTER(I32), C.POINTER(C.c_double)],
+            "kvc_selector_observe": [P, C.POINTER(RequestContext), I32, C.c_double],
+            "kvc_selector_state": [P, C.POINTER(RequestContext), I32, C.POINTER(C.c_double), C.POINTER(I64),
+                                   C.POINTER(I32)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -75,6 +104,10 @@ def lib():
         L.kvc_status_string.restype = C.c_char_p
         L.kvc_last_error.argtypes = []
         L.kvc_last_error.restype = C.c_char_p
+        for name in ("kvc_harmonic_throughput", "kvc_break_even_bandwidth"):
+            f = getattr(L, name)
+            f.argtypes = [C.c_double] * (2 if name == "kvc_harmonic_throughput" else 3)
+            f.restype = C.c_double
         _lib = L
     return _lib
 
@@ -209,3 +242,84 @@ def profile_query(kind) -> tuple:
     ms, n = C.c_double(0), C.c_int64(0)
     _check(lib().kvc_profile_query(k, C.byref(ms), C.byref(n)), "kvc_profile_query")
     return ms.value, n.value
+
+
+# ---------------------------------------------------------------- selection
+def harmonic_throughput(s_enc: float, s_dec: float) -> float:
+    return lib().kvc_harmonic_throughput(s_enc, s_dec)
+
+
+def break_even_bandwidth(cr: float, s_enc: float, s_dec: float) -> float:
+    return lib().kvc_break_even_bandwidth(cr, s_enc, s_dec)
+
+
+def _ctx(bucket: int, bandwidth: float, volume: float, t_model: float, t_slo: float) -> RequestContext:
+    return RequestContext(bucket=bucket, bandwidth=bandwidth, volume=volume, t_model=t_model, t_slo=t_slo)
+
+
+def predicted_jct(profile: Optional[tuple], bucket: int, bandwidth: float, volume: float, t_model: float,
+                  t_slo: float = 0.0) -> float:
+    """Eq. 1 prediction; profile = (id, bucket, cr, s_enc, s_dec) or None for raw transfer."""
+    out = C.c_double()
+    p = C.byref(Profile(*profile)) if profile is not None else None
+    _check(lib().kvc_predicted_jct(p, C.byref(_ctx(bucket, bandwidth, volume, t_model, t_slo)), C.byref(out)),
+           "kvc_predicted_jct")
+    return out.value
+
+
+class Selector:
+    """Service-aware profile selector over measured profiles (host only)."""
+
+    def __init__(self, profiles: Sequence[tuple], fallback_id: int = PROFILE_RAW, alpha: float = 0.2,
+                 epsilon: float = 0.1, cooldown_k: int = 2, cooldown_m: int = 8, cooldown_len: int = 16,
+                 seed: int = 0):
+        arr = (Profile * max(len(profiles), 1))(*[Profile(*p) for p in profiles])
+        cfg = SelectorConfig(struct_size=C.sizeof(SelectorConfig), fallback_id=fallback_id, alpha=alpha,
+                             epsilon=epsilon, cooldown_k=cooldown_k, cooldown_m=cooldown_m,
+                             cooldown_len=cooldown_len, seed=seed)
+        h = C.c_void_p()
+        _check(lib().kvc_selector_create(arr, len(profiles), C.byref(cfg), C.byref(h)), "kvc_selector_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().kvc_selector_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def envelope(self, bucket: int):
+        n = C.c_int32()
+        s = lib().kvc_selector_envelope(self._h, bucket, 0, None, None, C.byref(n))
+        if s not in (OK, ERR_BUFFER_TOO_SMALL):
+            _check(s, "kvc_selector_envelope")
+        ids = (C.c_int32 * n.value)()
+        xs = (C.c_double * n.value)()
+        _check(lib().kvc_selector_envelope(self._h, bucket, n.value, ids, xs, C.byref(n)), "kvc_selector_envelope")
+        return list(ids), list(xs)
+
+    def model_choice(self, bucket: int, bandwidth: float) -> int:
+        out = C.c_int32()
+        _check(lib().kvc_selector_model_choice(self._h, bucket, bandwidth, C.byref(out)), "kvc_selector_model_choice")
+        return out.value
+
+    def choose(self, bucket: int, bandwidth: float, volume: float, t_model: float, t_slo: float):
+        out, pred = C.c_int32(), C.c_double()
+        _check(lib().kvc_selector_choose(self._h, C.byref(_ctx(bucket, bandwidth, volume, t_model, t_slo)),
+                                         C.byref(out), C.byref(pred)), "kvc_selector_choose")
+        return out.value, pred.value
+
+    def observe(self, bucket: int, bandwidth: float, volume: float, t_model: float, t_slo: float, pid: int,
+                observed: float):
+        _check(lib().kvc_selector_observe(self._h, C.byref(_ctx(bucket, bandwidth, volume, t_model, t_slo)),
+                                          pid, observed), "kvc_selector_observe")
+
+    def state(self, bucket: int, bandwidth: float, pid: int):
+        r, n, cl = C.c_double(), C.c_int64(), C.c_int32()
+        _check(lib().kvc_selector_state(self._h, C.byref(_ctx(bucket, bandwidth, 0.0, 0.0, 0.0)), pid,
+                                        C.byref(r), C.byref(n), C.byref(cl)), "kvc_selector_state")
+        return r.value, n.value, cl.value

@@ -186,6 +186,11 @@ void prof_harvest_locked() {
 }  // namespace
 
 namespace kvc {
+// records msg as the calling thread's last error (kvc_last_error) and returns s
+kvc_status report_error(kvc_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace kvc
+
+namespace kvc {
 void prof_begin(int kind, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
