@@ -18,6 +18,8 @@ from __future__ import annotations
 import dataclasses
 from typing import Optional, Tuple
 
+import math
+
 import numpy as np
 import torch
 
@@ -220,6 +222,40 @@ def paged_pools(wl: Workload, batch: PagedBatch, seed: Optional[int] = None, dev
                 x[T:] = 0
                 pool[l, blocks] = x.view(npg, P, wl.heads, wl.head_dim)
     return kp, vp
+
+
+def correlated_kv(wl: Workload, layers: int, tokens: int, seed: int, device="cpu", rho=0.95):
+    """K/V whose values follow a first-order autoregression along tokens
+    (x_t = rho x_{t-1} + sqrt(1 - rho^2) e_t per layer, head and channel,
+    unit variance), with the workload's K outlier channels scaled as in
+    dense_kv.  A stand-in for the token locality of real KV caches (adjacent
+    tokens carry similar values), which gives the lossless stage something to
+    find; the values are synthetic, not taken from any model."""
+    H, D = wl.heads, wl.head_dim
+    out = []
+    for which in ("k", "v"):
+        t = torch.empty((layers, tokens, H, D), dtype=wl.torch_dtype, device=device)
+        for l in range(layers):
+            g = _gen(seed * 1000003 + l * 2 + (0 if which == "k" else 1), device)
+            x = torch.randn((tokens, H, D), generator=g, device=device, dtype=torch.float32)
+            x *= math.sqrt(1.0 - rho * rho)
+            x[0] /= math.sqrt(1.0 - rho * rho)
+            # y_t = sum_{s <= t} rho^(t - s) x_s by doubling: after the step
+            # with shift d each y_t holds the terms s > t - 2d
+            d, f = 1, rho
+            while d < tokens:
+                x[d:] = x[d:] + f * x[:-d].clone()
+                d, f = 2 * d, f * f
+            if which == "k":
+                chans, facs = _outlier_channels(wl, l, seed)
+                scale = torch.ones((H, D), dtype=torch.float32)
+                for h in range(H):
+                    for c, fc in zip(chans[h], facs[h]):
+                        scale[h, int(c)] = float(fc)
+                x = x * scale.to(device)
+            t[l] = x.to(wl.torch_dtype)
+        out.append(t)
+    return out[0], out[1]
 
 
 def zero_rich_kv(wl: Workload, layers: int, tokens: int, seed: int, device="cpu", zero_frac=0.9):
