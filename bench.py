@@ -80,6 +80,33 @@ def cpu_baseline(wl, layers: int):
             "seconds": round(t2 - t0, 2), "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count()}
 
 
+def selection_cost(U: float, s_enc: float, s_dec: float, cr: float, requests: int = 20000) -> dict:
+    """Host cost of the service-aware controller (KVServe Sec. 6.2) per request:
+    one choose + observe on the library's selector, with this run's measured
+    profile and two derived ones (quantization only at twice the ratio and
+    half the speed, and the reverse) in one bucket, over a sweep of link
+    speeds around the profile's break-even bandwidth."""
+    import random
+    import kv_cache_compression_kvc_amd as K
+    profs = [(0, 0, cr, s_enc, s_dec), (1, 0, 2 * cr, s_enc / 2, s_dec / 2), (2, 0, max(1.01, cr / 2), 2 * s_enc, 2 * s_dec)]
+    sel = K.Selector(profs, epsilon=0.1, seed=1)
+    rng = random.Random(0)
+    bstar = K.break_even_bandwidth(cr, s_enc, s_dec)
+    ctxs = [(0, bstar * 10 ** rng.uniform(-2, 0.5), U, 0.05, 1e9) for _ in range(requests)]
+    t0 = time.perf_counter()
+    for c in ctxs:
+        pid, pred = sel.choose(*c)
+        sel.observe(*c, pid, pred * 1.05)
+    dt = time.perf_counter() - t0
+    env = sel.envelope(0)
+    sel.close()
+    return {"us_per_request": round(dt / requests * 1e6, 3), "requests": requests,
+            "break_even_bandwidth_GBps": round(bstar / 1e9, 1),
+            "envelope": [{"profile": i, "from_GBps": (None if x == 0.0 else round(1 / x / 1e9, 1))}
+                         for i, x in zip(*env)],
+            "note": "python ctypes calls included; profile -1 = raw transfer"}
+
+
 def host_cpu() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -269,6 +296,7 @@ def main():
         fk[name + "_K+V"] = {"ms": round(ms_, 4), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     result["fused_kernels"] = fk
     result["pages_figures"] = PAGES_FIGURES
+    result["selection"] = selection_cost(U, U / (enc_ms * 1e-3), U / (dec_ms * 1e-3), U / n)
     t = counted_traffic(dom) if (args.workload == "c3_llama70b_32k" and args.values == "gaussian") else None
     if t is not None:
         result["roofline"]["traffic"] = t["bytes"]
