@@ -748,7 +748,8 @@ extern "C" int kvco_chunk_decode(const uint8_t* stages, const uint8_t* in, size_
 
 /* ======================================================================
  * Stream format (this project's; little-endian)
- *   [0,64)   header: magic "KVC1", u16 version 1, u8 dtype, u8 0,
+ *   [0,64)   header: magic "KVC1", u16 version 1, u8 dtype, u8 flags (bit 0:
+ *            mixed precision, below; other bits 0),
  *            i32 layers, tokens, heads, head_dim,
  *            K policy {u8 bits, u8 axis, u8 hadamard, u8 0, u16 group, u16 0},
  *            V policy (same), u64 seed, u8 stages[4], u32 chunk_bytes,
@@ -766,18 +767,76 @@ static int64_t align16(int64_t x) { return (x + 15) & ~(int64_t)15; }
 
 struct Layout {
   int64_t codes[2], params[2], nchunks[2];
-  int64_t table_off, params_off[2], payload_off, max_total;
+  int64_t table_off, map_off, params_off[2], payload_off, max_total;
 };
 
-static Layout layout_of(const kvco_cfg* cfg, int tokens) {
+/* ======================================================================
+ * Mixed precision per (layer, head).  KVServe Sec. 5.1 (MixHQ, and its
+ * layer-wise generalization) keeps some heads at high precision and others at
+ * very low bit widths; the mechanism here takes the width of every (tensor,
+ * layer, head) as input: 2, 4 or 8 bits through the quantizer, or 16 to keep
+ * the head's 16-bit values unchanged.  Stream: flags bit 0 set; right after
+ * the header the 2 * layers * heads widths (K then V, layer-major,
+ * head-minor), then, 16-byte aligned, the chunk table; every codes and
+ * parameter section is the
+ * concatenation, in the same (layer, head) order, of the sections a
+ * one-layer, one-head uniform stream with that head's width would hold
+ * (width 16: the tokens x head_dim 16-bit values, no parameters).
+ * ====================================================================== */
+static kvco_cfg slab_cfg(const kvco_cfg* cfg, int which, int bits) {
+  kvco_cfg s = *cfg;
+  s.layers = 1;
+  s.heads = 1;
+  if (which == 0) s.k_bits = bits; else s.v_bits = bits;
+  return s;
+}
+
+static int64_t slab_codes_bytes(const kvco_cfg* cfg, int which, int bits, int tokens) {
+  if (bits == 16) return (int64_t)tokens * cfg->head_dim * 2;
+  const kvco_cfg s = slab_cfg(cfg, which, bits);
+  return kvco_codes_bytes(&s, which, tokens);
+}
+
+static int64_t slab_params_bytes(const kvco_cfg* cfg, int which, int bits, int tokens) {
+  if (bits == 16) return 0;
+  const kvco_cfg s = slab_cfg(cfg, which, bits);
+  return kvco_params_bytes(&s, which, tokens);
+}
+
+static int check_bits_map(const kvco_cfg* cfg, const uint8_t* bits) {
+  if (!bits) return KVCO_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < 2 * (int64_t)cfg->layers * cfg->heads; ++i) {
+    const int b = bits[i];
+    if (b != 2 && b != 4 && b != 8 && b != 16) return KVCO_ERR_INVALID_ARG;
+    if (b != 16) {
+      const int which = i < (int64_t)cfg->layers * cfg->heads ? 0 : 1;
+      const kvco_cfg s = slab_cfg(cfg, which, b);
+      if (check_cfg(&s) != KVCO_OK) return KVCO_ERR_INVALID_ARG;
+    }
+  }
+  return KVCO_OK;
+}
+
+/* bits == NULL: uniform layout */
+static Layout layout_of(const kvco_cfg* cfg, int tokens, const uint8_t* bits = nullptr) {
   Layout L;
+  const int64_t LH = (int64_t)cfg->layers * cfg->heads;
   for (int w = 0; w < 2; ++w) {
-    L.codes[w] = kvco_codes_bytes(cfg, w, tokens);
-    L.params[w] = kvco_params_bytes(cfg, w, tokens);
+    if (!bits) {
+      L.codes[w] = kvco_codes_bytes(cfg, w, tokens);
+      L.params[w] = kvco_params_bytes(cfg, w, tokens);
+    } else {
+      L.codes[w] = L.params[w] = 0;
+      for (int64_t i = 0; i < LH; ++i) {
+        L.codes[w] += slab_codes_bytes(cfg, w, bits[w * LH + i], tokens);
+        L.params[w] += slab_params_bytes(cfg, w, bits[w * LH + i], tokens);
+      }
+    }
     L.nchunks[w] = ceil_div(L.codes[w], cfg->chunk_bytes);
   }
-  L.table_off = 64;
-  L.params_off[0] = align16(64 + 4 * (L.nchunks[0] + L.nchunks[1]));
+  L.map_off = 64;
+  L.table_off = bits ? align16(64 + 2 * LH) : 64;
+  L.params_off[0] = align16(L.table_off + 4 * (L.nchunks[0] + L.nchunks[1]));
   L.params_off[1] = align16(L.params_off[0] + L.params[0]);
   L.payload_off = align16(L.params_off[1] + L.params[1]);
   int64_t pay = 0;
@@ -803,11 +862,12 @@ static uint16_t r16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
 static uint32_t r32(const uint8_t* p) { uint32_t v = 0; for (int i = 0; i < 4; ++i) v |= (uint32_t)p[i] << (8 * i); return v; }
 static uint64_t r64(const uint8_t* p) { uint64_t v = 0; for (int i = 0; i < 8; ++i) v |= (uint64_t)p[i] << (8 * i); return v; }
 
-static void write_header(uint8_t* o, const kvco_cfg* cfg, int tokens, uint64_t total) {
+static void write_header(uint8_t* o, const kvco_cfg* cfg, int tokens, uint64_t total, int flags = 0) {
   std::memset(o, 0, 64);
   w32(o + 0, MAGIC);
   w16(o + 4, 1);
   o[6] = (uint8_t)cfg->dtype;
+  o[7] = (uint8_t)flags;
   w32(o + 8, (uint32_t)cfg->layers);
   w32(o + 12, (uint32_t)tokens);
   w32(o + 16, (uint32_t)cfg->heads);
@@ -824,22 +884,84 @@ static void write_header(uint8_t* o, const kvco_cfg* cfg, int tokens, uint64_t t
   w64(o + 56, total);
 }
 
-extern "C" int kvco_encode(const kvco_cfg* cfg, const uint16_t* k, const uint16_t* v, int tokens,
-                           uint8_t* out, size_t cap, size_t* out_bytes) {
+/* Codes and parameters of one tensor of a mixed stream: each (layer, head)
+ * slab is gathered into a one-layer, one-head tensor and quantized as a
+ * uniform stream of its width would be, or copied for width 16. */
+static int quantize_mixed(const kvco_cfg* cfg, const uint8_t* bits, int which, const uint16_t* x, int T,
+                          uint8_t* codes, uint8_t* params) {
+  const int H = cfg->heads, D = cfg->head_dim;
+  const int64_t LH = (int64_t)cfg->layers * H;
+  std::vector<uint16_t> slab((size_t)T * D);
+  int status = KVCO_OK;
+  int64_t co = 0, po = 0;
+  for (int l = 0; l < cfg->layers; ++l)
+    for (int h = 0; h < H; ++h) {
+      const int b = bits[which * LH + (int64_t)l * H + h];
+      for (int t = 0; t < T; ++t)
+        std::memcpy(&slab[(size_t)t * D], x + (((int64_t)l * T + t) * H + h) * D, (size_t)D * 2);
+      if (b == 16) {
+        std::memcpy(codes + co, slab.data(), (size_t)T * D * 2);
+      } else {
+        const kvco_cfg sc = slab_cfg(cfg, which, b);
+        const int r = kvco_quantize_tensor(&sc, which, slab.data(), T, codes + co, params + po);
+        if (r == KVCO_ERR_RANGE) status = KVCO_ERR_RANGE;
+        else if (r != KVCO_OK) return r;
+      }
+      co += slab_codes_bytes(cfg, which, b, T);
+      po += slab_params_bytes(cfg, which, b, T);
+    }
+  return status;
+}
+
+static int dequantize_mixed(const kvco_cfg* cfg, const uint8_t* bits, int which, const uint8_t* codes,
+                            const uint8_t* params, int T, uint16_t* x) {
+  const int H = cfg->heads, D = cfg->head_dim;
+  const int64_t LH = (int64_t)cfg->layers * H;
+  std::vector<uint16_t> slab((size_t)T * D);
+  int64_t co = 0, po = 0;
+  for (int l = 0; l < cfg->layers; ++l)
+    for (int h = 0; h < H; ++h) {
+      const int b = bits[which * LH + (int64_t)l * H + h];
+      if (b == 16) {
+        std::memcpy(slab.data(), codes + co, (size_t)T * D * 2);
+      } else {
+        const kvco_cfg sc = slab_cfg(cfg, which, b);
+        const int r = kvco_dequantize_tensor(&sc, which, codes + co, params + po, T, slab.data());
+        if (r != KVCO_OK) return r;
+      }
+      for (int t = 0; t < T; ++t)
+        std::memcpy(x + (((int64_t)l * T + t) * H + h) * D, &slab[(size_t)t * D], (size_t)D * 2);
+      co += slab_codes_bytes(cfg, which, b, T);
+      po += slab_params_bytes(cfg, which, b, T);
+    }
+  return KVCO_OK;
+}
+
+extern "C" int64_t kvco_max_stream_bytes_mixed(const kvco_cfg* cfg, const uint8_t* bits, int tokens) {
+  if (check_cfg(cfg) != KVCO_OK || tokens < 0 || check_bits_map(cfg, bits) != KVCO_OK) return -1;
+  return layout_of(cfg, tokens, bits).max_total;
+}
+
+static int encode_stream(const kvco_cfg* cfg, const uint8_t* bits, const uint16_t* k, const uint16_t* v,
+                         int tokens, uint8_t* out, size_t cap, size_t* out_bytes) {
   int st = check_cfg(cfg);
   if (st != KVCO_OK) return st;
   if (tokens < 0 || !out || !out_bytes || (tokens > 0 && (!k || !v))) return KVCO_ERR_INVALID_ARG;
-  const Layout L = layout_of(cfg, tokens);
+  if (bits && check_bits_map(cfg, bits) != KVCO_OK) return KVCO_ERR_INVALID_ARG;
+  const Layout L = layout_of(cfg, tokens, bits);
   if ((int64_t)cap < L.max_total) return KVCO_ERR_BUFFER_TOO_SMALL;
   std::memset(out, 0, (size_t)L.max_total);
   int status = KVCO_OK;
   std::vector<uint8_t> codes[2];
   for (int w = 0; w < 2; ++w) {
     codes[w].assign((size_t)L.codes[w], 0);
-    int r = kvco_quantize_tensor(cfg, w, w == 0 ? k : v, tokens, codes[w].data(), out + L.params_off[w]);
+    const uint16_t* x = w == 0 ? k : v;
+    int r = bits ? quantize_mixed(cfg, bits, w, x, tokens, codes[w].data(), out + L.params_off[w])
+                 : kvco_quantize_tensor(cfg, w, x, tokens, codes[w].data(), out + L.params_off[w]);
     if (r == KVCO_ERR_RANGE) status = KVCO_ERR_RANGE;
     else if (r != KVCO_OK) return r;
   }
+  if (bits) std::memcpy(out + L.map_off, bits, (size_t)(2 * (int64_t)cfg->layers * cfg->heads));
   int64_t pos = L.payload_off, ci = 0;
   std::vector<uint8_t> buf(cfg->chunk_bytes);
   for (int w = 0; w < 2; ++w) {
@@ -855,14 +977,36 @@ extern "C" int kvco_encode(const kvco_cfg* cfg, const uint16_t* k, const uint16_
       pos += align16((int64_t)stored);
     }
   }
-  write_header(out, cfg, tokens, (uint64_t)pos);
+  write_header(out, cfg, tokens, (uint64_t)pos, bits ? 1 : 0);
   *out_bytes = (size_t)pos;
   return status;
 }
 
+extern "C" int kvco_encode(const kvco_cfg* cfg, const uint16_t* k, const uint16_t* v, int tokens,
+                           uint8_t* out, size_t cap, size_t* out_bytes) {
+  return encode_stream(cfg, nullptr, k, v, tokens, out, cap, out_bytes);
+}
+
+extern "C" int kvco_encode_mixed(const kvco_cfg* cfg, const uint8_t* bits, const uint16_t* k, const uint16_t* v,
+                                 int tokens, uint8_t* out, size_t cap, size_t* out_bytes) {
+  if (!bits) return KVCO_ERR_INVALID_ARG;
+  return encode_stream(cfg, bits, k, v, tokens, out, cap, out_bytes);
+}
+
+/* The width map of a mixed stream (NULL for a uniform one), after checking
+ * that it lies inside the stream and holds valid widths. */
+static int stream_bits(const uint8_t* in, size_t in_bytes, const kvco_cfg* cfg, const uint8_t** bits) {
+  *bits = nullptr;
+  if (!(in[7] & 1)) return KVCO_OK;
+  if ((int64_t)in_bytes < 64 + 2 * (int64_t)cfg->layers * cfg->heads) return KVCO_ERR_CORRUPT_STREAM;
+  if (check_bits_map(cfg, in + 64) != KVCO_OK) return KVCO_ERR_CORRUPT_STREAM;
+  *bits = in + 64;
+  return KVCO_OK;
+}
+
 extern "C" int kvco_stream_info(const uint8_t* in, size_t in_bytes, kvco_cfg* cfg, int* tokens) {
   if (!in || !cfg || !tokens) return KVCO_ERR_INVALID_ARG;
-  if (in_bytes < 64 || r32(in) != MAGIC || r16(in + 4) != 1) return KVCO_ERR_CORRUPT_STREAM;
+  if (in_bytes < 64 || r32(in) != MAGIC || r16(in + 4) != 1 || (in[7] & ~1)) return KVCO_ERR_CORRUPT_STREAM;
   std::memset(cfg, 0, sizeof(*cfg));
   cfg->dtype = in[6];
   cfg->layers = (int32_t)r32(in + 8);
@@ -875,7 +1019,9 @@ extern "C" int kvco_stream_info(const uint8_t* in, size_t in_bytes, kvco_cfg* cf
   for (int i = 0; i < 4; ++i) cfg->stages[i] = in[48 + i];
   cfg->chunk_bytes = r32(in + 52);
   if (check_cfg(cfg) != KVCO_OK || *tokens < 0 || *tokens > (1 << 26)) return KVCO_ERR_CORRUPT_STREAM;
-  const Layout L = layout_of(cfg, *tokens);
+  const uint8_t* bits = nullptr;
+  if (stream_bits(in, in_bytes, cfg, &bits) != KVCO_OK) return KVCO_ERR_CORRUPT_STREAM;
+  const Layout L = layout_of(cfg, *tokens, bits);
   const uint64_t total = r64(in + 56);
   if ((int64_t)total < L.payload_off || (int64_t)total > L.max_total || total > in_bytes)
     return KVCO_ERR_CORRUPT_STREAM;
@@ -889,7 +1035,9 @@ extern "C" int kvco_decode(const uint8_t* in, size_t in_bytes, uint16_t* k, uint
   const size_t elems = (size_t)cfg.layers * tokens * cfg.heads * cfg.head_dim;
   if (elems > elems_cap) return KVCO_ERR_BUFFER_TOO_SMALL;
   if (elems > 0 && (!k || !v)) return KVCO_ERR_INVALID_ARG;
-  const Layout L = layout_of(&cfg, tokens);
+  const uint8_t* bits = nullptr;
+  stream_bits(in, in_bytes, &cfg, &bits);       /* checked by kvco_stream_info */
+  const Layout L = layout_of(&cfg, tokens, bits);
   const uint64_t total = r64(in + 56);
   int64_t pos = L.payload_off, ci = 0;
   for (int w = 0; w < 2; ++w) {
@@ -906,7 +1054,8 @@ extern "C" int kvco_decode(const uint8_t* in, size_t in_bytes, uint16_t* k, uint
       if (r != KVCO_OK) return r == KVCO_ERR_INVALID_ARG ? KVCO_ERR_CORRUPT_STREAM : r;
       pos += align16(stored);
     }
-    int r = kvco_dequantize_tensor(&cfg, w, codes.data(), in + L.params_off[w], tokens, w == 0 ? k : v);
+    int r = bits ? dequantize_mixed(&cfg, bits, w, codes.data(), in + L.params_off[w], tokens, w == 0 ? k : v)
+                 : kvco_dequantize_tensor(&cfg, w, codes.data(), in + L.params_off[w], tokens, w == 0 ? k : v);
     if (r != KVCO_OK) return r;
   }
   if (pos != (int64_t)total) return KVCO_ERR_CORRUPT_STREAM;

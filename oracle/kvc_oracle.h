@@ -100,6 +100,13 @@ int64_t kvco_max_stream_bytes(const kvco_cfg* cfg, int tokens);
 int kvco_encode(const kvco_cfg* cfg, const uint16_t* k, const uint16_t* v, int tokens,
                 uint8_t* out, size_t cap, size_t* out_bytes);
 int kvco_stream_info(const uint8_t* in, size_t in_bytes, kvco_cfg* cfg_out, int* tokens_out);
+
+/* ---- mixed precision per (layer, head): bits[2][layers][heads] holds 2, 4 or
+ * 8 (that width through the quantizer) or 16 (values kept); kvco_decode reads
+ * both kinds of stream ---- */
+int64_t kvco_max_stream_bytes_mixed(const kvco_cfg* cfg, const uint8_t* bits, int tokens);
+int kvco_encode_mixed(const kvco_cfg* cfg, const uint8_t* bits, const uint16_t* k, const uint16_t* v,
+                      int tokens, uint8_t* out, size_t cap, size_t* out_bytes);
 int kvco_decode(const uint8_t* in, size_t in_bytes, uint16_t* k, uint16_t* v, size_t elems_cap);
 
 /* ---- paged pools: [layers][num_blocks][page_tokens][heads][head_dim] ---- */

@@ -68,6 +68,8 @@ def lib():
             "kvco_chunk_decode": (C.c_int, [P, P, C.c_size_t, C.c_int, P, C.c_size_t]),
             "kvco_max_stream_bytes": (C.c_int64, [P, C.c_int]),
             "kvco_encode": (C.c_int, [P, P, P, C.c_int, P, C.c_size_t, P]),
+            "kvco_max_stream_bytes_mixed": (C.c_int64, [P, P, C.c_int]),
+            "kvco_encode_mixed": (C.c_int, [P, P, P, P, C.c_int, P, C.c_size_t, P]),
             "kvco_stream_info": (C.c_int, [P, C.c_size_t, P, P]),
             "kvco_decode": (C.c_int, [P, C.c_size_t, P, P, C.c_size_t]),
             "kvco_encode_paged": (C.c_int, [P, P, P, C.c_int64, C.c_int, P, C.c_int, P, C.c_int,
@@ -202,6 +204,20 @@ def encode(cfg: Cfg, k_u16: np.ndarray, v_u16: np.ndarray, tokens: int):
     k = np.ascontiguousarray(k_u16, np.uint16)
     v = np.ascontiguousarray(v_u16, np.uint16)
     st = lib().kvco_encode(C.byref(cfg), _p(k), _p(v), tokens, _p(out), cap, C.byref(nb))
+    return st, out[:nb.value]
+
+
+def encode_mixed(cfg: Cfg, bits: np.ndarray, k_u16: np.ndarray, v_u16: np.ndarray, tokens: int):
+    """bits: [2, layers, heads] of 2, 4, 8 or 16."""
+    b = np.ascontiguousarray(bits, np.uint8)
+    cap = lib().kvco_max_stream_bytes_mixed(C.byref(cfg), _p(b), tokens)
+    if cap < 0:
+        return INVALID_ARG, np.zeros(0, np.uint8)
+    out = np.zeros(cap, np.uint8)
+    nb = C.c_size_t(0)
+    k = np.ascontiguousarray(k_u16, np.uint16)
+    v = np.ascontiguousarray(v_u16, np.uint16)
+    st = lib().kvco_encode_mixed(C.byref(cfg), _p(b), _p(k), _p(v), tokens, _p(out), cap, C.byref(nb))
     return st, out[:nb.value]
 
 
