@@ -39,7 +39,8 @@
  * Stream format (version 1, little-endian), produced by kvc_encode and read
  * by kvc_decode:
  *   [0,64)          header: u32 magic 0x3143564B ("KVC1"), u16 version = 1,
- *                   u8 dtype, u8 0, i32 layers, tokens, kv_heads, head_dim,
+ *                   u8 dtype, u8 flags (bit 0: mixed precision, see
+ *                   kvc_plan_mixed; other bits 0), i32 layers, tokens, kv_heads, head_dim,
  *                   K policy {u8 bits, u8 axis, u8 hadamard, u8 0, u16 group,
  *                   u16 0}, V policy (same), u64 sign_seed, u8 lossless[4],
  *                   u32 chunk_bytes, u64 total_bytes
@@ -49,6 +50,11 @@
  *                   of (scale, minimum) fp16 pairs
  *   align 16        code chunks; chunk i starts at the sum over j < i of
  *                   align16(stored_j); all padding bytes are zero
+ *   Mixed-precision streams insert the 2 * L * H widths (K then V, layer-major)
+ *   at [64, 64 + 2LH) and start the chunk table at align16(64 + 2LH); each
+ *   codes / parameter section is then the concatenation over (layer, head) of
+ *   the sections a one-layer, one-head stream of that head's width holds
+ *   (width 16: the T x D 16-bit values, no parameters).
  *   Codes: per-token policy -> [L][T][H][D] packed along head_dim, LSB
  *   first; per-channel policy -> [L][ceil(T/G)][H][D][ceil(Gg*bits/8)]
  *   packed along the group's Gg tokens.  Parameters: per-token ->
@@ -125,6 +131,16 @@ typedef struct {
  * (head_dim != 128, per-channel groups other than 32/64, per-token groups
  * other than 16..128, kv_heads not dividing 32 for per-token policies). */
 kvc_status kvc_plan(const kvc_config* cfg, kvc_plan_t* out);
+
+/* A plan with mixed precision per (layer, head) (KVServe Sec. 5.1: head-wise
+ * and layer-wise mixed precision, e.g. retrieval heads at high precision and
+ * streaming heads at very low bit widths).  h_bits is a host array
+ * [2][layers][kv_heads] (K then V): 0 = the tensor policy's bits, 2 / 4 / 8 =
+ * that width for the head's quantizer (same axis, group and Hadamard), 16 =
+ * the head's 16-bit values kept as they are.  The plan copies it.  Dense
+ * calls only (page_tokens must be 0; paged calls return KVC_ERR_UNSUPPORTED).
+ * Errors as kvc_plan, and KVC_ERR_INVALID_ARG for other width values. */
+kvc_status kvc_plan_mixed(const kvc_config* cfg, const uint8_t* h_bits, kvc_plan_t* out);
 
 kvc_status kvc_plan_destroy(kvc_plan_t plan);
 

@@ -75,6 +75,7 @@ def lib():
         P, I32, I64, SZ, U64P = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.POINTER(C.c_uint64)
         sig = {
             "kvc_plan": [C.POINTER(Config), C.POINTER(C.c_void_p)],
+            "kvc_plan_mixed": [C.POINTER(Config), P, C.POINTER(C.c_void_p)],
             "kvc_plan_destroy": [P],
             "kvc_plan_sizes": [P, I64, C.POINTER(SZ), C.POINTER(SZ)],
             "kvc_plan_sizes_paged": [P, P, I32, C.POINTER(SZ), C.POINTER(SZ)],
@@ -166,10 +167,17 @@ def _stream(stream) -> int:
 class Plan:
     """An immutable plan (kvc_plan / kvc_plan_destroy)."""
 
-    def __init__(self, cfg: Config):
+    def __init__(self, cfg: Config, bits=None):
+        """bits: optional [2][layers][kv_heads] widths (0 / 2 / 4 / 8 / 16) for a
+        mixed-precision plan (kvc_plan_mixed)."""
         self.cfg = cfg
         h = C.c_void_p()
-        _check(lib().kvc_plan(C.byref(cfg), C.byref(h)), "kvc_plan")
+        if bits is None:
+            _check(lib().kvc_plan(C.byref(cfg), C.byref(h)), "kvc_plan")
+        else:
+            import numpy as np
+            b = np.ascontiguousarray(bits, dtype=np.uint8)
+            _check(lib().kvc_plan_mixed(C.byref(cfg), b.ctypes.data, C.byref(h)), "kvc_plan_mixed")
         self.handle = h
 
     def __del__(self):

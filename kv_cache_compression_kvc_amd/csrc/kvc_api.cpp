@@ -26,6 +26,8 @@ struct kvc_plan_s {
   kvc_config cfg;
   TensorPol pol[2];
   uint32_t signs[4];
+  bool mixed = false;
+  std::vector<uint8_t> widths;   // mixed: [2][layers][kv_heads] of 2, 4, 8 or 16
 };
 
 namespace {
@@ -113,20 +115,44 @@ bool fused_count_ok(const TensorPol& p, int T, uint32_t chunk_bytes) {
   return p.group == 64 && p.bits >= 4 && T % 64 == 0 && chunk_bytes % (kHeadDim * 64 * p.bits / 8) == 0;
 }
 
+// Codes / parameter bytes of one (layer, head) slab of width `bits` (16:
+// the 16-bit values themselves): the sections of a one-layer, one-head
+// uniform stream of that width.
+int64_t slab_codes_bytes(const TensorPol& p, int bits, int T) {
+  if (bits == 16) return (int64_t)T * kHeadDim * 2;
+  TensorPol q = p;
+  q.bits = bits;
+  return codes_bytes_of(q, 1, T, 1);
+}
+int64_t slab_params_bytes(const TensorPol& p, int bits, int T) {
+  if (bits == 16) return 0;
+  return params_bytes_of(p, 1, T, 1);
+}
+
 // Fill the stream layout of one request with T tokens (offsets inside its stream).
 void request_layout(const kvc_plan_s* p, int T, ReqDesc& rq) {
   const kvc_config& c = p->cfg;
   std::memset(&rq, 0, sizeof(rq));
   rq.T = T;
   int64_t nch = 0;
+  const int64_t LH = (int64_t)c.layers * c.kv_heads;
   for (int w = 0; w < 2; ++w) {
-    rq.codes_bytes[w] = codes_bytes_of(p->pol[w], c.layers, T, c.kv_heads);
-    rq.params_bytes[w] = params_bytes_of(p->pol[w], c.layers, T, c.kv_heads);
+    if (!p->mixed) {
+      rq.codes_bytes[w] = codes_bytes_of(p->pol[w], c.layers, T, c.kv_heads);
+      rq.params_bytes[w] = params_bytes_of(p->pol[w], c.layers, T, c.kv_heads);
+    } else {
+      for (int64_t i = 0; i < LH; ++i) {
+        rq.codes_bytes[w] += slab_codes_bytes(p->pol[w], p->widths[w * LH + i], T);
+        rq.params_bytes[w] += slab_params_bytes(p->pol[w], p->widths[w * LH + i], T);
+      }
+    }
     rq.nchunks[w] = (int32_t)cdiv(rq.codes_bytes[w], c.chunk_bytes);
     nch += rq.nchunks[w];
     rq.params_ws_off[w] = -1;
   }
-  rq.params_off[0] = a16(kHeaderBytes + 4 * nch);
+  // mixed streams carry the width map right after the header
+  rq.table_off = p->mixed ? a16(kHeaderBytes + 2 * LH) : kHeaderBytes;
+  rq.params_off[0] = a16(rq.table_off + 4 * nch);
   rq.params_off[1] = a16(rq.params_off[0] + rq.params_bytes[0]);
   rq.payload_off = a16(rq.params_off[1] + rq.params_bytes[1]);
   int64_t pay = 0;
@@ -138,10 +164,18 @@ void request_layout(const kvc_plan_s* p, int T, ReqDesc& rq) {
 
 // Workspace carving shared by all calls.
 struct WsLayout {
-  int64_t ctl, sizes, offs, worklist, codes, params, reqs, total;
+  int64_t ctl, sizes, offs, worklist, codes, params, reqs, slabs, total;
 };
 
-WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int64_t R) {
+// Bytes of the slab tables (a SlabDesc per (tensor, layer, head)) and the width
+// map that a mixed call uploads into its workspace.
+int64_t slab_area(const kvc_plan_s* p) {
+  if (!p->mixed) return 0;
+  const int64_t n = 2 * (int64_t)p->cfg.layers * p->cfg.kv_heads;
+  return a256(n * (int64_t)sizeof(SlabDesc)) + a256(n);
+}
+
+WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int64_t R, int64_t slabs = 0) {
   WsLayout w;
   w.ctl = 0;
   w.sizes = 256;
@@ -151,8 +185,47 @@ WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int
   w.codes = a256(w.worklist + 4 * std::max<int64_t>(nchunks, 1));
   w.params = a256(w.codes + codes_area);
   w.reqs = a256(w.params + params_area);
-  w.total = a256(w.reqs + (R > 1 ? R * (int64_t)sizeof(ReqDesc) : 0));
+  w.slabs = a256(w.reqs + (R > 1 ? R * (int64_t)sizeof(ReqDesc) : 0));
+  w.total = a256(w.slabs + slabs);
   return w;
+}
+
+// Slab tables of a mixed dense call with T tokens, grouped per tensor and width
+// (2, 4, 8, 16) in (layer, head) order, followed by the width map; first[w][k]
+// and count[w][k] index the group of width {2, 4, 8, 16}[k].
+struct SlabTables {
+  std::vector<uint8_t> bytes;
+  int first[2][4], count[2][4];
+  int64_t map_off;
+};
+
+SlabTables slab_tables(const kvc_plan_s* p, int T) {
+  static const int kW[4] = {2, 4, 8, 16};
+  SlabTables t;
+  const int L = p->cfg.layers, H = p->cfg.kv_heads;
+  const int64_t LH = (int64_t)L * H;
+  std::vector<SlabDesc> all;
+  for (int w = 0; w < 2; ++w) {
+    std::vector<int64_t> co(LH), po(LH);
+    int64_t c = 0, q = 0;
+    for (int64_t i = 0; i < LH; ++i) {
+      co[i] = c;
+      po[i] = q;
+      c += slab_codes_bytes(p->pol[w], p->widths[w * LH + i], T);
+      q += slab_params_bytes(p->pol[w], p->widths[w * LH + i], T);
+    }
+    for (int k = 0; k < 4; ++k) {
+      t.first[w][k] = (int)all.size();
+      for (int64_t i = 0; i < LH; ++i)
+        if (p->widths[w * LH + i] == kW[k]) all.push_back(SlabDesc{(int32_t)(i / H), (int32_t)(i % H), co[i], po[i]});
+      t.count[w][k] = (int)all.size() - t.first[w][k];
+    }
+  }
+  t.map_off = a256((int64_t)all.size() * (int64_t)sizeof(SlabDesc));
+  t.bytes.assign((size_t)(t.map_off + 2 * LH), 0);
+  std::memcpy(t.bytes.data(), all.data(), all.size() * sizeof(SlabDesc));
+  std::memcpy(t.bytes.data() + t.map_off, p->widths.data(), (size_t)(2 * LH));
+  return t;
 }
 
 // ---------------------------------------------------------------- profiling
@@ -312,6 +385,51 @@ PagedJob paged_job(const kvc_plan_s* p, const int32_t* lens, int R, bool encode)
   return j;
 }
 
+// Upload the slab tables and width map of a mixed dense call into the
+// workspace (a few KiB, host to device on the call's stream; the source
+// buffer may be reused once hipMemcpyAsync returns).
+kvc_status upload_slabs(const kvc_plan_s* p, int T, uint8_t* d_area, hipStream_t s, CallDesc& c, SlabTables& tb) {
+  try {
+    tb = slab_tables(p, T);
+  } catch (const std::bad_alloc&) {
+    return fail(KVC_ERR_NO_MEMORY, "slab table allocation failed");
+  }
+  const hipError_t e = hipMemcpyAsync(d_area, tb.bytes.data(), tb.bytes.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(slab tables)");
+  c.mixed = 1;
+  c.slabs = (const SlabDesc*)d_area;
+  c.width_map = d_area + tb.map_off;
+  return KVC_OK;
+}
+
+// The fused encode (or reconstruct) launches of one tensor: one launch for a
+// uniform plan; for a mixed plan one per width present over that width's
+// slabs, and the 16-bit slabs copied as they are.
+hipError_t fused_all(const kvc_plan_s* p, const CallDesc& c, const SlabTables& tb, int which, bool encode,
+                     hipStream_t s) {
+  if (!c.mixed) return encode ? launch_encode_fused(c, which, s) : launch_decode_fused(c, which, s);
+  static const int kW[4] = {2, 4, 8, 16};
+  const int T = c.one.T;
+  for (int k = 0; k < 4; ++k) {
+    const int n = tb.count[which][k];
+    if (n == 0) continue;
+    CallDesc cb = c;
+    cb.slabs = c.slabs + tb.first[which][k];
+    cb.nslabs = n;
+    hipError_t e;
+    if (kW[k] == 16) {
+      e = launch_slab_copy(cb, which, encode, s);
+    } else {
+      cb.pol[which].bits = kW[k];
+      const TensorPol& pol = p->pol[which];
+      cb.tiles[which] = pol.axis == 0 ? (int64_t)n * cdiv(T, 32) : (int64_t)n * cdiv(T, 64);
+      e = encode ? launch_encode_fused(cb, which, s) : launch_decode_fused(cb, which, s);
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 // ====================================================================== ABI
@@ -382,6 +500,38 @@ kvc_status kvc_plan(const kvc_config* cfg, kvc_plan_t* out) {
   return KVC_OK;
 }
 
+kvc_status kvc_plan_mixed(const kvc_config* cfg, const uint8_t* h_bits, kvc_plan_t* out) {
+  if (!h_bits || !out) return fail(KVC_ERR_INVALID_ARG, "h_bits and out must be non-NULL");
+  kvc_status st = kvc_plan(cfg, out);
+  if (st != KVC_OK) return st;
+  kvc_plan_s* p = *out;
+  if (cfg->page_tokens != 0) {
+    kvc_plan_destroy(p);
+    *out = nullptr;
+    return fail(KVC_ERR_UNSUPPORTED, "mixed-precision plans are dense only (page_tokens must be 0)");
+  }
+  const int64_t LH = (int64_t)cfg->layers * cfg->kv_heads;
+  try {
+    p->widths.assign(h_bits, h_bits + 2 * LH);
+  } catch (const std::bad_alloc&) {
+    kvc_plan_destroy(p);
+    *out = nullptr;
+    return fail(KVC_ERR_NO_MEMORY, "plan allocation failed");
+  }
+  for (int64_t i = 0; i < 2 * LH; ++i) {
+    uint8_t& b = p->widths[i];
+    if (b == 0) b = (uint8_t)p->pol[i < LH ? 0 : 1].bits;
+    if (!(b == 2 || b == 4 || b == 8 || b == 16)) {
+      const int given = h_bits[i];
+      kvc_plan_destroy(p);
+      *out = nullptr;
+      return fail(KVC_ERR_INVALID_ARG, "h_bits[%lld] = %d: widths must be 0, 2, 4, 8 or 16", (long long)i, given);
+    }
+  }
+  p->mixed = true;
+  return KVC_OK;
+}
+
 kvc_status kvc_plan_destroy(kvc_plan_t plan) {
   delete plan;
   return KVC_OK;
@@ -393,7 +543,7 @@ kvc_status kvc_plan_sizes(kvc_plan_t p, int64_t tokens, size_t* max_stream_bytes
   ReqDesc rq;
   request_layout(p, (int)tokens, rq);
   const int64_t codes_area = a256(rq.codes_bytes[0]) + a256(rq.codes_bytes[1]);
-  const WsLayout w = ws_layout(rq.nchunks[0] + rq.nchunks[1], codes_area, 0, 1);
+  const WsLayout w = ws_layout(rq.nchunks[0] + rq.nchunks[1], codes_area, 0, 1, slab_area(p));
   if (max_stream_bytes) *max_stream_bytes = (size_t)rq.max_stream;
   if (workspace_bytes) *workspace_bytes = (size_t)w.total;
   return KVC_OK;
@@ -434,7 +584,7 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   // them); compressed chunks and raw chunks that must move go through the
   // workspace codes area, which uses the same offsets.
   c.one.codes_off[1] = a16(c.one.codes_bytes[0]);
-  const WsLayout w = ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1);
+  const WsLayout w = ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1, slab_area(p));
   if ((int64_t)out_capacity < c.one.max_stream)
     return fail(KVC_ERR_BUFFER_TOO_SMALL, "out_capacity %zu < %lld", out_capacity, (long long)c.one.max_stream);
   if ((int64_t)ws_bytes < w.total) return fail(KVC_ERR_BUFFER_TOO_SMALL, "ws_bytes %zu < %lld", ws_bytes, (long long)w.total);
@@ -453,9 +603,14 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   for (int k = 0; k < 2; ++k) c.nnz_sec[k] = (c.nnz_pipe && fused_count_ok(p->pol[k], tokens, p->cfg.chunk_bytes)) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
+  SlabTables tb;
+  if (p->mixed) {
+    if ((st = upload_slabs(p, tokens, ws + w.slabs, s, c, tb)) != KVC_OK) return st;
+    c.nnz_sec[0] = c.nnz_sec[1] = 0;
+  }
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
-  if ((e = timed(KVC_KERNEL_ENCODE_K, s, [&] { return launch_encode_fused(c, 0, s); })) != hipSuccess) return hip_fail(e, "encode K");
-  if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return launch_encode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "encode V");
+  if ((e = timed(KVC_KERNEL_ENCODE_K, s, [&] { return fused_all(p, c, tb, 0, true, s); })) != hipSuccess) return hip_fail(e, "encode K");
+  if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return fused_all(p, c, tb, 1, true, s); })) != hipSuccess) return hip_fail(e, "encode V");
   if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_stash(c, s); })) != hipSuccess) return hip_fail(e, "stash");
@@ -489,7 +644,7 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
                 (long long)c.one.payload_off);
   const int64_t codes_area = a256(c.one.codes_bytes[0]) + a256(c.one.codes_bytes[1]);
   c.one.codes_off[1] = a256(c.one.codes_bytes[0]);
-  const WsLayout w = ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1);
+  const WsLayout w = ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1, slab_area(p));
   if ((int64_t)ws_bytes < w.total) return fail(KVC_ERR_BUFFER_TOO_SMALL, "ws_bytes %zu < %lld", ws_bytes, (long long)w.total);
   uint8_t* ws = (uint8_t*)d_ws;
   c.out_kv[0] = d_k;
@@ -506,12 +661,17 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
   for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads, false);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
+  SlabTables tb;
+  if (p->mixed) {
+    if ((st = upload_slabs(p, tokens, ws + w.slabs, s, c, tb)) != KVC_OK) return st;
+    c.direct[0] = c.direct[1] = 0;
+  }
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_validate(c, s); })) != hipSuccess) return hip_fail(e, "validate");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
   if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
-  if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return launch_decode_fused(c, 0, s); })) != hipSuccess) return hip_fail(e, "decode K");
-  if ((e = timed(KVC_KERNEL_DECODE_V, s, [&] { return launch_decode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "decode V");
+  if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return fused_all(p, c, tb, 0, false, s); })) != hipSuccess) return hip_fail(e, "decode K");
+  if ((e = timed(KVC_KERNEL_DECODE_V, s, [&] { return fused_all(p, c, tb, 1, false, s); })) != hipSuccess) return hip_fail(e, "decode V");
   return KVC_OK;
 }
 
@@ -519,6 +679,7 @@ static kvc_status paged_common(kvc_plan_t p, int64_t num_blocks, const int32_t* 
                                const int32_t* lens, int32_t R) {
   if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
   if (p->cfg.page_tokens < 1) return fail(KVC_ERR_INVALID_ARG, "plan was built without page_tokens");
+  if (p->mixed) return fail(KVC_ERR_UNSUPPORTED, "paged calls do not take mixed-precision plans");
   if (p->pol[0].axis != 0 || p->pol[1].axis != 0)
     return fail(KVC_ERR_UNSUPPORTED, "paged calls implement per-token policies only");
   if (((int64_t)p->cfg.page_tokens * p->cfg.kv_heads) % 32)

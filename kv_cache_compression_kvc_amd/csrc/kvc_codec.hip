@@ -639,6 +639,7 @@ __device__ __forceinline__ void fill_mask_table(const uint32_t* signs, uint32_t*
 // Where a per-token tile's vectors and outputs live.
 struct TokTile {
   const uint16_t* src;     // first input vector
+  uint32_t vstride;        // bytes between consecutive input vectors
   int nv;                  // vectors present (0..32)
   int64_t vg0;             // index of the first vector within its request
   uint8_t* codes_base;
@@ -648,7 +649,24 @@ struct TokTile {
 template <bool PAGED>
 __device__ __forceinline__ TokTile enc_token_tile(const CallDesc& c, int which, int64_t tile, const uint16_t* in) {
   TokTile t;
+  t.vstride = 256u;
   if constexpr (!PAGED) {
+    if (c.mixed) {
+      // 32 tokens of one (layer, head) slab; its codes and parameters are a
+      // one-head run inside the section
+      const int T = c.one.T;
+      const int64_t tps = (T + 31) >> 5;
+      const int sl = (int)(tile / tps);
+      const int64_t t0 = (tile - (int64_t)sl * tps) * 32;
+      const SlabDesc sd = c.slabs[sl];
+      t.vg0 = t0;
+      t.nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, T - t0));
+      t.src = in + (((int64_t)sd.l * T + t0) * c.heads + sd.h) * kHeadDim;
+      t.vstride = (uint32_t)c.heads * 256u;
+      t.codes_base = c.codes + pick(which, c.one.codes_off) + sd.codes_off;
+      t.params_base = c.stream + pick(which, c.one.params_off) + sd.params_off;
+      return t;
+    }
     const int64_t nvec = (int64_t)c.layers * c.one.T * c.heads;
     t.vg0 = tile * 32;
     t.nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec - t.vg0));
@@ -715,7 +733,7 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
   int64_t tile = (int64_t)blockIdx.x * 4 + wave;
   if (tile >= ntiles) return;
   TokTile cur = enc_token_tile<PAGED>(c, which, tile, in);
-  tile_dma(make_rsrc(cur.src, (uint32_t)cur.nv * 256u), 256u, wl_lds);
+  tile_dma(make_rsrc(cur.src, cur.nv ? (uint32_t)(cur.nv - 1) * cur.vstride + 256u : 0u), cur.vstride, wl_lds);
   bool first = true;
   for (; tile < ntiles; tile += stride) {
     if (first) wait_vmcnt<0>();
@@ -727,7 +745,7 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
     const TokTile t = cur;
     if (tile + stride < ntiles) {
       cur = enc_token_tile<PAGED>(c, which, tile + stride, in);
-      tile_dma(make_rsrc(cur.src, (uint32_t)cur.nv * 256u), 256u, wl_lds);
+      tile_dma(make_rsrc(cur.src, cur.nv ? (uint32_t)(cur.nv - 1) * cur.vstride + 256u : 0u), cur.vstride, wl_lds);
     }
     fwht64_inreg(f);
     fwht_cross(f);
@@ -880,6 +898,7 @@ struct DecTok {
   const uint8_t* psrc;    // the tile's parameter words
   uint32_t pbytes;
   uint16_t* dst;          // first output vector
+  uint32_t vstride;       // bytes between consecutive output vectors
   int nvo;                // output vectors to store
 };
 
@@ -888,10 +907,27 @@ __device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, i
   constexpr int CB = kHeadDim * BITS / 8;
   constexpr int NGV = kHeadDim / G;
   DecTok d;
+  d.vstride = 256u;
   int64_t vg0;
   int nv;
   const uint8_t* params_base;
   if constexpr (!PAGED) {
+    if (c.mixed) {
+      const int T = c.one.T;
+      const int64_t tps = (T + 31) >> 5;
+      const int sl = (int)(tile / tps);
+      const int64_t t0 = (tile - (int64_t)sl * tps) * 32;
+      const SlabDesc sd = c.slabs[sl];
+      nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, T - t0));
+      d.nvo = nv;
+      d.csrc = c.codes + pick(which, c.one.codes_off) + sd.codes_off + t0 * CB;
+      d.cbytes = (uint32_t)nv * CB;
+      d.psrc = c.stream + pick(which, c.one.params_off) + sd.params_off + t0 * NGV * 4;
+      d.pbytes = (uint32_t)nv * NGV * 4;
+      d.dst = out + (((int64_t)sd.l * T + t0) * c.heads + sd.h) * kHeadDim;
+      d.vstride = (uint32_t)c.heads * 256u;
+      return d;
+    }
     const int64_t nvec = (int64_t)c.layers * c.one.T * c.heads;
     vg0 = tile * 32;
     nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, nvec - vg0));
@@ -1008,7 +1044,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
 
     fwht64_inreg(f);
     fwht_cross(f);
-    stage_out<BF16>(f, wl, sm, make_rsrc(t.dst, (uint32_t)t.nvo * 256u), 256u);
+    stage_out<BF16>(f, wl, sm, make_rsrc(t.dst, t.nvo ? (uint32_t)(t.nvo - 1) * t.vstride + 256u : 0u), t.vstride);
   }
 }
 
@@ -1053,7 +1089,8 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
   const int H = c.heads;
   const int T = c.one.T;
   const int n64 = TAIL ? 1 : T / 64;                   // groups this kernel walks per layer
-  const int64_t ntiles = (int64_t)c.layers * n64 * H;
+  // mixed precision: the launch covers c.nslabs (layer, head) slabs of one width
+  const int64_t ntiles = c.mixed ? (int64_t)c.nslabs * n64 : (int64_t)c.layers * n64 * H;
   const int ngr = (T + G - 1) / G;
   uint8_t* codes_sec = c.codes + pick(which, c.one.codes_off);
   uint32_t* prm = (uint32_t*)(c.stream + pick(which, c.one.params_off));
@@ -1092,6 +1129,20 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
   decode_tile((int)blockIdx.x, l, g64, h);
   if constexpr (TAIL) g64 = T / 64;
   for (int tile = blockIdx.x; tile < (int)ntiles; tile += step) {
+    // output addressing: (layer, head) within the section layout, and its base
+    int lo = l, ho = h, Ho = H;
+    uint8_t* csec = codes_sec;
+    uint32_t* psec = prm;
+    if (c.mixed) {
+      const int sl = tile / n64;
+      const SlabDesc sd = c.slabs[sl];
+      l = sd.l;
+      h = sd.h;
+      g64 = TAIL ? T / 64 : tile - sl * n64;
+      lo = 0; ho = 0; Ho = 1;
+      csec = codes_sec + sd.codes_off;
+      psec = (uint32_t*)((uint8_t*)prm + sd.params_off);
+    }
     const int t0 = g64 * 64;
     const int gg = TAIL ? T - t0 : 64;                 // valid tokens in this tile
     const int nvw = TAIL ? max(0, min(32, gg - tw0)) : 32;
@@ -1157,11 +1208,11 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
         int colb;
         // complete tiles: the block of the tile's first group (both halves of a
         // G = 32 tile are complete groups, the second one block further on)
-        const int64_t boff = pc_block(T, G, H, BITS, l, FULL ? ((G == 64) ? g64 : 2 * g64) : grp, h, colb);
+        const int64_t boff = pc_block(T, G, Ho, BITS, lo, FULL ? ((G == 64) ? g64 : 2 * g64) : grp, ho, colb);
         const int tok0 = (G == 64) ? 32 * th : 0;        // first token of this thread in its group
         if constexpr (FULL) {
-          const uint32_t gstride = (G == 64) ? 0u : (uint32_t)H * kHeadDim * colb;
-          const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes_sec + boff, gstride + (uint32_t)kHeadDim * colb);
+          const uint32_t gstride = (G == 64) ? 0u : (uint32_t)Ho * kHeadDim * colb;
+          const __amdgpu_buffer_rsrc_t crs = make_rsrc(csec + boff, gstride + (uint32_t)kHeadDim * colb);
           const uint32_t co = (uint32_t)th * gstride + (uint32_t)ch * colb + (uint32_t)(tok0 * BITS / 8);
           if constexpr (BITS == 2) bstore8(make_uint2(w[0], w[1]), crs, co, 0);
           else if constexpr (BITS == 4) bstore16(make_uint4(w[0], w[1], w[2], w[3]), crs, co, 0);
@@ -1170,7 +1221,7 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
             bstore16(make_uint4(w[4], w[5], w[6], w[7]), crs, co + 16, 0);
           }
         } else if (nvt == 32 && colb == G * BITS / 8) {
-          uint8_t* dst = codes_sec + boff + (int64_t)ch * colb + tok0 * BITS / 8;
+          uint8_t* dst = csec + boff + (int64_t)ch * colb + tok0 * BITS / 8;
           if constexpr (BITS == 2) *(uint2*)dst = make_uint2(w[0], w[1]);
           else if constexpr (BITS == 4) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
           else {
@@ -1178,7 +1229,7 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
             *(uint4*)(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
           }
         } else if (ntok > 0 && nvt > 0) {
-          uint8_t* dst = codes_sec + boff + (int64_t)ch * colb + tok0 * BITS / 8;
+          uint8_t* dst = csec + boff + (int64_t)ch * colb + tok0 * BITS / 8;
           // partial group: this thread's codes start at byte tok0 * BITS / 8
           const int nbytes = (nvt * BITS + 7) / 8;
 #pragma unroll
@@ -1188,12 +1239,12 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
         const bool writer = (G == 64) ? (th == 0) : true;
         if constexpr (FULL) {
           const int grp0 = (G == 64) ? g64 : 2 * g64;
-          const uint32_t pstride = (G == 64) ? 0u : (uint32_t)H * kHeadDim;   // next group, in words
+          const uint32_t pstride = (G == 64) ? 0u : (uint32_t)Ho * kHeadDim;  // next group, in words
           const __amdgpu_buffer_rsrc_t prs =
-              make_rsrc(prm + (((int64_t)l * ngr + grp0) * H + h) * kHeadDim, 4u * (pstride + kHeadDim));
+              make_rsrc(psec + (((int64_t)lo * ngr + grp0) * Ho + ho) * kHeadDim, 4u * (pstride + kHeadDim));
           if (writer) bstore4(gq.packed, prs, 4u * ((uint32_t)th * pstride + (uint32_t)ch), 0);
         } else if (writer && ntok > 0) {
-          prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch] = gq.packed;
+          psec[(((int64_t)lo * ngr + grp) * Ho + ho) * kHeadDim + ch] = gq.packed;
         }
         if constexpr (G == 64 && FULL && BITS >= 4) {
           if (c.nnz_pipe && c.nnz_sec[which]) {
@@ -1263,6 +1314,7 @@ struct ChRegs {
 struct WaveTile {
   int l, g64, h, half;
   int k;                 // 2 h + half
+  int sl;                // mixed precision: index of the (layer, head) slab in the launch, else -1
 };
 
 // Wave-tile order of the per-channel decoder.  Workgroups go to the eight
@@ -1275,9 +1327,11 @@ struct ChDecOrder {
   int H, n64, full;
   int dk, dgA, dlA, dgB, dlB;
   bool stepwise;
-  __device__ ChDecOrder(int H_, int n64_, int64_t ntiles, int grid) : H(H_), n64(n64_) {
+  const SlabDesc* slabs;   // mixed precision: the launch's slabs, wave-tiles in plain order
+  __device__ ChDecOrder(int H_, int n64_, int64_t ntiles, int grid, const SlabDesc* slabs_)
+      : H(H_), n64(n64_), slabs(slabs_) {
     const int ngroups = (int)(ntiles / H);
-    full = (H % 2 == 0) ? (ngroups / 8) * 8 * 2 * H : 0;
+    full = (H % 2 == 0 && !slabs) ? (ngroups / 8) * 8 * 2 * H : 0;
     stepwise = (grid & 7) == 0;
     const int ds = grid / 2;                         // s advance per grid stride of wave-tiles
     dk = ds % (2 * H);
@@ -1287,6 +1341,15 @@ struct ChDecOrder {
   }
   __device__ WaveTile decode(int64_t u) const {
     WaveTile o;
+    o.sl = -1;
+    if (slabs) {
+      const int tile = (int)(u >> 1);
+      o.sl = tile / n64;
+      const SlabDesc sd = slabs[o.sl];
+      o.l = sd.l; o.h = sd.h; o.g64 = tile - o.sl * n64; o.half = (int)(u & 1);
+      o.k = 2 * o.h + o.half;
+      return o;
+    }
     int grp;
     if (u < full) {
       const int b = (int)(u >> 2);
@@ -1304,7 +1367,7 @@ struct ChDecOrder {
   }
   // wave-tile u, given o = wave-tile u - stride
   __device__ WaveTile advance(int64_t u, WaveTile o) const {
-    if (stepwise && u < full) {
+    if (stepwise && u < full && !slabs) {
       o.k += dk;
       const bool cy = o.k >= 2 * H;
       if (cy) o.k -= 2 * H;
@@ -1323,13 +1386,21 @@ __device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, WaveTi
   const int lane = __lane_id();
   const int H = c.heads, T = c.one.T;
   const int ngr = (T + G - 1) / G;
-  const int half = wt.half, h = wt.h, g64 = wt.g64, l = wt.l;
+  const int half = wt.half, g64 = wt.g64;
   const int gg = min(64, T - g64 * 64);
   const int nvw = max(0, min(32, gg - 32 * half));            // tokens of this wave-tile
   const int grp = (G == 64) ? g64 : 2 * g64 + half;
   const int tok0 = (G == 64) ? 32 * half : 0;                 // first token of the wave in its group
   const uint8_t* codes_sec = c.codes + pick(which, c.one.codes_off);
   const uint32_t* prm = (const uint32_t*)(c.stream + pick(which, c.one.params_off));
+  // (layer, head) within the section layout: a mixed slab is a one-layer, one-head run
+  int l = wt.l, h = wt.h, Ho = H;
+  if (wt.sl >= 0) {
+    const SlabDesc sd = c.slabs[wt.sl];
+    codes_sec += sd.codes_off;
+    prm = (const uint32_t*)((const uint8_t*)prm + sd.params_off);
+    l = 0; h = 0; Ho = 1;
+  }
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int ch = 64 * p + lane;
@@ -1338,7 +1409,7 @@ __device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, WaveTi
     R.pw[p] = 0;
     if (nvw > 0) {
       int colb;
-      const int64_t boff = pc_block(T, G, H, BITS, l, grp, h, colb);
+      const int64_t boff = pc_block(T, G, Ho, BITS, l, grp, h, colb);
       const uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
       bool have = true;
       if (c.direct[which]) {
@@ -1371,7 +1442,7 @@ __device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, WaveTi
         for (int i = 0; i < 4 * BITS; ++i)
           if (i < nbytes) R.w[p][i >> 2] |= (uint32_t)s[i] << (8 * (i & 3));
       }
-      R.pw[p] = prm[(((int64_t)l * ngr + grp) * H + h) * kHeadDim + ch];
+      R.pw[p] = prm[(((int64_t)l * ngr + grp) * Ho + h) * kHeadDim + ch];
     }
   }
 }
@@ -1396,7 +1467,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_channel(CallDesc c, int which
   const int64_t stride = (int64_t)gridDim.x * 4;
   int64_t wt = (int64_t)blockIdx.x * 4 + wave;
   if (wt >= nwt) return;
-  const ChDecOrder order(H, n64, nwt / 2, (int)gridDim.x);
+  const ChDecOrder order(H, n64, nwt / 2, (int)gridDim.x, c.mixed ? c.slabs : nullptr);
   WaveTile nxt = order.decode(wt);
   ChRegs<BITS> R;
   ch_dec_load<BITS, G>(c, which, nxt, R);
@@ -1480,17 +1551,46 @@ hipError_t launch_encode_fused(const CallDesc& c, int which, hipStream_t s) {
   } else {
     const dim3 block(128);
     const int T = c.one.T;
+    const int64_t units = c.mixed ? (int64_t)c.nslabs : (int64_t)c.layers * c.heads;   // (layer, head) pairs
     if (T >= 64) {
-      const int grid = grid_for((int64_t)c.layers * (T / 64) * c.heads, 256 * 32);
+      const int grid = grid_for(units * (T / 64), 256 * 32);
       if (c.dtype == 1) { KVC_BITS_CASES(KVC_ENC_CHANNEL_CASES, true, false) }
       else { KVC_BITS_CASES(KVC_ENC_CHANNEL_CASES, false, false) }
     }
     if (T % 64) {
-      const int grid = grid_for((int64_t)c.layers * c.heads, 256 * 32);
+      const int grid = grid_for(units, 256 * 32);
       if (c.dtype == 1) { KVC_BITS_CASES(KVC_ENC_CHANNEL_CASES, true, true) }
       else { KVC_BITS_CASES(KVC_ENC_CHANNEL_CASES, false, true) }
     }
   }
+  return hipGetLastError();
+}
+
+// 16-bit passthrough slabs: slab i of the launch holds the T x head_dim values
+// of its (layer, head) in token order; one 16-byte piece per thread.
+__global__ __launch_bounds__(256) void k_slab_copy(CallDesc c, int which, int encode) {
+  const int T = c.one.T, H = c.heads;
+  const int64_t per = (int64_t)T * 16;                     // 16-byte pieces per slab
+  const int64_t n = (int64_t)c.nslabs * per;
+  uint8_t* sec = c.codes + pick(which, c.one.codes_off);
+  uint16_t* x = (uint16_t*)(encode ? const_cast<void*>(c.in_kv[which]) : c.out_kv[which]);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int sl = (int)(i / per);
+    const int64_t r = i - (int64_t)sl * per;
+    const int64_t t = r >> 4;
+    const int q = (int)(r & 15);
+    const SlabDesc sd = c.slabs[sl];
+    uint4* a = (uint4*)(sec + sd.codes_off) + r;
+    uint4* b = (uint4*)(x + (((int64_t)sd.l * T + t) * H + sd.h) * kHeadDim) + q;
+    if (encode) *a = *b;
+    else *b = *a;
+  }
+}
+
+hipError_t launch_slab_copy(const CallDesc& c, int which, bool encode, hipStream_t s) {
+  const int64_t n = (int64_t)c.nslabs * c.one.T * 16;
+  if (n == 0) return hipSuccess;
+  k_slab_copy<<<grid_for((n + 255) / 256, 256 * 32), 256, 0, s>>>(c, which, encode ? 1 : 0);
   return hipGetLastError();
 }
 

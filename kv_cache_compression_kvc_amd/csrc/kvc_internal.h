@@ -40,6 +40,13 @@ struct TensorPol {
   float c;               // 1/sqrt(head_dim) rounded to binary32 (1 if no transform)
 };
 
+// One (layer, head) slab of a mixed-precision tensor: its codes and
+// parameters start codes_off / params_off bytes into the tensor's sections.
+struct SlabDesc {
+  int32_t l, h;
+  int64_t codes_off, params_off;
+};
+
 // One request of a call; a dense call is a single request.
 struct ReqDesc {
   int32_t T;                 // tokens
@@ -52,6 +59,7 @@ struct ReqDesc {
   int64_t params_ws_off[2];  // parameter staging in the workspace (paged encode), -1 if direct
   int64_t params_off[2];     // parameter sections inside this request's stream
   int64_t params_bytes[2];
+  int64_t table_off;         // chunk table offset inside this request's stream
   int64_t payload_off;       // payload offset inside this request's stream
   int64_t max_stream;        // stream bytes with every chunk raw
   int64_t piece_begin;       // first parameter-copy piece (paged encode)
@@ -95,6 +103,12 @@ struct CallDesc {
   int64_t total_chunks;
   int64_t total_pieces;      // paged encode: parameter copy pieces
   int64_t tiles[2];          // fused-kernel tiles of K and V over all requests
+  // mixed precision per (layer, head): codes and parameters are (layer, head)
+  // slabs; each fused launch covers the `nslabs` slabs of `slabs` (one width)
+  int mixed;
+  const SlabDesc* slabs;
+  int nslabs;
+  const uint8_t* width_map;  // device copy of the 2 * L * H widths (header)
 };
 
 // Kernel launch wrappers (defined in the .hip files).  Each returns the HIP
@@ -108,6 +122,9 @@ hipError_t launch_compact(const CallDesc& c, hipStream_t s);
 hipError_t launch_stash(const CallDesc& c, hipStream_t s);
 hipError_t launch_validate(const CallDesc& c, hipStream_t s);
 hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s);
+// 16-bit passthrough slabs of a mixed tensor: gather into the codes section
+// (encode) or scatter back into the tensor (decode)
+hipError_t launch_slab_copy(const CallDesc& c, int which, bool encode, hipStream_t s);
 
 // Per-kernel timing hooks (kvc_api.cpp).
 void prof_begin(int kind, hipStream_t s);

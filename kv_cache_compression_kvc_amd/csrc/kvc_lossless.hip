@@ -804,7 +804,7 @@ __global__ __launch_bounds__(1024) void k_scan(CallDesc c, int from_table) {
       const int r = find_req_by_chunk(c, i);
       const ReqDesc rq = req_at(c, r);
       const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
-      const uint64_t pos = base + 64 + 4 * (uint64_t)(i - rq.chunk_begin);
+      const uint64_t pos = base + (uint64_t)rq.table_off + 4 * (uint64_t)(i - rq.chunk_begin);
       uint32_t e = 0;
       if (pos + 4 <= c.stream_bytes && pos + 4 <= base + (uint64_t)rq.payload_off) e = *(const uint32_t*)(c.stream + pos);
       else set_status2(c.ctl, kStCorrupt);
@@ -865,7 +865,7 @@ __device__ void write_header(const CallDesc& c, const ReqDesc& rq, uint8_t* o, u
   if (t < 4) b = byte_of(kMagic, t);
   else if (t < 6) b = byte_of(1, t - 4);
   else if (t == 6) b = (uint8_t)c.dtype;
-  else if (t == 7) b = 0;
+  else if (t == 7) b = c.mixed ? 1 : 0;              // flags: bit 0 = mixed precision
   else if (t < 12) b = byte_of((uint32_t)c.layers, t - 8);
   else if (t < 16) b = byte_of((uint32_t)rq.T, t - 12);
   else if (t < 20) b = byte_of((uint32_t)c.heads, t - 16);
@@ -885,12 +885,15 @@ __device__ void write_header(const CallDesc& c, const ReqDesc& rq, uint8_t* o, u
   o[t] = b;
 }
 
-// zero the alignment gaps between table, parameter sections and payload
-__device__ void zero_gaps(const ReqDesc& rq, uint8_t* o) {
-  const int64_t tend = 64 + 4 * (int64_t)(rq.nchunks[0] + rq.nchunks[1]);
-  const int64_t g0[3] = {tend, rq.params_off[0] + rq.params_bytes[0], rq.params_off[1] + rq.params_bytes[1]};
-  const int64_t g1[3] = {rq.params_off[0], rq.params_off[1], rq.payload_off};
-  for (int k = 0; k < 3; ++k)
+// zero the alignment gaps between table, parameter sections and payload; a
+// mixed-precision stream also gets its width map after the header
+__device__ void zero_gaps(const CallDesc& c, const ReqDesc& rq, uint8_t* o) {
+  const int64_t tend = rq.table_off + 4 * (int64_t)(rq.nchunks[0] + rq.nchunks[1]);
+  const int64_t mapn = c.mixed ? 2 * (int64_t)c.layers * c.heads : 0;
+  for (int64_t p = threadIdx.x; p < mapn; p += blockDim.x) o[64 + p] = c.width_map[p];
+  const int64_t g0[4] = {64 + mapn, tend, rq.params_off[0] + rq.params_bytes[0], rq.params_off[1] + rq.params_bytes[1]};
+  const int64_t g1[4] = {rq.table_off, rq.params_off[0], rq.params_off[1], rq.payload_off};
+  for (int k = 0; k < 4; ++k)
     for (int64_t p = g0[k] + threadIdx.x; p < g1[k]; p += blockDim.x) o[p] = 0;
 }
 
@@ -925,7 +928,7 @@ __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
         if ((e >> 31) && fin == (uint64_t)L.src) {
           const int64_t pad = align16(stored) - stored;
           if (threadIdx.x < pad) dst[stored + threadIdx.x] = 0;
-          if (threadIdx.x == 0) *(uint32_t*)(out + 64 + 4 * (ch - rq.chunk_begin)) = e;
+          if (threadIdx.x == 0) *(uint32_t*)(out + rq.table_off + 4 * (ch - rq.chunk_begin)) = e;
           continue;
         }
         src = c.codes_out + L.src;
@@ -940,7 +943,7 @@ __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
         }
         ((uint4*)dst)[k] = x;
       }
-      if (threadIdx.x == 0) *(uint32_t*)(out + 64 + 4 * (ch - rq.chunk_begin)) = e;
+      if (threadIdx.x == 0) *(uint32_t*)(out + rq.table_off + 4 * (ch - rq.chunk_begin)) = e;
     } else if (it < c.total_chunks + c.R) {
       const int r = (int)(it - c.total_chunks);
       const ReqDesc rq = req_at(c, r);
@@ -948,7 +951,7 @@ __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
       const uint64_t total = (c.req_offsets_out != nullptr) ? c.req_offsets_out[r + 1] - c.req_offsets_out[r]
                                                             : c.ctl->total;
       write_header(c, rq, c.stream + base, total);
-      zero_gaps(rq, c.stream + base);
+      zero_gaps(c, rq, c.stream + base);
     } else {
       const int64_t piece = it - c.total_chunks - c.R;
       const int r = find_req_by_piece(c, piece);
@@ -1027,6 +1030,7 @@ __global__ __launch_bounds__(64) void k_validate(CallDesc c) {
                      *(const uint16_t*)(p + 4) != c.pol[w].group) << (7 + w);
           }
           for (int k = 0; k < 4; ++k) diag |= (h[48 + k] != c.stages[k]) << (9 + k);
+          diag |= (h[7] != (c.mixed ? 1 : 0)) << 13;
           if (diag) {
             bad |= kStMismatch;
             // which header fields differ (bit per field), kept for diagnosis
@@ -1038,7 +1042,14 @@ __global__ __launch_bounds__(64) void k_validate(CallDesc c) {
         }
       }
     }
-    if (bad && t == 0) set_status2(c.ctl, bad);
+    if (!bad && c.mixed) {
+      // the width map must be the plan's
+      const uint8_t* h = c.stream + base;
+      const int64_t mapn = 2 * (int64_t)c.layers * c.heads;
+      for (int64_t p = t; p < mapn; p += blockDim.x)
+        if (h[64 + p] != c.width_map[p]) bad = kStMismatch;
+    }
+    if (bad) set_status2(c.ctl, bad);
   }
 }
 
