@@ -107,6 +107,30 @@ def selection_cost(U: float, s_enc: float, s_dec: float, cr: float, requests: in
             "note": "python ctypes calls included; profile -1 = raw transfer"}
 
 
+def mixed_widths(pattern: str, wl):
+    """[2][layers][heads] widths of a named mixed-precision pattern (None = uniform)."""
+    if pattern == "none":
+        return None
+    import numpy as np
+    hi = 8 if pattern == "mixhq" else 16
+    b = np.full((2, wl.layers, wl.heads), 2, np.uint8)
+    b[:, :, :2] = hi
+    return b
+
+
+def mixed_bytes(widths, pol, elems: int) -> float:
+    """Algorithmic bytes of one tensor's fused encode (or decode) under a width
+    map: 2 bytes read per element, and per element b/8 code bytes plus a
+    4-byte parameter word per group (16-bit heads: 2 bytes written)."""
+    import numpy as np
+    w = np.asarray(widths).reshape(-1)
+    per_head = elems / w.size
+    total = 0.0
+    for b in w:
+        total += per_head * (2.0 + (2.0 if b == 16 else b / 8.0 + 4.0 / pol.group))
+    return total
+
+
 def host_cpu() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -144,6 +168,9 @@ def main():
                     help="value model: the workload's Gaussian KV (headline), or KV whose 64-token blocks "
                          "are zero with probability --zero-frac (exercises compressing chunks)")
     ap.add_argument("--zero-frac", type=float, default=0.5)
+    ap.add_argument("--mixed", choices=["none", "mixhq", "mixhq16"], default="none",
+                    help="mixed precision per (layer, head): mixhq = heads 0-1 of every layer at 8 bits and the "
+                         "others at 2 bits (K and V); mixhq16 = heads 0-1 kept at 16 bits, the others at 2")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30,
                     help="size of the plain device copy timed as the practical bandwidth reference")
     args = ap.parse_args()
@@ -181,7 +208,8 @@ def main():
         k, v = W.dense_kv(wl, device=dev)
     else:
         k, v = W.zero_rich_kv(wl, L, T, seed=W.SEED_BASE + 7, device=dev, zero_frac=args.zero_frac)
-    plan = K.Plan(K.config_from_workload(wl))
+    bits = mixed_widths(args.mixed, wl)
+    plan = K.Plan(K.config_from_workload(wl), bits)
     ms, wsb = plan.sizes(T)
     out = torch.empty(ms, dtype=torch.uint8, device=dev)
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
@@ -240,18 +268,20 @@ def main():
 
     # roofline of the dominant fused kernel, algorithmic bytes per launch
     elems = L * T * wl.heads * wl.head_dim
-    cand = {
-        "ENCODE_K": elems * fused_bytes_per_elem(wl.k), "ENCODE_V": elems * fused_bytes_per_elem(wl.v),
-        "DECODE_K": elems * fused_bytes_per_elem(wl.k), "DECODE_V": elems * fused_bytes_per_elem(wl.v),
-    }
+    per_k = elems * fused_bytes_per_elem(wl.k) if bits is None else mixed_bytes(bits[0], wl.k, elems)
+    per_v = elems * fused_bytes_per_elem(wl.v) if bits is None else mixed_bytes(bits[1], wl.v, elems)
+    cand = {"ENCODE_K": per_k, "ENCODE_V": per_v, "DECODE_K": per_k, "DECODE_V": per_v}
     avg = {k_: prof[k_][0] / max(prof[k_][1], 1) for k_ in cand}
     dom = max(avg, key=avg.get)
     achieved = cand[dom] / (avg[dom] * 1e-3) / 1e9
     import ctypes as C
     codes_params = 0
     # quantized bytes (codes + parameters) from the closed form
-    for pol in (wl.k, wl.v):
-        codes_params += elems * (pol.bits / 8.0 + 4.0 / pol.group)
+    for w, pol in enumerate((wl.k, wl.v)):
+        if bits is None:
+            codes_params += elems * (pol.bits / 8.0 + 4.0 / pol.group)
+        else:
+            codes_params += mixed_bytes(bits[w], pol, elems) - 2.0 * elems
     result = {
         "metric": "KV encode / decode GB/s (uncompressed bytes) + % HBM peak, compression ratio",
         "value": round(U / step_ms / 1e6, 3),
@@ -269,7 +299,7 @@ def main():
                    "head_dim": wl.head_dim, "io_dtype": wl.dtype,
                    "k_policy": f"int{wl.k.bits} per-{wl.k.axis} g{wl.k.group} hadamard",
                    "v_policy": f"int{wl.v.bits} per-{wl.v.axis} g{wl.v.group} hadamard",
-                   "lossless": ">".join(wl.stages), "chunk_bytes": wl.chunk_bytes,
+                   "lossless": ">".join(wl.stages), "chunk_bytes": wl.chunk_bytes, "mixed": args.mixed,
                    "uncompressed_bytes": U},
         "encode_GBps": round(U / enc_ms / 1e6, 3),
         "decode_GBps": round(U / dec_ms / 1e6, 3),
@@ -297,7 +327,8 @@ def main():
     result["fused_kernels"] = fk
     result["pages_figures"] = PAGES_FIGURES
     result["selection"] = selection_cost(U, U / (enc_ms * 1e-3), U / (dec_ms * 1e-3), U / n)
-    t = counted_traffic(dom) if (args.workload == "c3_llama70b_32k" and args.values == "gaussian") else None
+    t = (counted_traffic(dom) if (args.workload == "c3_llama70b_32k" and args.values == "gaussian"
+                                   and args.mixed == "none") else None)
     if t is not None:
         result["roofline"]["traffic"] = t["bytes"]
         result["roofline"]["traffic_read_write"] = [t["read_bytes"], t["write_bytes"]]
