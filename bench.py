@@ -164,10 +164,12 @@ def main():
     ap.add_argument("--workload", default="c3_llama70b_32k")
     ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--values", choices=["gaussian", "zero_rich"], default="gaussian",
-                    help="value model: the workload's Gaussian KV (headline), or KV whose 64-token blocks "
-                         "are zero with probability --zero-frac (exercises compressing chunks)")
+    ap.add_argument("--values", choices=["gaussian", "zero_rich", "correlated"], default="gaussian",
+                    help="value model: the workload's Gaussian KV (headline), KV whose 64-token blocks "
+                         "are zero with probability --zero-frac, or KV correlated along tokens (AR(1), "
+                         "--rho); the last two exercise compressing chunks")
     ap.add_argument("--zero-frac", type=float, default=0.5)
+    ap.add_argument("--rho", type=float, default=0.95)
     ap.add_argument("--mixed", choices=["none", "mixhq", "mixhq16"], default="none",
                     help="mixed precision per (layer, head): mixhq = heads 0-1 of every layer at 8 bits and the "
                          "others at 2 bits (K and V); mixhq16 = heads 0-1 kept at 16 bits, the others at 2")
@@ -206,6 +208,8 @@ def main():
     log(f"generating {wl.name}: {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype} on {dev}")
     if args.values == "gaussian":
         k, v = W.dense_kv(wl, device=dev)
+    elif args.values == "correlated":
+        k, v = W.correlated_kv(wl, L, T, W.SEED_BASE + 7, device=dev, rho=args.rho)
     else:
         k, v = W.zero_rich_kv(wl, L, T, seed=W.SEED_BASE + 7, device=dev, zero_frac=args.zero_frac)
     bits = mixed_widths(args.mixed, wl)
@@ -294,7 +298,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic" if args.values == "gaussian" else f"synthetic-zero-rich-{args.zero_frac}",
+        "data": {"gaussian": "synthetic", "zero_rich": f"synthetic-zero-rich-{args.zero_frac}",
+                 "correlated": f"synthetic-correlated-rho-{args.rho}"}[args.values],
         "config": {"workload": "llama3.1-70b-kv-32k-tokens", "layers": L, "tokens": T, "kv_heads": wl.heads,
                    "head_dim": wl.head_dim, "io_dtype": wl.dtype,
                    "k_policy": f"int{wl.k.bits} per-{wl.k.axis} g{wl.k.group} hadamard",

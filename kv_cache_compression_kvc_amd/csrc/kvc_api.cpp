@@ -164,7 +164,7 @@ void request_layout(const kvc_plan_s* p, int T, ReqDesc& rq) {
 
 // Workspace carving shared by all calls.
 struct WsLayout {
-  int64_t ctl, sizes, offs, worklist, codes, params, reqs, slabs, total;
+  int64_t ctl, sizes, offs, worklist, flags, codes, params, reqs, slabs, total;
 };
 
 // Bytes of the slab tables (a SlabDesc per (tensor, layer, head)) and the width
@@ -182,7 +182,9 @@ WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int
   w.offs = w.sizes + a256(4 * std::max<int64_t>(nchunks, 1));
   // the worklist follows the offsets directly (kernels locate it there)
   w.worklist = w.offs + 8 * (nchunks + 1);
-  w.codes = a256(w.worklist + 4 * std::max<int64_t>(nchunks, 1));
+  // read announcements of the single-pass placement: one word per chunk, one per 64 chunks
+  w.flags = a256(w.worklist + 4 * std::max<int64_t>(nchunks, 1));
+  w.codes = a256(w.flags + 4 * (nchunks + (nchunks + 63) / 64 + 1));
   w.params = a256(w.codes + codes_area);
   w.reqs = a256(w.params + params_area);
   w.slabs = a256(w.reqs + (R > 1 ? R * (int64_t)sizeof(ReqDesc) : 0));
@@ -341,6 +343,7 @@ kvc_status device_status(uint32_t bits) {
   if (bits & kStCorrupt) return fail(KVC_ERR_CORRUPT_STREAM, "stream failed validation on the device");
   if (bits & kStBadBlock) return fail(KVC_ERR_INVALID_ARG, "block table entry out of range");
   if (bits & kStRange) return fail(KVC_ERR_RANGE, "a quantization parameter is not a finite fp16 value");
+  if (bits & kStStall) return fail(KVC_ERR_HIP, "single-pass placement: a wait ran out or a chunk size disagreed");
   return KVC_OK;
 }
 
@@ -598,6 +601,8 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   c.chunk_offs = (uint64_t*)(ws + w.offs);
   c.ctl = (Control*)(ws + w.ctl);
   c.total_chunks = c.one.nchunks[0] + c.one.nchunks[1];
+  c.place = 1;
+  c.place_flags = (uint32_t*)(ws + w.flags);
   for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads, false);
   c.nnz_pipe = lossless_pipe(p->cfg.lossless);
   for (int k = 0; k < 2; ++k) c.nnz_sec[k] = (c.nnz_pipe && fused_count_ok(p->pol[k], tokens, p->cfg.chunk_bytes)) ? 1 : 0;
@@ -613,8 +618,7 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return fused_all(p, c, tb, 1, true, s); })) != hipSuccess) return hip_fail(e, "encode V");
   if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
-  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_stash(c, s); })) != hipSuccess) return hip_fail(e, "stash");
-  if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_compact(c, s); })) != hipSuccess) return hip_fail(e, "compact");
+  if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_place(c, s); })) != hipSuccess) return hip_fail(e, "place");
   if (h_out_bytes) {
     Control h;
     if ((st = sync_and_read(c.ctl, s, h)) != KVC_OK) return st;

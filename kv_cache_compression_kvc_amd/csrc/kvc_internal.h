@@ -20,6 +20,7 @@ enum : uint32_t {
   kStMismatch = 1u << 1,
   kStRange = 1u << 2,
   kStBadBlock = 1u << 3,
+  kStStall = 1u << 4,        // a bounded wait of the single-pass placement ran out
 };
 
 // Workspace control block (first 256 bytes of every workspace).
@@ -90,6 +91,8 @@ struct CallDesc {
                              // stream's payload laid out as if every chunk were raw
   uint8_t* codes_out;        // encode: where compressed chunk bytes go (== codes: in place)
   int direct[2];             // decode: reconstruct kernels read raw chunks of K / V from the stream
+  int place;                 // dense encode: finish the stream in one in-place pass (k_place)
+  uint32_t* place_flags;     //   [total chunks] read announcements, then [ceil(total / 64)] group counts
   int nnz_pipe;              // encode: 1 or 2 when the fused kernels count the non-zero RZE
   int nnz_sec[2];            //   words of pipeline P1 / P2 per chunk (into chunk_sizes), per section
   uint8_t* params_ws;        // workspace parameter staging area (paged encode)
@@ -119,7 +122,7 @@ hipError_t launch_decode_fused(const CallDesc& c, int which, hipStream_t s);
 hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s);
 hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s);
 hipError_t launch_compact(const CallDesc& c, hipStream_t s);
-hipError_t launch_stash(const CallDesc& c, hipStream_t s);
+hipError_t launch_place(const CallDesc& c, hipStream_t s);
 hipError_t launch_validate(const CallDesc& c, hipStream_t s);
 hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s);
 // 16-bit passthrough slabs of a mixed tensor: gather into the codes section

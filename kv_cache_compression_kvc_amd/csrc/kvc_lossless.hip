@@ -21,9 +21,11 @@
 // rest (and chunks of other pipelines or partial chunks) go on a worklist
 // for the second kernel, which runs the stages in LDS (two 64 KiB buffers)
 // and writes the result in place into the chunk's slot.  A single-block scan
-// turns stored sizes into 16-byte aligned offsets; the compaction kernel
-// copies chunks and parameter pieces to their final places and writes the
-// headers and the chunk tables.
+// turns stored sizes into 16-byte aligned offsets.  A dense encode then ends
+// with one in-place pass (k_place) that encodes the standard pipeline's
+// chunks and puts every chunk at its final offset; paged encodes use the
+// compaction kernel, which copies chunks and parameter pieces to their final
+// places.  Both write the headers and the chunk tables.
 #include <algorithm>
 
 #include "kvc_internal.h"
@@ -82,15 +84,19 @@ __global__ void k_reset(CallDesc c) {
     ctl->total = 0;
     ctl->pad[0] = 0;   // header-field diagnosis bits
     ctl->pad[1] = 0;   // worklist entries for the general stage engine (from the back)
+    ctl->pad[2] = 0;   // tickets of the single-pass placement
   }
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, di = (int64_t)gridDim.x * blockDim.x;
   // the fused encoders accumulate per-chunk non-zero word counts here
   if (c.nnz_pipe)
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < c.total_chunks; i += (int64_t)gridDim.x * blockDim.x)
-      c.chunk_sizes[i] = 0;
+    for (int64_t i = i0; i < c.total_chunks; i += di) c.chunk_sizes[i] = 0;
+  if (c.place)
+    for (int64_t i = i0; i < c.total_chunks + (c.total_chunks + 63) / 64; i += di) c.place_flags[i] = 0;
 }
 
 hipError_t launch_reset(const CallDesc& c, hipStream_t s) {
-  const int grid = c.nnz_pipe ? (int)std::max<int64_t>(1, std::min<int64_t>((c.total_chunks + 255) / 256, 1024)) : 1;
+  const bool wide = c.nnz_pipe || c.place;
+  const int grid = wide ? (int)std::max<int64_t>(1, std::min<int64_t>((c.total_chunks + 255) / 256, 1024)) : 1;
   k_reset<<<grid, 256, 0, s>>>(c);
   return hipGetLastError();
 }
@@ -361,6 +367,10 @@ __global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, uint32_t* worklist
       const int64_t size = n / 16 + 2 * (int64_t)nnz;
       if (size >= n) {
         if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
+        work = false;
+      } else if (c.place && pipe == 1) {
+        // the single-pass placement encodes it; it needs only the size
+        if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
         work = false;
       }
     } else if (c.stages[0] == 0) {
@@ -780,7 +790,7 @@ hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
   const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
   const int fgrid = (int)std::min<int64_t>(c.total_chunks, 512);
-  if (p1) k_ll_encode_p1<<<fgrid, 256, 0, s>>>(c, worklist);
+  if (p1 && !c.place) k_ll_encode_p1<<<fgrid, 256, 0, s>>>(c, worklist);
   else if (p2) k_ll_encode_p2<<<fgrid, 256, 0, s>>>(c, worklist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k_ll_encode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
@@ -816,11 +826,27 @@ __global__ __launch_bounds__(1024) void k_scan(CallDesc c, int from_table) {
   for (int64_t i = i0; i < i1; ++i) sum += (uint64_t)align16(c.chunk_sizes[i] & 0x7fffffffu);
   uint64_t total;
   uint64_t acc = block_exclusive_scan<uint64_t>(sum, sh, total);
+  // dense encode with single-pass placement: the first chunk that is not a
+  // raw chunk at its all-raw place (every earlier one is, and needs no work)
+  int64_t first_work = N;
   for (int64_t i = i0; i < i1; ++i) {
     c.chunk_offs[i] = acc;
-    acc += (uint64_t)align16(c.chunk_sizes[i] & 0x7fffffffu);
+    const uint32_t e = c.chunk_sizes[i];
+    if (c.place && first_work == N && !((e >> 31) && acc == (uint64_t)locate_chunk(c, c.one, 0, i).src)) first_work = i;
+    acc += (uint64_t)align16(e & 0x7fffffffu);
   }
   if (t == 0) c.chunk_offs[N] = total;
+  if (c.place) {
+    __syncthreads();
+    int64_t* shm = (int64_t*)sh;
+    shm[t] = first_work;
+    __syncthreads();
+    for (int off = nt / 2; off > 0; off >>= 1) {
+      if (t < off) shm[t] = min(shm[t], shm[t + off]);
+      __syncthreads();
+    }
+    if (t == 0) c.ctl->pad[3] = (uint64_t)shm[0];
+  }
   __syncthreads();
   if (from_table) return;
   if (c.req_offsets_out == nullptr) {
@@ -969,34 +995,219 @@ __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
   }
 }
 
-// Before compaction of a stream whose codes sit at their all-raw places: raw
-// chunks that move (some earlier chunk compressed) are copied to the staging
-// area first, so that no compaction write lands on bytes still to be read.
-__global__ __launch_bounds__(256) void k_stash(CallDesc c) {
-  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
-    const uint32_t e = c.chunk_sizes[ch];
-    if (!(e >> 31)) continue;
-    const int r = find_req_by_chunk(c, ch);
-    const ReqDesc rq = req_at(c, r);
-    const ChunkLoc L = locate_chunk(c, rq, r, ch);
-    if (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin] == (uint64_t)L.src) continue;
-    const uint4* src = (const uint4*)(c.codes + L.src);
-    uint4* dst = (uint4*)(c.codes_out + L.src);
-    const int64_t nv = align16(L.n) / 16;
-    for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) dst[k] = src[k];
-  }
-}
-
-hipError_t launch_stash(const CallDesc& c, hipStream_t s) {
-  if (c.codes_out == c.codes || c.total_chunks == 0) return hipSuccess;
-  k_stash<<<(int)std::min<int64_t>(c.total_chunks, 256 * 16), 256, 0, s>>>(c);
-  return hipGetLastError();
-}
-
 hipError_t launch_compact(const CallDesc& c, hipStream_t s) {
   const int64_t items = c.total_chunks + c.R + c.total_pieces;
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(items, 256 * 16));
   k_compact<<<grid, 256, 0, s>>>(c);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ single-pass placement
+
+// Dense encode, after the sizes and their scan: one in-place pass writes every
+// chunk to its final offset.  The fused encoders left the codes where a stream
+// whose chunks are all raw keeps them, so a raw chunk whose offset did not
+// change needs nothing; a chunk of TUPL8_1 -> BIT_8 -> RZE_2 (whole 4 KiB
+// blocks) is read once, transformed in registers, assembled in LDS and
+// written once; a raw chunk that moves is read into LDS and written; a chunk
+// the stage engines encoded (other pipelines, partial chunks) is copied from
+// the staging area.  A chunk's final offset never exceeds its codes' offset,
+// so its output can only cover codes of itself and of earlier chunks.  Blocks
+// take chunks in index order from a ticket counter (the leading raw chunks
+// that keep their place, found by the scan, go 64 to a ticket and need only
+// their table entries); every chunk announces once it has read its codes (a
+// raw chunk at its place needs none), and a chunk writes only
+// after all earlier chunks whose codes its output covers have announced.  A
+// chunk waits only on earlier chunks, whose blocks already run, so the waits
+// end; they are bounded all the same (kStStall, and every later write is
+// skipped).  The last ticket writes the header and the gaps between the
+// sections.
+// Bound of one wait, in ticks of the 100 MHz real-time counter (about 1.3 s).
+constexpr uint64_t kPlaceWaitTicks = 1ull << 27;
+
+__device__ __forceinline__ uint32_t ld_flag(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// first chunk whose codes end after payload offset `fin` (dense stream)
+__device__ __forceinline__ int64_t first_covered(const CallDesc& c, uint64_t fin) {
+  const ReqDesc& rq = c.one;
+  if ((int64_t)fin < rq.codes_bytes[0]) return (int64_t)(fin / c.chunk_bytes);
+  if ((int64_t)fin < rq.codes_off[1]) return rq.nchunks[0];
+  return rq.nchunks[0] + (int64_t)((fin - (uint64_t)rq.codes_off[1]) / c.chunk_bytes);
+}
+
+// Block-wide: wait until every chunk in [j0, k) has announced.  Whole groups
+// of 64 chunks are checked through their counters, the ragged ends chunk by
+// chunk.  Returns false if a wait ran out or an earlier one did (kStStall).
+__device__ bool wait_announced(const CallDesc& c, const uint32_t* ann, const uint32_t* grp, int64_t j0, int64_t k) {
+  bool ok = true;
+  if (j0 < k) {
+    const int64_t ga = (j0 + 63) >> 6, gb = k >> 6;
+    const int64_t h1 = min(k, ga * 64);                  // head chunks [j0, h1)
+    const int64_t ng = (ga < gb) ? gb - ga : 0;          // groups [ga, gb)
+    const int64_t t0 = max(h1, gb * 64);                 // tail chunks [t0, k)
+    const int64_t nh = h1 - j0, nt = k - t0, items = nh + ng + nt;
+    for (int64_t i = threadIdx.x; i < items && ok; i += blockDim.x) {
+      const uint32_t* f;
+      uint32_t want;
+      if (i < nh) { f = ann + j0 + i; want = 1; }
+      else if (i < nh + ng) { f = grp + ga + (i - nh); want = 64; }
+      else { f = ann + t0 + (i - nh - ng); want = 1; }
+      if (ld_flag(f) >= want) continue;
+      const uint64_t t_start = wall_clock64();
+      while (ld_flag(f) < want) {
+        if ((ld_flag(&c.ctl->status) & kStStall) || wall_clock64() - t_start > kPlaceWaitTicks) { ok = false; break; }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+  }
+  return __syncthreads_and(ok ? 1 : 0) != 0;
+}
+
+__global__ __launch_bounds__(256) void k_place(CallDesc c) {
+  __shared__ __attribute__((aligned(16))) uint32_t ob[16384];   // output assembly / raw chunk (64 KiB)
+  __shared__ uint32_t bm[1024];
+  __shared__ uint32_t offs[1024];
+  __shared__ uint32_t sh32[256];
+  __shared__ int64_t tk;
+  const int64_t N = c.total_chunks;
+  uint32_t* ann = c.place_flags;
+  uint32_t* grp = c.place_flags + N;
+  // tickets: batches of 64 chunks below the first chunk with work (table
+  // entries only), then every chunk from there on, then the header
+  const int64_t kf = (int64_t)c.ctl->pad[3];
+  const int64_t nb0 = (kf + 63) / 64, last = nb0 + (N - kf);
+  const ReqDesc& rq = c.one;
+  const bool p1 = fast_pipeline(c) == 1;
+  const XposeLane X = xpose_lane();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint32_t* ticket = (uint32_t*)&c.ctl->pad[2];
+  for (;;) {
+    if (threadIdx.x == 0) tk = (int64_t)__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int64_t t = tk;
+    __syncthreads();
+    if (t > last) break;
+    if (t == last) {
+      write_header(c, rq, c.stream, c.ctl->total);
+      zero_gaps(c, rq, c.stream);
+      continue;
+    }
+    if (t < nb0) {
+      // raw chunks at their all-raw places: table entries and padding; nothing
+      // waits on them (no later output reaches their codes)
+      const int64_t k = 64 * t + threadIdx.x;
+      if (threadIdx.x < 64 && k < kf) {
+        const ChunkLoc L = locate_chunk(c, rq, 0, k);
+        uint8_t* dst = c.stream + rq.payload_off + L.src;
+        for (int64_t b = L.n; b < align16(L.n); ++b) dst[b] = 0;
+        *(uint32_t*)(c.stream + rq.table_off + 4 * k) = c.chunk_sizes[k];
+      }
+      continue;
+    }
+    const int64_t k = kf + (t - nb0);
+    const ChunkLoc L = locate_chunk(c, rq, 0, k);
+    const uint32_t e = c.chunk_sizes[k];
+    const int64_t stored = e & 0x7fffffffu;
+    const uint64_t fin = c.chunk_offs[k] - c.chunk_offs[0];
+    uint8_t* dst = c.stream + rq.payload_off + fin;
+    const uint8_t* slot = c.codes + L.src;
+    // 0: raw, in place; 1: raw, moves; 2: TUPL8_1 -> BIT_8 -> RZE_2 here; 3: from the staging area
+    const int mode = (e >> 31) ? (fin == (uint64_t)L.src ? 0 : 1) : ((p1 && fast_eligible(1, L.n)) ? 2 : 3);
+    const int n = (int)L.n;
+    const int ngi = n >> 12, nd = n >> 6, dpj = n >> 9;
+    uint32_t rlo[4][8], rhi[4][8];      // mode 2: this lane's row of each (block, kk) transpose
+    if (mode == 2) {
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int gi = wave + 4 * s4;
+        if (gi < ngi) {
+          const uint4* src = (const uint4*)(slot + (int64_t)gi * 4096 + 64 * lane);
+          uint32_t w[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 x = src[q];
+            w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+          }
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            uint32_t lo = w[2 * kk], hi = w[2 * kk + 1];
+            xpose64(lo, hi, X);
+            rlo[s4][kk] = lo;
+            rhi[s4][kk] = hi;
+            const uint32_t dw = or8(nz_quarters(lo, hi) << (4 * (lane & 7)));
+            if ((lane & 7) == 0) bm[(lane >> 3) * dpj + 8 * gi + kk] = dw;
+          }
+        }
+      }
+    } else if (mode == 1) {
+      const int64_t nv = align16(stored) / 16;
+      for (int64_t q = threadIdx.x; q < nv; q += blockDim.x) ((uint4*)ob)[q] = ((const uint4*)slot)[q];
+    }
+    __syncthreads();
+    // every load of this chunk's codes has returned: announce
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(ann + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(grp + (k >> 6), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    bool consistent = true;
+    if (mode == 2) {
+      const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
+      consistent = n / 16 + 2 * (int64_t)nnz == stored;    // the size the scan used
+      if (!consistent && threadIdx.x == 0) set_status2(c.ctl, kStStall);
+    }
+    if (mode == 2 && consistent) {
+      for (int d = threadIdx.x; d < nd; d += blockDim.x) ob[d] = bm[d];
+      uint16_t* ow = (uint16_t*)(ob + nd);
+      const int j = lane >> 3, r4 = 4 * (lane & 7);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int gi = wave + 4 * s4;
+        if (gi < ngi) {
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const int d = j * dpj + 8 * gi + kk;
+            const uint32_t bits = bm[d], base = offs[d];
+            const uint32_t v[4] = {rlo[s4][kk] & 0xFFFFu, rlo[s4][kk] >> 16, rhi[s4][kk] & 0xFFFFu, rhi[s4][kk] >> 16};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t rr = (uint32_t)(r4 + q);
+              if ((bits >> rr) & 1u) ow[base + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u))] = (uint16_t)v[q];
+            }
+          }
+        }
+      }
+    }
+    if (mode == 0) {
+      const int64_t pad = align16(stored) - stored;
+      if (threadIdx.x < pad) dst[stored + threadIdx.x] = 0;
+    } else if (consistent) {
+      // chunks below kf are raw at their places: their codes are never covered
+      const int64_t j0 = min(max(first_covered(c, fin), kf), k);
+      if (!wait_announced(c, ann, grp, j0, k)) {
+        if (threadIdx.x == 0) set_status2(c.ctl, kStStall);
+      } else {
+        const uint4* src = (mode == 3) ? (const uint4*)(c.codes_out + L.src) : (const uint4*)ob;
+        const int64_t nv = align16(stored) / 16;
+        for (int64_t q = threadIdx.x; q < nv; q += blockDim.x) {
+          uint4 x = src[q];
+          const int64_t lim = stored - 16 * q;
+          if (lim < 16) {
+            uint8_t* xb = (uint8_t*)&x;
+            for (int b = 0; b < 16; ++b) if (b >= lim) xb[b] = 0;
+          }
+          ((uint4*)dst)[q] = x;
+        }
+      }
+    }
+    if (threadIdx.x == 0) *(uint32_t*)(c.stream + rq.table_off + 4 * k) = e;
+    __syncthreads();                                     // LDS reused by the next chunk
+  }
+}
+
+hipError_t launch_place(const CallDesc& c, hipStream_t s) {
+  k_place<<<(int)std::min<int64_t>(c.total_chunks + 1, 512), 256, 0, s>>>(c);
   return hipGetLastError();
 }
 

@@ -128,6 +128,18 @@ def test_fused_size_counts(stages, k, v):
     assert s["chunks_compressed"] >= 4, s
 
 
+@pytest.mark.parametrize("zero_frac,L,T", [(1.0, 8, 2048), (0.5, 8, 1024), (0.97, 4, 4096)])
+def test_single_pass_placement(zero_frac, L, T):
+    # a dense encode ends with one in-place pass over 64 KiB chunks: with
+    # all-zero input every chunk shrinks to its bitmap and lands far below its
+    # codes, so each write waits on announcements spanning many groups of 64
+    # chunks; mixed inputs move raw chunks behind compressed ones
+    wl = C3.with_(chunk_bytes=65536, name="placement")
+    s = run_case(wl, L, T, zero_rich=True, zero_frac=zero_frac, seed=21)
+    assert s["identical"]
+    assert s["chunks_compressed"] >= 8, s
+
+
 def test_range_error_is_reported():
     wl = C1
     k = torch.full((1, 64, 8, 128), 60000.0, dtype=torch.float16)
