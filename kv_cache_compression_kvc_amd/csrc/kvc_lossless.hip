@@ -650,6 +650,24 @@ __global__ __launch_bounds__(256) void k_ll_encode_p2(CallDesc c, const uint32_t
   }
 }
 
+// Copy nv <= 4096 16-byte lines from global memory to LDS with 256 threads:
+// every load of a thread is issued before the first LDS store, so a block has
+// the whole chunk in flight at once.  Lines past `avail` bytes read as zero.
+__device__ __forceinline__ void stage_lines(const uint4* src, int nv, uint64_t avail, uint4* dst) {
+  uint4 x[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int k = (int)threadIdx.x + 256 * u;
+    x[u] = make_uint4(0, 0, 0, 0);
+    if (k < nv && (uint64_t)(16 * k + 16) <= avail) x[u] = src[k];
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int k = (int)threadIdx.x + 256 * u;
+    if (k < nv) dst[k] = x[u];
+  }
+}
+
 // Stage a compressed chunk into LDS and check that its bitmap accounts for
 // its length.  Returns false (and flags the stream) if not.
 __device__ __forceinline__ bool load_compressed(const CallDesc& c, uint64_t pos, int stored, int n, uint4* buf,
@@ -657,11 +675,7 @@ __device__ __forceinline__ bool load_compressed(const CallDesc& c, uint64_t pos,
   const uint64_t avail = (c.stream_bytes > pos) ? c.stream_bytes - pos : 0;
   const int nv = (stored + 15) / 16;
   const uint4* src = (const uint4*)(c.stream + pos);
-  for (int k = threadIdx.x; k < nv; k += blockDim.x) {
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if ((uint64_t)(16 * k + 16) <= avail) x = src[k];
-    buf[k] = x;
-  }
+  stage_lines(src, nv, avail, buf);
   __syncthreads();
   // bytes of the last 16-byte line past the stored length are ignored
   if (stored < n / 16) return false;
@@ -1070,7 +1084,7 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
   __shared__ uint32_t bm[1024];
   __shared__ uint32_t offs[1024];
   __shared__ uint32_t sh32[256];
-  __shared__ int64_t tk;
+  __shared__ int64_t tk[1];
   const int64_t N = c.total_chunks;
   uint32_t* ann = c.place_flags;
   uint32_t* grp = c.place_flags + N;
@@ -1083,15 +1097,19 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
   const XposeLane X = xpose_lane();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint32_t* ticket = (uint32_t*)&c.ctl->pad[2];
+  // A ticket is taken only when its work can start: every chunk waits for its
+  // predecessor's read, so a ticket held while the block finishes another
+  // chunk would delay the whole chain behind it.
   for (;;) {
-    if (threadIdx.x == 0) tk = (int64_t)__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) tk[0] = (int64_t)__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const int64_t t = tk;
+    const int64_t t = tk[0];
     __syncthreads();
     if (t > last) break;
     if (t == last) {
       write_header(c, rq, c.stream, c.ctl->total);
       zero_gaps(c, rq, c.stream);
+      __syncthreads();
       continue;
     }
     if (t < nb0) {
@@ -1104,6 +1122,7 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
         for (int64_t b = L.n; b < align16(L.n); ++b) dst[b] = 0;
         *(uint32_t*)(c.stream + rq.table_off + 4 * k) = c.chunk_sizes[k];
       }
+      __syncthreads();
       continue;
     }
     const int64_t k = kf + (t - nb0);
