@@ -683,22 +683,36 @@ __device__ __forceinline__ bool load_compressed(const CallDesc& c, uint64_t pos,
   return n / 16 + 2 * (int)nnz == stored && (uint64_t)(16 * nv) <= avail + 15;
 }
 
+// Decode: whether chunk ch is a well-formed compressed chunk of a standard
+// pipeline, which the word-parallel kernels decode.  They take every such
+// chunk by index (a shared worklist counter would serialize thousands of
+// atomics); the stage engine takes the other compressed chunks from its
+// worklist.
+__device__ __forceinline__ bool wp_decode_chunk(const CallDesc& c, int64_t ch, int pipe, ChunkLoc& L, uint64_t& pos,
+                                                int& stored) {
+  const int r = find_req_by_chunk(c, ch);
+  const ReqDesc rq = req_at(c, r);
+  L = locate_chunk(c, rq, r, ch);
+  const uint32_t e = c.chunk_sizes[ch];
+  stored = (int)(e & 0x7fffffffu);
+  if ((e >> 31) || !fast_eligible(pipe, L.n)) return false;
+  const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+  pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+  return stored < L.n && stored > 0 && pos + (uint64_t)stored <= c.stream_bytes && (pos & 15) == 0;
+}
+
 __global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
   __shared__ __attribute__((aligned(16))) uint4 buf[4096];
   __shared__ uint32_t offs[1024];
   __shared__ uint32_t sh32[256];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const XposeLane X = xpose_lane();
-  const uint32_t count = c.ctl->pad0;
-  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
-    const int64_t ch = worklist[item];
-    const int r = find_req_by_chunk(c, ch);
-    const ReqDesc rq = req_at(c, r);
-    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+    ChunkLoc L;
+    uint64_t pos;
+    int stored;
+    if (!wp_decode_chunk(c, ch, 1, L, pos, stored)) continue;
     const int n = (int)L.n;
-    const int stored = (int)(c.chunk_sizes[ch] & 0x7fffffffu);
-    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
-    const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
     uint32_t nnz = 0;
     const bool ok = load_compressed(c, pos, stored, n, buf, offs, sh32, nnz);
     if (!ok) {
@@ -746,16 +760,12 @@ __global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t
   __shared__ uint32_t offs[1024];
   __shared__ uint32_t sh32[256];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const uint32_t count = c.ctl->pad0;
-  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
-    const int64_t ch = worklist[item];
-    const int r = find_req_by_chunk(c, ch);
-    const ReqDesc rq = req_at(c, r);
-    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+    ChunkLoc L;
+    uint64_t pos;
+    int stored;
+    if (!wp_decode_chunk(c, ch, 2, L, pos, stored)) continue;
     const int n = (int)L.n;
-    const int stored = (int)(c.chunk_sizes[ch] & 0x7fffffffu);
-    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
-    const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
     uint32_t nnz = 0;
     const bool ok = load_compressed(c, pos, stored, n, buf, offs, sh32, nnz);
     if (!ok) {
@@ -1324,8 +1334,8 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
       const int64_t nv = L.n / 16;
       for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) dst[k] = src[k];
       for (int64_t p = nv * 16 + threadIdx.x; p < L.n; p += blockDim.x) c.codes[L.src + p] = c.stream[pos + p];
-    } else if (threadIdx.x == 0) {
-      push_work(c, worklist, ch, fast_eligible(fast_pipeline(c), L.n));
+    } else if (!fast_eligible(fast_pipeline(c), L.n) && threadIdx.x == 0) {
+      push_work(c, worklist, ch, false);            // the stage engine; the word-parallel kernels find theirs
     }
   }
 }
