@@ -93,6 +93,7 @@ struct CallDesc {
   int direct[2];             // decode: reconstruct kernels read raw chunks of K / V from the stream
   int place;                 // dense encode: finish the stream in one in-place pass (k_place)
   uint32_t* place_flags;     //   [total chunks] read announcements, then [ceil(total / 64)] group counts
+  uint64_t* scan_state;      // dense calls: look-back words of the chunk-size scan, one per 1024 chunks
   int nnz_pipe;              // encode: 1 or 2 when the fused kernels count the non-zero RZE
   int nnz_sec[2];            //   words of pipeline P1 / P2 per chunk (into chunk_sizes), per section
   uint8_t* params_ws;        // workspace parameter staging area (paged encode)
@@ -121,6 +122,7 @@ hipError_t launch_encode_fused(const CallDesc& c, int which, hipStream_t s);
 hipError_t launch_decode_fused(const CallDesc& c, int which, hipStream_t s);
 hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s);
 hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s);
+hipError_t launch_scan_dense(const CallDesc& c, bool from_table, hipStream_t s);
 hipError_t launch_compact(const CallDesc& c, hipStream_t s);
 hipError_t launch_place(const CallDesc& c, hipStream_t s);
 hipError_t launch_validate(const CallDesc& c, hipStream_t s);

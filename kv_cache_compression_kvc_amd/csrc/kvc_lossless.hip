@@ -85,7 +85,11 @@ __global__ void k_reset(CallDesc c) {
     ctl->pad[0] = 0;   // header-field diagnosis bits
     ctl->pad[1] = 0;   // worklist entries for the general stage engine (from the back)
     ctl->pad[2] = 0;   // tickets of the single-pass placement
+    ctl->pad[3] = ~0ull;  // first chunk with placement work (a minimum)
+    ctl->pad[4] = 0;   // tickets of the dense scan
   }
+  if (c.scan_state && blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i <= c.total_chunks / 1024; i += blockDim.x) c.scan_state[i] = 0;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, di = (int64_t)gridDim.x * blockDim.x;
   // the fused encoders accumulate per-chunk non-zero word counts here
   if (c.nnz_pipe)
@@ -707,11 +711,25 @@ __global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t
   __shared__ uint32_t sh32[256];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const XposeLane X = xpose_lane();
-  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+  // this block's chunks are blockIdx.x + gridDim.x * i; 256 at a time are
+  // checked in parallel and the block then works through those to decode
+  __shared__ uint32_t cand[256];
+  for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += 256) {
+  {
+    const int64_t mine = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + threadIdx.x);
     ChunkLoc L;
     uint64_t pos;
     int stored;
-    if (!wp_decode_chunk(c, ch, 1, L, pos, stored)) continue;
+    cand[threadIdx.x] = (mine < c.total_chunks && wp_decode_chunk(c, mine, 1, L, pos, stored)) ? 1u : 0u;
+  }
+  __syncthreads();
+  for (int i = 0; i < 256; ++i) {
+    if (!cand[i]) continue;
+    const int64_t ch = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i);
+    ChunkLoc L;
+    uint64_t pos;
+    int stored;
+    wp_decode_chunk(c, ch, 1, L, pos, stored);
     const int n = (int)L.n;
     uint32_t nnz = 0;
     const bool ok = load_compressed(c, pos, stored, n, buf, offs, sh32, nnz);
@@ -753,6 +771,8 @@ __global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t
     // a set bitmap bit must mark a non-zero word
     if (__syncthreads_or((int)bad) && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
   }
+  __syncthreads();                                   // cand is rewritten next round
+  }
 }
 
 __global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t* worklist) {
@@ -760,11 +780,25 @@ __global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t
   __shared__ uint32_t offs[1024];
   __shared__ uint32_t sh32[256];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+  // this block's chunks are blockIdx.x + gridDim.x * i; 256 at a time are
+  // checked in parallel and the block then works through those to decode
+  __shared__ uint32_t cand[256];
+  for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += 256) {
+  {
+    const int64_t mine = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + threadIdx.x);
     ChunkLoc L;
     uint64_t pos;
     int stored;
-    if (!wp_decode_chunk(c, ch, 2, L, pos, stored)) continue;
+    cand[threadIdx.x] = (mine < c.total_chunks && wp_decode_chunk(c, mine, 2, L, pos, stored)) ? 1u : 0u;
+  }
+  __syncthreads();
+  for (int i = 0; i < 256; ++i) {
+    if (!cand[i]) continue;
+    const int64_t ch = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i);
+    ChunkLoc L;
+    uint64_t pos;
+    int stored;
+    wp_decode_chunk(c, ch, 2, L, pos, stored);
     const int n = (int)L.n;
     uint32_t nnz = 0;
     const bool ok = load_compressed(c, pos, stored, n, buf, offs, sh32, nnz);
@@ -801,6 +835,8 @@ __global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t
       ((uint4*)(c.codes + L.src))[64 * blk + lane] = x;
     }
     if (__syncthreads_or((int)bad) && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+  }
+  __syncthreads();                                   // cand is rewritten next round
   }
 }
 
@@ -850,27 +886,11 @@ __global__ __launch_bounds__(1024) void k_scan(CallDesc c, int from_table) {
   for (int64_t i = i0; i < i1; ++i) sum += (uint64_t)align16(c.chunk_sizes[i] & 0x7fffffffu);
   uint64_t total;
   uint64_t acc = block_exclusive_scan<uint64_t>(sum, sh, total);
-  // dense encode with single-pass placement: the first chunk that is not a
-  // raw chunk at its all-raw place (every earlier one is, and needs no work)
-  int64_t first_work = N;
   for (int64_t i = i0; i < i1; ++i) {
     c.chunk_offs[i] = acc;
-    const uint32_t e = c.chunk_sizes[i];
-    if (c.place && first_work == N && !((e >> 31) && acc == (uint64_t)locate_chunk(c, c.one, 0, i).src)) first_work = i;
-    acc += (uint64_t)align16(e & 0x7fffffffu);
+    acc += (uint64_t)align16(c.chunk_sizes[i] & 0x7fffffffu);
   }
   if (t == 0) c.chunk_offs[N] = total;
-  if (c.place) {
-    __syncthreads();
-    int64_t* shm = (int64_t*)sh;
-    shm[t] = first_work;
-    __syncthreads();
-    for (int off = nt / 2; off > 0; off >>= 1) {
-      if (t < off) shm[t] = min(shm[t], shm[t + off]);
-      __syncthreads();
-    }
-    if (t == 0) c.ctl->pad[3] = (uint64_t)shm[0];
-  }
   __syncthreads();
   if (from_table) return;
   if (c.req_offsets_out == nullptr) {
@@ -901,6 +921,98 @@ __global__ __launch_bounds__(1024) void k_scan(CallDesc c, int from_table) {
 
 hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s) {
   k_scan<<<1, 1024, 0, s>>>(c, from_table ? 1 : 0);
+  return hipGetLastError();
+}
+
+// The same scan for a dense call (one request) over many blocks, one per 1024
+// chunks, chained by decoupled look-back: a block publishes its sum, then
+// walks back over earlier blocks' words (sum, or running total once a block
+// has one) until it meets a running total.  Blocks take their index from a
+// ticket counter in the order they start, so a block waits only on blocks
+// already running; the wait is bounded all the same (kStStall).  A dense
+// encode also gets the first chunk that is not raw at its all-raw place (the
+// minimum over blocks) for the placement.
+constexpr int kScanPer = 1024;
+constexpr uint64_t kLbAgg = 1ull << 62, kLbIncl = 2ull << 62, kLbVal = (1ull << 62) - 1;
+
+__global__ __launch_bounds__(256) void k_scan_dense(CallDesc c, int from_table) {
+  __shared__ uint64_t sh[256];
+  __shared__ int64_t sb[2];
+  const int t = threadIdx.x;
+  const int64_t N = c.total_chunks;
+  const ReqDesc& rq = c.one;
+  if (t == 0) sb[0] = (int64_t)__hip_atomic_fetch_add((uint32_t*)&c.ctl->pad[4], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int64_t vb = sb[0];
+  const int64_t k0 = vb * kScanPer + 4 * t;
+  uint32_t e[4];
+  uint64_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t k = k0 + i;
+    e[i] = 0;
+    if (k < N) {
+      if (from_table) {
+        const uint64_t pos = (uint64_t)rq.table_off + 4 * (uint64_t)k;
+        if (pos + 4 <= c.stream_bytes && pos + 4 <= (uint64_t)rq.payload_off) e[i] = *(const uint32_t*)(c.stream + pos);
+        else set_status2(c.ctl, kStCorrupt);
+        c.chunk_sizes[k] = e[i];
+      } else {
+        e[i] = c.chunk_sizes[k];
+      }
+    }
+    sum += (uint64_t)align16(e[i] & 0x7fffffffu);
+  }
+  uint64_t agg;
+  const uint64_t ex = block_exclusive_scan<uint64_t>(sum, sh, agg);
+  if (t == 0) {
+    uint64_t* st = c.scan_state;
+    uint64_t prefix = 0;
+    if (vb == 0) {
+      __hip_atomic_store(st, kLbIncl | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      __hip_atomic_store(st + vb, kLbAgg | agg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int64_t j = vb - 1; j >= 0; --j) {
+        uint64_t w = __hip_atomic_load(st + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (w == 0) {
+          const uint64_t t0 = wall_clock64();
+          while ((w = __hip_atomic_load(st + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0) {
+            if (wall_clock64() - t0 > (1ull << 27)) break;
+            __builtin_amdgcn_s_sleep(2);
+          }
+          if (w == 0) { set_status2(c.ctl, kStStall); break; }
+        }
+        prefix += w & kLbVal;
+        if (w & kLbIncl) break;
+      }
+      __hip_atomic_store(st + vb, kLbIncl | (prefix + agg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    sb[1] = (int64_t)prefix;
+  }
+  __syncthreads();
+  uint64_t acc = (uint64_t)sb[1] + ex;
+  int64_t first_work = N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t k = k0 + i;
+    if (k < N) {
+      c.chunk_offs[k] = acc;
+      if (c.place && first_work == N && !((e[i] >> 31) && acc == (uint64_t)locate_chunk(c, rq, 0, k).src)) first_work = k;
+      acc += (uint64_t)align16(e[i] & 0x7fffffffu);
+    }
+  }
+  if (c.place && first_work < N)
+    __hip_atomic_fetch_min(&c.ctl->pad[3], (uint64_t)first_work, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == 0 && (vb + 1) * kScanPer >= N) {
+    const uint64_t total = (uint64_t)sb[1] + agg;
+    c.chunk_offs[N] = total;
+    if (!from_table) c.ctl->total = (uint64_t)rq.payload_off + total;
+  }
+}
+
+hipError_t launch_scan_dense(const CallDesc& c, bool from_table, hipStream_t s) {
+  const int64_t nb = std::max<int64_t>(1, (c.total_chunks + kScanPer - 1) / kScanPer);
+  k_scan_dense<<<(int)nb, 256, 0, s>>>(c, from_table ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1100,7 +1212,7 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
   uint32_t* grp = c.place_flags + N;
   // tickets: batches of 64 chunks below the first chunk with work (table
   // entries only), then every chunk from there on, then the header
-  const int64_t kf = (int64_t)c.ctl->pad[3];
+  const int64_t kf = (int64_t)min<uint64_t>(c.ctl->pad[3], (uint64_t)N);
   const int64_t nb0 = (kf + 63) / 64, last = nb0 + (N - kf);
   const ReqDesc& rq = c.one;
   const bool p1 = fast_pipeline(c) == 1;
