@@ -1128,6 +1128,9 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
   int l, g64, h;
   decode_tile((int)blockIdx.x, l, g64, h);
   if constexpr (TAIL) g64 = T / 64;
+  // the sign table is written; from here on each pass ends with a barrier, so
+  // a tile's staging writes never meet the previous tile's readers
+  __syncthreads();
   for (int tile = blockIdx.x; tile < (int)ntiles; tile += step) {
     // output addressing: (layer, head) within the section layout, and its base
     int lo = l, ho = h, Ho = H;
@@ -1147,7 +1150,6 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
     const int gg = TAIL ? T - t0 : 64;                 // valid tokens in this tile
     const int nvw = TAIL ? max(0, min(32, gg - tw0)) : 32;
 
-    __syncthreads();                                    // previous tile's readers are done
     float f[64];
     const uint16_t* src = in + (((int64_t)l * T + t0 + tw0) * H + h) * kHeadDim;
     stage_in<BF16>(make_rsrc(src, nvw ? (uint32_t)(nvw - 1) * vstride + 256u : 0u), vstride, stg, smt, f);
