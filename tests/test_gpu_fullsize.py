@@ -124,6 +124,67 @@ def test_llama70b_128k_full_size_sampled_layer():
     check_dense_full("c5_llama70b_128k", [37], Tp=8192)
 
 
+def stream_chunks(stream: np.ndarray, wl, L, T):
+    """Per section: (table entries, byte offset of each chunk) of a dense stream."""
+    cfg = O.cfg_from_workload(wl, layers=L)
+    lib = O.lib()
+    cb = wl.chunk_bytes
+    codes_b = [lib.kvco_codes_bytes(C.byref(cfg), w, T) for w in range(2)]
+    params_b = [lib.kvco_params_bytes(C.byref(cfg), w, T) for w in range(2)]
+    nch = [-(-c // cb) for c in codes_b]
+    table = np.frombuffer(stream[64:64 + 4 * sum(nch)].tobytes(), np.uint32)
+    stored = (table & 0x7FFFFFFF).astype(np.int64)
+    offs = np.concatenate([[0], np.cumsum((stored + 15) & ~15)])
+    pay = a16(a16(a16(64 + 4 * sum(nch)) + params_b[0]) + params_b[1])
+    return table, pay + offs, nch
+
+
+def test_llama70b_32k_full_size_compressible_sampled_layers():
+    # half of the 64-token blocks zero: nearly every one of the 30720 chunks
+    # compresses, so the single-pass placement moves every chunk far below its
+    # codes and the look-back scan chains 30 blocks; the sampled layers' chunk
+    # table entries and stored chunk bytes must equal the oracle's
+    wl = W.WORKLOADS["c3_llama70b_32k"]
+    L, T = wl.layers, wl.tokens
+    log(f"{wl.name}: generating zero-rich {L} x {T} x {wl.heads} x {wl.head_dim} on the GPU")
+    k, v = W.zero_rich_kv(wl, L, T, seed=W.SEED_BASE + 7, device=DEV, zero_frac=0.5)
+    plan = K.Plan(K.config_from_workload(wl))
+    ms, wsb = plan.sizes(T)
+    out = torch.empty(ms, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    n = plan.encode(k, v, T, out, ws)
+    log(f"{wl.name}: GPU stream {n} bytes (CR {wl.uncompressed_bytes() / n:.3f})")
+    kd = torch.empty_like(k)
+    vd = torch.empty_like(v)
+    plan.decode(out, n, T, kd, vd, ws)
+    assert plan.query_status(ws) == K.OK
+    gtab, gpos, gnch = stream_chunks(out[:1 << 18].cpu().numpy(), wl, L, T)      # header + chunk table
+    assert int(gpos[-1]) == n, "chunk offsets must end at the stream size"
+    compressed = int(np.count_nonzero((gtab >> 31) == 0))
+    log(f"{wl.name}: {compressed} of {len(gtab)} chunks compressed")
+    assert compressed > len(gtab) // 2
+    for l in (0, 41, 79):
+        t0 = time.time()
+        ku, vu = to_u16(k[l:l + 1]), to_u16(v[l:l + 1])
+        st, ref = O.encode(O.cfg_from_workload(wl, layers=1), ku, vu, T)
+        assert st == O.OK
+        rtab, rpos, rnch = stream_chunks(ref, wl, 1, T)
+        for w in range(2):
+            g0 = (gnch[0] if w else 0) + l * rnch[w]
+            r0 = rnch[0] if w else 0
+            assert np.array_equal(gtab[g0:g0 + rnch[w]], rtab[r0:r0 + rnch[w]]), f"layer {l} section {w}: table"
+            gb = out[int(gpos[g0]):int(gpos[g0 + rnch[w]])].cpu().numpy()
+            rb = ref[int(rpos[r0]):int(rpos[r0 + rnch[w]])]
+            assert np.array_equal(gb, rb), f"layer {l} section {w}: chunk bytes differ"
+        st, kr, vr = O.decode(ref, T * wl.heads * wl.head_dim)
+        assert st == O.OK
+        assert np.array_equal(to_u16(kd[l:l + 1]).reshape(-1), kr), f"layer {l}: K reconstruction differs"
+        assert np.array_equal(to_u16(vd[l:l + 1]).reshape(-1), vr), f"layer {l}: V reconstruction differs"
+        log(f"{wl.name}: layer {l} identical ({time.time() - t0:.1f} s)")
+    del k, v, kd, vd, out, ws
+    free()
+
+
 def test_paged_llama8b_full_size_sampled_requests():
     wl = W.WORKLOADS["c4_paged_llama8b"]
     batch = W.paged_layout(wl)
