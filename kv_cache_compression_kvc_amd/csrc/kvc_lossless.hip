@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, uint32_t* worklist
       if (size >= n) {
         if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
         work = false;
-      } else if (c.place && pipe == 1) {
+      } else if (c.place) {
         // the single-pass placement encodes it; it needs only the size
         if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
         work = false;
@@ -851,7 +851,7 @@ hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
   const int fgrid = (int)std::min<int64_t>(c.total_chunks, 512);
   if (p1 && !c.place) k_ll_encode_p1<<<fgrid, 256, 0, s>>>(c, worklist);
-  else if (p2) k_ll_encode_p2<<<fgrid, 256, 0, s>>>(c, worklist);
+  else if (p2 && !c.place) k_ll_encode_p2<<<fgrid, 256, 0, s>>>(c, worklist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   k_ll_encode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
   return hipGetLastError();
@@ -1165,6 +1165,20 @@ __device__ __forceinline__ uint32_t ld_flag(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Raw buffer access (wave-uniform base and size; out-of-range lanes read zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ll_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 ll_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef int int4v_ __attribute__((ext_vector_type(4)));
+  const int4v_ x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4((uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w);
+}
+
 // first chunk whose codes end after payload offset `fin` (dense stream)
 __device__ __forceinline__ int64_t first_covered(const CallDesc& c, uint64_t fin) {
   const ReqDesc& rq = c.one;
@@ -1201,6 +1215,10 @@ __device__ bool wait_announced(const CallDesc& c, const uint32_t* ann, const uin
   return __syncthreads_and(ok ? 1 : 0) != 0;
 }
 
+// PIPE: the plan's pipeline when it is one of the two encoded here (1:
+// TUPL8_1 -> BIT_8 -> RZE_2, 2: TUPL8_1 -> RZE_2), else 0; one instantiation
+// each, so none carries the other's registers.
+template <int PIPE>
 __global__ __launch_bounds__(256) void k_place(CallDesc c) {
   __shared__ __attribute__((aligned(16))) uint32_t ob[16384];   // output assembly / raw chunk (64 KiB)
   __shared__ uint32_t bm[1024];
@@ -1215,7 +1233,7 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
   const int64_t kf = (int64_t)min<uint64_t>(c.ctl->pad[3], (uint64_t)N);
   const int64_t nb0 = (kf + 63) / 64, last = nb0 + (N - kf);
   const ReqDesc& rq = c.one;
-  const bool p1 = fast_pipeline(c) == 1;
+  constexpr int pipe = PIPE;
   const XposeLane X = xpose_lane();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint32_t* ticket = (uint32_t*)&c.ctl->pad[2];
@@ -1254,31 +1272,70 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
     const uint64_t fin = c.chunk_offs[k] - c.chunk_offs[0];
     uint8_t* dst = c.stream + rq.payload_off + fin;
     const uint8_t* slot = c.codes + L.src;
-    // 0: raw, in place; 1: raw, moves; 2: TUPL8_1 -> BIT_8 -> RZE_2 here; 3: from the staging area
-    const int mode = (e >> 31) ? (fin == (uint64_t)L.src ? 0 : 1) : ((p1 && fast_eligible(1, L.n)) ? 2 : 3);
+    // 0: raw, in place; 1: raw, moves; 2: TUPL8_1 -> BIT_8 -> RZE_2 here;
+    // 3: from the staging area; 4: TUPL8_1 -> RZE_2 here
+    const int mode = (e >> 31) ? (fin == (uint64_t)L.src ? 0 : 1)
+                               : ((pipe == 0 || !fast_eligible(pipe, L.n)) ? 3 : (pipe == 1 ? 2 : 4));
     const int n = (int)L.n;
     const int ngi = n >> 12, nd = n >> 6, dpj = n >> 9;
-    uint32_t rlo[4][8], rhi[4][8];      // mode 2: this lane's row of each (block, kk) transpose
+    // R: this lane's 64 bytes of the chunk.  Mode 2: R[16 s4 .. 16 s4 + 15] =
+    // bytes 64 lane .. 64 lane + 63 of 4 KiB block gi = wave + 4 s4, input
+    // word 8 lane + kk at R[16 s4 + 2 kk], transposed there in place.  Mode 4:
+    // R[4 s16 .. 4 s16 + 3] = 16-byte unit `lane` of 1 KiB block wave + 4 s16.
+    uint32_t R[64];
+    if (mode == 4) {
+      // every load first, so the whole chunk is in flight at once: buffer
+      // loads with one lane offset and wave-uniform block offsets (blocks past
+      // the chunk read zero)
+      const __amdgpu_buffer_rsrc_t rs = ll_rsrc(slot, (uint32_t)n);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint4 x = ll_load16(rs, 16u * (uint32_t)lane, 1024u * (uint32_t)(wave + 4 * u));
+        R[4 * u] = x.x; R[4 * u + 1] = x.y; R[4 * u + 2] = x.z; R[4 * u + 3] = x.w;
+      }
+    }
     if (mode == 2) {
+      // block by block (measured faster here than issuing the whole chunk first)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
         const int gi = wave + 4 * s4;
         if (gi < ngi) {
           const uint4* src = (const uint4*)(slot + (int64_t)gi * 4096 + 64 * lane);
-          uint32_t w[16];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const uint4 x = src[q];
-            w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+            R[16 * s4 + 4 * q] = x.x; R[16 * s4 + 4 * q + 1] = x.y; R[16 * s4 + 4 * q + 2] = x.z; R[16 * s4 + 4 * q + 3] = x.w;
           }
 #pragma unroll
           for (int kk = 0; kk < 8; ++kk) {
-            uint32_t lo = w[2 * kk], hi = w[2 * kk + 1];
+            uint32_t lo = R[16 * s4 + 2 * kk], hi = R[16 * s4 + 2 * kk + 1];
             xpose64(lo, hi, X);
-            rlo[s4][kk] = lo;
-            rhi[s4][kk] = hi;
+            R[16 * s4 + 2 * kk] = lo;
+            R[16 * s4 + 2 * kk + 1] = hi;
             const uint32_t dw = or8(nz_quarters(lo, hi) << (4 * (lane & 7)));
             if ((lane & 7) == 0) bm[(lane >> 3) * dpj + 8 * gi + kk] = dw;
+          }
+        }
+      }
+    } else if (mode == 4) {
+      // RZE word (j, p) is byte j of input words 2 p and 2 p + 1; lane `lane`
+      // of block blk holds pair p = 64 blk + lane, and the 64 pairs of a block
+      // and byte j make two bitmap dwords (ballot)
+      const int nblk = n >> 10;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int blk = wave + 4 * u;
+        if (blk < nblk) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t a = (j < 4) ? R[4 * u] : R[4 * u + 1], b = (j < 4) ? R[4 * u + 2] : R[4 * u + 3];
+            const uint32_t jj = (uint32_t)(j & 3);
+            const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
+            const uint64_t m = __ballot(word != 0u);
+            if (lane == 0) {
+              bm[j * dpj + 2 * blk] = (uint32_t)m;
+              bm[j * dpj + 2 * blk + 1] = (uint32_t)(m >> 32);
+            }
           }
         }
       }
@@ -1293,7 +1350,7 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
       __hip_atomic_fetch_add(grp + (k >> 6), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     bool consistent = true;
-    if (mode == 2) {
+    if (mode == 2 || mode == 4) {
       const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
       consistent = n / 16 + 2 * (int64_t)nnz == stored;    // the size the scan used
       if (!consistent && threadIdx.x == 0) set_status2(c.ctl, kStStall);
@@ -1310,12 +1367,33 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
           for (int kk = 0; kk < 8; ++kk) {
             const int d = j * dpj + 8 * gi + kk;
             const uint32_t bits = bm[d], base = offs[d];
-            const uint32_t v[4] = {rlo[s4][kk] & 0xFFFFu, rlo[s4][kk] >> 16, rhi[s4][kk] & 0xFFFFu, rhi[s4][kk] >> 16};
+            const uint32_t lo = R[16 * s4 + 2 * kk], hi = R[16 * s4 + 2 * kk + 1];
+            const uint32_t v[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const uint32_t rr = (uint32_t)(r4 + q);
               if ((bits >> rr) & 1u) ow[base + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u))] = (uint16_t)v[q];
             }
+          }
+        }
+      }
+    } else if (mode == 4 && consistent) {
+      for (int d = threadIdx.x; d < nd; d += blockDim.x) ob[d] = bm[d];
+      uint16_t* ow = (uint16_t*)(ob + nd);
+      const int nblk = n >> 10;
+      const uint32_t rr = (uint32_t)(lane & 31);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int blk = wave + 4 * u;
+        if (blk < nblk) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t a = (j < 4) ? R[4 * u] : R[4 * u + 1], b = (j < 4) ? R[4 * u + 2] : R[4 * u + 3];
+            const uint32_t jj = (uint32_t)(j & 3);
+            const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
+            const int d = j * dpj + 2 * blk + (lane >> 5);
+            const uint32_t bits = bm[d];
+            if ((bits >> rr) & 1u) ow[offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u))] = (uint16_t)word;
           }
         }
       }
@@ -1348,7 +1426,12 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
 }
 
 hipError_t launch_place(const CallDesc& c, hipStream_t s) {
-  k_place<<<(int)std::min<int64_t>(c.total_chunks + 1, 512), 256, 0, s>>>(c);
+  const int grid = (int)std::min<int64_t>(c.total_chunks + 1, 512);
+  const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
+  const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
+  if (p1) k_place<1><<<grid, 256, 0, s>>>(c);
+  else if (p2) k_place<2><<<grid, 256, 0, s>>>(c);
+  else k_place<0><<<grid, 256, 0, s>>>(c);
   return hipGetLastError();
 }
 

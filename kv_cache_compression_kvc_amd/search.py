@@ -149,6 +149,8 @@ def main(argv=None):
     ap.add_argument("--rho", type=float, default=0.95)
     ap.add_argument("--max-stages", type=int, default=3)
     ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--pipelines", default="", help="comma-separated lossless lists to time instead of all "
+                    "candidates, stages joined by '>' (e.g. 'TUPL8_1>RZE_2,none')")
     ap.add_argument("--json", default="")
     args = ap.parse_args(argv)
     import torch
@@ -164,7 +166,10 @@ def main(argv=None):
         k, v = W.zero_rich_kv(wl, args.layers, T, wl.seed, device=dev, zero_frac=0.5)
     else:
         k, v = W.dense_kv(wl, layers=args.layers, tokens=T, device=dev)
-    pipes = candidate_pipelines(args.max_stages)
+    if args.pipelines:
+        pipes = [() if x == "none" else tuple(x.split(">")) for x in args.pipelines.split(",")]
+    else:
+        pipes = candidate_pipelines(args.max_stages)
     print(f"{len(pipes)} pipelines", flush=True)
     pts = measure(wl, k, v, T, pipes, reps=args.reps, log=lambda m: print(m, flush=True))
     front = pareto_front(pts)
