@@ -22,8 +22,8 @@
 // for the second kernel, which runs the stages in LDS (two 64 KiB buffers)
 // and writes the result in place into the chunk's slot.  A single-block scan
 // turns stored sizes into 16-byte aligned offsets.  A dense encode then ends
-// with one in-place pass (k_place) that encodes the standard pipeline's
-// chunks and puts every chunk at its final offset; paged encodes use the
+// with one in-place pass (k_place) that encodes the chunks of the two
+// standard pipelines and puts every chunk at its final offset; paged encodes use the
 // compaction kernel, which copies chunks and parameter pieces to their final
 // places.  Both write the headers and the chunk tables.
 #include <algorithm>
@@ -1144,10 +1144,10 @@ hipError_t launch_compact(const CallDesc& c, hipStream_t s) {
 // chunk to its final offset.  The fused encoders left the codes where a stream
 // whose chunks are all raw keeps them, so a raw chunk whose offset did not
 // change needs nothing; a chunk of TUPL8_1 -> BIT_8 -> RZE_2 (whole 4 KiB
-// blocks) is read once, transformed in registers, assembled in LDS and
-// written once; a raw chunk that moves is read into LDS and written; a chunk
-// the stage engines encoded (other pipelines, partial chunks) is copied from
-// the staging area.  A chunk's final offset never exceeds its codes' offset,
+// blocks) or TUPL8_1 -> RZE_2 (whole 1 KiB blocks) is read once, transformed
+// in registers, assembled in LDS and written once; a raw chunk that moves is
+// read into LDS and written; a chunk the stage engines encoded (other
+// pipelines, partial chunks) is copied from the staging area.  A chunk's final offset never exceeds its codes' offset,
 // so its output can only cover codes of itself and of earlier chunks.  Blocks
 // take chunks in index order from a ticket counter (the leading raw chunks
 // that keep their place, found by the scan, go 64 to a ticket and need only
