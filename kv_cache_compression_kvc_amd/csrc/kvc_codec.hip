@@ -1157,6 +1157,8 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
     fwht_cross(f);
 
     // two passes of 64 channels: pass p holds channels [64p, 64p + 64)
+    uint32_t tile_cnt = 0;                             // this lane's RZE word counts, both passes
+    int64_t tile_gci = 0;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       float* wrow = zb + (tw0 + v) * RP + ((32 * hf) ^ (32 * wave));   // rows >= 32 swizzled by 32
@@ -1271,19 +1273,26 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
               for (int u = 0; u < BITS / 4; ++u)
                 cnt += nz_bytes64(u64of(w[4 * u], w[4 * u + 1]) | u64of(w[4 * u + 2], w[4 * u + 3]));
             }
-            const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + chunk_of(c, boff);
-            if (c.nnz_pipe == 1) {
-              if constexpr (BITS == 4) add_chunk_nnz4<0, 1, 32, 33>(c, gci, cnt);
-              else add_chunk_nnz4<0, 16, 32, 48>(c, gci, cnt);
-            } else {
-              add_chunk_nnz(c, gci, cnt);
-            }
+            // both passes' codes lie in the same group block, hence the same
+            // chunk: one atomic per tile
+            tile_cnt += cnt;
+            tile_gci = (which ? (int64_t)c.one.nchunks[0] : 0) + chunk_of(c, boff);
           }
         }
       };
       if constexpr (TAIL) pass(std::false_type{});
       else pass(std::true_type{});
       __syncthreads();                                   // before the next pass overwrites zb
+    }
+    if constexpr (G == 64 && !TAIL && BITS >= 4) {
+      if (c.nnz_pipe && c.nnz_sec[which]) {
+        if (c.nnz_pipe == 1) {
+          if constexpr (BITS == 4) add_chunk_nnz4<0, 1, 32, 33>(c, tile_gci, tile_cnt);
+          else add_chunk_nnz4<0, 16, 32, 48>(c, tile_gci, tile_cnt);
+        } else {
+          add_chunk_nnz(c, tile_gci, tile_cnt);
+        }
+      }
     }
     const int nt = tile + step;
     if (stepwise && nt < full) {
