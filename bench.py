@@ -268,6 +268,23 @@ def main():
     dec_ms = timed(lambda: plan.decode(out, ms, T, kd, vd, ws))
     st = plan.query_status(ws)
     assert st == K.OK, K.status_string(st)
+
+    # the same step captured once in a HIP graph and replayed (a serving loop's
+    # form: the dense calls enqueue kernels only)
+    graph_ms = None
+    if bits is None:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(s)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                step()
+        s.wait_stream(side)
+        torch.cuda.synchronize()
+        graph_ms = timed(g.replay)
+        st = plan.query_status(ws)
+        assert st == K.OK, K.status_string(st)
+        log(f"graph replay {graph_ms:.3f} ms per step")
     log(f"encode {enc_ms:.3f} ms ({U / enc_ms / 1e6:.1f} GB/s), decode {dec_ms:.3f} ms ({U / dec_ms / 1e6:.1f} GB/s)")
 
     # roofline of the dominant fused kernel, algorithmic bytes per launch
@@ -316,6 +333,8 @@ def main():
         "stream_bytes": n,
         "kernel_ms_per_launch": {k_: round(t / max(c, 1), 4) for k_, (t, c) in prof.items() if c},
         "device_copy_GBps": round(copy_gbps, 1),
+        "graph_replay": (None if graph_ms is None else
+                         {"ms_per_step": round(graph_ms, 4), "GBps": round(U / graph_ms / 1e6, 3)}),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "algorithmic_bytes": round(cand[dom]), "traffic": None},
