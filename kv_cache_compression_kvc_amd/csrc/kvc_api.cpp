@@ -743,6 +743,7 @@ kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_
   c.total_pieces = j.pieces;
   c.tiles[0] = j.tiles[0];
   c.tiles[1] = j.tiles[1];
+  c.place = 2;                   // chunks go from the workspace straight into the request streams
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (R > 1) {
@@ -755,6 +756,7 @@ kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_
   if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
   if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_compact(c, s); })) != hipSuccess) return hip_fail(e, "compact");
+  if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_place(c, s); })) != hipSuccess) return hip_fail(e, "place");
   if (h_out_bytes) {
     Control h;
     if ((st = sync_and_read(c.ctl, s, h)) != KVC_OK) return st;

@@ -91,7 +91,8 @@ struct CallDesc {
                              // stream's payload laid out as if every chunk were raw
   uint8_t* codes_out;        // encode: where compressed chunk bytes go (== codes: in place)
   int direct[2];             // decode: reconstruct kernels read raw chunks of K / V from the stream
-  int place;                 // dense encode: finish the stream in one in-place pass (k_place)
+  int place;                 // encode: 1 = dense, finish the stream in one in-place pass (k_place);
+                             //   2 = paged, chunks placed from the workspace (k_place_paged)
   uint32_t* place_flags;     //   [total chunks] read announcements, then [ceil(total / 64)] group counts
   uint64_t* scan_state;      // dense calls: look-back words of the chunk-size scan, one per 1024 chunks
   int nnz_pipe;              // encode: 1 or 2 when the fused kernels count the non-zero RZE

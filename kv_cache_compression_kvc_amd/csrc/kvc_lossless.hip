@@ -94,7 +94,7 @@ __global__ void k_reset(CallDesc c) {
   // the fused encoders accumulate per-chunk non-zero word counts here
   if (c.nnz_pipe)
     for (int64_t i = i0; i < c.total_chunks; i += di) c.chunk_sizes[i] = 0;
-  if (c.place)
+  if (c.place_flags)
     for (int64_t i = i0; i < c.total_chunks + (c.total_chunks + 63) / 64; i += di) c.place_flags[i] = 0;
 }
 
@@ -1070,7 +1070,8 @@ __device__ __forceinline__ int find_req_by_piece(const CallDesc& c, int64_t piec
 
 __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
   const int64_t items = c.total_chunks + c.R + c.total_pieces;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+  // with the paged placement (place == 2) the chunks are placed there
+  for (int64_t it = blockIdx.x + (c.place == 2 ? c.total_chunks : 0); it < items; it += gridDim.x) {
     if (it < c.total_chunks) {
       const int64_t ch = it;
       const int r = find_req_by_chunk(c, ch);
@@ -1218,6 +1219,176 @@ __device__ bool wait_announced(const CallDesc& c, const uint32_t* ann, const uin
 // PIPE: the plan's pipeline when it is one of the two encoded here (1:
 // TUPL8_1 -> BIT_8 -> RZE_2, 2: TUPL8_1 -> RZE_2), else 0; one instantiation
 // each, so none carries the other's registers.
+// One chunk of the placement (dense: k at or past the first chunk with work,
+// in ticket order; paged: any order, written to the request's own stream).
+template <int PIPE, bool PAGED>
+__device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_t kf, uint32_t* ann, uint32_t* grp,
+                                            const XposeLane& X, int wave, int lane, uint32_t* ob, uint32_t* bm,
+                                            uint32_t* offs, uint32_t* sh32) {
+  constexpr int pipe = PIPE;
+  const int r = PAGED ? find_req_by_chunk(c, k) : 0;
+  const ReqDesc rq = req_at(c, r);
+  const uint64_t base = PAGED ? stream_base(c, r, true) : 0;
+  const ChunkLoc L = locate_chunk(c, rq, r, k);
+  const uint32_t e = c.chunk_sizes[k];
+  const int64_t stored = e & 0x7fffffffu;
+  const uint64_t fin = c.chunk_offs[k] - c.chunk_offs[rq.chunk_begin];
+  uint8_t* dst = c.stream + base + rq.payload_off + fin;
+  const uint8_t* slot = c.codes + L.src;
+  // 0: raw, in place; 1: raw, moves; 2: TUPL8_1 -> BIT_8 -> RZE_2 here;
+  // 3: from the staging area; 4: TUPL8_1 -> RZE_2 here
+  const int mode = (e >> 31) ? ((!PAGED && fin == (uint64_t)L.src) ? 0 : 1)
+                             : ((pipe == 0 || !fast_eligible(pipe, L.n)) ? 3 : (pipe == 1 ? 2 : 4));
+  const int n = (int)L.n;
+  const int ngi = n >> 12, nd = n >> 6, dpj = n >> 9;
+  // R: this lane's 64 bytes of the chunk.  Mode 2: R[16 s4 .. 16 s4 + 15] =
+  // bytes 64 lane .. 64 lane + 63 of 4 KiB block gi = wave + 4 s4, input
+  // word 8 lane + kk at R[16 s4 + 2 kk], transposed there in place.  Mode 4:
+  // R[4 s16 .. 4 s16 + 3] = 16-byte unit `lane` of 1 KiB block wave + 4 s16.
+  uint32_t R[64];
+  if (mode == 4) {
+    // every load first, so the whole chunk is in flight at once: buffer
+    // loads with one lane offset and wave-uniform block offsets (blocks past
+    // the chunk read zero)
+    const __amdgpu_buffer_rsrc_t rs = ll_rsrc(slot, (uint32_t)n);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint4 x = ll_load16(rs, 16u * (uint32_t)lane, 1024u * (uint32_t)(wave + 4 * u));
+      R[4 * u] = x.x; R[4 * u + 1] = x.y; R[4 * u + 2] = x.z; R[4 * u + 3] = x.w;
+    }
+  }
+  if (mode == 2) {
+    // block by block (measured faster here than issuing the whole chunk first)
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int gi = wave + 4 * s4;
+      if (gi < ngi) {
+        const uint4* src = (const uint4*)(slot + (int64_t)gi * 4096 + 64 * lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 x = src[q];
+          R[16 * s4 + 4 * q] = x.x; R[16 * s4 + 4 * q + 1] = x.y; R[16 * s4 + 4 * q + 2] = x.z; R[16 * s4 + 4 * q + 3] = x.w;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          uint32_t lo = R[16 * s4 + 2 * kk], hi = R[16 * s4 + 2 * kk + 1];
+          xpose64(lo, hi, X);
+          R[16 * s4 + 2 * kk] = lo;
+          R[16 * s4 + 2 * kk + 1] = hi;
+          const uint32_t dw = or8(nz_quarters(lo, hi) << (4 * (lane & 7)));
+          if ((lane & 7) == 0) bm[(lane >> 3) * dpj + 8 * gi + kk] = dw;
+        }
+      }
+    }
+  } else if (mode == 4) {
+    // RZE word (j, p) is byte j of input words 2 p and 2 p + 1; lane `lane`
+    // of block blk holds pair p = 64 blk + lane, and the 64 pairs of a block
+    // and byte j make two bitmap dwords (ballot)
+    const int nblk = n >> 10;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int blk = wave + 4 * u;
+      if (blk < nblk) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t a = (j < 4) ? R[4 * u] : R[4 * u + 1], b = (j < 4) ? R[4 * u + 2] : R[4 * u + 3];
+          const uint32_t jj = (uint32_t)(j & 3);
+          const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
+          const uint64_t m = __ballot(word != 0u);
+          if (lane == 0) {
+            bm[j * dpj + 2 * blk] = (uint32_t)m;
+            bm[j * dpj + 2 * blk + 1] = (uint32_t)(m >> 32);
+          }
+        }
+      }
+    }
+  } else if (mode == 1 && !PAGED) {
+    const int64_t nv = align16(stored) / 16;
+    for (int64_t q = threadIdx.x; q < nv; q += blockDim.x) ((uint4*)ob)[q] = ((const uint4*)slot)[q];
+  }
+  __syncthreads();
+  // every load of this chunk's codes has returned: announce (a paged stream is
+  // written to a buffer of its own: no ordering)
+  if (!PAGED && threadIdx.x == 0) {
+    __hip_atomic_store(ann + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(grp + (k >> 6), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  bool consistent = true;
+  if (mode == 2 || mode == 4) {
+    const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
+    consistent = n / 16 + 2 * (int64_t)nnz == stored;    // the size the scan used
+    if (!consistent && threadIdx.x == 0) set_status2(c.ctl, kStStall);
+  }
+  if (mode == 2 && consistent) {
+    for (int d = threadIdx.x; d < nd; d += blockDim.x) ob[d] = bm[d];
+    uint16_t* ow = (uint16_t*)(ob + nd);
+    const int j = lane >> 3, r4 = 4 * (lane & 7);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int gi = wave + 4 * s4;
+      if (gi < ngi) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const int d = j * dpj + 8 * gi + kk;
+          const uint32_t bits = bm[d], base = offs[d];
+          const uint32_t lo = R[16 * s4 + 2 * kk], hi = R[16 * s4 + 2 * kk + 1];
+          const uint32_t v[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t rr = (uint32_t)(r4 + q);
+            if ((bits >> rr) & 1u) ow[base + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u))] = (uint16_t)v[q];
+          }
+        }
+      }
+    }
+  } else if (mode == 4 && consistent) {
+    for (int d = threadIdx.x; d < nd; d += blockDim.x) ob[d] = bm[d];
+    uint16_t* ow = (uint16_t*)(ob + nd);
+    const int nblk = n >> 10;
+    const uint32_t rr = (uint32_t)(lane & 31);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int blk = wave + 4 * u;
+      if (blk < nblk) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t a = (j < 4) ? R[4 * u] : R[4 * u + 1], b = (j < 4) ? R[4 * u + 2] : R[4 * u + 3];
+          const uint32_t jj = (uint32_t)(j & 3);
+          const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
+          const int d = j * dpj + 2 * blk + (lane >> 5);
+          const uint32_t bits = bm[d];
+          if ((bits >> rr) & 1u) ow[offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u))] = (uint16_t)word;
+        }
+      }
+    }
+  }
+  if (mode == 0) {
+    const int64_t pad = align16(stored) - stored;
+    if (threadIdx.x < pad) dst[stored + threadIdx.x] = 0;
+  } else if (consistent) {
+    // chunks below kf are raw at their places: their codes are never covered
+    const int64_t j0 = PAGED ? k : min(max(first_covered(c, fin), kf), k);
+    if (!wait_announced(c, ann, grp, j0, k)) {
+      if (threadIdx.x == 0) set_status2(c.ctl, kStStall);
+    } else {
+      const uint4* src = (mode == 3) ? (const uint4*)(c.codes_out + L.src)
+                                     : (PAGED && mode == 1) ? (const uint4*)slot : (const uint4*)ob;
+      const int64_t nv = align16(stored) / 16;
+      for (int64_t q = threadIdx.x; q < nv; q += blockDim.x) {
+        uint4 x = src[q];
+        const int64_t lim = stored - 16 * q;
+        if (lim < 16) {
+          uint8_t* xb = (uint8_t*)&x;
+          for (int b = 0; b < 16; ++b) if (b >= lim) xb[b] = 0;
+        }
+        ((uint4*)dst)[q] = x;
+      }
+    }
+  }
+  if (threadIdx.x == 0) *(uint32_t*)(c.stream + base + rq.table_off + 4 * (k - rq.chunk_begin)) = e;
+  __syncthreads();                                     // LDS reused by the next chunk
+}
+
 template <int PIPE>
 __global__ __launch_bounds__(256) void k_place(CallDesc c) {
   __shared__ __attribute__((aligned(16))) uint32_t ob[16384];   // output assembly / raw chunk (64 KiB)
@@ -1233,7 +1404,6 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
   const int64_t kf = (int64_t)min<uint64_t>(c.ctl->pad[3], (uint64_t)N);
   const int64_t nb0 = (kf + 63) / 64, last = nb0 + (N - kf);
   const ReqDesc& rq = c.one;
-  constexpr int pipe = PIPE;
   const XposeLane X = xpose_lane();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint32_t* ticket = (uint32_t*)&c.ctl->pad[2];
@@ -1265,173 +1435,41 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
       __syncthreads();
       continue;
     }
-    const int64_t k = kf + (t - nb0);
-    const ChunkLoc L = locate_chunk(c, rq, 0, k);
-    const uint32_t e = c.chunk_sizes[k];
-    const int64_t stored = e & 0x7fffffffu;
-    const uint64_t fin = c.chunk_offs[k] - c.chunk_offs[0];
-    uint8_t* dst = c.stream + rq.payload_off + fin;
-    const uint8_t* slot = c.codes + L.src;
-    // 0: raw, in place; 1: raw, moves; 2: TUPL8_1 -> BIT_8 -> RZE_2 here;
-    // 3: from the staging area; 4: TUPL8_1 -> RZE_2 here
-    const int mode = (e >> 31) ? (fin == (uint64_t)L.src ? 0 : 1)
-                               : ((pipe == 0 || !fast_eligible(pipe, L.n)) ? 3 : (pipe == 1 ? 2 : 4));
-    const int n = (int)L.n;
-    const int ngi = n >> 12, nd = n >> 6, dpj = n >> 9;
-    // R: this lane's 64 bytes of the chunk.  Mode 2: R[16 s4 .. 16 s4 + 15] =
-    // bytes 64 lane .. 64 lane + 63 of 4 KiB block gi = wave + 4 s4, input
-    // word 8 lane + kk at R[16 s4 + 2 kk], transposed there in place.  Mode 4:
-    // R[4 s16 .. 4 s16 + 3] = 16-byte unit `lane` of 1 KiB block wave + 4 s16.
-    uint32_t R[64];
-    if (mode == 4) {
-      // every load first, so the whole chunk is in flight at once: buffer
-      // loads with one lane offset and wave-uniform block offsets (blocks past
-      // the chunk read zero)
-      const __amdgpu_buffer_rsrc_t rs = ll_rsrc(slot, (uint32_t)n);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const uint4 x = ll_load16(rs, 16u * (uint32_t)lane, 1024u * (uint32_t)(wave + 4 * u));
-        R[4 * u] = x.x; R[4 * u + 1] = x.y; R[4 * u + 2] = x.z; R[4 * u + 3] = x.w;
-      }
-    }
-    if (mode == 2) {
-      // block by block (measured faster here than issuing the whole chunk first)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int gi = wave + 4 * s4;
-        if (gi < ngi) {
-          const uint4* src = (const uint4*)(slot + (int64_t)gi * 4096 + 64 * lane);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 x = src[q];
-            R[16 * s4 + 4 * q] = x.x; R[16 * s4 + 4 * q + 1] = x.y; R[16 * s4 + 4 * q + 2] = x.z; R[16 * s4 + 4 * q + 3] = x.w;
-          }
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            uint32_t lo = R[16 * s4 + 2 * kk], hi = R[16 * s4 + 2 * kk + 1];
-            xpose64(lo, hi, X);
-            R[16 * s4 + 2 * kk] = lo;
-            R[16 * s4 + 2 * kk + 1] = hi;
-            const uint32_t dw = or8(nz_quarters(lo, hi) << (4 * (lane & 7)));
-            if ((lane & 7) == 0) bm[(lane >> 3) * dpj + 8 * gi + kk] = dw;
-          }
-        }
-      }
-    } else if (mode == 4) {
-      // RZE word (j, p) is byte j of input words 2 p and 2 p + 1; lane `lane`
-      // of block blk holds pair p = 64 blk + lane, and the 64 pairs of a block
-      // and byte j make two bitmap dwords (ballot)
-      const int nblk = n >> 10;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int blk = wave + 4 * u;
-        if (blk < nblk) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t a = (j < 4) ? R[4 * u] : R[4 * u + 1], b = (j < 4) ? R[4 * u + 2] : R[4 * u + 3];
-            const uint32_t jj = (uint32_t)(j & 3);
-            const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
-            const uint64_t m = __ballot(word != 0u);
-            if (lane == 0) {
-              bm[j * dpj + 2 * blk] = (uint32_t)m;
-              bm[j * dpj + 2 * blk + 1] = (uint32_t)(m >> 32);
-            }
-          }
-        }
-      }
-    } else if (mode == 1) {
-      const int64_t nv = align16(stored) / 16;
-      for (int64_t q = threadIdx.x; q < nv; q += blockDim.x) ((uint4*)ob)[q] = ((const uint4*)slot)[q];
-    }
-    __syncthreads();
-    // every load of this chunk's codes has returned: announce
-    if (threadIdx.x == 0) {
-      __hip_atomic_store(ann + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(grp + (k >> 6), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    bool consistent = true;
-    if (mode == 2 || mode == 4) {
-      const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
-      consistent = n / 16 + 2 * (int64_t)nnz == stored;    // the size the scan used
-      if (!consistent && threadIdx.x == 0) set_status2(c.ctl, kStStall);
-    }
-    if (mode == 2 && consistent) {
-      for (int d = threadIdx.x; d < nd; d += blockDim.x) ob[d] = bm[d];
-      uint16_t* ow = (uint16_t*)(ob + nd);
-      const int j = lane >> 3, r4 = 4 * (lane & 7);
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int gi = wave + 4 * s4;
-        if (gi < ngi) {
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const int d = j * dpj + 8 * gi + kk;
-            const uint32_t bits = bm[d], base = offs[d];
-            const uint32_t lo = R[16 * s4 + 2 * kk], hi = R[16 * s4 + 2 * kk + 1];
-            const uint32_t v[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t rr = (uint32_t)(r4 + q);
-              if ((bits >> rr) & 1u) ow[base + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u))] = (uint16_t)v[q];
-            }
-          }
-        }
-      }
-    } else if (mode == 4 && consistent) {
-      for (int d = threadIdx.x; d < nd; d += blockDim.x) ob[d] = bm[d];
-      uint16_t* ow = (uint16_t*)(ob + nd);
-      const int nblk = n >> 10;
-      const uint32_t rr = (uint32_t)(lane & 31);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int blk = wave + 4 * u;
-        if (blk < nblk) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t a = (j < 4) ? R[4 * u] : R[4 * u + 1], b = (j < 4) ? R[4 * u + 2] : R[4 * u + 3];
-            const uint32_t jj = (uint32_t)(j & 3);
-            const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
-            const int d = j * dpj + 2 * blk + (lane >> 5);
-            const uint32_t bits = bm[d];
-            if ((bits >> rr) & 1u) ow[offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u))] = (uint16_t)word;
-          }
-        }
-      }
-    }
-    if (mode == 0) {
-      const int64_t pad = align16(stored) - stored;
-      if (threadIdx.x < pad) dst[stored + threadIdx.x] = 0;
-    } else if (consistent) {
-      // chunks below kf are raw at their places: their codes are never covered
-      const int64_t j0 = min(max(first_covered(c, fin), kf), k);
-      if (!wait_announced(c, ann, grp, j0, k)) {
-        if (threadIdx.x == 0) set_status2(c.ctl, kStStall);
-      } else {
-        const uint4* src = (mode == 3) ? (const uint4*)(c.codes_out + L.src) : (const uint4*)ob;
-        const int64_t nv = align16(stored) / 16;
-        for (int64_t q = threadIdx.x; q < nv; q += blockDim.x) {
-          uint4 x = src[q];
-          const int64_t lim = stored - 16 * q;
-          if (lim < 16) {
-            uint8_t* xb = (uint8_t*)&x;
-            for (int b = 0; b < 16; ++b) if (b >= lim) xb[b] = 0;
-          }
-          ((uint4*)dst)[q] = x;
-        }
-      }
-    }
-    if (threadIdx.x == 0) *(uint32_t*)(c.stream + rq.table_off + 4 * k) = e;
-    __syncthreads();                                     // LDS reused by the next chunk
+    place_chunk<PIPE, false>(c, kf + (t - nb0), kf, ann, grp, X, wave, lane, ob, bm, offs, sh32);
   }
+}
+
+// Paged encodes: the codes sit in the workspace and every request has its own
+// stream, so chunks are placed in any order, with no announcements; the
+// compaction kernel writes the headers and parameter sections.
+template <int PIPE>
+__global__ __launch_bounds__(256) void k_place_paged(CallDesc c) {
+  __shared__ __attribute__((aligned(16))) uint32_t ob[16384];
+  __shared__ uint32_t bm[1024];
+  __shared__ uint32_t offs[1024];
+  __shared__ uint32_t sh32[256];
+  const XposeLane X = xpose_lane();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  for (int64_t k = blockIdx.x; k < c.total_chunks; k += gridDim.x)
+    place_chunk<PIPE, true>(c, k, 0, nullptr, nullptr, X, wave, lane, ob, bm, offs, sh32);
 }
 
 hipError_t launch_place(const CallDesc& c, hipStream_t s) {
   const int grid = (int)std::min<int64_t>(c.total_chunks + 1, 512);
   const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
-  if (p1) k_place<1><<<grid, 256, 0, s>>>(c);
-  else if (p2) k_place<2><<<grid, 256, 0, s>>>(c);
-  else k_place<0><<<grid, 256, 0, s>>>(c);
+  if (c.place == 2) {
+    if (c.total_chunks == 0) return hipSuccess;
+    if (p1) k_place_paged<1><<<grid, 256, 0, s>>>(c);
+    else if (p2) k_place_paged<2><<<grid, 256, 0, s>>>(c);
+    else k_place_paged<0><<<grid, 256, 0, s>>>(c);
+  } else if (p1) {
+    k_place<1><<<grid, 256, 0, s>>>(c);
+  } else if (p2) {
+    k_place<2><<<grid, 256, 0, s>>>(c);
+  } else {
+    k_place<0><<<grid, 256, 0, s>>>(c);
+  }
   return hipGetLastError();
 }
 
