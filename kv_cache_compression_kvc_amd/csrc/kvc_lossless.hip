@@ -23,9 +23,10 @@
 // and writes the result in place into the chunk's slot.  A single-block scan
 // turns stored sizes into 16-byte aligned offsets.  A dense encode then ends
 // with one in-place pass (k_place) that encodes the chunks of the two
-// standard pipelines and puts every chunk at its final offset; paged encodes use the
-// compaction kernel, which copies chunks and parameter pieces to their final
-// places.  Both write the headers and the chunk tables.
+// standard pipelines and puts every chunk at its final offset; a paged encode
+// places its chunks the same way from the workspace (k_place_paged) while the
+// compaction kernel copies the parameter pieces.  Headers and chunk tables
+// are written along the way.
 #include <algorithm>
 
 #include "kvc_internal.h"
