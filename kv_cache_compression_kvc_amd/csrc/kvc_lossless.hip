@@ -13,18 +13,18 @@
 //            words, then the tail bytes.
 // A chunk whose result is not smaller than its input is stored raw.
 //
-// Encode runs in two kernels.  The first computes every chunk's exact
-// compressed size without materializing the transform: for the two standard
-// pipelines a 2-byte RZE word of the output is zero exactly when a fixed set
-// of input bits is zero, so the count of non-zero output words is a popcount
-// of OR-reductions of the input words.  Chunks that stay raw are done; the
-// rest (and chunks of other pipelines or partial chunks) go on a worklist
-// for the second kernel, which runs the stages in LDS (two 64 KiB buffers)
-// and writes the result in place into the chunk's slot.  A single-block scan
-// turns stored sizes into 16-byte aligned offsets.  A dense encode then ends
-// with one in-place pass (k_place) that encodes the chunks of the two
-// standard pipelines and puts every chunk at its final offset; a paged encode
-// places its chunks the same way from the workspace (k_place_paged) while the
+// Encode: every chunk's exact compressed size comes first, without
+// materializing the transform: for the two standard pipelines a 2-byte RZE
+// word of the output is zero exactly when a fixed set of input bits is zero,
+// so the count of non-zero output words is a popcount of OR-reductions of the
+// input words (the fused encoders usually count it while the codes are in
+// registers).  Chunks of other pipelines, and partial chunks, go on a
+// worklist for the stage engine, which runs the stages in LDS (two 64 KiB
+// buffers) and writes the result into the chunk's staging slot.  A scan turns
+// stored sizes into 16-byte aligned offsets.  A dense encode then ends with
+// one in-place pass (k_place) that encodes the chunks of the two standard
+// pipelines and puts every chunk at its final offset; a paged encode places
+// its chunks the same way from the workspace (k_place_paged) while the
 // compaction kernel copies the parameter pieces.  Headers and chunk tables
 // are written along the way.
 #include <algorithm>
@@ -81,7 +81,7 @@ __global__ void k_reset(CallDesc c) {
   Control* ctl = c.ctl;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     ctl->status = 0;
-    ctl->pad0 = 0;     // worklist entries for the word-parallel kernels (from the front)
+    ctl->pad0 = 0;
     ctl->total = 0;
     ctl->pad[0] = 0;   // header-field diagnosis bits
     ctl->pad[1] = 0;   // worklist entries for the general stage engine (from the back)
@@ -302,14 +302,10 @@ __device__ __forceinline__ int fast_pipeline(const CallDesc& c) {
 __device__ __forceinline__ bool fast_eligible(int pipe, int64_t n) {
   return (pipe == 1 && n % 4096 == 0) || (pipe == 2 && n % 1024 == 0);
 }
-__device__ __forceinline__ void push_work(const CallDesc& c, uint32_t* worklist, int64_t ch, bool fast) {
-  if (fast) {
-    const uint32_t slot = __hip_atomic_fetch_add(&c.ctl->pad0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    worklist[slot] = (uint32_t)ch;
-  } else {
-    const uint32_t k = __hip_atomic_fetch_add(generic_count(c), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    worklist[c.total_chunks - 1 - k] = (uint32_t)ch;
-  }
+// a chunk for the stage engine (entries from the back of the list)
+__device__ __forceinline__ void push_work(const CallDesc& c, uint32_t* worklist, int64_t ch) {
+  const uint32_t k = __hip_atomic_fetch_add(generic_count(c), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  worklist[c.total_chunks - 1 - k] = (uint32_t)ch;
 }
 
 // ------------------------------------------------------------------ encode: sizes
@@ -369,20 +365,16 @@ __global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, uint32_t* worklist
       } else {
         nnz = (pipe == 1) ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
       }
+      // a compressible chunk is encoded by the placement, which needs only
+      // its size
       const int64_t size = n / 16 + 2 * (int64_t)nnz;
-      if (size >= n) {
-        if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
-        work = false;
-      } else if (c.place) {
-        // the single-pass placement encodes it; it needs only the size
-        if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
-        work = false;
-      }
+      if (threadIdx.x == 0) c.chunk_sizes[ch] = (size >= n) ? ((uint32_t)n | kRawFlag) : (uint32_t)size;
+      work = false;
     } else if (c.stages[0] == 0) {
       if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
       work = false;
     }
-    if (work && threadIdx.x == 0) push_work(c, worklist, ch, fast);
+    if (work && threadIdx.x == 0) push_work(c, worklist, ch);
     __syncthreads();
   }
 }
@@ -432,8 +424,9 @@ __global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uin
 //      The RZE_2 words are the four 16-bit quarters of those rows.
 //  P2: the RZE_2 word (j, p), index j m/2 + p, is byte j of w[2p] followed
 //      by byte j of w[2p+1].
-// Every 32 consecutive RZE words share one bitmap dword.  Both kernels build
-// the bitmap, scan its popcounts for the word offsets and write the words.
+// Every 32 consecutive RZE words share one bitmap dword.  The placement
+// builds the bitmap, scans its popcounts for the word offsets and writes the
+// words; the decode kernels below read them back.
 
 __device__ __forceinline__ uint32_t rotr32(uint32_t x, uint32_t s) { return __builtin_amdgcn_alignbit(x, x, s); }
 __device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
@@ -526,134 +519,7 @@ __device__ __forceinline__ uint32_t scan_bitmap(const uint32_t* bm, uint32_t* of
   return total;
 }
 
-// 16-bit store to global memory
-__device__ __forceinline__ void st16(uint8_t* p, uint32_t v) { *(uint16_t*)p = (uint16_t)v; }
 
-__global__ __launch_bounds__(256) void k_ll_encode_p1(CallDesc c, const uint32_t* worklist) {
-  __shared__ __attribute__((aligned(16))) uint64_t pre[8192];   // BIT_8 rows, [gi][kk][c] order
-  __shared__ uint32_t bm[1024];
-  __shared__ uint32_t offs[1024];
-  __shared__ uint32_t sh32[256];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const XposeLane X = xpose_lane();
-  const uint32_t count = c.ctl->pad0;
-  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
-    const int64_t ch = worklist[item];
-    const int r = find_req_by_chunk(c, ch);
-    const ReqDesc rq = req_at(c, r);
-    const ChunkLoc L = locate_chunk(c, rq, r, ch);
-    const int n = (int)L.n;                 // multiple of 4096
-    const int ngi = n / 4096, nd = n / 64, dpj = n / 512;     // bitmap dwords per plane
-    const uint8_t* slot = c.codes + L.src;
-    uint8_t* oslot = c.codes_out + L.src;
-    for (int gi = wave; gi < ngi; gi += 4) {
-      const uint4* src = (const uint4*)(slot + (int64_t)gi * 4096 + 64 * lane);
-      uint32_t w[16];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint4 x = src[k];
-        w[4 * k] = x.x; w[4 * k + 1] = x.y; w[4 * k + 2] = x.z; w[4 * k + 3] = x.w;
-      }
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        uint32_t lo = w[2 * kk], hi = w[2 * kk + 1];
-        xpose64(lo, hi, X);
-        pre[(gi * 8 + kk) * 64 + lane] = ((uint64_t)hi << 32) | lo;
-        const uint32_t dw = or8(nz_quarters(lo, hi) << (4 * (lane & 7)));
-        if ((lane & 7) == 0) bm[(lane >> 3) * dpj + 8 * gi + kk] = dw;
-      }
-    }
-    __syncthreads();
-    const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
-    const int size = n / 16 + 2 * (int)nnz;
-    if (size >= n) {
-      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
-    } else {
-      for (int d = threadIdx.x; d < nd; d += blockDim.x) ((uint32_t*)oslot)[d] = bm[d];
-      uint8_t* words = oslot + n / 16;
-      const uint16_t* pre16 = (const uint16_t*)pre;
-      const int rr = lane & 31;
-      for (int d0 = 2 * wave; d0 < nd; d0 += 8) {
-        const int d = d0 + (lane >> 5);
-        if (d < nd) {
-          const int j = d / dpj, rem = d - j * dpj;
-          const int gi = rem >> 3, kk = rem & 7;
-          const uint32_t bits = bm[d];
-          const uint32_t v = pre16[((gi * 8 + kk) * 64 + 8 * j) * 4 + rr];
-          if ((bits >> rr) & 1u) {
-            const uint32_t pos = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u));
-            st16(words + 2 * pos, v);
-          }
-        }
-      }
-      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
-    }
-    __syncthreads();
-  }
-}
-
-__global__ __launch_bounds__(256) void k_ll_encode_p2(CallDesc c, const uint32_t* worklist) {
-  __shared__ __attribute__((aligned(16))) uint4 buf[4096];     // the chunk, one input word pair per entry
-  __shared__ uint32_t bm[1024];
-  __shared__ uint32_t offs[1024];
-  __shared__ uint32_t sh32[256];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const uint32_t count = c.ctl->pad0;
-  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
-    const int64_t ch = worklist[item];
-    const int r = find_req_by_chunk(c, ch);
-    const ReqDesc rq = req_at(c, r);
-    const ChunkLoc L = locate_chunk(c, rq, r, ch);
-    const int n = (int)L.n;                 // multiple of 1024
-    const int np = n / 16, nblk = np / 64, nd = n / 64, dpj = n / 512;
-    const uint8_t* slot = c.codes + L.src;
-    uint8_t* oslot = c.codes_out + L.src;
-    for (int blk = wave; blk < nblk; blk += 4) {
-      const int p = 64 * blk + lane;
-      const uint4 x = ((const uint4*)slot)[p];
-      buf[p] = x;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t a = (j < 4) ? x.x : x.y, b = (j < 4) ? x.z : x.w;
-        const uint32_t jj = (uint32_t)(j & 3);
-        const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
-        const uint64_t m = __ballot(word != 0u);
-        if (lane == 0) {
-          bm[j * dpj + 2 * blk] = (uint32_t)m;
-          bm[j * dpj + 2 * blk + 1] = (uint32_t)(m >> 32);
-        }
-      }
-    }
-    __syncthreads();
-    const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
-    const int size = n / 16 + 2 * (int)nnz;
-    if (size >= n) {
-      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
-    } else {
-      for (int d = threadIdx.x; d < nd; d += blockDim.x) ((uint32_t*)oslot)[d] = bm[d];
-      uint8_t* words = oslot + n / 16;
-      const int rr = lane & 31;
-      for (int blk = wave; blk < nblk; blk += 4) {
-        const int p = 64 * blk + lane;
-        const uint4 x = buf[p];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint32_t a = (j < 4) ? x.x : x.y, b = (j < 4) ? x.z : x.w;
-          const uint32_t jj = (uint32_t)(j & 3);
-          const uint32_t word = __builtin_amdgcn_perm(b, a, 0x0C0C0000u | ((4u + jj) << 8) | jj);
-          const int d = j * dpj + 2 * blk + (lane >> 5);
-          const uint32_t bits = bm[d];
-          if ((bits >> rr) & 1u) {
-            const uint32_t pos = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u));
-            st16(words + 2 * pos, word);
-          }
-        }
-      }
-      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)size;
-    }
-    __syncthreads();
-  }
-}
 
 // Copy nv <= 4096 16-byte lines from global memory to LDS with 256 threads:
 // every load of a thread is issued before the first LDS store, so a block has
@@ -848,12 +714,6 @@ hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
   k_ll_sizes<<<grid, 256, 0, s>>>(c, worklist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
-  const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
-  const int fgrid = (int)std::min<int64_t>(c.total_chunks, 512);
-  if (p1 && !c.place) k_ll_encode_p1<<<fgrid, 256, 0, s>>>(c, worklist);
-  else if (p2 && !c.place) k_ll_encode_p2<<<fgrid, 256, 0, s>>>(c, worklist);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   k_ll_encode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
   return hipGetLastError();
 }
@@ -1569,7 +1429,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
       for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) dst[k] = src[k];
       for (int64_t p = nv * 16 + threadIdx.x; p < L.n; p += blockDim.x) c.codes[L.src + p] = c.stream[pos + p];
     } else if (!fast_eligible(fast_pipeline(c), L.n) && threadIdx.x == 0) {
-      push_work(c, worklist, ch, false);            // the stage engine; the word-parallel kernels find theirs
+      push_work(c, worklist, ch);                   // the stage engine; the word-parallel kernels find theirs
     }
   }
 }
