@@ -215,7 +215,7 @@ typedef enum {
   KVC_KERNEL_ENCODE_V = 1,     /* fused transform + quantize, V */
   KVC_KERNEL_LOSSLESS_ENC = 2,
   KVC_KERNEL_SCAN = 3,
-  KVC_KERNEL_COMPACT = 4,      /* dense encode: single-pass placement; paged: compaction */
+  KVC_KERNEL_COMPACT = 4,      /* single-pass placement of the chunks (and, paged, the headers and parameters) */
   KVC_KERNEL_LOSSLESS_DEC = 5,
   KVC_KERNEL_DECODE_K = 6,     /* fused reconstruct, K */
   KVC_KERNEL_DECODE_V = 7,     /* fused reconstruct, V */
