@@ -140,6 +140,17 @@ def test_single_pass_placement(zero_frac, L, T):
     assert s["chunks_compressed"] >= 8, s
 
 
+@pytest.mark.parametrize("stages", [("TUPL8_1", "BIT_8", "RZE_2"), ("TUPL8_1", "RZE_2")])
+@pytest.mark.parametrize("cb", [4096, 12288, 45056])
+def test_chunk_sizes_not_powers_of_two(stages, cb):
+    # chunk sizes the placement, the scan and the decoders locate by division
+    # (12288 and 45056 bytes) and the smallest one (4096), with ragged tails
+    wl = C3.with_(stages=stages, chunk_bytes=cb, name="chunk_sizes")
+    s = run_case(wl, 2, 448, zero_rich=True, zero_frac=0.5, seed=17)
+    assert s["identical"]
+    assert s["chunks_compressed"] >= 4, s
+
+
 def test_range_error_is_reported():
     wl = C1
     k = torch.full((1, 64, 8, 128), 60000.0, dtype=torch.float16)
