@@ -659,6 +659,11 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
   c.codes = ws + w.codes;
   c.codes_out = c.codes;
   for (int k = 0; k < 2; ++k) c.direct[k] = tiles_within_chunks(p->pol[k], tokens, p->cfg.chunk_bytes) ? 1 : 0;
+  // 2-bit per-token codes: the reconstruct kernel decodes compressed chunks of
+  // TUPL8_1 -> BIT_8 -> RZE_2 itself (four tiles share one 4 KiB transpose block)
+  for (int k = 0; k < 2; ++k)
+    c.mirror[k] = (c.direct[k] && !p->mixed && lossless_pipe(p->cfg.lossless) == 1 && p->pol[k].axis == 0 &&
+                   p->pol[k].bits == 2 && p->cfg.chunk_bytes % 4096 == 0) ? 1 : 0;
   c.stream = (uint8_t*)const_cast<void*>(d_in);
   c.stream_bytes = in_bytes;
   c.chunk_sizes = (uint32_t*)(ws + w.sizes);

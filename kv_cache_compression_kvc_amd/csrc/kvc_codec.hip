@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "kvc_internal.h"
+#include "kvc_xpose.h"
 
 namespace kvc {
 
@@ -102,6 +103,14 @@ __device__ __forceinline__ void bstore8(uint2 v, __amdgpu_buffer_rsrc_t r, uint3
 }
 __device__ __forceinline__ void bstore4(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32((int)v, r, (int)voff, (int)soff, kNarrowStorePol);
+}
+
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const int2v x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kLoadPol);
+  return make_uint2((uint32_t)x.x, (uint32_t)x.y);
+}
+__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
 }
 
 __device__ __forceinline__ uint32_t h16_from(float f) {
@@ -900,14 +909,21 @@ struct DecTok {
   uint16_t* dst;          // first output vector
   uint32_t vstride;       // bytes between consecutive output vectors
   int nvo;                // output vectors to store
+  // a TUPL8_1 -> BIT_8 -> RZE_2 chunk decoded by the block (2-bit codes): csrc
+  // is the stored chunk (cbytes readable), p1_n its raw size, the tile quarter
+  // p1_q of 4 KiB block p1_gi, p1_pref the non-zero words before each bitmap
+  // dword of the chunk
+  int p1, p1_n, p1_gi, p1_q;
+  const uint32_t* p1_pref;
 };
 
-template <int BITS, int G, bool PAGED>
+template <int BITS, int G, bool PAGED, bool MIRROR = false>
 __device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, int64_t tile, uint16_t* out) {
   constexpr int CB = kHeadDim * BITS / 8;
   constexpr int NGV = kHeadDim / G;
   DecTok d;
   d.vstride = 256u;
+  d.p1 = 0;
   int64_t vg0;
   int nv;
   const uint8_t* params_base;
@@ -944,6 +960,19 @@ __device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, i
         const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] + (uint64_t)(coff - ci * c.chunk_bytes);
         d.csrc = c.stream + pos;
         d.cbytes = (pos >= c.stream_bytes) ? 0u : (uint32_t)std::min<uint64_t>(d.cbytes, c.stream_bytes - pos);
+      } else if (MIRROR && BITS == 2 && c.mirror[which]) {
+        const int64_t n = std::min<int64_t>((int64_t)c.chunk_bytes, pick(which, c.one.codes_bytes) - ci * (int64_t)c.chunk_bytes);
+        if ((n & 4095) == 0) {
+          const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci];
+          const int64_t toff = coff - ci * (int64_t)c.chunk_bytes;
+          d.p1 = 1;
+          d.p1_n = (int)n;
+          d.p1_gi = (int)(toff >> 12);
+          d.p1_q = (int)((toff >> 10) & 3);
+          d.p1_pref = (const uint32_t*)(c.codes + pick(which, c.one.codes_off) + ci * (int64_t)c.chunk_bytes);
+          d.csrc = c.stream + pos;
+          d.cbytes = (pos >= c.stream_bytes) ? 0u : (uint32_t)std::min<uint64_t>(e & 0x7fffffffu, c.stream_bytes - pos);
+        }
       }
     }
     params_base = c.stream + pick(which, c.one.params_off);
@@ -987,18 +1016,38 @@ struct DecRegs {
 };
 
 template <int BITS, int G>
+__device__ __forceinline__ void dec_token_params(const DecTok& t, DecRegs<BITS, G>& R);
+
+// codes and parameters of a tile; for a tile the block decodes from a
+// TUPL8_1 -> BIT_8 -> RZE_2 chunk, in place of the codes the two bitmap dwords
+// this lane expands and the non-zero words before each
+template <int BITS, int G, bool MIRROR = false>
 __device__ __forceinline__ void dec_token_load(const DecTok& t, DecRegs<BITS, G>& R) {
   constexpr int CB = kHeadDim * BITS / 8;
+  const int lane = __lane_id();
+  const int v = lane & 31, hf = lane >> 5;
+  if (MIRROR && t.p1) {
+    const uint32_t d0 = (uint32_t)((lane >> 3) * (t.p1_n >> 9) + 8 * t.p1_gi + 2 * t.p1_q);
+    const uint2 b = bload8(make_rsrc(t.csrc, t.cbytes), 4u * d0);
+    const uint2 p = bload8(make_rsrc(t.p1_pref, (uint32_t)t.p1_n / 16u), 4u * d0);
+    R.w[0] = b.x; R.w[1] = b.y; R.w[2] = p.x; R.w[3] = p.y;
+  } else {
+    const __amdgpu_buffer_rsrc_t crs = make_rsrc(t.csrc, t.cbytes);
+    const uint32_t coff = (uint32_t)v * CB + 64 * hf * BITS / 8;
+#pragma unroll
+    for (int i = 0; i < 2 * BITS; i += 4) {
+      const uint4 x = bload16(crs, coff + 4 * i, 0);
+      R.w[i] = x.x; R.w[i + 1] = x.y; R.w[i + 2] = x.z; R.w[i + 3] = x.w;
+    }
+  }
+  dec_token_params(t, R);
+}
+
+template <int BITS, int G>
+__device__ __forceinline__ void dec_token_params(const DecTok& t, DecRegs<BITS, G>& R) {
   constexpr int NGV = kHeadDim / G;
   const int lane = __lane_id();
   const int v = lane & 31, hf = lane >> 5;
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(t.csrc, t.cbytes);
-  const uint32_t coff = (uint32_t)v * CB + 64 * hf * BITS / 8;
-#pragma unroll
-  for (int i = 0; i < 2 * BITS; i += 4) {
-    const uint4 x = bload16(crs, coff + 4 * i, 0);
-    R.w[i] = x.x; R.w[i + 1] = x.y; R.w[i + 2] = x.z; R.w[i + 3] = x.w;
-  }
   const __amdgpu_buffer_rsrc_t prs = make_rsrc(t.psrc, t.pbytes);
 #pragma unroll
   for (int j = 0; j < DecRegs<BITS, G>::NLG; ++j)
@@ -1031,6 +1080,108 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
     if (tile + stride < ntiles) {
       cur = dec_token_tile<BITS, G, PAGED>(c, which, tile + stride, out);
       dec_token_load(cur, R);
+    }
+    float sg[NLG], mu[NLG];
+#pragma unroll
+    for (int j = 0; j < NLG; ++j) {
+      sg[j] = f_from_h16(q.pw[j] & 0xffffu) * cc;
+      mu[j] = f_from_h16(q.pw[j] >> 16) * cc;
+    }
+    float f[64];
+#pragma unroll
+    for (int r2 = 0; r2 < 64; ++r2) f[r2] = __builtin_fmaf(unpack_code<BITS>(q.w, r2), sg[r2 / LG], mu[r2 / LG]);
+
+    fwht64_inreg(f);
+    fwht_cross(f);
+    stage_out<BF16>(f, wl, sm, make_rsrc(t.dst, t.nvo ? (uint32_t)(t.nvo - 1) * t.vstride + 256u : 0u), t.vstride);
+  }
+}
+
+// -------------------------------------------------------------------
+// Per-token decode that also decodes TUPL8_1 -> BIT_8 -> RZE_2 chunks of 2-bit
+// codes (the mirror of the single-pass placement).  A stored chunk of n bytes
+// is the RZE bitmap (n / 16 bytes; bit r of dword d = j dpj + 8 gi + kk,
+// dpj = n / 512, marks 16-bit quarter r % 4 of row 8 j + r / 4 of the (4 KiB
+// block gi, kk) transpose) followed by the non-zero words in order;
+// k_ll_decode_raw leaves the count of non-zero words before each bitmap dword
+// in the chunk's codes slot.  A block's four tiles are one 4 KiB block: wave w
+// gathers rows of transposes kk = 2 w, 2 w + 1 (lane c row c), transposes
+// them back (lane i then holds input word 8 i + kk) and puts them in LDS; each
+// wave then reads its tile's codes from there.  Reads are buffer loads bounded
+// by the stored size: a set bit over a zero word marks a corrupt stream.
+// -------------------------------------------------------------------
+__device__ __forceinline__ uint32_t p1_block_to_lds(const DecTok& t, const uint32_t* seg, uint32_t* blk) {
+  const int lane = __lane_id();
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.csrc, t.cbytes);
+  const uint32_t words = (uint32_t)t.p1_n / 16u;
+  const uint32_t sh = 4u * (uint32_t)(lane & 7);
+  uint32_t bad = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t kb = seg[h];                 // bitmap dword of transpose kk = 2 p1_q + h
+    const uint32_t nib = (kb >> sh) & 15u;
+    const uint32_t r0 = seg[2 + h] + (uint32_t)__builtin_popcount(kb & ((1u << sh) - 1u));
+    uint32_t q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t on = (nib >> u) & 1u;
+      const uint32_t rk = r0 + (uint32_t)__builtin_popcount(nib & ((1u << u) - 1u));
+      q[u] = bload2(rs, on ? words + 2u * rk : 0x7ffffff0u);
+      bad |= on & (uint32_t)(q[u] == 0u);
+    }
+    uint32_t lo = q[0] | (q[1] << 16), hi = q[2] | (q[3] << 16);
+    xpose64_lean(lo, hi);
+    *(uint2*)(blk + 2 * (8 * lane + 2 * t.p1_q + h)) = make_uint2(lo, hi);
+  }
+  return bad;
+}
+
+template <int G, bool BF16>
+__global__ __launch_bounds__(256, 4) void k_decode_token_m(CallDesc c, int which) {
+  constexpr int BITS = 2;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[4 * kWaveLds];
+  __shared__ __attribute__((aligned(16))) uint32_t blk[1024];      // one decoded 4 KiB block
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  uint32_t* wl = lds + wave * kWaveLds;
+  const TensorPol pol = which ? c.pol[1] : c.pol[0];
+  const float cc = pol.c;
+  uint32_t sm[4];
+  slot_sign_masks(c.signs, lane & 15, sm);
+  uint16_t* out = (uint16_t*)(which ? c.out_kv[1] : c.out_kv[0]);
+  const int64_t ntiles = which ? c.tiles[1] : c.tiles[0];
+  constexpr int LG = DecRegs<BITS, G>::LG;
+  constexpr int NLG = DecRegs<BITS, G>::NLG;
+  const int v = lane & 31, hf = lane >> 5;
+
+  // every wave runs the block's iterations (block barriers around the shared
+  // decode); a wave past the last tile stores nothing
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  int64_t b0 = (int64_t)blockIdx.x * 4;
+  if (b0 >= ntiles) return;
+  auto tile_at = [&](int64_t base) {
+    const int64_t tl = base + wave;
+    DecTok d = dec_token_tile<BITS, G, false, true>(c, which, tl < ntiles ? tl : base, out);
+    if (tl >= ntiles) d.nvo = 0;
+    d.p1_q = wave;                               // the wave's quarter (also past the end)
+    return d;
+  };
+  DecTok cur = tile_at(b0);
+  DecRegs<BITS, G> R;
+  dec_token_load<BITS, G, true>(cur, R);
+  for (; b0 < ntiles; b0 += stride) {
+    const DecTok t = cur;
+    DecRegs<BITS, G> q = R;
+    if (b0 + stride < ntiles) {
+      cur = tile_at(b0 + stride);
+      dec_token_load<BITS, G, true>(cur, R);
+    }
+    if (t.p1) {                                  // the same for the block's four tiles
+      __syncthreads();                           // the previous block's readers are done
+      const uint32_t bad = p1_block_to_lds(t, q.w, blk);
+      if (bad) set_status(c.ctl, kStCorrupt);
+      __syncthreads();
+      const uint4 x = *(const uint4*)(blk + 256 * t.p1_q + 8 * v + 4 * hf);
+      q.w[0] = x.x; q.w[1] = x.y; q.w[2] = x.z; q.w[3] = x.w;
     }
     float sg[NLG], mu[NLG];
 #pragma unroll
@@ -1612,7 +1763,18 @@ hipError_t launch_decode_fused(const CallDesc& c, int which, hipStream_t s) {
   if (pol.axis == 0) {
     const dim3 block(256);
     const int grid = grid_for((tiles + 3) / 4, 256 * 16);
-    if (c.dtype == 1) { KVC_BITS_CASES(KVC_TOKEN_CASES, k_decode_token, true) }
+    if (c.mirror[which] && pol.bits == 2 && c.page_tokens == 0) {
+#define KVC_TOKEN_M_CASES(BF)                                                       \
+  switch (pol.group) {                                                              \
+    case 16: k_decode_token_m<16, BF><<<grid, block, 0, s>>>(c, which); break;      \
+    case 32: k_decode_token_m<32, BF><<<grid, block, 0, s>>>(c, which); break;      \
+    case 64: k_decode_token_m<64, BF><<<grid, block, 0, s>>>(c, which); break;      \
+    default: k_decode_token_m<128, BF><<<grid, block, 0, s>>>(c, which); break;     \
+  }
+      if (c.dtype == 1) { KVC_TOKEN_M_CASES(true) }
+      else { KVC_TOKEN_M_CASES(false) }
+#undef KVC_TOKEN_M_CASES
+    } else if (c.dtype == 1) { KVC_BITS_CASES(KVC_TOKEN_CASES, k_decode_token, true) }
     else { KVC_BITS_CASES(KVC_TOKEN_CASES, k_decode_token, false) }
   } else {
     const dim3 block(256);

@@ -91,6 +91,9 @@ struct CallDesc {
                              // stream's payload laid out as if every chunk were raw
   uint8_t* codes_out;        // encode: where compressed chunk bytes go (== codes: in place)
   int direct[2];             // decode: reconstruct kernels read raw chunks of K / V from the stream
+  int mirror[2];             // decode: ... and decode TUPL8_1 -> BIT_8 -> RZE_2 chunks of 2-bit
+                             //   per-token codes themselves, from per-segment word counts that
+                             //   k_ll_decode_raw leaves in the chunk's slot of the codes area
   int place;                 // encode: 1 = dense, finish the stream in one in-place pass (k_place);
                              //   2 = paged, chunks placed from the workspace (k_place_paged)
   uint32_t* place_flags;     //   [total chunks] read announcements, then [ceil(total / 64)] group counts

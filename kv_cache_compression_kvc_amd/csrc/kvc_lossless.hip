@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "kvc_internal.h"
+#include "kvc_xpose.h"
 
 namespace kvc {
 
@@ -428,59 +429,6 @@ __global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uin
 // builds the bitmap, scans its popcounts for the word offsets and writes the
 // words; the decode kernels below read them back.
 
-__device__ __forceinline__ uint32_t rotr32(uint32_t x, uint32_t s) { return __builtin_amdgcn_alignbit(x, x, s); }
-__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
-
-// Lane constants of the 64x64 bit transpose: for the rounds exchanging with
-// lane ^ 16, ^ 8, ^ 4, ^ 2, ^ 1, the bits this lane keeps and the rotation
-// that aligns the partner's bits.
-struct XposeLane {
-  uint32_t mk[5];
-  uint32_t sh[5];
-};
-__device__ __forceinline__ XposeLane xpose_lane() {
-  XposeLane x;
-  const int lane = __lane_id();
-  const uint32_t m[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
-#pragma unroll
-  for (int r = 0; r < 5; ++r) {
-    const int j = 16 >> r;
-    const bool lower = (lane & j) == 0;
-    x.mk[r] = lower ? m[r] : ~m[r];
-    x.sh[r] = lower ? (uint32_t)(32 - j) : (uint32_t)j;
-  }
-  return x;
-}
-// partner values: lane ^ 16 and lane ^ 4 through the swizzle unit, lane ^ 8
-// (rotate a 16-lane row by 8), lane ^ 2 and lane ^ 1 (quad permutes) by DPP
-__device__ __forceinline__ uint32_t xchg16(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); }
-__device__ __forceinline__ uint32_t xchg8(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false); }
-__device__ __forceinline__ uint32_t xchg4(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); }
-__device__ __forceinline__ uint32_t xchg2(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ uint32_t xchg1(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false); }
-
-// Lane i holds row i of a 64x64 bit matrix (lo: bits 0..31, hi: 32..63);
-// afterwards lane c holds column c.  Each round swaps the off-diagonal
-// blocks of one bit of the row and column index.
-__device__ __forceinline__ void xpose64(uint32_t& lo, uint32_t& hi, const XposeLane& X) {
-  {
-    auto p = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
-    lo = p[0];
-    hi = p[1];
-  }
-  uint32_t a, b;
-  a = xchg16(lo); b = xchg16(hi);
-  lo = bfi32(X.mk[0], lo, rotr32(a, X.sh[0])); hi = bfi32(X.mk[0], hi, rotr32(b, X.sh[0]));
-  a = xchg8(lo); b = xchg8(hi);
-  lo = bfi32(X.mk[1], lo, rotr32(a, X.sh[1])); hi = bfi32(X.mk[1], hi, rotr32(b, X.sh[1]));
-  a = xchg4(lo); b = xchg4(hi);
-  lo = bfi32(X.mk[2], lo, rotr32(a, X.sh[2])); hi = bfi32(X.mk[2], hi, rotr32(b, X.sh[2]));
-  a = xchg2(lo); b = xchg2(hi);
-  lo = bfi32(X.mk[3], lo, rotr32(a, X.sh[3])); hi = bfi32(X.mk[3], hi, rotr32(b, X.sh[3]));
-  a = xchg1(lo); b = xchg1(hi);
-  lo = bfi32(X.mk[4], lo, rotr32(a, X.sh[4])); hi = bfi32(X.mk[4], hi, rotr32(b, X.sh[4]));
-}
-
 // bits 0..3: which 16-bit quarters of (lo, hi) are non-zero
 __device__ __forceinline__ uint32_t nz_quarters(uint32_t lo, uint32_t hi) {
   const uint32_t a = ((lo & 0xFFFFu) != 0u) | ((uint32_t)((lo >> 16) != 0u) << 1);
@@ -566,7 +514,7 @@ __device__ __forceinline__ bool wp_decode_chunk(const CallDesc& c, int64_t ch, i
   L = locate_chunk(c, rq, r, ch);
   const uint32_t e = c.chunk_sizes[ch];
   stored = (int)(e & 0x7fffffffu);
-  if ((e >> 31) || !fast_eligible(pipe, L.n)) return false;
+  if ((e >> 31) || !fast_eligible(pipe, L.n) || c.mirror[L.w]) return false;   // mirror: the reconstruct kernel
   const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
   pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
   return stored < L.n && stored > 0 && pos + (uint64_t)stored <= c.stream_bytes && (pos & 15) == 0;
@@ -1395,6 +1343,7 @@ hipError_t launch_validate(const CallDesc& c, hipStream_t s) {
 // Raw chunks are copied to their code slot; compressed chunks go to a worklist.
 // Block 0 also checks that each stream's chunk sizes add up to its header total.
 __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* worklist) {
+  __shared__ uint32_t sh32[256];
   if (blockIdx.x == 0) {
     for (int r = threadIdx.x; r < c.R; r += blockDim.x) {
       const ReqDesc rq = req_at(c, r);
@@ -1422,6 +1371,33 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
     }
     if (raw && c.direct[L.w]) {
       // the reconstruct kernels read this chunk from the stream
+    } else if (!raw && c.mirror[L.w] && fast_eligible(1, L.n)) {
+      // the reconstruct kernels decode this chunk from the stream; they need
+      // the number of non-zero words before each bitmap dword: n / 64 words
+      // in the chunk's codes slot
+      const int n = (int)L.n, nd = n / 64;
+      if (stored < n / 16) {
+        if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+        continue;
+      }
+      const uint32_t* bmg = (const uint32_t*)(c.stream + pos);
+      uint32_t* pref = (uint32_t*)(c.codes + L.src);
+      uint32_t cnt[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 4 * (int)threadIdx.x + i;
+        cnt[i] = (d < nd) ? (uint32_t)__builtin_popcount(bmg[d]) : 0u;
+        sum += cnt[i];
+      }
+      uint32_t total;
+      uint32_t run = block_exclusive_scan<uint32_t>(sum, sh32, total);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 4 * (int)threadIdx.x + i;
+        if (d < nd) pref[d] = run;
+        run += cnt[i];
+      }
+      if (n / 16 + 2 * (int64_t)total != stored && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
     } else if (raw) {
       const uint4* src = (const uint4*)(c.stream + pos);
       uint4* dst = (uint4*)(c.codes + L.src);

@@ -1,0 +1,87 @@
+// 64x64 bit-matrix transpose across a wavefront (gfx950), shared by the
+// word-parallel lossless kernels and the reconstruct kernels that decode
+// TUPL8_1 -> BIT_8 -> RZE_2 chunks themselves.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+__device__ __forceinline__ uint32_t rotr32(uint32_t x, uint32_t s) { return __builtin_amdgcn_alignbit(x, x, s); }
+__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
+
+// Lane constants of the 64x64 bit transpose: for the rounds exchanging with
+// lane ^ 16, ^ 8, ^ 4, ^ 2, ^ 1, the bits this lane keeps and the rotation
+// that aligns the partner's bits.
+struct XposeLane {
+  uint32_t mk[5];
+  uint32_t sh[5];
+};
+__device__ __forceinline__ XposeLane xpose_lane() {
+  XposeLane x;
+  const int lane = __lane_id();
+  const uint32_t m[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+#pragma unroll
+  for (int r = 0; r < 5; ++r) {
+    const int j = 16 >> r;
+    const bool lower = (lane & j) == 0;
+    x.mk[r] = lower ? m[r] : ~m[r];
+    x.sh[r] = lower ? (uint32_t)(32 - j) : (uint32_t)j;
+  }
+  return x;
+}
+// partner values: lane ^ 16 and lane ^ 4 through the swizzle unit, lane ^ 8
+// (rotate a 16-lane row by 8), lane ^ 2 and lane ^ 1 (quad permutes) by DPP
+__device__ __forceinline__ uint32_t xchg16(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); }
+__device__ __forceinline__ uint32_t xchg8(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t xchg4(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); }
+__device__ __forceinline__ uint32_t xchg2(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t xchg1(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false); }
+
+// Lane i holds row i of a 64x64 bit matrix (lo: bits 0..31, hi: 32..63);
+// afterwards lane c holds column c.  Each round swaps the off-diagonal
+// blocks of one bit of the row and column index.
+__device__ __forceinline__ void xpose64(uint32_t& lo, uint32_t& hi, const XposeLane& X) {
+  {
+    auto p = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+    lo = p[0];
+    hi = p[1];
+  }
+  uint32_t a, b;
+  a = xchg16(lo); b = xchg16(hi);
+  lo = bfi32(X.mk[0], lo, rotr32(a, X.sh[0])); hi = bfi32(X.mk[0], hi, rotr32(b, X.sh[0]));
+  a = xchg8(lo); b = xchg8(hi);
+  lo = bfi32(X.mk[1], lo, rotr32(a, X.sh[1])); hi = bfi32(X.mk[1], hi, rotr32(b, X.sh[1]));
+  a = xchg4(lo); b = xchg4(hi);
+  lo = bfi32(X.mk[2], lo, rotr32(a, X.sh[2])); hi = bfi32(X.mk[2], hi, rotr32(b, X.sh[2]));
+  a = xchg2(lo); b = xchg2(hi);
+  lo = bfi32(X.mk[3], lo, rotr32(a, X.sh[3])); hi = bfi32(X.mk[3], hi, rotr32(b, X.sh[3]));
+  a = xchg1(lo); b = xchg1(hi);
+  lo = bfi32(X.mk[4], lo, rotr32(a, X.sh[4])); hi = bfi32(X.mk[4], hi, rotr32(b, X.sh[4]));
+}
+
+// xpose64 with the lane constants derived in place (for kernels with no
+// registers to spare for XposeLane)
+__device__ __forceinline__ void xpose64_lean(uint32_t& lo, uint32_t& hi) {
+  {
+    auto p = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+    lo = p[0];
+    hi = p[1];
+  }
+  const uint32_t lane = (uint32_t)__lane_id();
+  uint32_t a, b, mk, sh;
+#define KVC_XROUND(J, M, XCHG)                                            \
+  mk = (lane & (J)) ? ~(uint32_t)(M) : (uint32_t)(M);                     \
+  sh = (lane & (J)) ? (uint32_t)(J) : (uint32_t)(32 - (J));               \
+  a = XCHG(lo); b = XCHG(hi);                                             \
+  lo = bfi32(mk, lo, rotr32(a, sh)); hi = bfi32(mk, hi, rotr32(b, sh));
+  KVC_XROUND(16, 0x0000FFFFu, xchg16)
+  KVC_XROUND(8, 0x00FF00FFu, xchg8)
+  KVC_XROUND(4, 0x0F0F0F0Fu, xchg4)
+  KVC_XROUND(2, 0x33333333u, xchg2)
+  KVC_XROUND(1, 0x55555555u, xchg1)
+#undef KVC_XROUND
+}
+
+}  // namespace kvc

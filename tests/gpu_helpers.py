@@ -100,6 +100,27 @@ def split_stream(stream: np.ndarray, wl, L, T):
     return codes, params
 
 
+def chunk_layout(stream: np.ndarray, wl, L, T):
+    """Every chunk of a dense stream: (section, index, raw size, byte offset,
+    stored size, raw flag)."""
+    cfg = O.cfg_from_workload(wl, layers=L)
+    import ctypes as C
+    codes_b = [O.lib().kvco_codes_bytes(C.byref(cfg), w, T) for w in range(2)]
+    params_b = [O.lib().kvco_params_bytes(C.byref(cfg), w, T) for w in range(2)]
+    cb = wl.chunk_bytes
+    nch = [-(-c // cb) for c in codes_b]
+    table = np.frombuffer(stream.tobytes(), np.uint32, sum(nch), 64)
+    pos = a16(a16(a16(64 + 4 * sum(nch)) + params_b[0]) + params_b[1])
+    out, ci = [], 0
+    for w in range(2):
+        for i in range(nch[w]):
+            e = int(table[ci])
+            out.append((w, i, min(cb, codes_b[w] - i * cb), pos, e & 0x7FFFFFFF, e >> 31))
+            pos += a16(e & 0x7FFFFFFF)
+            ci += 1
+    return out
+
+
 def chunk_kinds(stream: np.ndarray, wl, L, T):
     """(raw, compressed) chunk counts of a stream, from its chunk table."""
     cfg = O.cfg_from_workload(wl, layers=L)

@@ -13,8 +13,8 @@ import torch
 
 import kvc_workloads as W
 import oracle_api as O
-from gpu_helpers import (DEV, assert_encode_parity, assert_values_close, chunk_kinds, compare_encode, gpu_decode, gpu_encode,
-                         log, oracle_encode, to_u16)
+from gpu_helpers import (DEV, assert_encode_parity, assert_values_close, chunk_kinds, chunk_layout, compare_encode, gpu_decode,
+                         gpu_encode, log, oracle_encode, to_u16)
 import kv_cache_compression_kvc_amd as K
 
 pytestmark = pytest.mark.gpu
@@ -189,6 +189,32 @@ def test_corrupt_and_mismatched_streams_are_detected():
     with pytest.raises(K.KvcError) as e:                          # truncated below the fixed sections
         gpu_decode(plan, ref[:100], wl, T, L)
     assert e.value.status == K.ERR_CORRUPT_STREAM
+
+
+@pytest.mark.parametrize("section", [0, 1])
+def test_zeroed_word_under_a_set_bitmap_bit_is_detected(section):
+    # TUPL8_1 -> BIT_8 -> RZE_2 chunks whose bitmap still matches their size
+    # but one of whose kept words was zeroed: keys go through the lossless
+    # pass, 2-bit per-token values through the reconstruct kernel's own chunk
+    # decoder; both must report the stream corrupt
+    wl = C3.with_(chunk_bytes=8192, name="zeroed_word")
+    L, T = 2, 512
+    k, v = W.zero_rich_kv(wl, L, T, seed=9, zero_frac=0.5)
+    st, ref = oracle_encode(wl, to_u16(k), to_u16(v), T, L)
+    assert st == O.OK
+    plan = K.Plan(K.config_from_workload(wl, max_tokens=T, layers=L))
+    assert gpu_decode(plan, ref, wl, T, L)[0] == K.OK
+    comp = [c for c in chunk_layout(ref, wl, L, T) if c[0] == section and not c[5] and c[4] > c[2] // 16]
+    assert len(comp) >= 2, comp
+    rng = np.random.default_rng(section)
+    for w, i, n, pos, stored, raw in [comp[0], comp[-1], comp[int(rng.integers(0, len(comp)))]]:
+        words = np.frombuffer(ref[pos + n // 16:pos + stored].tobytes(), np.uint16)
+        assert (words != 0).all()
+        bad = ref.copy()
+        at = pos + n // 16 + 2 * int(rng.integers(0, words.size))
+        bad[at:at + 2] = 0
+        log(f"  section {w} chunk {i}: zeroed the word at byte {at - pos} of {stored}")
+        assert gpu_decode(plan, bad, wl, T, L)[0] == K.ERR_CORRUPT_STREAM
 
 
 def test_paged_matches_oracle():
