@@ -35,6 +35,7 @@ class TensorPolicy:
     axis: str          # "token" (groups along head_dim) or "channel" (groups along tokens)
     group: int
     hadamard: bool = True
+    delta: int = 0     # token-delta run length (0 = none)
 
 
 @dataclasses.dataclass(frozen=True)

@@ -305,6 +305,7 @@ static Pol policy(const kvco_cfg* cfg, int which) {
 }
 
 static bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+static int which_delta(const kvco_cfg* cfg, int which) { return which == 0 ? cfg->k_delta : cfg->v_delta; }
 
 static int check_cfg(const kvco_cfg* cfg) {
   if (!cfg) return KVCO_ERR_INVALID_ARG;
@@ -320,6 +321,8 @@ static int check_cfg(const kvco_cfg* cfg) {
     if (!is_pow2(p.group)) return KVCO_ERR_INVALID_ARG;
     if (p.axis == 0 && (p.group < 8 || p.group > cfg->head_dim)) return KVCO_ERR_INVALID_ARG;
     if (p.axis == 1 && (p.group < 16 || p.group > 256)) return KVCO_ERR_INVALID_ARG;
+    const int dr = which_delta(cfg, w);
+    if (dr != 0 && (!is_pow2(dr) || dr < 2 || dr > 32768)) return KVCO_ERR_INVALID_ARG;
   }
   if (cfg->chunk_bytes < 4096 || cfg->chunk_bytes > (1u << 20) || (cfg->chunk_bytes % 4096) != 0)
     return KVCO_ERR_INVALID_ARG;
@@ -747,11 +750,63 @@ extern "C" int kvco_chunk_decode(const uint8_t* stages, const uint8_t* in, size_
 }
 
 /* ======================================================================
+ * Token delta.  KVServe Sec. 5.1 lists Delta (from CacheGen) among the
+ * transformer modules that reshape the value distribution before
+ * quantization, and names it only.  The reading taken here: in each (layer,
+ * head) the tokens form runs of D consecutive tokens from token 0 (the last
+ * run may be shorter); a run's first token, its anchor, is kept, and every
+ * other token is replaced, channel by channel, by its difference from the
+ * anchor, formed in binary32 from the two 16-bit values and rounded to the
+ * tensor's 16-bit type (nearest, ties to even).  The result is quantized like
+ * any input.  Decoding reverses it on the reconstructed 16-bit tensor: a
+ * non-anchor value becomes the rounded binary32 sum of itself and its anchor.
+ * ====================================================================== */
+extern "C" int kvco_delta_forward(const kvco_cfg* cfg, int which, const uint16_t* x, int tokens, uint16_t* y) {
+  if (check_cfg(cfg) != KVCO_OK || (which != 0 && which != 1) || tokens < 0) return KVCO_ERR_INVALID_ARG;
+  const int64_t H = cfg->heads, D = cfg->head_dim, run = which_delta(cfg, which);
+  const int64_t n = (int64_t)cfg->layers * tokens * H * D;
+  if (n > 0 && (!x || !y)) return KVCO_ERR_INVALID_ARG;
+  for (int l = 0; l < cfg->layers; ++l)
+    for (int t = 0; t < tokens; ++t)
+      for (int h = 0; h < H; ++h) {
+        const int a = run ? (int)(t - t % run) : t;           /* the anchor of token t */
+        const int64_t xi = (((int64_t)l * tokens + t) * H + h) * D;
+        const int64_t ai = (((int64_t)l * tokens + a) * H + h) * D;
+        for (int d = 0; d < D; ++d) {
+          if (a == t) { y[xi + d] = x[xi + d]; continue; }
+          const float diff = load16(x[xi + d], cfg->dtype) - load16(x[ai + d], cfg->dtype);
+          y[xi + d] = store16(diff, cfg->dtype);
+        }
+      }
+  return KVCO_OK;
+}
+
+extern "C" int kvco_delta_inverse(const kvco_cfg* cfg, int which, uint16_t* x, int tokens) {
+  if (check_cfg(cfg) != KVCO_OK || (which != 0 && which != 1) || tokens < 0) return KVCO_ERR_INVALID_ARG;
+  const int64_t H = cfg->heads, D = cfg->head_dim, run = which_delta(cfg, which);
+  if (!run) return KVCO_OK;
+  if ((int64_t)cfg->layers * tokens * H * D > 0 && !x) return KVCO_ERR_INVALID_ARG;
+  for (int l = 0; l < cfg->layers; ++l)
+    for (int t = 0; t < tokens; ++t) {
+      const int a = (int)(t - t % run);
+      if (a == t) continue;                                  /* anchors are stored as they are */
+      for (int h = 0; h < H; ++h) {
+        const int64_t xi = (((int64_t)l * tokens + t) * H + h) * D;
+        const int64_t ai = (((int64_t)l * tokens + a) * H + h) * D;
+        for (int d = 0; d < D; ++d)
+          x[xi + d] = store16(load16(x[xi + d], cfg->dtype) + load16(x[ai + d], cfg->dtype), cfg->dtype);
+      }
+    }
+  return KVCO_OK;
+}
+
+/* ======================================================================
  * Stream format (this project's; little-endian)
  *   [0,64)   header: magic "KVC1", u16 version 1, u8 dtype, u8 flags (bit 0:
  *            mixed precision, below; other bits 0),
  *            i32 layers, tokens, heads, head_dim,
- *            K policy {u8 bits, u8 axis, u8 hadamard, u8 0, u16 group, u16 0},
+ *            K policy {u8 bits, u8 axis, u8 hadamard, u8 0, u16 group,
+ *            u16 token-delta run length (0 = none)},
  *            V policy (same), u64 seed, u8 stages[4], u32 chunk_bytes,
  *            u64 total_bytes
  *   [64, 64 + 4*nc) chunk table, K chunks then V chunks: bit 31 = stored raw,
@@ -877,6 +932,7 @@ static void write_header(uint8_t* o, const kvco_cfg* cfg, int tokens, uint64_t t
     uint8_t* q = o + 24 + 8 * w;
     q[0] = (uint8_t)p.bits; q[1] = (uint8_t)p.axis; q[2] = (uint8_t)p.had;
     w16(q + 4, (uint16_t)p.group);
+    w16(q + 6, (uint16_t)which_delta(cfg, w));
   }
   w64(o + 40, cfg->seed);
   for (int i = 0; i < 4; ++i) o[48 + i] = cfg->stages[i];
@@ -953,9 +1009,16 @@ static int encode_stream(const kvco_cfg* cfg, const uint8_t* bits, const uint16_
   std::memset(out, 0, (size_t)L.max_total);
   int status = KVCO_OK;
   std::vector<uint8_t> codes[2];
+  std::vector<uint16_t> delta;
   for (int w = 0; w < 2; ++w) {
     codes[w].assign((size_t)L.codes[w], 0);
     const uint16_t* x = w == 0 ? k : v;
+    if (which_delta(cfg, w) && tokens > 0) {
+      delta.assign((size_t)cfg->layers * tokens * cfg->heads * cfg->head_dim, 0);
+      const int r = kvco_delta_forward(cfg, w, x, tokens, delta.data());
+      if (r != KVCO_OK) return r;
+      x = delta.data();
+    }
     int r = bits ? quantize_mixed(cfg, bits, w, x, tokens, codes[w].data(), out + L.params_off[w])
                  : kvco_quantize_tensor(cfg, w, x, tokens, codes[w].data(), out + L.params_off[w]);
     if (r == KVCO_ERR_RANGE) status = KVCO_ERR_RANGE;
@@ -1014,7 +1077,9 @@ extern "C" int kvco_stream_info(const uint8_t* in, size_t in_bytes, kvco_cfg* cf
   cfg->heads = (int32_t)r32(in + 16);
   cfg->head_dim = (int32_t)r32(in + 20);
   cfg->k_bits = in[24]; cfg->k_axis = in[25]; cfg->k_hadamard = in[26]; cfg->k_group = r16(in + 28);
+  cfg->k_delta = r16(in + 30);
   cfg->v_bits = in[32]; cfg->v_axis = in[33]; cfg->v_hadamard = in[34]; cfg->v_group = r16(in + 36);
+  cfg->v_delta = r16(in + 38);
   cfg->seed = r64(in + 40);
   for (int i = 0; i < 4; ++i) cfg->stages[i] = in[48 + i];
   cfg->chunk_bytes = r32(in + 52);
@@ -1056,6 +1121,8 @@ extern "C" int kvco_decode(const uint8_t* in, size_t in_bytes, uint16_t* k, uint
     }
     int r = bits ? dequantize_mixed(&cfg, bits, w, codes.data(), in + L.params_off[w], tokens, w == 0 ? k : v)
                  : kvco_dequantize_tensor(&cfg, w, codes.data(), in + L.params_off[w], tokens, w == 0 ? k : v);
+    if (r != KVCO_OK) return r;
+    r = kvco_delta_inverse(&cfg, w, w == 0 ? k : v, tokens);
     if (r != KVCO_OK) return r;
   }
   if (pos != (int64_t)total) return KVCO_ERR_CORRUPT_STREAM;

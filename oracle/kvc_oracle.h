@@ -61,6 +61,7 @@ typedef struct {
   uint64_t seed;
   uint8_t stages[4];                   /* 0-terminated lossless pipeline */
   uint32_t chunk_bytes;
+  int32_t k_delta, v_delta;            /* token-delta run length: 0 = none, else a power of two in [2, 32768] */
 } kvco_cfg;
 
 /* ---- scalar building blocks (exported so tests can pin them) ---- */
@@ -86,6 +87,10 @@ int kvco_quantize_tensor(const kvco_cfg* cfg, int which, const uint16_t* x, int 
                          uint8_t* codes, uint8_t* params);
 int kvco_dequantize_tensor(const kvco_cfg* cfg, int which, const uint8_t* codes,
                            const uint8_t* params, int tokens, uint16_t* x);
+
+/* ---- token delta (a pre-transform; identity when the tensor's run length is 0) ---- */
+int kvco_delta_forward(const kvco_cfg* cfg, int which, const uint16_t* x, int tokens, uint16_t* y);
+int kvco_delta_inverse(const kvco_cfg* cfg, int which, uint16_t* x, int tokens);
 
 /* ---- lossless components ---- */
 int kvco_stage_encode(int stage, const uint8_t* in, size_t n, uint8_t* out, size_t cap, size_t* out_n);

@@ -27,7 +27,8 @@ class Cfg(C.Structure):
                 ("dtype", C.c_int32),
                 ("k_bits", C.c_int32), ("k_axis", C.c_int32), ("k_group", C.c_int32), ("k_hadamard", C.c_int32),
                 ("v_bits", C.c_int32), ("v_axis", C.c_int32), ("v_group", C.c_int32), ("v_hadamard", C.c_int32),
-                ("seed", C.c_uint64), ("stages", C.c_uint8 * 4), ("chunk_bytes", C.c_uint32)]
+                ("seed", C.c_uint64), ("stages", C.c_uint8 * 4), ("chunk_bytes", C.c_uint32),
+                ("k_delta", C.c_int32), ("v_delta", C.c_int32)]
 
 
 _lib = None
@@ -62,6 +63,8 @@ def lib():
             "kvco_params_bytes": (C.c_int64, [P, C.c_int, C.c_int]),
             "kvco_quantize_tensor": (C.c_int, [P, C.c_int, P, C.c_int, P, P]),
             "kvco_dequantize_tensor": (C.c_int, [P, C.c_int, P, P, C.c_int, P]),
+            "kvco_delta_forward": (C.c_int, [P, C.c_int, P, C.c_int, P]),
+            "kvco_delta_inverse": (C.c_int, [P, C.c_int, P, C.c_int]),
             "kvco_stage_encode": (C.c_int, [C.c_int, P, C.c_size_t, P, C.c_size_t, P]),
             "kvco_stage_decode": (C.c_int, [C.c_int, P, C.c_size_t, P, C.c_size_t]),
             "kvco_chunk_encode": (C.c_int, [P, P, C.c_size_t, P, P, P]),
@@ -98,6 +101,7 @@ def cfg_from_workload(wl, layers=None) -> Cfg:
         setattr(c, pre + "_axis", 0 if pol.axis == "token" else 1)
         setattr(c, pre + "_group", pol.group)
         setattr(c, pre + "_hadamard", 1 if pol.hadamard else 0)
+        setattr(c, pre + "_delta", pol.delta)
     c.seed = wl.sign_seed
     ids = [STAGE_IDS[s] for s in wl.stages] + [0] * (4 - len(wl.stages))
     for i in range(4):
@@ -153,6 +157,19 @@ def dequantize_tensor(cfg: Cfg, which: int, codes: np.ndarray, params: np.ndarra
     params = np.ascontiguousarray(params, np.uint8)
     st = lib().kvco_dequantize_tensor(C.byref(cfg), which, _p(codes), _p(params), tokens, _p(x))
     return st, x[:cfg.layers * tokens * cfg.heads * cfg.head_dim]
+
+
+def delta_forward(cfg: Cfg, which: int, x_u16: np.ndarray, tokens: int):
+    x = np.ascontiguousarray(x_u16, dtype=np.uint16).reshape(-1)
+    y = np.zeros(max(x.size, 1), np.uint16)
+    st = lib().kvco_delta_forward(C.byref(cfg), which, _p(x), tokens, _p(y))
+    return st, y[:x.size]
+
+
+def delta_inverse(cfg: Cfg, which: int, y_u16: np.ndarray, tokens: int):
+    x = np.array(y_u16, dtype=np.uint16).reshape(-1)
+    st = lib().kvco_delta_inverse(C.byref(cfg), which, _p(x), tokens)
+    return st, x
 
 
 # ---------------------------------------------------------------- lossless
