@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--mixed", choices=["none", "mixhq", "mixhq16"], default="none",
                     help="mixed precision per (layer, head): mixhq = heads 0-1 of every layer at 8 bits and the "
                          "others at 2 bits (K and V); mixhq16 = heads 0-1 kept at 16 bits, the others at 2")
+    ap.add_argument("--delta", default="0:0",
+                    help="token-delta run lengths K:V before the transform (0 = none, the headline)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30,
                     help="size of the plain device copy timed as the practical bandwidth reference")
     args = ap.parse_args()
@@ -203,6 +205,10 @@ def main():
     del ca, cb
 
     wl = W.WORKLOADS[args.workload]
+    dk, dv = (int(x) for x in args.delta.split(":"))
+    if dk or dv:
+        import dataclasses
+        wl = wl.with_(k=dataclasses.replace(wl.k, delta=dk), v=dataclasses.replace(wl.v, delta=dv))
     L, T = wl.layers, wl.tokens
     dev = torch.device("cuda:0")
     log(f"generating {wl.name}: {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype} on {dev}")
@@ -322,6 +328,7 @@ def main():
                    "k_policy": f"int{wl.k.bits} per-{wl.k.axis} g{wl.k.group} hadamard",
                    "v_policy": f"int{wl.v.bits} per-{wl.v.axis} g{wl.v.group} hadamard",
                    "lossless": ">".join(wl.stages), "chunk_bytes": wl.chunk_bytes, "mixed": args.mixed,
+                   "token_delta": [dk, dv],
                    "uncompressed_bytes": U},
         "encode_GBps": round(U / enc_ms / 1e6, 3),
         "decode_GBps": round(U / dec_ms / 1e6, 3),
@@ -352,7 +359,7 @@ def main():
     result["pages_figures"] = PAGES_FIGURES
     result["selection"] = selection_cost(U, U / (enc_ms * 1e-3), U / (dec_ms * 1e-3), U / n)
     t = (counted_traffic(dom) if (args.workload == "c3_llama70b_32k" and args.values == "gaussian"
-                                   and args.mixed == "none") else None)
+                                   and args.mixed == "none" and not (dk or dv)) else None)
     if t is not None:
         result["roofline"]["traffic"] = t["bytes"]
         result["roofline"]["traffic_read_write"] = [t["read_bytes"], t["write_bytes"]]

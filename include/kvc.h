@@ -106,7 +106,15 @@ typedef struct {
                          only: kvc_plan returns KVC_ERR_UNSUPPORTED for it) */
   uint8_t reserved0;
   uint16_t group;     /* power of two */
-  uint16_t reserved1;
+  uint16_t delta;     /* token delta before the transform (KVServe Sec. 5.1, the Delta
+                         transformer module, after CacheGen): 0 = none; else a power of
+                         two D in [2, 32768].  In each (layer, head) the tokens form runs
+                         of D from token 0; a run's first token is kept and every other
+                         token is replaced by its binary32 difference from it, rounded
+                         to the 16-bit type; decoding adds the anchor back with the same
+                         rounding.  Dense calls only (the paged calls return
+                         KVC_ERR_UNSUPPORTED); an encode needs 2 bytes of workspace per
+                         value of each tensor that uses it. */
 } kvc_tensor_policy;
 
 typedef struct {
@@ -220,7 +228,8 @@ typedef enum {
   KVC_KERNEL_DECODE_K = 6,     /* fused reconstruct, K */
   KVC_KERNEL_DECODE_V = 7,     /* fused reconstruct, V */
   KVC_KERNEL_AUX = 8,          /* header, validation and status kernels */
-  KVC_KERNEL_COUNT = 9
+  KVC_KERNEL_DELTA = 9,        /* token delta: forward before encoding, inverse after decoding */
+  KVC_KERNEL_COUNT = 10
 } kvc_kernel_kind;
 
 kvc_status kvc_profile_enable(int on);

@@ -22,12 +22,12 @@ STAGES = {name: i + 1 for i, name in enumerate(
     ("TUPL2_1", "TUPL4_1", "TUPL8_1", "DIFF1", "DIFF2", "DIFF4", "DIFF8",
      "BIT_1", "BIT_2", "BIT_4", "BIT_8", "RZE_1", "RZE_2", "RZE_4", "RZE_8"))}
 KERNELS = ("ENCODE_K", "ENCODE_V", "LOSSLESS_ENC", "SCAN", "COMPACT", "LOSSLESS_DEC",
-           "DECODE_K", "DECODE_V", "AUX")
+           "DECODE_K", "DECODE_V", "AUX", "DELTA")
 
 
 class TensorPolicy(C.Structure):
     _fields_ = [("bits", C.c_uint8), ("axis", C.c_uint8), ("hadamard", C.c_uint8), ("reserved0", C.c_uint8),
-                ("group", C.c_uint16), ("reserved1", C.c_uint16)]
+                ("group", C.c_uint16), ("delta", C.c_uint16)]
 
 
 class Config(C.Structure):
@@ -129,12 +129,13 @@ def _check(s: int, where: str):
 def make_config(layers: int, max_tokens: int, kv_heads: int, head_dim: int, dtype: int,
                 k: Sequence[int], v: Sequence[int], sign_seed: int, lossless: Sequence[str],
                 chunk_bytes: int = 65536, page_tokens: int = 0) -> Config:
-    """k, v: (bits, axis, group, hadamard)."""
+    """k, v: (bits, axis, group, hadamard[, delta run length])."""
     c = Config()
     c.struct_size = C.sizeof(Config)
     c.layers, c.max_tokens, c.kv_heads, c.head_dim, c.dtype = layers, max_tokens, kv_heads, head_dim, dtype
     for dst, pol in ((c.k, k), (c.v, v)):
         dst.bits, dst.axis, dst.group, dst.hadamard = pol[0], pol[1], pol[2], pol[3]
+        dst.delta = pol[4] if len(pol) > 4 else 0
     c.sign_seed = sign_seed
     ids = [STAGES[s] for s in lossless] + [0] * (4 - len(lossless))
     for i in range(4):
@@ -146,7 +147,8 @@ def make_config(layers: int, max_tokens: int, kv_heads: int, head_dim: int, dtyp
 
 def config_from_workload(wl, max_tokens: Optional[int] = None, layers: Optional[int] = None) -> Config:
     """Config for an object with the fields of kvc_workloads.Workload."""
-    pol = lambda p: (p.bits, PER_TOKEN if p.axis == "token" else PER_CHANNEL, p.group, 1 if p.hadamard else 0)
+    pol = lambda p: (p.bits, PER_TOKEN if p.axis == "token" else PER_CHANNEL, p.group, 1 if p.hadamard else 0,
+                     getattr(p, "delta", 0))
     return make_config(wl.layers if layers is None else layers,
                        wl.tokens if max_tokens is None else max_tokens,
                        wl.heads, wl.head_dim, F16 if wl.dtype == "f16" else BF16,

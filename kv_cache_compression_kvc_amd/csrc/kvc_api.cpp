@@ -164,8 +164,17 @@ void request_layout(const kvc_plan_s* p, int T, ReqDesc& rq) {
 
 // Workspace carving shared by all calls.
 struct WsLayout {
-  int64_t ctl, sizes, offs, worklist, flags, scan, codes, params, reqs, slabs, total;
+  int64_t ctl, sizes, offs, worklist, flags, scan, codes, params, reqs, slabs, delta, total;
 };
+
+// Bytes of the token-delta area of a dense encode: the transformed copy of
+// each tensor that uses the delta.
+int64_t delta_area(const kvc_plan_s* p, int64_t T, int64_t* k_bytes = nullptr) {
+  const int64_t one = a256((int64_t)p->cfg.layers * T * p->cfg.kv_heads * kHeadDim * 2);
+  const int64_t k = p->pol[0].delta ? one : 0, v = p->pol[1].delta ? one : 0;
+  if (k_bytes) *k_bytes = k;
+  return k + v;
+}
 
 // Bytes of the slab tables (a SlabDesc per (tensor, layer, head)) and the width
 // map that a mixed call uploads into its workspace.
@@ -175,7 +184,8 @@ int64_t slab_area(const kvc_plan_s* p) {
   return a256(n * (int64_t)sizeof(SlabDesc)) + a256(n);
 }
 
-WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int64_t R, int64_t slabs = 0) {
+WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int64_t R, int64_t slabs = 0,
+                   int64_t delta = 0) {
   WsLayout w;
   w.ctl = 0;
   w.sizes = 256;
@@ -190,7 +200,8 @@ WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int
   w.params = a256(w.codes + codes_area);
   w.reqs = a256(w.params + params_area);
   w.slabs = a256(w.reqs + (R > 1 ? R * (int64_t)sizeof(ReqDesc) : 0));
-  w.total = a256(w.slabs + slabs);
+  w.delta = a256(w.slabs + slabs);
+  w.total = a256(w.delta + delta);
   return w;
 }
 
@@ -307,6 +318,8 @@ kvc_status check_policy(const kvc_tensor_policy& t, const char* name, int head_d
     return fail(KVC_ERR_INVALID_ARG, "%s.group must be in [8, head_dim] for per-token groups", name);
   if (t.axis == 1 && (t.group < 16 || t.group > 256))
     return fail(KVC_ERR_INVALID_ARG, "%s.group must be in [16, 256] for per-channel groups", name);
+  if (t.delta != 0 && (!pow2(t.delta) || t.delta < 2 || t.delta > 32768))
+    return fail(KVC_ERR_INVALID_ARG, "%s.delta must be 0 or a power of two in [2, 32768]", name);
   return KVC_OK;
 }
 
@@ -496,6 +509,7 @@ kvc_status kvc_plan(const kvc_config* cfg, kvc_plan_t* out) {
     p->pol[w].group = tp[w]->group;
     p->pol[w].hadamard = tp[w]->hadamard;
     p->pol[w].c = tp[w]->hadamard ? (float)(1.0 / std::sqrt((double)cfg->head_dim)) : 1.0f;
+    p->pol[w].delta = tp[w]->delta;
   }
   std::memset(p->signs, 0, sizeof(p->signs));
   uint64_t st64 = cfg->sign_seed;
@@ -548,7 +562,7 @@ kvc_status kvc_plan_sizes(kvc_plan_t p, int64_t tokens, size_t* max_stream_bytes
   ReqDesc rq;
   request_layout(p, (int)tokens, rq);
   const int64_t codes_area = a256(rq.codes_bytes[0]) + a256(rq.codes_bytes[1]);
-  const WsLayout w = ws_layout(rq.nchunks[0] + rq.nchunks[1], codes_area, 0, 1, slab_area(p));
+  const WsLayout w = ws_layout(rq.nchunks[0] + rq.nchunks[1], codes_area, 0, 1, slab_area(p), delta_area(p, tokens));
   if (max_stream_bytes) *max_stream_bytes = (size_t)rq.max_stream;
   if (workspace_bytes) *workspace_bytes = (size_t)w.total;
   return KVC_OK;
@@ -589,7 +603,9 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   // them); compressed chunks and raw chunks that must move go through the
   // workspace codes area, which uses the same offsets.
   c.one.codes_off[1] = a16(c.one.codes_bytes[0]);
-  const WsLayout w = ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1, slab_area(p));
+  int64_t delta_k = 0;
+  const WsLayout w =
+      ws_layout(c.one.nchunks[0] + c.one.nchunks[1], codes_area, 0, 1, slab_area(p), delta_area(p, tokens, &delta_k));
   if ((int64_t)out_capacity < c.one.max_stream)
     return fail(KVC_ERR_BUFFER_TOO_SMALL, "out_capacity %zu < %lld", out_capacity, (long long)c.one.max_stream);
   if ((int64_t)ws_bytes < w.total) return fail(KVC_ERR_BUFFER_TOO_SMALL, "ws_bytes %zu < %lld", ws_bytes, (long long)w.total);
@@ -617,6 +633,15 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
     c.nnz_sec[0] = c.nnz_sec[1] = 0;
   }
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
+  // token delta: the fused encoders read the transformed copy in the workspace
+  for (int k = 0; k < 2; ++k) {
+    if (!p->pol[k].delta || tokens == 0) continue;
+    uint8_t* y = ws + w.delta + (k ? delta_k : 0);
+    const void* x = c.in_kv[k];
+    if ((e = timed(KVC_KERNEL_DELTA, s, [&] { return launch_delta(c, k, tokens, true, x, y, s); })) != hipSuccess)
+      return hip_fail(e, "delta");
+    c.in_kv[k] = y;
+  }
   if ((e = timed(KVC_KERNEL_ENCODE_K, s, [&] { return fused_all(p, c, tb, 0, true, s); })) != hipSuccess) return hip_fail(e, "encode K");
   if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return fused_all(p, c, tb, 1, true, s); })) != hipSuccess) return hip_fail(e, "encode V");
   if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
@@ -685,6 +710,12 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
   if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return fused_all(p, c, tb, 0, false, s); })) != hipSuccess) return hip_fail(e, "decode K");
   if ((e = timed(KVC_KERNEL_DECODE_V, s, [&] { return fused_all(p, c, tb, 1, false, s); })) != hipSuccess) return hip_fail(e, "decode V");
+  for (int k = 0; k < 2; ++k) {
+    if (!p->pol[k].delta || tokens == 0) continue;
+    void* x = c.out_kv[k];
+    if ((e = timed(KVC_KERNEL_DELTA, s, [&] { return launch_delta(c, k, tokens, false, x, x, s); })) != hipSuccess)
+      return hip_fail(e, "delta");
+  }
   return KVC_OK;
 }
 
@@ -693,6 +724,7 @@ static kvc_status paged_common(kvc_plan_t p, int64_t num_blocks, const int32_t* 
   if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
   if (p->cfg.page_tokens < 1) return fail(KVC_ERR_INVALID_ARG, "plan was built without page_tokens");
   if (p->mixed) return fail(KVC_ERR_UNSUPPORTED, "paged calls do not take mixed-precision plans");
+  if (p->pol[0].delta || p->pol[1].delta) return fail(KVC_ERR_UNSUPPORTED, "the token delta runs on dense calls only");
   if (p->pol[0].axis != 0 || p->pol[1].axis != 0)
     return fail(KVC_ERR_UNSUPPORTED, "paged calls implement per-token policies only");
   if (((int64_t)p->cfg.page_tokens * p->cfg.kv_heads) % 32)

@@ -1674,6 +1674,77 @@ static int grid_for(int64_t blocks_needed, int cap) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(blocks_needed, (int64_t)cap));
 }
 
+// -------------------------------------------------------------------
+// Token delta (KVServe Sec. 5.1 lists Delta, after CacheGen, among the
+// transforms applied before quantization).  In each (layer, head) the tokens
+// form runs of `run` (a power of two) from token 0; a run's first token is
+// kept, every other token is replaced by its binary32 difference from it,
+// rounded to the 16-bit type (forward), and decoding adds the anchor back the
+// same way (inverse, in place: anchors are never written there).  A thread
+// takes 8 channels (16 bytes) of one head over 32 consecutive tokens; threads
+// of a wave cover consecutive 16-byte slots of a token, so every step of the
+// token loop is a contiguous 1 KiB access per wave.  Memory-bound: forward
+// reads 2 bytes and writes 2 per value, inverse reads 2 and writes 2 per
+// non-anchor value (anchors come from cache).
+// -------------------------------------------------------------------
+template <bool BF16, bool FWD>
+__global__ __launch_bounds__(256) void k_delta(const uint16_t* x, uint16_t* y, int L, int T, int H, int run) {
+  const int64_t slots = (int64_t)H * 16;             // 16-byte slots per token
+  const int64_t nblk = (T + 31) / 32;
+  const int64_t total = (int64_t)L * nblk * slots;
+  const int64_t vec = slots * 8;                     // values per token
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t slot = i % slots;
+    const int64_t r = i / slots;
+    const int64_t l = r / nblk;
+    const int t0 = (int)(r - l * nblk) * 32;
+    const int t1 = std::min(T, t0 + 32);
+    const int64_t base = l * (int64_t)T * vec + slot * 8;
+    uint4 anc = make_uint4(0, 0, 0, 0);
+    int acur = -1;
+    for (int t = t0; t < t1; ++t) {
+      const int a = t & ~(run - 1);
+      const uint4 v = *(const uint4*)(x + base + (int64_t)t * vec);
+      if (a == t) {
+        anc = v;
+        acur = a;
+        if constexpr (FWD) *(uint4*)(y + base + (int64_t)t * vec) = v;
+        continue;
+      }
+      if (a != acur) {
+        anc = *(const uint4*)(x + base + (int64_t)a * vec);
+        acur = a;
+      }
+      const uint32_t vw[4] = {v.x, v.y, v.z, v.w}, aw[4] = {anc.x, anc.y, anc.z, anc.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float v0, v1, a0, a1;
+        unpack16<BF16>(vw[k], v0, v1);
+        unpack16<BF16>(aw[k], a0, a1);
+        o[k] = FWD ? pack16<BF16>(v0 - a0, v1 - a1) : pack16<BF16>(v0 + a0, v1 + a1);
+      }
+      *(uint4*)(y + base + (int64_t)t * vec) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+hipError_t launch_delta(const CallDesc& c, int which, int T, bool forward, const void* x, void* y, hipStream_t s) {
+  const int run = c.pol[which].delta;
+  const int64_t threads = (int64_t)c.layers * ((T + 31) / 32) * c.heads * 16;
+  const int grid = grid_for((threads + 255) / 256, 256 * 64);
+  const uint16_t* xi = (const uint16_t*)x;
+  uint16_t* yo = (uint16_t*)y;
+  if (c.dtype == 1) {
+    if (forward) k_delta<true, true><<<grid, 256, 0, s>>>(xi, yo, c.layers, T, c.heads, run);
+    else k_delta<true, false><<<grid, 256, 0, s>>>(xi, yo, c.layers, T, c.heads, run);
+  } else {
+    if (forward) k_delta<false, true><<<grid, 256, 0, s>>>(xi, yo, c.layers, T, c.heads, run);
+    else k_delta<false, false><<<grid, 256, 0, s>>>(xi, yo, c.layers, T, c.heads, run);
+  }
+  return hipGetLastError();
+}
+
 #define KVC_TOKEN_CASES_P(KERNEL, BITS, BF, PG)                                    \
   switch (pol.group) {                                                             \
     case 16: KERNEL<BITS, 16, BF, PG><<<grid, block, 0, s>>>(c, which); break;    \

@@ -39,6 +39,7 @@ struct TensorPol {
   int group;
   int hadamard;
   float c;               // 1/sqrt(head_dim) rounded to binary32 (1 if no transform)
+  int delta;             // token-delta run length (0 = none)
 };
 
 // One (layer, head) slab of a mixed-precision tensor: its codes and
@@ -126,6 +127,9 @@ hipError_t launch_encode_fused(const CallDesc& c, int which, hipStream_t s);
 hipError_t launch_decode_fused(const CallDesc& c, int which, hipStream_t s);
 hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s);
 hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s);
+// Token delta over a dense [layers][T][heads][128] tensor of 16-bit values:
+// forward (x -> y, out of place) or inverse (in place, x == y).
+hipError_t launch_delta(const CallDesc& c, int which, int T, bool forward, const void* x, void* y, hipStream_t s);
 hipError_t launch_scan_dense(const CallDesc& c, bool from_table, hipStream_t s);
 hipError_t launch_compact(const CallDesc& c, hipStream_t s);
 hipError_t launch_place(const CallDesc& c, hipStream_t s);

@@ -849,6 +849,8 @@ __device__ void write_header(const CallDesc& c, const ReqDesc& rq, uint8_t* o, u
     else if (k == 2) b = (uint8_t)p.hadamard;
     else if (k == 4) b = byte_of((uint32_t)p.group, 0);
     else if (k == 5) b = byte_of((uint32_t)p.group, 1);
+    else if (k == 6) b = byte_of((uint32_t)p.delta, 0);
+    else if (k == 7) b = byte_of((uint32_t)p.delta, 1);
   } else if (t < 48) b = byte_of(c.seed, t - 40);
   else if (t < 52) b = c.stages[t - 48];
   else if (t < 56) b = byte_of(c.chunk_bytes, t - 52);
@@ -1309,7 +1311,8 @@ __global__ __launch_bounds__(64) void k_validate(CallDesc c) {
           for (int w = 0; w < 2; ++w) {
             const uint8_t* p = h + 24 + 8 * w;
             diag |= (p[0] != c.pol[w].bits || p[1] != c.pol[w].axis || p[2] != c.pol[w].hadamard ||
-                     *(const uint16_t*)(p + 4) != c.pol[w].group) << (7 + w);
+                     *(const uint16_t*)(p + 4) != c.pol[w].group ||
+                     *(const uint16_t*)(p + 6) != c.pol[w].delta) << (7 + w);
           }
           for (int k = 0; k < 4; ++k) diag |= (h[48 + k] != c.stages[k]) << (9 + k);
           diag |= (h[7] != (c.mixed ? 1 : 0)) << 13;

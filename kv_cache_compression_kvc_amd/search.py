@@ -6,9 +6,12 @@ pipelines of LC-style stages are run on the GPU, their encode time, decode
 time and compressed size measured, and the Pareto-optimal ones kept and
 ranked for the deployment's bandwidth.  Here a candidate is a plan whose
 lossless list is one or two transform stages (TUPL, DIFF, BIT) followed by a
-zero-elimination stage (RZE), or no lossless stage at all; each is timed
-end to end (fused quantize + lossless + scan + compaction, and the mirror)
-on the same K/V, through the library.  Ranking uses KVServe's Eq. 5-6
+zero-elimination stage (RZE), or no lossless stage at all, optionally
+behind the token delta that KVServe Sec. 5.1 lists among its transformer
+modules (run lengths for K and V); each is timed end to end (delta, fused
+quantize + lossless + scan + placement, and the mirror) on the same K/V,
+through the library, and its reconstruction error is recorded (the delta
+changes what is quantized; the lossless stages do not).  Ranking uses KVServe's Eq. 5-6
 ("KVServe: Service-Aware KV Cache Compression for Communication-Efficient
 Disaggregated LLM Serving", Sec. 6.1): the break-even bandwidth of each
 profile and the lower envelope of the latency lines, via the library's
@@ -42,6 +45,11 @@ def candidate_pipelines(max_stages: int = 3, include_none: bool = True) -> List[
     return out
 
 
+# what the search minimizes: stream size, encode and decode time, and the
+# reconstruction error (which only the token delta changes)
+SEARCH_KEYS = ("stream_bytes", "enc_ms", "dec_ms", "rel_err")
+
+
 def pareto_front(points: Sequence[Dict], keys=("stream_bytes", "enc_ms", "dec_ms")) -> List[int]:
     """Indices of the points no other point dominates (lower or equal in every
     key, lower in one), minimizing all keys; sorted by the first key."""
@@ -73,9 +81,12 @@ def profile_numbers(uncompressed: int, stream_bytes: int, enc_ms: float, dec_ms:
             "b_star": K.break_even_bandwidth(cr, s_enc, s_dec)}
 
 
-def measure(wl, k, v, tokens: int, pipelines: Sequence[tuple], reps: int = 3, log=print) -> List[Dict]:
-    """Encode + decode k, v ([L, T, H, D] on the GPU) under each pipeline;
-    time both directions with HIP events over `reps` runs after one warm-up."""
+def measure(wl, k, v, tokens: int, pipelines: Sequence[tuple], reps: int = 3, log=print,
+            deltas: Sequence[tuple] = ((0, 0),)) -> List[Dict]:
+    """Encode + decode k, v ([L, T, H, D] on the GPU) under each (token-delta
+    run lengths (K, V), pipeline) pair; time both directions with HIP events
+    over `reps` runs after one warm-up, and record the relative error
+    ||x' - x|| / ||x|| of the reconstruction (K and V together)."""
     import torch
     import kv_cache_compression_kvc_amd as K
     L = k.shape[0]
@@ -86,10 +97,12 @@ def measure(wl, k, v, tokens: int, pipelines: Sequence[tuple], reps: int = 3, lo
     res = []
     out = ws = None
     t_start = time.time()
-    for n, pipe in enumerate(pipelines):
+    cands = [(d, p) for d in deltas for p in pipelines]
+    norm = float(torch.sqrt(k.float().square().sum() + v.float().square().sum()))
+    for n, (dl, pipe) in enumerate(cands):
         cfg = K.make_config(L, tokens, wl.heads, wl.head_dim, base.dtype,
-                            (base.k.bits, base.k.axis, base.k.group, base.k.hadamard),
-                            (base.v.bits, base.v.axis, base.v.group, base.v.hadamard),
+                            (base.k.bits, base.k.axis, base.k.group, base.k.hadamard, dl[0]),
+                            (base.v.bits, base.v.axis, base.v.group, base.v.hadamard, dl[1]),
                             base.sign_seed, list(pipe), base.chunk_bytes, 0)
         plan = K.Plan(cfg)
         ms, wsb = plan.sizes(tokens)
@@ -102,6 +115,7 @@ def measure(wl, k, v, tokens: int, pipelines: Sequence[tuple], reps: int = 3, lo
         st = plan.query_status(ws)
         if st != K.OK:
             raise RuntimeError(f"pipeline {pipe}: {K.status_string(st)}")
+        err = float(torch.sqrt((kd.float() - k.float()).square().sum() + (vd.float() - v.float()).square().sum()))
         s = torch.cuda.current_stream()
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record(s)
@@ -114,12 +128,15 @@ def measure(wl, k, v, tokens: int, pipelines: Sequence[tuple], reps: int = 3, lo
         torch.cuda.synchronize()
         enc_ms = e[0].elapsed_time(e[1]) / reps
         dec_ms = e[1].elapsed_time(e[2]) / reps
-        r = {"pipeline": ">".join(pipe) if pipe else "none", "stream_bytes": int(nbytes),
-             "enc_ms": enc_ms, "dec_ms": dec_ms}
+        name = ">".join(pipe) if pipe else "none"
+        if dl != (0, 0):
+            name = f"delta{dl[0]}/{dl[1]} " + name
+        r = {"pipeline": name, "delta": list(dl), "stream_bytes": int(nbytes),
+             "enc_ms": enc_ms, "dec_ms": dec_ms, "rel_err": err / norm if norm > 0 else 0.0}
         r.update(profile_numbers(U, nbytes, enc_ms, dec_ms))
         res.append(r)
-        if (n + 1) % 25 == 0 or n + 1 == len(pipelines):
-            log(f"  {n + 1}/{len(pipelines)} pipelines ({time.time() - t_start:.0f} s)")
+        if (n + 1) % 25 == 0 or n + 1 == len(cands):
+            log(f"  {n + 1}/{len(cands)} candidates ({time.time() - t_start:.0f} s)")
     return res
 
 
@@ -151,6 +168,8 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--pipelines", default="", help="comma-separated lossless lists to time instead of all "
                     "candidates, stages joined by '>' (e.g. 'TUPL8_1>RZE_2,none')")
+    ap.add_argument("--deltas", default="0:0", help="comma-separated token-delta run lengths K:V to combine "
+                    "with every pipeline (0 = none; e.g. '0:0,16:16')")
     ap.add_argument("--json", default="")
     args = ap.parse_args(argv)
     import torch
@@ -170,18 +189,20 @@ def main(argv=None):
         pipes = [() if x == "none" else tuple(x.split(">")) for x in args.pipelines.split(",")]
     else:
         pipes = candidate_pipelines(args.max_stages)
-    print(f"{len(pipes)} pipelines", flush=True)
-    pts = measure(wl, k, v, T, pipes, reps=args.reps, log=lambda m: print(m, flush=True))
-    front = pareto_front(pts)
+    deltas = [tuple(int(x) for x in d.split(":")) for d in args.deltas.split(",")]
+    print(f"{len(pipes)} pipelines x {len(deltas)} delta settings", flush=True)
+    pts = measure(wl, k, v, T, pipes, reps=args.reps, log=lambda m: print(m, flush=True), deltas=deltas)
+    front = pareto_front(pts, SEARCH_KEYS)
     ranking = rank(pts, front, (10, 25, 50, 100, 200, 400, 800, 1600))
     for i in front:
         p = pts[i]
         print(f"{p['pipeline']:28s} cr {p['cr']:.4f} enc {p['enc_ms']:.3f} ms dec {p['dec_ms']:.3f} ms "
-              f"s_p {p['s_p'] / 1e9:.0f} GB/s B* {p['b_star'] / 1e9:.0f} GB/s")
+              f"s_p {p['s_p'] / 1e9:.0f} GB/s B* {p['b_star'] / 1e9:.0f} GB/s rel_err {p['rel_err']:.5f}")
     print(json.dumps(ranking), flush=True)
     if args.json:
         with open(args.json, "w") as f:
             json.dump({"workload": args.workload, "layers": args.layers, "tokens": T, "values": args.values,
+                       "deltas": deltas,
                        "rho": args.rho if args.values == "correlated" else None, "reps": args.reps,
                        "points": pts, "front": front, "ranking": ranking}, f, indent=1)
 

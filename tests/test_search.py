@@ -27,6 +27,9 @@ def test_pareto_matches_definition():
         pts = [{"stream_bytes": rng.randrange(grid), "enc_ms": rng.randrange(grid) / 7,
                 "dec_ms": rng.randrange(grid) / 3} for _ in range(n)]
         assert sorted(S.pareto_front(pts)) == PO.pareto_front(pts), trial
+        for q in pts:
+            q["rel_err"] = rng.randrange(grid) / 11
+        assert sorted(S.pareto_front(pts, S.SEARCH_KEYS)) == PO.pareto_front(pts, S.SEARCH_KEYS), trial
 
 
 def test_candidates():
