@@ -191,6 +191,20 @@ def test_corrupt_and_mismatched_streams_are_detected():
     assert e.value.status == K.ERR_CORRUPT_STREAM
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("g", [16, 64, 128])
+@pytest.mark.parametrize("cb", [8192, 65536])
+def test_value_reconstruct_decodes_compressed_chunks(dtype, g, cb):
+    # 2-bit per-token values with the standard pipeline: the reconstruct
+    # kernel decodes their compressed chunks itself, for every group size
+    # and both dtypes; T = 1000 leaves a last chunk whose size is not a
+    # multiple of 4 KiB (decoded by the lossless pass instead)
+    wl = C3.with_(dtype=dtype, v=TP(2, "token", g), chunk_bytes=cb, name="value_chunks")
+    s = run_case(wl, 2, 1000, zero_rich=True, zero_frac=0.5, seed=23)
+    assert s["identical"]
+    assert s["chunks_compressed"] >= 2, s
+
+
 @pytest.mark.parametrize("section", [0, 1])
 def test_zeroed_word_under_a_set_bitmap_bit_is_detected(section):
     # TUPL8_1 -> BIT_8 -> RZE_2 chunks whose bitmap still matches their size
