@@ -42,7 +42,8 @@
  *                   u8 dtype, u8 flags (bit 0: mixed precision, see
  *                   kvc_plan_mixed; other bits 0), i32 layers, tokens, kv_heads, head_dim,
  *                   K policy {u8 bits, u8 axis, u8 hadamard, u8 0, u16 group,
- *                   u16 0}, V policy (same), u64 sign_seed, u8 lossless[4],
+ *                   u16 token-delta run length}, V policy (same), u64 sign_seed,
+ *                   u8 lossless[4],
  *                   u32 chunk_bytes, u64 total_bytes
  *   [64, 64+4n)     chunk table for the K code chunks then the V code chunks:
  *                   bit 31 = stored raw, bits 0..30 = stored bytes
