@@ -162,7 +162,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3_llama70b_32k")
-    ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the oracle's timed sample")
+    ap.add_argument("--cpu-layers", type=int, default=8, help="layers of the oracle's timed sample (about 15 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--values", choices=["gaussian", "zero_rich", "correlated"], default="gaussian",
                     help="value model: the workload's Gaussian KV (headline), KV whose 64-token blocks "
