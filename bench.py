@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--mixed", choices=["none", "mixhq", "mixhq16"], default="none",
                     help="mixed precision per (layer, head): mixhq = heads 0-1 of every layer at 8 bits and the "
                          "others at 2 bits (K and V); mixhq16 = heads 0-1 kept at 16 bits, the others at 2")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="override kv_heads (e.g. 1: one tensor-parallel rank's share of the 70B shape at TP = 8)")
     ap.add_argument("--delta", default="0:0",
                     help="token-delta run lengths K:V before the transform (0 = none, the headline)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30,
@@ -209,6 +211,8 @@ def main():
     if dk or dv:
         import dataclasses
         wl = wl.with_(k=dataclasses.replace(wl.k, delta=dk), v=dataclasses.replace(wl.v, delta=dv))
+    if args.heads:
+        wl = wl.with_(heads=args.heads)
     L, T = wl.layers, wl.tokens
     dev = torch.device("cuda:0")
     log(f"generating {wl.name}: {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype} on {dev}")
@@ -323,7 +327,8 @@ def main():
         "dtype": "f32",
         "data": {"gaussian": "synthetic", "zero_rich": f"synthetic-zero-rich-{args.zero_frac}",
                  "correlated": f"synthetic-correlated-rho-{args.rho}"}[args.values],
-        "config": {"workload": "llama3.1-70b-kv-32k-tokens", "layers": L, "tokens": T, "kv_heads": wl.heads,
+        "config": {"workload": ("llama3.1-70b-kv-32k-tokens" if args.workload == "c3_llama70b_32k" else wl.name)
+                   + (f"-{wl.heads}-heads" if args.heads else ""), "layers": L, "tokens": T, "kv_heads": wl.heads,
                    "head_dim": wl.head_dim, "io_dtype": wl.dtype,
                    "k_policy": f"int{wl.k.bits} per-{wl.k.axis} g{wl.k.group} hadamard",
                    "v_policy": f"int{wl.v.bits} per-{wl.v.axis} g{wl.v.group} hadamard",
@@ -359,7 +364,7 @@ def main():
     result["pages_figures"] = PAGES_FIGURES
     result["selection"] = selection_cost(U, U / (enc_ms * 1e-3), U / (dec_ms * 1e-3), U / n)
     t = (counted_traffic(dom) if (args.workload == "c3_llama70b_32k" and args.values == "gaussian"
-                                   and args.mixed == "none" and not (dk or dv)) else None)
+                                   and args.mixed == "none" and not (dk or dv) and not args.heads) else None)
     if t is not None:
         result["roofline"]["traffic"] = t["bytes"]
         result["roofline"]["traffic_read_write"] = [t["read_bytes"], t["write_bytes"]]
