@@ -69,34 +69,33 @@ typedef int int2v __attribute__((ext_vector_type(2)));
 #define KVC_NARROW_STORE_POLICY 0
 #endif
 constexpr int kLoadPol = KVC_LOAD_POLICY;
-// Grid sizes of the per-token kernels: at most this many blocks, and at least
-// this many tiles per wave, so that each wave's next tile loads while the
-// current one computes.  Measured on the 70B shape: the per-token encoder
-// 1.32 -> 1.28 ms at 80 layers and 52 -> 40 us at one layer with 2048 blocks
-// of at least two tiles per wave instead of 4096 blocks of one or more; the
-// per-token decoder 1.266 -> 1.262 ms.  The per-channel decoder was slower
-// with fewer blocks and keeps 4096.
+// Grid sizes of the fused kernels: at most KVC_*_BLOCKS blocks, and for the
+// per-token ones at least KVC_*_MIN_TILES tiles per wave.  Chosen by
+// measurement on the 70B shape (80 x 32768 x 8 x 128): every kernel runs
+// fastest with many short-lived blocks, whose loads overlap the arithmetic of
+// the other blocks resident on a CU (per-channel encode 1.44 ms at 8192
+// blocks, 1.30 at 65536; per-channel decode 1.41 at 4096, 1.30-1.34 at 65536;
+// per-token decode 1.26 at 2048, 1.21-1.25 at 32768; per-token encode 1.28 at
+// 2048, 1.20 at 65536).  The per-token encoder's waves prefetch their next
+// tile, so it keeps at least two tiles per wave: one layer (8192 tiles) takes
+// 41 us in 1024 blocks against 53 us in 2048 blocks of one tile per wave.
 #ifndef KVC_ET_BLOCKS
-#define KVC_ET_BLOCKS 2048      // per-token encoder
+#define KVC_ET_BLOCKS 65536     // per-token encoder
 #endif
 #ifndef KVC_ET_MIN_TILES
 #define KVC_ET_MIN_TILES 2
 #endif
 #ifndef KVC_DT_BLOCKS
-#define KVC_DT_BLOCKS 2048      // per-token decoder
+#define KVC_DT_BLOCKS 32768     // per-token decoder
 #endif
 #ifndef KVC_DT_MIN_TILES
-#define KVC_DT_MIN_TILES 2
+#define KVC_DT_MIN_TILES 1
 #endif
-// The per-channel encoder has no cross-tile prefetch inside a block: its
-// loads overlap other blocks' arithmetic, and short-lived blocks keep more of
-// them in flight.  70B shape, 80 layers: 1.44 ms at 8192 blocks, 1.30 at 65536
-// (327680 tiles), 1.29 at 131072, 1.36 with one block per tile.
 #ifndef KVC_EK_BLOCKS
-#define KVC_EK_BLOCKS 65536       // per-channel encoder (two-wave blocks)
+#define KVC_EK_BLOCKS 65536     // per-channel encoder (two-wave blocks)
 #endif
 #ifndef KVC_DC_BLOCKS
-#define KVC_DC_BLOCKS (256 * 16)  // per-channel decoder
+#define KVC_DC_BLOCKS 65536     // per-channel decoder
 #endif
 #ifndef KVC_DC_MIN_TILES
 #define KVC_DC_MIN_TILES 1
