@@ -173,6 +173,10 @@ def main():
     ap.add_argument("--mixed", choices=["none", "mixhq", "mixhq16"], default="none",
                     help="mixed precision per (layer, head): mixhq = heads 0-1 of every layer at 8 bits and the "
                          "others at 2 bits (K and V); mixhq16 = heads 0-1 kept at 16 bits, the others at 2")
+    ap.add_argument("--overlap", action="store_true",
+                    help="also time a layer pipeline: layer l encoded on one stream while the other stream "
+                         "decodes layer l - 1 (one-layer calls, an event between them)")
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (e.g. 1: one layer per call)")
     ap.add_argument("--heads", type=int, default=0,
                     help="override kv_heads (e.g. 1: one tensor-parallel rank's share of the 70B shape at TP = 8)")
     ap.add_argument("--delta", default="0:0",
@@ -213,6 +217,8 @@ def main():
         wl = wl.with_(k=dataclasses.replace(wl.k, delta=dk), v=dataclasses.replace(wl.v, delta=dv))
     if args.heads:
         wl = wl.with_(heads=args.heads)
+    if args.layers:
+        wl = wl.with_(layers=args.layers)
     L, T = wl.layers, wl.tokens
     dev = torch.device("cuda:0")
     log(f"generating {wl.name}: {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype} on {dev}")
@@ -297,6 +303,44 @@ def main():
         log(f"graph replay {graph_ms:.3f} ms per step")
     log(f"encode {enc_ms:.3f} ms ({U / enc_ms / 1e6:.1f} GB/s), decode {dec_ms:.3f} ms ({U / dec_ms / 1e6:.1f} GB/s)")
 
+    overlap = None
+    if args.overlap and bits is None:
+        # one-layer calls: layer l is encoded on stream A into its own stream
+        # buffer; stream B waits for that encode's event and decodes it, so
+        # B's decode of layer l overlaps A's encode of layer l + 1
+        p1 = K.Plan(K.config_from_workload(wl, layers=1))
+        ms1, ws1 = p1.sizes(T)
+        bufs = torch.empty((L, ms1), dtype=torch.uint8, device=dev)
+        wa = torch.empty(ws1, dtype=torch.uint8, device=dev)
+        wb = torch.empty(ws1, dtype=torch.uint8, device=dev)
+        sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+        evs = [torch.cuda.Event() for _ in range(L)]
+
+        def pipe(do_enc=True, do_dec=True):
+            sa.wait_stream(s)
+            sb.wait_stream(s)
+            for l in range(L):
+                if do_enc:
+                    p1.encode(k[l], v[l], T, bufs[l], wa, sync=False, stream=sa)
+                    evs[l].record(sa)
+                if do_dec:
+                    if do_enc:
+                        sb.wait_event(evs[l])
+                    p1.decode(bufs[l], ms1, T, kd[l], vd[l], wb, stream=sb)
+            s.wait_stream(sa)
+            s.wait_stream(sb)
+
+        pipe_ms = timed(pipe)
+        enc1_ms = timed(lambda: pipe(True, False))
+        dec1_ms = timed(lambda: pipe(False, True))
+        assert p1.query_status(wa) == K.OK and p1.query_status(wb) == K.OK
+        overlap = {"ms_per_step": round(pipe_ms, 4), "GBps": round(U / pipe_ms / 1e6, 3),
+                   "encode_ms": round(enc1_ms, 4), "encode_GBps": round(U / enc1_ms / 1e6, 3),
+                   "decode_ms": round(dec1_ms, 4), "decode_GBps": round(U / dec1_ms / 1e6, 3),
+                   "calls": f"{L} one-layer encodes on one stream, {L} one-layer decodes on another"}
+        log(f"layer pipeline {pipe_ms:.3f} ms ({U / pipe_ms / 1e6:.1f} GB/s); one-layer calls alone: "
+            f"encode {enc1_ms:.3f} ms, decode {dec1_ms:.3f} ms")
+
     # roofline of the dominant fused kernel, algorithmic bytes per launch
     elems = L * T * wl.heads * wl.head_dim
     per_k = elems * fused_bytes_per_elem(wl.k) if bits is None else mixed_bytes(bits[0], wl.k, elems)
@@ -328,7 +372,8 @@ def main():
         "data": {"gaussian": "synthetic", "zero_rich": f"synthetic-zero-rich-{args.zero_frac}",
                  "correlated": f"synthetic-correlated-rho-{args.rho}"}[args.values],
         "config": {"workload": ("llama3.1-70b-kv-32k-tokens" if args.workload == "c3_llama70b_32k" else wl.name)
-                   + (f"-{wl.heads}-heads" if args.heads else ""), "layers": L, "tokens": T, "kv_heads": wl.heads,
+                   + (f"-{wl.heads}-heads" if args.heads else "") + (f"-{L}-layers" if args.layers else ""),
+                   "layers": L, "tokens": T, "kv_heads": wl.heads,
                    "head_dim": wl.head_dim, "io_dtype": wl.dtype,
                    "k_policy": f"int{wl.k.bits} per-{wl.k.axis} g{wl.k.group} hadamard",
                    "v_policy": f"int{wl.v.bits} per-{wl.v.axis} g{wl.v.group} hadamard",
@@ -340,6 +385,7 @@ def main():
         "encode_frac_hbm_peak": round(U / enc_ms / 1e6 / HBM_PEAK_GBPS, 4),
         "decode_frac_hbm_peak": round(U / dec_ms / 1e6 / HBM_PEAK_GBPS, 4),
         "compression_ratio": round(U / n, 4),
+        "layer_pipeline": overlap,
         "compression_ratio_quant": round(U / codes_params, 4),
         "compression_ratio_lossless": round(codes_params / n, 4),
         "stream_bytes": n,
@@ -364,7 +410,8 @@ def main():
     result["pages_figures"] = PAGES_FIGURES
     result["selection"] = selection_cost(U, U / (enc_ms * 1e-3), U / (dec_ms * 1e-3), U / n)
     t = (counted_traffic(dom) if (args.workload == "c3_llama70b_32k" and args.values == "gaussian"
-                                   and args.mixed == "none" and not (dk or dv) and not args.heads) else None)
+                                   and args.mixed == "none" and not (dk or dv) and not args.heads
+                                   and not args.layers) else None)
     if t is not None:
         result["roofline"]["traffic"] = t["bytes"]
         result["roofline"]["traffic_read_write"] = [t["read_bytes"], t["write_bytes"]]
