@@ -655,6 +655,23 @@ __global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t
   }
 }
 
+// Whether every chunk of a one-request call goes to the word-parallel
+// kernels (a standard pipeline, and every chunk size a multiple of its
+// block): then the stage engine's worklist stays empty and it is not launched.
+static bool all_word_parallel(const CallDesc& c) {
+  const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
+  const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
+  if (c.R != 1 || !(p1 || p2)) return false;
+  const int64_t blk = p1 ? 4096 : 1024;
+  for (int w = 0; w < 2; ++w) {
+    const int64_t cb = c.one.codes_bytes[w];
+    if (cb == 0) continue;
+    const int64_t last = cb - (int64_t)(c.one.nchunks[w] - 1) * c.chunk_bytes;
+    if (last % blk) return false;
+  }
+  return true;
+}
+
 hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
   if (c.total_chunks == 0) return hipSuccess;
   uint32_t* worklist = (uint32_t*)(c.chunk_offs + c.total_chunks + 1);
@@ -662,6 +679,7 @@ hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
   k_ll_sizes<<<grid, 256, 0, s>>>(c, worklist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (all_word_parallel(c)) return hipSuccess;
   k_ll_encode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
   return hipGetLastError();
 }
@@ -1464,6 +1482,7 @@ hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s) {
   if (p1) k_ll_decode_p1<<<fgrid, 256, 0, s>>>(c, worklist);
   else if (p2) k_ll_decode_p2<<<fgrid, 256, 0, s>>>(c, worklist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (all_word_parallel(c)) return hipSuccess;
   k_ll_decode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
   return hipGetLastError();
 }
