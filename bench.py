@@ -186,8 +186,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the compression path runs on one device and this build "
-              "has no multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the compression path runs on one device and has no "
+              "multi-GPU mode; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -76,7 +76,7 @@ typedef struct kvc_plan_s* kvc_plan_t;
 typedef enum {
   KVC_OK = 0,
   KVC_ERR_INVALID_ARG = 1,      /* NULL pointer, bad shape, bad policy value */
-  KVC_ERR_UNSUPPORTED = 2,      /* valid policy this build does not run on the GPU */
+  KVC_ERR_UNSUPPORTED = 2,      /* valid policy the GPU kernels do not implement */
   KVC_ERR_NO_MEMORY = 3,        /* host allocation failed */
   KVC_ERR_BUFFER_TOO_SMALL = 4, /* output capacity or workspace too small */
   KVC_ERR_CORRUPT_STREAM = 5,   /* stream fails validation (device-detected) */
