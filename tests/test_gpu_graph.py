@@ -54,3 +54,45 @@ def test_encode_decode_replay_in_a_graph(stages):
         assert torch.equal(kd2, kref) and torch.equal(vd2, vref), f"replay {rep}: reconstruction differs"
         assert plan.query_status(ws2) == K.OK
         log(f"replay {rep} identical ({n} stream bytes)")
+
+
+def test_one_plan_on_two_streams_at_once():
+    # a plan is immutable: calls on two streams with their own workspaces may
+    # run at the same time (here one stream encodes layer l while the other
+    # decodes layer l - 1, ordered only by events), and every stream and
+    # reconstruction equals the one-stream result
+    wl = W.WORKLOADS["c3_llama70b_32k"].with_(chunk_bytes=65536)
+    L, T = 6, 2048
+    k, v = W.zero_rich_kv(wl, L, T, seed=31, device=DEV, zero_frac=0.5)
+    plan = K.Plan(K.config_from_workload(wl, max_tokens=T, layers=1))
+    ms, wsb = plan.sizes(T)
+    ref_streams, ref_k, ref_v = [], [], []
+    ws0 = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    for l in range(L):
+        out = torch.empty(ms, dtype=torch.uint8, device=DEV)
+        n = plan.encode(k[l], v[l], T, out, ws0)
+        ref_streams.append(out[:n].clone())
+        kd, vd = torch.empty_like(k[l]), torch.empty_like(v[l])
+        plan.decode(out, n, T, kd, vd, ws0)
+        ref_k.append(kd)
+        ref_v.append(vd)
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    wa = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    wb = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    bufs = torch.empty((L, ms), dtype=torch.uint8, device=DEV)
+    kd, vd = torch.empty_like(k), torch.empty_like(v)
+    evs = [torch.cuda.Event() for _ in range(L)]
+    sa.wait_stream(torch.cuda.current_stream())
+    sb.wait_stream(torch.cuda.current_stream())
+    for l in range(L):
+        plan.encode(k[l], v[l], T, bufs[l], wa, sync=False, stream=sa)
+        evs[l].record(sa)
+        sb.wait_event(evs[l])
+        plan.decode(bufs[l], ms, T, kd[l], vd[l], wb, stream=sb)
+    torch.cuda.synchronize()
+    assert plan.query_status(wa) == K.OK and plan.query_status(wb) == K.OK
+    for l in range(L):
+        n = ref_streams[l].numel()
+        assert torch.equal(bufs[l, :n], ref_streams[l]), l
+        assert torch.equal(kd[l], ref_k[l]) and torch.equal(vd[l], ref_v[l]), l
