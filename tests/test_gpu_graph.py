@@ -3,7 +3,8 @@ capture on the current stream) and replayed: the library's dense calls
 enqueue only kernels (no host synchronization, no memset or copy nodes), so a
 serving loop can capture them.  Every replay must reproduce the eager
 stream byte for byte and the eager reconstruction bit for bit; eager work
-and synchronizations run between the replays."""
+and synchronizations run between the replays.  Also: one plan used from two
+streams at once, each with its own workspace."""
 import pytest
 import torch
 
