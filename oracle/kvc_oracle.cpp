@@ -51,34 +51,37 @@ extern "C" float kvco_f16_to_f32(uint16_t h) {
   return sign ? -f : f;
 }
 
-/* binary32 -> binary16, round to nearest, ties to even.  Works on the exact
- * value: finds the two neighbouring fp16 values by search over the ordered
- * bit patterns and picks the nearer one.  Slow and obviously correct. */
-static double f16_value(uint16_t h) { return (double)kvco_f16_to_f32(h); }
-
+/* binary32 -> binary16, round to nearest, ties to even (IEEE 754 default
+ * rounding), done on the bit fields.  The binary32 value is
+ * (1.M) * 2^(E-127) for 0 < E < 255; binary16 normals have exponent field
+ * E - 112 in [1, 30] and keep the top 10 of M's 23 bits, subnormals are
+ * integer multiples of 2^-24.  Rounding looks at the dropped bits: above half
+ * of the kept unit rounds up, exactly half rounds to the even neighbour.  A
+ * carry out of the mantissa moves to the next exponent (or from the largest
+ * subnormal to the smallest normal), which is what the bit layout gives. */
 extern "C" uint16_t kvco_f32_to_f16_rn(float f) {
-  if (std::isnan(f)) return (uint16_t)(0x7e00u | ((f2u(f) >> 16) & 0x8000u));
-  uint16_t sign = (f2u(f) >> 31) ? 0x8000 : 0;
-  double a = std::fabs((double)f);
-  /* magnitudes >= 65520 round to infinity (65504 + half its ulp of 32) */
-  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00);
-  /* binary search the largest finite magnitude pattern p with value(p) <= a */
-  uint16_t lo = 0, hi = 0x7bff;
-  while (lo < hi) {
-    uint16_t mid = (uint16_t)((lo + hi + 1) / 2);
-    if (f16_value(mid) <= a) lo = mid; else hi = (uint16_t)(mid - 1);
+  const uint32_t u = f2u(f);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t E = (u >> 23) & 0xffu, M = u & 0x7fffffu;
+  if (E == 0xffu && M != 0) return (uint16_t)(sign | 0x7e00u);            /* NaN -> quiet NaN */
+  /* |f| >= 65520 = 65504 + half an ulp rounds to infinity (the tie goes to the
+   * even neighbour 65536, which does not exist as a finite fp16) */
+  if ((u & 0x7fffffffu) >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);
+  if (E >= 113) {                                   /* binary16 normal range */
+    uint32_t h = ((E - 112) << 10) | (M >> 13);
+    const uint32_t rem = M & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1;
+    return (uint16_t)(sign | h);
   }
-  uint16_t p = lo;
-  double below = f16_value(p);
-  if (below == a) return (uint16_t)(sign | p);
-  uint16_t q = (uint16_t)(p + 1);                        /* next magnitude (0x7c00 = inf) */
-  double above = (q == 0x7c00) ? 65536.0 : f16_value(q);
-  double d_below = a - below, d_above = above - a;
-  uint16_t pick;
-  if (d_below < d_above) pick = p;
-  else if (d_above < d_below) pick = q;
-  else pick = (p & 1) ? q : p;                           /* tie: even mantissa */
-  return (uint16_t)(sign | pick);
+  /* subnormal (or zero) result: n = |f| / 2^-24 = (1.M) * 2^(E - 103), an
+   * integer part of (2^23 + M) >> s with s = 126 - E, rounded */
+  if (E < 102) return sign;                         /* |f| < 2^-25: below half the smallest subnormal */
+  const uint32_t mant = M | 0x800000u;
+  const uint32_t s = 126 - E;                       /* 14 .. 24 */
+  uint32_t n = mant >> s;
+  const uint32_t rem = mant & ((1u << s) - 1u), half = 1u << (s - 1);
+  if (rem > half || (rem == half && (n & 1u))) n += 1;
+  return (uint16_t)(sign | n);
 }
 
 /* next representable fp16 toward +inf / -inf */
@@ -232,12 +235,17 @@ extern "C" int kvco_fwht(float* v, int n) {
  *       m  = RD16(lo),
  *       s  = RU16( RU32( RU32(hi - m) / (2^b - 1) ) ),
  *       inv = 1/s rounded to nearest binary32 (0 when s == 0).
- * Returns KVCO_ERR_RANGE when m or s is not a finite fp16. */
+ * Returns KVCO_ERR_RANGE when m or s is not a finite fp16, and when any z is
+ * infinite or NaN (the pages define no codes for such values; with the
+ * Hadamard on, one non-finite input value makes every transform output of
+ * its head vector non-finite, so every group it reaches reports it). */
 extern "C" int kvco_group_params(const float* z, int count, int bits, float c,
                                  uint16_t* s_out, uint16_t* m_out, float* inv_out) {
   if (!z || count < 1 || !(bits == 2 || bits == 4 || bits == 8)) return KVCO_ERR_INVALID_ARG;
   float zmin = z[0], zmax = z[0];
-  for (int i = 1; i < count; ++i) {
+  bool nonfinite = false;
+  for (int i = 0; i < count; ++i) {
+    if (!std::isfinite(z[i])) nonfinite = true;
     if (z[i] < zmin) zmin = z[i];
     if (z[i] > zmax) zmax = z[i];
   }
@@ -256,7 +264,7 @@ extern "C" int kvco_group_params(const float* z, int count, int bits, float c,
   if (s_out) *s_out = s;
   if (m_out) *m_out = m;
   if (inv_out) *inv_out = (sf == 0.0f) ? 0.0f : 1.0f / sf;
-  if (!std::isfinite(mf) || !std::isfinite(sf) || std::isnan(lo) || std::isnan(hi)) return KVCO_ERR_RANGE;
+  if (nonfinite || !std::isfinite(mf) || !std::isfinite(sf) || std::isnan(lo) || std::isnan(hi)) return KVCO_ERR_RANGE;
   return KVCO_OK;
 }
 
@@ -466,27 +474,33 @@ extern "C" int kvco_quantize_tensor(const kvco_cfg* cfg, int which, const uint16
   return status;
 }
 
-/* Reconstruction of one head vector from its dequantized (already
- * normalization-scaled) values w: inverse Hadamard, sign restoration, rounding
- * to the 16-bit dtype.  The orthonormal inverse of c*H*diag(d) is
- * diag(d)*H*c; the factor c is folded into the group parameters
- * (sigma = fl32(s*c), mu = fl32(m*c)) so that dequantization already
- * yields c*y.  Reading: FastKVComp Sec. 4.1 lists dequantization, inverse
- * Hadamard, normalization and sign restoration as one fused operator without
- * an evaluation order; this order is ours. */
-static void inverse_vector(float* w, int D, int dtype, const Pol& p, const int8_t* signs, uint16_t* out) {
+/* Reconstruction of one head vector from its dequantized values w (in the
+ * transform domain, unnormalized grid: w = q*s + m): the inverse of the
+ * orthonormal rotation c*H*diag(d) is diag(d)*c*H, applied as the pages list
+ * the fused reconstruction's steps (FastKVComp Sec. 4.1, "Fused
+ * Reconstruction": dequantization, inverse Hadamard transformation,
+ * normalization, sign restoration): the FWHT in the same fixed stage order as
+ * the forward transform, then the product with c (rounded once), then the
+ * sign, then rounding to the 16-bit dtype (nearest, ties to even). */
+static void inverse_vector(float* w, int D, int dtype, const Pol& p, float c, const int8_t* signs, uint16_t* out) {
   if (p.had) kvco_fwht(w, D);
   for (int i = 0; i < D; ++i) {
-    float f = p.had ? w[i] * (float)signs[i] : w[i];
+    float f = w[i];
+    if (p.had) {
+      f = f * c;                                   /* normalization */
+      f = f * (float)signs[i];                     /* sign restoration (exact) */
+    }
     out[i] = store16(f, dtype);
   }
 }
 
-static void dequant_params(const uint8_t* params, int64_t g, float c, float* sigma, float* mu) {
+/* Dequantization of one group's parameters: the stored fp16 scale and
+ * minimum as binary32 (exact). */
+static void dequant_params(const uint8_t* params, int64_t g, float* sigma, float* mu) {
   uint16_t s, m;
   get_params(params, g, &s, &m);
-  *sigma = kvco_f16_to_f32(s) * c;
-  *mu = kvco_f16_to_f32(m) * c;
+  *sigma = kvco_f16_to_f32(s);
+  *mu = kvco_f16_to_f32(m);
 }
 
 extern "C" int kvco_dequantize_tensor(const kvco_cfg* cfg, int which, const uint8_t* codes,
@@ -507,11 +521,11 @@ extern "C" int kvco_dequantize_tensor(const kvco_cfg* cfg, int which, const uint
       const uint8_t* row = codes + vec * D * p.bits / 8;
       for (int g = 0; g < NGv; ++g) {
         float sigma, mu;
-        dequant_params(params, vec * NGv + g, c, &sigma, &mu);
+        dequant_params(params, vec * NGv + g, &sigma, &mu);
         for (int i = 0; i < G; ++i)
           w[g * G + i] = std::fmaf((float)get_code(row, g * G + i, p.bits), sigma, mu);
       }
-      inverse_vector(w.data(), D, cfg->dtype, p, signs.data(), x + vec * D);
+      inverse_vector(w.data(), D, cfg->dtype, p, c, signs.data(), x + vec * D);
     }
     return KVCO_OK;
   }
@@ -526,14 +540,14 @@ extern "C" int kvco_dequantize_tensor(const kvco_cfg* cfg, int which, const uint
       const int64_t cb = col_bytes(gg, p.bits);
       for (int h = 0; h < H; ++h) {
         for (int ch = 0; ch < D; ++ch)
-          dequant_params(params, (((int64_t)l * NG + g) * H + h) * D + ch, c, &sig[ch], &mus[ch]);
+          dequant_params(params, (((int64_t)l * NG + g) * H + h) * D + ch, &sig[ch], &mus[ch]);
         for (int tt = 0; tt < gg; ++tt) {
           for (int ch = 0; ch < D; ++ch) {
             const uint8_t* src = codes + off + ((int64_t)h * D + ch) * cb;
             w[ch] = std::fmaf((float)get_code(src, tt, p.bits), sig[ch], mus[ch]);
           }
           const int64_t vec = ((int64_t)l * T + (int64_t)g * G + tt) * H + h;
-          inverse_vector(w.data(), D, cfg->dtype, p, signs.data(), x + vec * D);
+          inverse_vector(w.data(), D, cfg->dtype, p, c, signs.data(), x + vec * D);
         }
       }
       off += (int64_t)H * D * cb;

@@ -44,6 +44,32 @@ def test_f32_to_f16_rn_matches_numpy():
     assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
 
 
+def test_f32_to_f16_rn_every_pattern_and_midpoint_matches_numpy():
+    """Round to nearest-even on the bit fields, against numpy's conversion at
+    every fp16 value of both signs, at every exact midpoint between
+    neighbours (ties) and one binary32 step either side of each, and one
+    step either side of each value."""
+    L = O.lib()
+    h = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)       # finite magnitudes
+    lo = h.view(np.float16).astype(np.float64)
+    hi = np.append(lo[1:], 65536.0)
+    mid = ((lo + hi) / 2).astype(np.float32)                            # exact in binary32
+    assert np.all(mid.astype(np.float64) == (lo + hi) / 2)
+    f = lo.astype(np.float32)
+    x = np.concatenate([f, mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(np.inf)),
+                        np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(0)),
+                        np.array([np.inf, 2.0 ** -25, 2.0 ** -26, 1e-45, 3.0 * 2.0 ** -26], np.float32)])
+    x = np.concatenate([x, -x]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    fn = L.kvco_f32_to_f16_rn
+    got = np.fromiter((fn(float(v)) for v in x), dtype=np.uint16, count=x.size)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:5]]
+    nan = fn(float("nan"))
+    assert (nan & 0x7C00) == 0x7C00 and (nan & 0x3FF) != 0
+
+
 def test_f32_to_f16_directed_rounding_exact():
     L = O.lib()
     rng = np.random.default_rng(2)
