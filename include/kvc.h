@@ -10,7 +10,9 @@
  *            and a compacted write of the final stream;
  *   decode:  lossless decode, then a fused dequantize + inverse Hadamard +
  *            normalization + sign restoration kernel (Sec. 4.1, fused
- *            reconstruction).
+ *            reconstruction), applied in that order: x = d * fl32(c * H w),
+ *            w = q * s + m (one fused multiply-add), c = fl32(1/sqrt(128)),
+ *            rounded to the 16-bit type to nearest-even.
  *
  * FastKVComp Sec. 4.2 describes the runtime as device-pointer encode/decode
  * calls that keep the bitstream on the GPU, reuse persistent scratch and send
@@ -27,7 +29,8 @@
  *     [layers][num_blocks][page_tokens][kv_heads][head_dim].
  *   - Argument errors are detected on the host and returned before anything
  *     is enqueued.  Errors only the device can see (corrupt stream, fp16
- *     parameter overflow) are recorded in a status word inside the workspace;
+ *     parameter overflow, non-finite input values) are recorded in a status
+ *     word inside the workspace;
  *     they are returned by kvc_encode when h_out_bytes is non-NULL and
  *     otherwise by kvc_query_status.
  *   - No exceptions cross the ABI.  kvc_last_error() returns a thread-local
@@ -81,7 +84,9 @@ typedef enum {
   KVC_ERR_BUFFER_TOO_SMALL = 4, /* output capacity or workspace too small */
   KVC_ERR_CORRUPT_STREAM = 5,   /* stream fails validation (device-detected) */
   KVC_ERR_PLAN_MISMATCH = 6,    /* stream header differs from the plan / tokens */
-  KVC_ERR_RANGE = 7,            /* a quantization parameter is not a finite fp16 */
+  KVC_ERR_RANGE = 7,            /* a quantization parameter is not a finite fp16, or an
+                                   input value is infinite or NaN (device-detected: the
+                                   stream is then not decodable) */
   KVC_ERR_HIP = 8               /* a HIP runtime call failed */
 } kvc_status;
 

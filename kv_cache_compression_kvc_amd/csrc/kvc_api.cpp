@@ -357,7 +357,7 @@ kvc_status device_status(uint32_t bits) {
   if (bits & kStMismatch) return fail(KVC_ERR_PLAN_MISMATCH, "stream header does not match the plan or token count");
   if (bits & kStCorrupt) return fail(KVC_ERR_CORRUPT_STREAM, "stream failed validation on the device");
   if (bits & kStBadBlock) return fail(KVC_ERR_INVALID_ARG, "block table entry out of range");
-  if (bits & kStRange) return fail(KVC_ERR_RANGE, "a quantization parameter is not a finite fp16 value");
+  if (bits & kStRange) return fail(KVC_ERR_RANGE, "a quantization parameter is not a finite fp16 value (or an input value is infinite or NaN)");
   if (bits & kStStall) return fail(KVC_ERR_HIP, "single-pass placement: a wait ran out or a chunk size disagreed");
   return KVC_OK;
 }

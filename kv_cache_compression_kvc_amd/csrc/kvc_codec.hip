@@ -6,9 +6,9 @@
 // seeded sign flip and a Hadamard transform over head_dim, computes per-group
 // min/max, derives fp16 (scale, minimum) parameters and writes packed 2/4/8-bit
 // codes, all in one pass over the input; no transformed tensor is written to
-// HBM.  The decoder dequantizes, applies the inverse transform with the
-// normalization folded into the group parameters, restores the signs and
-// writes 16-bit values.
+// HBM.  The decoder dequantizes, applies the inverse transform, normalizes,
+// restores the signs and writes 16-bit values, in the order the page lists
+// the steps of its fused reconstruction.
 //
 // Arithmetic (fixed so that results are reproducible bit for bit):
 //   z      = unnormalized Walsh-Hadamard transform of d*x in binary32, stages
@@ -17,7 +17,9 @@
 //   m      = lo rounded down to fp16;  s = ((hi - m) rounded up) / (2^b - 1)
 //            rounded up to binary32, then up to fp16;  inv = 1/s (0 if s = 0);
 //   q      = round-half-even( fma(z, c, -m) * inv ), product exact;
-//   decode = d * FWHT( fma(q, fl(s*c), fl(m*c)) ), rounded to nearest-even.
+//   decode = d * fl( c * FWHT( fma(q, s, m) ) ), rounded to nearest-even
+//            (the sign commutes with round-to-nearest-even, so it is applied
+//            to the 16-bit result).
 // Directed roundings use error-free transforms (TwoProduct with fma, TwoSum).
 //
 // Work layout.  A head vector (128 channels) is held by two lanes, 64 values
@@ -252,28 +254,22 @@ __device__ __forceinline__ GroupQ group_params(float zmin, float zmax, float c) 
   return g;
 }
 
-// min / max without NaN canonicalization of the operands: every value reduced
-// here is the result of arithmetic (never a signaling NaN)
+// min / max in the sense of IEEE 754-2019 minimum / maximum (gfx950's
+// v_minimum3_f32 / v_maximum3_f32): a NaN operand gives NaN, so one
+// non-finite transform output anywhere in a group makes its parameters
+// non-finite and the group is reported as out of range; -0 orders below +0.
 __device__ __forceinline__ float vmin3(float a, float b, float c) {
   float r;
-  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  asm("v_minimum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
   float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  asm("v_maximum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
-__device__ __forceinline__ float vmin(float a, float b) {
-  float r;
-  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float vmax(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+__device__ __forceinline__ float vmin(float a, float b) { return vmin3(a, b, b); }
+__device__ __forceinline__ float vmax(float a, float b) { return vmax3(a, b, b); }
 // min and max of n >= 1 values
 template <int N>
 __device__ __forceinline__ void minmax_n(const float* x, float& mn, float& mx) {
@@ -395,6 +391,13 @@ __device__ __forceinline__ void fwht_cross(float* v) {
     v[r] = a;
     v[r + 32] = b;
   }
+}
+
+// Normalization of a lane's 64 inverse-transform outputs: the product with
+// c = fl32(1/sqrt(128)), rounded once.
+__device__ __forceinline__ void normalize64(float* v, float c) {
+#pragma unroll
+  for (int r = 0; r < 64; ++r) v[r] = v[r] * c;
 }
 
 // value of the partner lane (L xor 32)
@@ -1115,8 +1118,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
     float sg[NLG], mu[NLG];
 #pragma unroll
     for (int j = 0; j < NLG; ++j) {
-      sg[j] = f_from_h16(q.pw[j] & 0xffffu) * cc;
-      mu[j] = f_from_h16(q.pw[j] >> 16) * cc;
+      sg[j] = f_from_h16(q.pw[j] & 0xffffu);
+      mu[j] = f_from_h16(q.pw[j] >> 16);
     }
     float f[64];
 #pragma unroll
@@ -1124,6 +1127,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
 
     fwht64_inreg(f);
     fwht_cross(f);
+    normalize64(f, cc);
     stage_out<BF16>(f, wl, sm, make_rsrc(t.dst, t.nvo ? (uint32_t)(t.nvo - 1) * t.vstride + 256u : 0u), t.vstride);
   }
 }
@@ -1217,8 +1221,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_token_m(CallDesc c, int which
     float sg[NLG], mu[NLG];
 #pragma unroll
     for (int j = 0; j < NLG; ++j) {
-      sg[j] = f_from_h16(q.pw[j] & 0xffffu) * cc;
-      mu[j] = f_from_h16(q.pw[j] >> 16) * cc;
+      sg[j] = f_from_h16(q.pw[j] & 0xffffu);
+      mu[j] = f_from_h16(q.pw[j] >> 16);
     }
     float f[64];
 #pragma unroll
@@ -1226,6 +1230,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_token_m(CallDesc c, int which
 
     fwht64_inreg(f);
     fwht_cross(f);
+    normalize64(f, cc);
     stage_out<BF16>(f, wl, sm, make_rsrc(t.dst, t.nvo ? (uint32_t)(t.nvo - 1) * t.vstride + 256u : 0u), t.vstride);
   }
 }
@@ -1676,8 +1681,8 @@ __global__ __launch_bounds__(256, 4) void k_decode_channel(CallDesc c, int which
     float f[64];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const float sg = f_from_h16(q.pw[p] & 0xffffu) * cc;
-      const float mu = f_from_h16(q.pw[p] >> 16) * cc;
+      const float sg = f_from_h16(q.pw[p] & 0xffffu);
+      const float mu = f_from_h16(q.pw[p] >> 16);
       // rows of tokens past the end hold finite filler that is never stored
 #pragma unroll
       for (int i = 0; i < 32; ++i) zw[i * RP + lane] = __builtin_fmaf(unpack_code<BITS>(q.w[p], i), sg, mu);
@@ -1694,6 +1699,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_channel(CallDesc c, int which
     }
     fwht64_inreg(f);
     fwht_cross(f);
+    normalize64(f, cc);
     uint16_t* dst = out + (((int64_t)l * T + t0) * H + h) * kHeadDim;
     stage_out<BF16>(f, stg, sm, make_rsrc(dst, nvw ? (uint32_t)(nvw - 1) * vstride + 256u : 0u), vstride);
   }

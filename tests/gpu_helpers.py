@@ -166,6 +166,9 @@ def assert_encode_parity(stats):
     assert not stats.get("lossless_mismatch"), "codes equal but lossless bytes differ"
     if stats["identical"]:
         return
+    # the fp16 (scale, minimum) words follow the same min / max rule on both
+    # sides: they must be equal even where a code sits on a rounding tie
+    assert stats["param_diffs"] == 0, stats
     assert stats["max_code_diff"] <= 1, stats
     assert stats["code_diffs"] <= 1e-5 * stats["ncodes"], stats
 

@@ -120,8 +120,8 @@ def test_llama70b_32k_full_size_sampled_layers():
 
 
 def test_llama70b_128k_full_size_sampled_layer():
-    # fp16 outputs: the oracle's plain fp16 rounding is slow, so a token prefix
-    check_dense_full("c5_llama70b_128k", [37], Tp=8192)
+    # one whole layer of 131072 tokens (both fp16 tensors, 268 MB of K+V)
+    check_dense_full("c5_llama70b_128k", [37])
 
 
 def stream_chunks(stream: np.ndarray, wl, L, T):
@@ -185,7 +185,15 @@ def test_llama70b_32k_full_size_compressible_sampled_layers():
     free()
 
 
-def test_paged_llama8b_full_size_sampled_requests():
+def test_paged_llama8b_full_size_every_request():
+    """The whole paged batch (64 requests, 1024..16384 tokens, pages scattered
+    over the pool) encoded and decoded in one call each.  Every request is
+    checked on the GPU: its gathered pages encoded by a one-request dense call
+    must give its stream byte for byte, and that stream's dense decode must
+    equal what the paged decode scattered through the second page map.  The
+    shortest, a median and the longest request are also compared with the
+    oracle (stream bytes and reconstruction), in parallel host threads."""
+    from concurrent.futures import ThreadPoolExecutor
     wl = W.WORKLOADS["c4_paged_llama8b"]
     batch = W.paged_layout(wl)
     R = len(batch.seq_lens)
@@ -209,28 +217,57 @@ def test_paged_llama8b_full_size_sampled_requests():
     plan.decode_paged(out, n, offs, dst.seq_lens, kq, vq, dst.num_blocks, btd, ws)
     assert plan.query_status(ws) == K.OK
     offs_h = offs.cpu().numpy()
+    assert int(offs_h[R]) == n
     P = wl.page_tokens
-    order = np.argsort(batch.seq_lens)
-    sample = [int(order[0]), int(order[1])]            # the oracle's fp16 rounding is slow
+
+    def gather(pool, table, r, T):
+        npg = (T + P - 1) // P
+        blocks = table[r, :npg].long()
+        return pool[:, blocks].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T].contiguous()
+
+    order = np.argsort(batch.seq_lens, kind="stable")
+    sample = [int(order[0]), int(order[R // 2]), int(order[-1])]
+    inputs = {r: (to_u16(gather(kp, bt, r, int(batch.seq_lens[r]))),
+                  to_u16(gather(vp, bt, r, int(batch.seq_lens[r])))) for r in sample}
     cfg = O.cfg_from_workload(wl)
+
+    def oracle_job(r):
+        T = int(batch.seq_lens[r])
+        st, ref = O.encode(cfg, inputs[r][0], inputs[r][1], T)
+        st2, kr, vr = O.decode(ref, wl.layers * T * wl.heads * wl.head_dim)
+        return st, ref, st2, kr, vr
+
+    pool = ThreadPoolExecutor(max_workers=len(sample))          # the oracle's ctypes calls release the GIL
+    futs = {r: pool.submit(oracle_job, r) for r in sample}
+    log(f"c4: oracle running on requests {sample} ({[int(batch.seq_lens[r]) for r in sample]} tokens)")
+
+    for r in range(R):
+        T = int(batch.seq_lens[r])
+        kin, vin = gather(kp, bt, r, T), gather(vp, bt, r, T)
+        p1 = K.Plan(K.config_from_workload(wl, max_tokens=T))
+        ms1, ws1 = p1.sizes(T)
+        o1 = torch.empty(ms1, dtype=torch.uint8, device=DEV)
+        w1 = torch.empty(ws1, dtype=torch.uint8, device=DEV)
+        n1 = p1.encode(kin, vin, T, o1, w1)
+        assert n1 == int(offs_h[r + 1] - offs_h[r]), f"request {r}: stream size differs"
+        assert torch.equal(o1[:n1], out[int(offs_h[r]):int(offs_h[r + 1])]), f"request {r}: stream differs"
+        kd, vd = torch.empty_like(kin), torch.empty_like(vin)
+        p1.decode(o1, n1, T, kd, vd, w1)
+        assert p1.query_status(w1) == K.OK
+        assert torch.equal(kd.view(torch.int16), gather(kq, btd, r, T).view(torch.int16)), f"request {r}: K pages"
+        assert torch.equal(vd.view(torch.int16), gather(vq, btd, r, T).view(torch.int16)), f"request {r}: V pages"
+        del kin, vin, kd, vd, o1, w1
+    log(f"c4: all {R} requests equal their dense encodes and decodes ({time.time() - t0:.1f} s)")
+
     for r in sample:
         T = int(batch.seq_lens[r])
-        npg = (T + P - 1) // P
-        log(f"c4: request {r} ({T} tokens): oracle encode + decode")
-        blocks = bt[r, :npg].long()
-        kr_in = kp[:, blocks].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T]
-        vr_in = vp[:, blocks].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T]
-        st, ref = O.encode(cfg, to_u16(kr_in), to_u16(vr_in), T)
-        assert st == O.OK
+        st, ref, st2, kr, vr = futs[r].result()
+        assert st == O.OK and st2 == O.OK
         got = out[int(offs_h[r]):int(offs_h[r + 1])].cpu().numpy()
-        assert np.array_equal(got, ref), f"request {r}: stream differs"
-        st, kr, vr = O.decode(ref, wl.layers * T * wl.heads * wl.head_dim)
-        assert st == O.OK
-        bd = btd[r, :npg].long()
-        kg = kq[:, bd].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T]
-        vg = vq[:, bd].reshape(wl.layers, npg * P, wl.heads, wl.head_dim)[:, :T]
-        assert np.array_equal(to_u16(kg).reshape(-1), kr), f"request {r}: K reconstruction differs"
-        assert np.array_equal(to_u16(vg).reshape(-1), vr), f"request {r}: V reconstruction differs"
-        log(f"c4: request {r} identical ({time.time() - t0:.1f} s)")
+        assert np.array_equal(got, ref), f"request {r}: stream differs from the oracle's"
+        assert np.array_equal(to_u16(gather(kq, btd, r, T)).reshape(-1), kr), f"request {r}: K reconstruction"
+        assert np.array_equal(to_u16(gather(vq, btd, r, T)).reshape(-1), vr), f"request {r}: V reconstruction"
+        log(f"c4: request {r} ({T} tokens) identical to the oracle ({time.time() - t0:.1f} s)")
+    pool.shutdown()
     del kp, vp, kq, vq, out, ws
     free()

@@ -40,12 +40,21 @@ def run_case(wl, L, T, seed=1, zero_rich=False, check_decode=True, zero_frac=0.9
         n = L * T * wl.heads * wl.head_dim
         st, kd, vd = O.decode(ref, n)
         assert st == O.OK
+        # the GPU decoder on the oracle's stream: bit for bit
         st, kg, vg = gpu_decode(plan, ref, wl, T, L)
         assert st == K.OK, K.status_string(st)
         ek = assert_values_close(to_u16(kg).reshape(-1), kd, wl.dtype)
         ev = assert_values_close(to_u16(vg).reshape(-1), vd, wl.dtype)
         log(f"  decode exact fraction K {ek:.6f} V {ev:.6f}")
         assert ek == 1.0 and ev == 1.0
+        # the GPU decoder on the GPU's own stream, against the oracle's
+        # reconstruction (bit for bit when the streams are identical)
+        if not stats["identical"]:
+            st, kg, vg = gpu_decode(plan, got, wl, T, L)
+            assert st == K.OK, K.status_string(st)
+            ek = assert_values_close(to_u16(kg).reshape(-1), kd, wl.dtype)
+            ev = assert_values_close(to_u16(vg).reshape(-1), vd, wl.dtype)
+            log(f"  own-stream decode exact fraction K {ek:.6f} V {ev:.6f}")
     return stats
 
 
@@ -93,6 +102,17 @@ def test_policy_grid(bits, axis, group, dtype):
     wl = C1.with_(dtype=dtype, k=TP(bits, axis, group), v=TP(bits, "token", 32), chunk_bytes=8192,
                   name=f"grid_{bits}_{axis}_{group}_{dtype}")
     run_case(wl, 2, 200)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_channel_groups_of_32_with_a_long_tail(bits, dtype):
+    # T = 250: the last 64-token tile holds one complete 32-token group and
+    # one of 26 tokens (the tail tile's second half is partial)
+    wl = C1.with_(dtype=dtype, k=TP(bits, "channel", 32), v=TP(bits, "token", 32), chunk_bytes=8192,
+                  name=f"tail32_{bits}_{dtype}")
+    s = run_case(wl, 2, 250)
+    assert s["identical"]
 
 
 @pytest.mark.parametrize("stages", [("TUPL8_1", "BIT_8", "RZE_2"), ("TUPL8_1", "RZE_2"),
