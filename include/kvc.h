@@ -181,6 +181,28 @@ kvc_status kvc_encode(kvc_plan_t plan, const void* d_k, const void* d_v, int32_t
                       void* d_out, size_t out_capacity, void* d_ws, size_t ws_bytes,
                       size_t* h_out_bytes, void* stream);
 
+/* kvc_encode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a fixed array of
+ * KVC_NOALLOC_SCRATCH_BYTES inside the library's device code; each device
+ * that runs this call holds its own copy until the process ends.  The call
+ * allocates nothing (no hipMalloc / hipFree); the caller passes the inputs
+ * and d_out as for kvc_encode, with the same stream format and results.
+ * Returns KVC_ERR_BUFFER_TOO_SMALL, before enqueuing anything, when the call's
+ * workspace (kvc_plan_sizes) exceeds the array (e.g. more than one layer of
+ * 131072 tokens of 8 KV heads at 2 bits), and KVC_ERR_UNSUPPORTED for
+ * mixed-precision plans.  Every call on one device shares that device's
+ * array: calls that overlap in time on one device (two streams, two threads)
+ * race and must be ordered by the caller.  The array keeps the last call's
+ * contents; each call clears what must start at zero itself.  Device-detected
+ * errors are returned when h_out_bytes is non-NULL (the call then
+ * synchronizes as kvc_encode does); with NULL the call is asynchronous, the
+ * size is the header's total_bytes field and the device status is not
+ * reported. */
+#define KVC_NOALLOC_SCRATCH_BYTES (128u << 20)
+kvc_status kvc_encode_noalloc(kvc_plan_t plan, const void* d_k, const void* d_v, int32_t tokens,
+                              void* d_out, size_t out_capacity, size_t* h_out_bytes, void* stream);
+
 /* Decode a stream of in_bytes bytes holding `tokens` tokens into d_k and d_v
  * ([layers][tokens][kv_heads][head_dim]).  The device validates the header
  * against the plan and every chunk against in_bytes; failures are recorded

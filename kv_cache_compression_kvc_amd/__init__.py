@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libkvc.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_MEMORY, ERR_BUFFER_TOO_SMALL, ERR_CORRUPT_STREAM, \
     ERR_PLAN_MISMATCH, ERR_RANGE, ERR_HIP = range(9)
 F16, BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 128 << 20     # KVC_NOALLOC_SCRATCH_BYTES
 PER_TOKEN, PER_CHANNEL = 0, 1
 STAGES = {name: i + 1 for i, name in enumerate(
     ("TUPL2_1", "TUPL4_1", "TUPL8_1", "DIFF1", "DIFF2", "DIFF4", "DIFF8",
@@ -80,6 +81,7 @@ def lib():
             "kvc_plan_sizes": [P, I64, C.POINTER(SZ), C.POINTER(SZ)],
             "kvc_plan_sizes_paged": [P, P, I32, C.POINTER(SZ), C.POINTER(SZ)],
             "kvc_encode": [P, P, P, I32, P, SZ, P, SZ, C.POINTER(SZ), P],
+            "kvc_encode_noalloc": [P, P, P, I32, P, SZ, C.POINTER(SZ), P],
             "kvc_decode": [P, P, SZ, I32, P, P, P, SZ, P],
             "kvc_encode_paged": [P, P, P, I64, P, I32, P, I32, P, SZ, P, P, SZ, C.POINTER(SZ), P],
             "kvc_decode_paged": [P, P, SZ, P, P, I32, P, P, I64, P, I32, P, SZ, P],
@@ -206,6 +208,16 @@ class Plan:
                              _ptr(ws), ws.numel() * ws.element_size(), C.byref(nb) if sync else None,
                              _stream(stream))
         _check(s, "kvc_encode")
+        return nb.value if sync else None
+
+    def encode_noalloc(self, k, v, tokens: int, out, sync: bool = True, stream=None) -> Optional[int]:
+        """kvc_encode_noalloc: kvc_encode with the library's fixed device scratch
+        (NOALLOC_SCRATCH_BYTES) as the workspace."""
+        nb = C.c_size_t(0)
+        s = lib().kvc_encode_noalloc(self.handle, _ptr(k), _ptr(v), tokens, _ptr(out),
+                                     out.numel() * out.element_size(), C.byref(nb) if sync else None,
+                                     _stream(stream))
+        _check(s, "kvc_encode_noalloc")
         return nb.value if sync else None
 
     def decode(self, stream_buf, in_bytes: int, tokens: int, k, v, ws, stream=None):

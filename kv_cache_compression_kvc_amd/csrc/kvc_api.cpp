@@ -854,6 +854,63 @@ kvc_status kvc_decode_paged(kvc_plan_t p, const void* d_in, size_t in_bytes, con
   return KVC_OK;
 }
 
+// ---------------------------------------------------------------- no-allocation encode
+
+}  // extern "C"
+
+// Workspace of kvc_encode_noalloc.  Every device the library runs this entry
+// point on holds its own copy until the process ends.  In host code the name
+// is only a stand-in for the device symbol: kernels and copies get the
+// per-device address that hipGetSymbolAddress returns, never this name.
+static __device__ __align__(256) uint8_t scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch`, looked up once per
+// device with that device current.
+kvc_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVC_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || ((uintptr_t)ptr) % 256) return fail(KVC_ERR_HIP, "scratch symbol address is NULL or misaligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kvc_status kvc_encode_noalloc(kvc_plan_t p, const void* d_k, const void* d_v, int32_t tokens, void* d_out,
+                              size_t out_capacity, size_t* h_out_bytes, void* stream) {
+  if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
+  if (p->mixed)
+    return fail(KVC_ERR_UNSUPPORTED, "kvc_encode_noalloc: mixed-precision plans upload slab tables from the host; "
+                                     "use kvc_encode");
+  if (tokens < 0 || tokens > p->cfg.max_tokens) return fail(KVC_ERR_INVALID_ARG, "tokens must be in [0, max_tokens]");
+  size_t ms = 0, need = 0;
+  kvc_status st = kvc_plan_sizes(p, tokens, &ms, &need);
+  if (st != KVC_OK) return st;
+  if (need > (size_t)KVC_NOALLOC_SCRATCH_BYTES)
+    return fail(KVC_ERR_BUFFER_TOO_SMALL,
+                "kvc_encode_noalloc: this call needs %zu bytes of workspace, more than the library's fixed %zu-byte "
+                "scratch; use kvc_encode with a workspace", need, (size_t)KVC_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != KVC_OK) return st;
+  return kvc_encode(p, d_k, d_v, tokens, d_out, out_capacity, ws, (size_t)KVC_NOALLOC_SCRATCH_BYTES, h_out_bytes,
+                    stream);
+}
+
 kvc_status kvc_query_status(kvc_plan_t p, const void* d_ws, void* stream) {
   if (!p) return fail(KVC_ERR_INVALID_ARG, "plan is NULL");
   kvc_status st = check_ptr(d_ws, 256, "d_ws");
