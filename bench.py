@@ -2,19 +2,25 @@
 """Throughput of the KV-cache compression path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic KV:
-fused transform + quantize (K and V), lossless encode, scan, compaction,
+fused transform + quantize (K and V), lossless encode, scan and placement,
 then lossless decode and fused reconstruction of the produced stream.  The
-default workload is the Llama-3.1-70B-shaped cache at 32768 tokens (80
+headline workload is the Llama-3.1-70B-shaped cache at 32768 tokens (80
 layers x 8 KV heads x 128, bf16, K int4 per-channel groups of 64 tokens, V
 int2 per-token groups of 32, lossless TUPL8_1 -> BIT_8 -> RZE_2), with all
 inputs resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is uncompressed K+V bytes per second of a
-whole step (encode + decode); encode and decode rates are reported too.
+whole headline step (encode + decode).  `sub_results` carries the other
+workloads measured the same way: the headline shape on zero-rich KV (the
+lossless stage compresses), the 131072-token 70B shape as one call and as
+a layer-by-layer pipeline on two streams, and the paged 64-request batch.
+Per-kernel times come from HIP events the library records around each
+launch on its stream, averaged over the timed steps.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -26,6 +32,9 @@ for p in (ROOT, os.path.join(ROOT, "tests")):
         sys.path.insert(0, p)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E peak
+METRIC = "KV encode / decode GB/s (uncompressed bytes) + % HBM peak, compression ratio"
+TIMING_NOTE = ("per-kernel ms: HIP events recorded by the library around each launch on its stream, "
+               "averaged over the timed steps")
 
 
 def log(msg):
@@ -40,8 +49,8 @@ def fused_bytes_per_elem(pol):
 def counted_traffic(kind: str):
     """HBM bytes per launch of a fused kernel as counted by rocprofv3
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's counts), taken from the
-    committed profile summary of this workload; None when that summary was
-    made from a different version of the kernel source."""
+    committed profile summary of the headline workload; None when that
+    summary was made from a different version of the kernel source."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "fused_codec_llama70b_32k_hbm_bytes.json")
     src = os.path.join(ROOT, "kv_cache_compression_kvc_amd", "csrc", "kvc_codec.hip")
@@ -59,25 +68,76 @@ def counted_traffic(kind: str):
             "bytes": round(k["read_bytes"] + k["write_bytes"])}
 
 
-def cpu_baseline(wl, layers: int):
-    """The oracle as it stands, single-threaded, on the first `layers` layers
-    of the workload (same value model, generated on the host)."""
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, layers: int, threads: int):
+    """The oracle as it stands on the first `layers` layers of the workload
+    (same value model, generated on the host): once on one thread, then on
+    `threads` threads, each encoding and decoding its own layers (the oracle's
+    ctypes calls release the interpreter lock; its arithmetic is unchanged)."""
+    from concurrent.futures import ThreadPoolExecutor
     import kvc_workloads as W
     import oracle_api as O
     k, v = W.dense_kv(wl, layers=layers, device="cpu")
     ku, vu = W.as_u16(k), W.as_u16(v)
+    n_layer = wl.tokens * wl.heads * wl.head_dim
+    U = wl.uncompressed_bytes() / wl.layers * layers
     cfg = O.cfg_from_workload(wl, layers=layers)
     t0 = time.perf_counter()
     st, s = O.encode(cfg, ku, vu, wl.tokens)
     t1 = time.perf_counter()
-    st2, _, _ = O.decode(s, layers * wl.tokens * wl.heads * wl.head_dim)
+    st2, _, _ = O.decode(s, layers * n_layer)
     t2 = time.perf_counter()
     assert st == O.OK and st2 == O.OK
-    U = wl.uncompressed_bytes() / wl.layers * layers
-    return {"value": round(U / (t2 - t0) / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layers 0..{layers - 1} of the workload ({U / 1e9:.3f} GB of K+V), encode + decode",
-            "encode_GBps": round(U / (t1 - t0) / 1e9, 6), "decode_GBps": round(U / (t2 - t1) / 1e9, 6),
-            "seconds": round(t2 - t0, 2), "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count()}
+    one = {"value": round(U / (t2 - t0) / 1e9, 6), "unit": "GB/s", "cores": 1,
+           "encode_GBps": round(U / (t1 - t0) / 1e9, 6), "decode_GBps": round(U / (t2 - t1) / 1e9, 6),
+           "seconds": round(t2 - t0, 2)}
+    cfg1 = O.cfg_from_workload(wl, layers=1)
+    kl = ku.reshape(layers, -1)
+    vl = vu.reshape(layers, -1)
+
+    def layer_job(l):
+        a = time.perf_counter()
+        st_, s_ = O.encode(cfg1, kl[l], vl[l], wl.tokens)
+        b = time.perf_counter()
+        st2_, _, _ = O.decode(s_, n_layer)
+        c = time.perf_counter()
+        assert st_ == O.OK and st2_ == O.OK
+        return b - a, c - b
+
+    reps = max(1, (threads + layers - 1) // layers)       # at least one layer per thread
+    jobs = [l for _ in range(reps) for l in range(layers)]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        res = list(ex.map(layer_job, jobs))
+        t1 = time.perf_counter()
+    Ua = U * reps
+    enc_cpu = sum(r[0] for r in res)
+    dec_cpu = sum(r[1] for r in res)
+    wall = t1 - t0
+    return {"value": round(Ua / wall / 1e9, 6), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"layers 0..{layers - 1} of the workload ({U / 1e9:.3f} GB of K+V) x {reps}, encode + decode, "
+                      f"one (layer, repeat) per task on {threads} threads",
+            "encode_GBps": round(Ua / wall / 1e9 * (enc_cpu + dec_cpu) / enc_cpu, 6),
+            "decode_GBps": round(Ua / wall / 1e9 * (enc_cpu + dec_cpu) / dec_cpu, 6),
+            "seconds": round(wall, 2), "single_thread": one,
+            "host_cpu": host_cpu(), "host_logical_cpus": os.cpu_count()}
 
 
 def selection_cost(U: float, s_enc: float, s_dec: float, cr: float, requests: int = 20000) -> dict:
@@ -131,17 +191,6 @@ def mixed_bytes(widths, pol, elems: int) -> float:
     return total
 
 
-def host_cpu() -> str:
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown"
-
-
 # Figures the pages report for their own implementation, with the hardware
 # they name (other machines: context, not a target for this metric).
 PAGES_FIGURES = {
@@ -156,14 +205,334 @@ PAGES_FIGURES = {
 }
 
 
+def gbps(nbytes: float, ms: float) -> float:
+    return nbytes / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+
+
+def kern(ms: float, nbytes: float) -> dict:
+    g = gbps(nbytes, ms)
+    return {"ms": round(ms, 4), "algorithmic_bytes": round(nbytes), "GBps": round(g, 1),
+            "frac": round(g / HBM_PEAK_GBPS, 4)}
+
+
+def chunk_stats(out, wl, L: int, T: int, plan_layout) -> dict:
+    """Per code section of a dense stream: chunks, compressed chunks, their
+    raw and stored bytes, the raw chunks the placement moves, and the bytes
+    the section occupies in the stream (from the chunk table)."""
+    import numpy as np
+    codes_b, nch = plan_layout
+    table = out[64:64 + 4 * sum(nch)].cpu().numpy().view(np.uint32)
+    cb = wl.chunk_bytes
+    secs = []
+    allraw_pos = 0
+    pos = 0
+    gi = 0
+    for w in range(2):
+        n = np.minimum(cb, codes_b[w] - np.arange(nch[w], dtype=np.int64) * cb)
+        e = table[gi:gi + nch[w]]
+        raw = (e >> 31).astype(bool)
+        stored = (e & 0x7FFFFFFF).astype(np.int64)
+        a16 = (stored + 15) & ~15
+        start = pos + np.concatenate([[0], np.cumsum(a16)[:-1]])
+        start_raw = allraw_pos + np.concatenate([[0], np.cumsum((n + 15) & ~15)[:-1]])
+        moved = raw & (start != start_raw)
+        secs.append({"chunks": int(nch[w]), "compressed": int((~raw).sum()),
+                     "compressed_raw_bytes": int(n[~raw].sum()), "compressed_stored_bytes": int(stored[~raw].sum()),
+                     "moved_raw_bytes": int(n[moved].sum()), "stored_bytes": int(stored.sum()),
+                     "raw_bytes": int(n.sum()), "sizes": n, "stored": stored, "raw": raw})
+        pos += int(a16.sum())
+        allraw_pos += int(((n + 15) & ~15).sum())
+        gi += nch[w]
+    return {"sections": secs}
+
+
+def layout_of(wl, L: int, T: int):
+    """Code bytes and chunk counts of the two sections of a dense stream (the
+    closed-form layout the format defines)."""
+    out = []
+    for pol in (wl.k, wl.v):
+        H, D = wl.heads, wl.head_dim
+        if pol.axis == "token":
+            c = L * T * H * D * pol.bits // 8
+        else:
+            ng = -(-T // pol.group)
+            glast = T - (ng - 1) * pol.group
+            c = L * ((ng - 1) * H * D * (pol.group * pol.bits // 8) + H * D * (-(-glast * pol.bits // 8)))
+        out.append(c)
+    return out, [-(-c // wl.chunk_bytes) for c in out]
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def profiled(fn, steps, warmup, stream):
+    """(ms per call of fn, {kernel kind: ms per launch}) over `steps` timed calls."""
+    import torch
+    import kv_cache_compression_kvc_amd as K
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    K.profile_reset()
+    K.profile_enable(True)
+    ms = timed(fn, steps, 0, stream)
+    K.profile_enable(False)
+    prof = {name: K.profile_query(name) for name in K.KERNELS}
+    return ms, {k: t / c for k, (t, c) in prof.items() if c}
+
+
+class Dense:
+    """One dense workload resident on the GPU: inputs, outputs, stream and
+    workspace, and its plan."""
+
+    def __init__(self, wl, values: str, zero_frac: float = 0.5, rho: float = 0.95, bits=None):
+        import torch
+        import kv_cache_compression_kvc_amd as K
+        import kvc_workloads as W
+        self.wl = wl
+        L, T = wl.layers, wl.tokens
+        self.L, self.T = L, T
+        dev = torch.device("cuda:0")
+        log(f"generating {wl.name} ({values}): {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype}")
+        if values == "gaussian":
+            self.k, self.v = W.dense_kv(wl, device=dev)
+        elif values == "correlated":
+            self.k, self.v = W.correlated_kv(wl, L, T, W.SEED_BASE + 7, device=dev, rho=rho)
+        else:
+            self.k, self.v = W.zero_rich_kv(wl, L, T, seed=W.SEED_BASE + 7, device=dev, zero_frac=zero_frac)
+        self.bits = bits
+        self.plan = K.Plan(K.config_from_workload(wl), bits)
+        self.ms, wsb = self.plan.sizes(T)
+        self.out = torch.empty(self.ms, dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        self.kd = torch.empty_like(self.k)
+        self.vd = torch.empty_like(self.v)
+        self.U = wl.uncompressed_bytes()
+        self.elems = L * T * wl.heads * wl.head_dim
+        torch.cuda.synchronize()
+        self.n = self.plan.encode(self.k, self.v, T, self.out, self.ws)          # synchronous: size and status
+        self.plan.decode(self.out, self.n, T, self.kd, self.vd, self.ws)
+        st = self.plan.query_status(self.ws)
+        assert st == K.OK, K.status_string(st)
+        log(f"stream {self.n} bytes, ratio {self.U / self.n:.4f}")
+
+    def encode(self):
+        self.plan.encode(self.k, self.v, self.T, self.out, self.ws, sync=False)
+
+    def decode(self):
+        self.plan.decode(self.out, self.ms, self.T, self.kd, self.vd, self.ws)
+
+    def step(self):
+        self.encode()
+        self.decode()
+
+    def fused_bytes(self):
+        wl, bits, elems = self.wl, self.bits, self.elems
+        per_k = elems * fused_bytes_per_elem(wl.k) if bits is None else mixed_bytes(bits[0], wl.k, elems)
+        per_v = elems * fused_bytes_per_elem(wl.v) if bits is None else mixed_bytes(bits[1], wl.v, elems)
+        return {"ENCODE_K": per_k, "ENCODE_V": per_v, "DECODE_K": per_k, "DECODE_V": per_v}
+
+    def codes_params(self):
+        wl, bits, elems = self.wl, self.bits, self.elems
+        total = 0.0
+        for w, pol in enumerate((wl.k, wl.v)):
+            if bits is None:
+                total += elems * (pol.bits / 8.0 + 4.0 / pol.group)
+            else:
+                total += mixed_bytes(bits[w], pol, elems) - 2.0 * elems
+        return total
+
+    def measure(self, steps, warmup):
+        """Step, encode-only and decode-only times and per-kernel figures."""
+        import torch
+        s = torch.cuda.current_stream()
+        step_ms, kms = profiled(self.step, steps, warmup, s)
+        enc_ms = timed(self.encode, steps, 2, s)
+        dec_ms = timed(self.decode, steps, 2, s)
+        import kv_cache_compression_kvc_amd as K
+        st = self.plan.query_status(self.ws)
+        assert st == K.OK, K.status_string(st)
+        U, n = self.U, self.n
+        cp = self.codes_params()
+        fb = self.fused_bytes()
+        kernels = {}
+        for k_, ms_ in kms.items():
+            kernels[k_] = kern(ms_, fb[k_]) if k_ in fb else {"ms": round(ms_, 4)}
+        for name, a_, b_ in (("ENCODE_K+V", "ENCODE_K", "ENCODE_V"), ("DECODE_K+V", "DECODE_K", "DECODE_V")):
+            if a_ in kms and b_ in kms:
+                kernels[name] = kern(kms[a_] + kms[b_], fb[a_] + fb[b_])
+        s_enc, s_dec = gbps(U, enc_ms), gbps(U, dec_ms)
+        s_p = s_enc * s_dec / (s_enc + s_dec)
+        return {"uncompressed_bytes": U, "ms_per_step": round(step_ms, 4), "GBps": round(gbps(U, step_ms), 3),
+                "encode_ms": round(enc_ms, 4), "encode_GBps": round(s_enc, 3),
+                "encode_frac_hbm_peak": round(s_enc / HBM_PEAK_GBPS, 4),
+                "decode_ms": round(dec_ms, 4), "decode_GBps": round(s_dec, 3),
+                "decode_frac_hbm_peak": round(s_dec / HBM_PEAK_GBPS, 4),
+                "compression_ratio": round(U / n, 4), "compression_ratio_quant": round(U / cp, 4),
+                "compression_ratio_lossless": round(cp / n, 4), "stream_bytes": n,
+                "harmonic_s_p_GBps": round(s_p, 3), "break_even_bandwidth_GBps": round((1 - n / U) * s_p, 3),
+                "kernels": kernels}, kms
+
+    def lossless_kernels(self, kms) -> dict:
+        """Algorithmic bytes of the lossless kernels of a step, from the
+        stream's chunk table: the placement reads each compressed chunk's codes
+        and writes its stored bytes, and moves raw chunks whose offset changed;
+        the lossless decode pass reads and expands the compressed chunks the
+        reconstruct kernels do not decode themselves (2-bit per-token values of
+        TUPL8_1 -> BIT_8 -> RZE_2 in whole 4 KiB blocks are decoded by the
+        value reconstruct kernel), and the value reconstruct then reads the
+        stored bytes of its section in place of the raw codes."""
+        wl = self.wl
+        cs = chunk_stats(self.out, wl, self.L, self.T, layout_of(wl, self.L, self.T))["sections"]
+        place = sum(s["compressed_raw_bytes"] + s["compressed_stored_bytes"] + 2 * s["moved_raw_bytes"] for s in cs)
+        std = tuple(wl.stages) == ("TUPL8_1", "BIT_8", "RZE_2")
+        dec = 0
+        mirror = [std and pol.axis == "token" and pol.bits == 2 and wl.chunk_bytes % 4096 == 0 for pol in (wl.k, wl.v)]
+        for w, s in enumerate(cs):
+            comp = ~s["raw"]
+            if mirror[w]:
+                comp = comp & (s["sizes"] % 4096 != 0)
+            dec += int(s["sizes"][comp].sum()) + int(s["stored"][comp].sum())
+        out = {"chunks": sum(s["chunks"] for s in cs), "compressed_chunks": sum(s["compressed"] for s in cs)}
+        if "COMPACT" in kms:
+            out["COMPACT (single-pass placement)"] = kern(kms["COMPACT"], place)
+        if "LOSSLESS_DEC" in kms:
+            out["LOSSLESS_DEC"] = kern(kms["LOSSLESS_DEC"], dec)
+        if mirror[1] and "DECODE_V" in kms:
+            pol = wl.v
+            v_read = cs[1]["stored_bytes"] + self.elems * 4.0 / pol.group
+            out["DECODE_V (reads stored chunks)"] = kern(kms["DECODE_V"], v_read + 2.0 * self.elems)
+        return out
+
+    def release(self):
+        for a in ("k", "v", "kd", "vd", "out", "ws"):
+            setattr(self, a, None)
+
+
+def layer_pipeline(d: Dense, steps, warmup) -> dict:
+    """One-layer calls: layer l is encoded on stream A into its own stream
+    buffer; stream B waits for that encode's event and decodes it, so B's
+    decode of layer l overlaps A's encode of layer l + 1."""
+    import torch
+    import kv_cache_compression_kvc_amd as K
+    wl, L, T, U = d.wl, d.L, d.T, d.U
+    s = torch.cuda.current_stream()
+    p1 = K.Plan(K.config_from_workload(wl, layers=1))
+    ms1, ws1 = p1.sizes(T)
+    bufs = torch.empty((L, ms1), dtype=torch.uint8, device=d.k.device)
+    wa = torch.empty(ws1, dtype=torch.uint8, device=d.k.device)
+    wb = torch.empty(ws1, dtype=torch.uint8, device=d.k.device)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    evs = [torch.cuda.Event() for _ in range(L)]
+
+    def pipe(do_enc=True, do_dec=True):
+        sa.wait_stream(s)
+        sb.wait_stream(s)
+        for l in range(L):
+            if do_enc:
+                p1.encode(d.k[l], d.v[l], T, bufs[l], wa, sync=False, stream=sa)
+                evs[l].record(sa)
+            if do_dec:
+                if do_enc:
+                    sb.wait_event(evs[l])
+                p1.decode(bufs[l], ms1, T, d.kd[l], d.vd[l], wb, stream=sb)
+        s.wait_stream(sa)
+        s.wait_stream(sb)
+
+    pipe_ms = timed(pipe, steps, warmup, s)
+    enc1_ms = timed(lambda: pipe(True, False), steps, 2, s)
+    dec1_ms = timed(lambda: pipe(False, True), steps, 2, s)
+    assert p1.query_status(wa) == K.OK and p1.query_status(wb) == K.OK
+    del bufs, wa, wb
+    return {"ms_per_step": round(pipe_ms, 4), "GBps": round(gbps(U, pipe_ms), 3),
+            "encode_ms": round(enc1_ms, 4), "encode_GBps": round(gbps(U, enc1_ms), 3),
+            "decode_ms": round(dec1_ms, 4), "decode_GBps": round(gbps(U, dec1_ms), 3),
+            "calls": f"{L} one-layer encodes on one stream, {L} one-layer decodes on another, "
+                     "each decode after its layer's encode (an event)"}
+
+
+def paged(wl, steps, warmup) -> dict:
+    """The paged batch: every request's pages gathered by the fused encoder
+    into its own stream (one call), then decoded and scattered into a second
+    pool through an independent page map (one call)."""
+    import torch
+    import kv_cache_compression_kvc_amd as K
+    import kvc_workloads as W
+    dev = torch.device("cuda:0")
+    batch = W.paged_layout(wl)
+    dst = W.paged_layout(wl, stream=1)
+    R = len(batch.seq_lens)
+    log(f"generating {wl.name}: {R} requests, {batch.num_blocks} pages of {wl.page_tokens} tokens")
+    kp, vp = W.paged_pools(wl, batch, device=dev)
+    kq, vq = torch.zeros_like(kp), torch.zeros_like(vp)
+    plan = K.Plan(K.config_from_workload(wl, max_tokens=0))
+    ms, wsb = plan.sizes_paged(batch.seq_lens)
+    out = torch.empty(ms, dtype=torch.uint8, device=dev)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    offs = torch.zeros(R + 1, dtype=torch.int64, device=dev)
+    bt = torch.from_numpy(batch.block_table).to(dev)
+    btd = torch.from_numpy(dst.block_table).to(dev)
+    n = plan.encode_paged(kp, vp, batch.num_blocks, bt, batch.seq_lens, out, offs, ws)
+    toks = int(batch.seq_lens.sum())
+    U = 2 * wl.layers * toks * wl.heads * wl.head_dim * 2
+    elems = wl.layers * toks * wl.heads * wl.head_dim
+
+    def enc():
+        plan.encode_paged(kp, vp, batch.num_blocks, bt, batch.seq_lens, out, offs, ws, sync=False)
+
+    def dec():
+        plan.decode_paged(out, n, offs, dst.seq_lens, kq, vq, dst.num_blocks, btd, ws)
+
+    s = torch.cuda.current_stream()
+    enc_ms, ke = profiled(enc, steps, warmup, s)
+    dec_ms, kd = profiled(dec, steps, warmup, s)
+    st = plan.query_status(ws)
+    assert st == K.OK, K.status_string(st)
+    fb = {"ENCODE_K": elems * fused_bytes_per_elem(wl.k), "ENCODE_V": elems * fused_bytes_per_elem(wl.v),
+          "DECODE_K": elems * fused_bytes_per_elem(wl.k), "DECODE_V": elems * fused_bytes_per_elem(wl.v)}
+    kernels = {}
+    for k_, ms_ in list(ke.items()) + list(kd.items()):
+        kernels[k_] = kern(ms_, fb[k_]) if k_ in fb else {"ms": round(ms_, 4)}
+    cp = elems * (wl.k.bits / 8 + 4 / wl.k.group + wl.v.bits / 8 + 4 / wl.v.group)
+    res = {"requests": R, "tokens": toks, "pages": batch.num_blocks, "uncompressed_bytes": U,
+           "encode_ms": round(enc_ms, 4), "encode_GBps": round(gbps(U, enc_ms), 3),
+           "encode_frac_hbm_peak": round(gbps(U, enc_ms) / HBM_PEAK_GBPS, 4),
+           "decode_ms": round(dec_ms, 4), "decode_GBps": round(gbps(U, dec_ms), 3),
+           "decode_frac_hbm_peak": round(gbps(U, dec_ms) / HBM_PEAK_GBPS, 4),
+           "compression_ratio": round(U / n, 4), "compression_ratio_quant": round(U / cp, 4),
+           "compression_ratio_lossless": round(cp / n, 4), "stream_bytes": n, "kernels": kernels}
+    del kp, vp, kq, vq, out, ws
+    return res
+
+
+def free():
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3_llama70b_32k")
-    ap.add_argument("--cpu-layers", type=int, default=8, help="layers of the oracle's timed sample (about 15 s)")
+    ap.add_argument("--cpu-layers", type=int, default=8, help="layers of the oracle's timed sample")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="threads of the oracle's all-cores run (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--sub-steps", type=int, default=0, help="timed steps of each sub-result (0: min(steps, 10))")
     ap.add_argument("--values", choices=["gaussian", "zero_rich", "correlated"], default="gaussian",
                     help="value model: the workload's Gaussian KV (headline), KV whose 64-token blocks "
                          "are zero with probability --zero-frac, or KV correlated along tokens (AR(1), "
@@ -174,8 +543,7 @@ def main():
                     help="mixed precision per (layer, head): mixhq = heads 0-1 of every layer at 8 bits and the "
                          "others at 2 bits (K and V); mixhq16 = heads 0-1 kept at 16 bits, the others at 2")
     ap.add_argument("--overlap", action="store_true",
-                    help="also time a layer pipeline: layer l encoded on one stream while the other stream "
-                         "decodes layer l - 1 (one-layer calls, an event between them)")
+                    help="also time the headline workload as a layer pipeline on two streams")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (e.g. 1: one layer per call)")
     ap.add_argument("--heads", type=int, default=0,
                     help="override kv_heads (e.g. 1: one tensor-parallel rank's share of the 70B shape at TP = 8)")
@@ -191,7 +559,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import kv_cache_compression_kvc_amd as K
     import kvc_workloads as W
 
     # plain device copy of known size: practical bandwidth reference, and the
@@ -219,71 +586,13 @@ def main():
         wl = wl.with_(heads=args.heads)
     if args.layers:
         wl = wl.with_(layers=args.layers)
-    L, T = wl.layers, wl.tokens
-    dev = torch.device("cuda:0")
-    log(f"generating {wl.name}: {L} x {T} x {wl.heads} x {wl.head_dim} {wl.dtype} on {dev}")
-    if args.values == "gaussian":
-        k, v = W.dense_kv(wl, device=dev)
-    elif args.values == "correlated":
-        k, v = W.correlated_kv(wl, L, T, W.SEED_BASE + 7, device=dev, rho=args.rho)
-    else:
-        k, v = W.zero_rich_kv(wl, L, T, seed=W.SEED_BASE + 7, device=dev, zero_frac=args.zero_frac)
     bits = mixed_widths(args.mixed, wl)
-    plan = K.Plan(K.config_from_workload(wl), bits)
-    ms, wsb = plan.sizes(T)
-    out = torch.empty(ms, dtype=torch.uint8, device=dev)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    kd = torch.empty_like(k)
-    vd = torch.empty_like(v)
-    U = wl.uncompressed_bytes()
-    torch.cuda.synchronize()
-
-    n = plan.encode(k, v, T, out, ws)                       # synchronous: size and status
-    plan.decode(out, n, T, kd, vd, ws)
-    st = plan.query_status(ws)
-    assert st == K.OK, K.status_string(st)
-    log(f"stream {n} bytes, ratio {U / n:.4f}")
-
-    def step():
-        plan.encode(k, v, T, out, ws, sync=False)
-        plan.decode(out, ms, T, kd, vd, ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
+    d = Dense(wl, args.values, args.zero_frac, args.rho, bits)
+    L, T, U = d.L, d.T, d.U
+    head, kms = d.measure(args.steps, args.warmup)
     s = torch.cuda.current_stream()
-    K.profile_reset()
-    K.profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(s)
-    for _ in range(args.steps):
-        step()
-    e1.record(s)
-    torch.cuda.synchronize()
-    K.profile_enable(False)
-    step_ms = e0.elapsed_time(e1) / args.steps
-    prof = {name: K.profile_query(name) for name in K.KERNELS}
-    log(f"step {step_ms:.3f} ms; per-kernel ms/launch: " +
-        ", ".join(f"{k_}={t / max(c, 1):.3f}" for k_, (t, c) in prof.items() if c))
-
-    def timed(fn):
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(s)
-        for _ in range(args.steps):
-            fn()
-        b.record(s)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
-
-    enc_ms = timed(lambda: plan.encode(k, v, T, out, ws, sync=False))
-    dec_ms = timed(lambda: plan.decode(out, ms, T, kd, vd, ws))
-    st = plan.query_status(ws)
-    assert st == K.OK, K.status_string(st)
+    log(f"step {head['ms_per_step']:.3f} ms; per-kernel ms/launch: " +
+        ", ".join(f"{k_}={v_:.3f}" for k_, v_ in kms.items()))
 
     # the same step captured once in a HIP graph and replayed (a serving loop's
     # form: the dense calls enqueue kernels only)
@@ -294,77 +603,33 @@ def main():
         side.wait_stream(s)
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                step()
+                d.step()
         s.wait_stream(side)
         torch.cuda.synchronize()
-        graph_ms = timed(g.replay)
-        st = plan.query_status(ws)
+        graph_ms = timed(g.replay, args.steps, 2, s)
+        import kv_cache_compression_kvc_amd as K
+        st = d.plan.query_status(d.ws)
         assert st == K.OK, K.status_string(st)
+        del g
         log(f"graph replay {graph_ms:.3f} ms per step")
-    log(f"encode {enc_ms:.3f} ms ({U / enc_ms / 1e6:.1f} GB/s), decode {dec_ms:.3f} ms ({U / dec_ms / 1e6:.1f} GB/s)")
-
-    overlap = None
-    if args.overlap and bits is None:
-        # one-layer calls: layer l is encoded on stream A into its own stream
-        # buffer; stream B waits for that encode's event and decodes it, so
-        # B's decode of layer l overlaps A's encode of layer l + 1
-        p1 = K.Plan(K.config_from_workload(wl, layers=1))
-        ms1, ws1 = p1.sizes(T)
-        bufs = torch.empty((L, ms1), dtype=torch.uint8, device=dev)
-        wa = torch.empty(ws1, dtype=torch.uint8, device=dev)
-        wb = torch.empty(ws1, dtype=torch.uint8, device=dev)
-        sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-        evs = [torch.cuda.Event() for _ in range(L)]
-
-        def pipe(do_enc=True, do_dec=True):
-            sa.wait_stream(s)
-            sb.wait_stream(s)
-            for l in range(L):
-                if do_enc:
-                    p1.encode(k[l], v[l], T, bufs[l], wa, sync=False, stream=sa)
-                    evs[l].record(sa)
-                if do_dec:
-                    if do_enc:
-                        sb.wait_event(evs[l])
-                    p1.decode(bufs[l], ms1, T, kd[l], vd[l], wb, stream=sb)
-            s.wait_stream(sa)
-            s.wait_stream(sb)
-
-        pipe_ms = timed(pipe)
-        enc1_ms = timed(lambda: pipe(True, False))
-        dec1_ms = timed(lambda: pipe(False, True))
-        assert p1.query_status(wa) == K.OK and p1.query_status(wb) == K.OK
-        overlap = {"ms_per_step": round(pipe_ms, 4), "GBps": round(U / pipe_ms / 1e6, 3),
-                   "encode_ms": round(enc1_ms, 4), "encode_GBps": round(U / enc1_ms / 1e6, 3),
-                   "decode_ms": round(dec1_ms, 4), "decode_GBps": round(U / dec1_ms / 1e6, 3),
-                   "calls": f"{L} one-layer encodes on one stream, {L} one-layer decodes on another"}
-        log(f"layer pipeline {pipe_ms:.3f} ms ({U / pipe_ms / 1e6:.1f} GB/s); one-layer calls alone: "
-            f"encode {enc1_ms:.3f} ms, decode {dec1_ms:.3f} ms")
+    log(f"encode {head['encode_ms']:.3f} ms ({head['encode_GBps']:.1f} GB/s), "
+        f"decode {head['decode_ms']:.3f} ms ({head['decode_GBps']:.1f} GB/s)")
+    overlap = layer_pipeline(d, args.steps, args.warmup) if (args.overlap and bits is None) else None
 
     # roofline of the dominant fused kernel, algorithmic bytes per launch
-    elems = L * T * wl.heads * wl.head_dim
-    per_k = elems * fused_bytes_per_elem(wl.k) if bits is None else mixed_bytes(bits[0], wl.k, elems)
-    per_v = elems * fused_bytes_per_elem(wl.v) if bits is None else mixed_bytes(bits[1], wl.v, elems)
-    cand = {"ENCODE_K": per_k, "ENCODE_V": per_v, "DECODE_K": per_k, "DECODE_V": per_v}
-    avg = {k_: prof[k_][0] / max(prof[k_][1], 1) for k_ in cand}
-    dom = max(avg, key=avg.get)
-    achieved = cand[dom] / (avg[dom] * 1e-3) / 1e9
-    import ctypes as C
-    codes_params = 0
-    # quantized bytes (codes + parameters) from the closed form
-    for w, pol in enumerate((wl.k, wl.v)):
-        if bits is None:
-            codes_params += elems * (pol.bits / 8.0 + 4.0 / pol.group)
-        else:
-            codes_params += mixed_bytes(bits[w], pol, elems) - 2.0 * elems
+    fb = d.fused_bytes()
+    dom = max((k_ for k_ in fb if k_ in kms), key=lambda k_: kms[k_])
+    achieved = gbps(fb[dom], kms[dom])
+    headline = (args.workload == "c3_llama70b_32k" and args.values == "gaussian" and args.mixed == "none"
+                and not (dk or dv) and not args.heads and not args.layers)
     result = {
-        "metric": "KV encode / decode GB/s (uncompressed bytes) + % HBM peak, compression ratio",
-        "value": round(U / step_ms / 1e6, 3),
+        "metric": METRIC,
+        "value": head["GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -380,48 +645,64 @@ def main():
                    "lossless": ">".join(wl.stages), "chunk_bytes": wl.chunk_bytes, "mixed": args.mixed,
                    "token_delta": [dk, dv],
                    "uncompressed_bytes": U},
-        "encode_GBps": round(U / enc_ms / 1e6, 3),
-        "decode_GBps": round(U / dec_ms / 1e6, 3),
-        "encode_frac_hbm_peak": round(U / enc_ms / 1e6 / HBM_PEAK_GBPS, 4),
-        "decode_frac_hbm_peak": round(U / dec_ms / 1e6 / HBM_PEAK_GBPS, 4),
-        "compression_ratio": round(U / n, 4),
-        "layer_pipeline": overlap,
-        "compression_ratio_quant": round(U / codes_params, 4),
-        "compression_ratio_lossless": round(codes_params / n, 4),
-        "stream_bytes": n,
-        "kernel_ms_per_launch": {k_: round(t / max(c, 1), 4) for k_, (t, c) in prof.items() if c},
-        "device_copy_GBps": round(copy_gbps, 1),
-        "graph_replay": (None if graph_ms is None else
-                         {"ms_per_step": round(graph_ms, 4), "GBps": round(U / graph_ms / 1e6, 3)}),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "algorithmic_bytes": round(cand[dom]), "traffic": None},
     }
-    # each fused kernel, and the K and V kernels of one direction together
-    fk = {}
-    for k_ in cand:
-        gbps = cand[k_] / (avg[k_] * 1e-3) / 1e9
-        fk[k_] = {"ms": round(avg[k_], 4), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
-    for name, a_, b_ in (("ENCODE", "ENCODE_K", "ENCODE_V"), ("DECODE", "DECODE_K", "DECODE_V")):
-        ms_ = avg[a_] + avg[b_]
-        gbps = (cand[a_] + cand[b_]) / (ms_ * 1e-3) / 1e9
-        fk[name + "_K+V"] = {"ms": round(ms_, 4), "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
-    result["fused_kernels"] = fk
-    result["pages_figures"] = PAGES_FIGURES
-    result["selection"] = selection_cost(U, U / (enc_ms * 1e-3), U / (dec_ms * 1e-3), U / n)
-    t = (counted_traffic(dom) if (args.workload == "c3_llama70b_32k" and args.values == "gaussian"
-                                   and args.mixed == "none" and not (dk or dv) and not args.heads
-                                   and not args.layers) else None)
+    for key in ("encode_GBps", "decode_GBps", "encode_frac_hbm_peak", "decode_frac_hbm_peak", "compression_ratio",
+                "compression_ratio_quant", "compression_ratio_lossless", "stream_bytes", "harmonic_s_p_GBps",
+                "break_even_bandwidth_GBps"):
+        result[key] = head[key]
+    result["layer_pipeline"] = overlap
+    result["kernel_ms_per_launch"] = {k_: round(v_, 4) for k_, v_ in kms.items()}
+    result["fused_kernels"] = {k_: v_ for k_, v_ in head["kernels"].items() if "ENCODE" in k_ or "DECODE" in k_}
+    result["device_copy_GBps"] = round(copy_gbps, 1)
+    result["graph_replay"] = (None if graph_ms is None else
+                              {"ms_per_step": round(graph_ms, 4), "GBps": round(gbps(U, graph_ms), 3)})
+    result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                          "algorithmic_bytes": round(fb[dom]), "traffic": None, "timing": TIMING_NOTE}
+    t = counted_traffic(dom) if headline else None
     if t is not None:
         result["roofline"]["traffic"] = t["bytes"]
         result["roofline"]["traffic_read_write"] = [t["read_bytes"], t["write_bytes"]]
-    s_enc, s_dec = U / enc_ms / 1e6, U / dec_ms / 1e6
-    s_p = s_enc * s_dec / (s_enc + s_dec)
-    result["harmonic_s_p_GBps"] = round(s_p, 3)
-    result["break_even_bandwidth_GBps"] = round((1 - n / U) * s_p, 3)
+    result["pages_figures"] = PAGES_FIGURES
+    result["selection"] = selection_cost(U, U / (head["encode_ms"] * 1e-3), U / (head["decode_ms"] * 1e-3),
+                                         U / d.n)
+    d.release()
+    del d
+    free()
+
+    if not args.no_sub and headline:
+        sub = {}
+        ss = args.sub_steps or min(args.steps, 10)
+        sw = min(args.warmup, 3)
+        # the headline shape on zero-rich KV: the lossless stage compresses
+        dz = Dense(wl, "zero_rich", 0.5)
+        r, kz = dz.measure(ss, sw)
+        r["values"] = "half of the 64-token blocks of each (layer, head) zero"
+        r["lossless_kernels"] = dz.lossless_kernels(kz)
+        sub["llama70b_32k_zero_rich"] = r
+        dz.release()
+        del dz
+        free()
+        # the 131072-token 70B shape (fp16, int2 K and V): one call, then a layer pipeline
+        w5 = W.WORKLOADS["c5_llama70b_128k"]
+        d5 = Dense(w5, "gaussian")
+        r, _ = d5.measure(ss, sw)
+        r["layer_pipeline"] = layer_pipeline(d5, max(2, ss // 2), 1)
+        sub["llama70b_128k"] = r
+        d5.release()
+        del d5
+        free()
+        # the paged 64-request batch
+        sub["llama8b_paged_64_requests"] = paged(W.WORKLOADS["c4_paged_llama8b"], max(2, ss // 2), 1)
+        free()
+        result["sub_results"] = sub
+        for name, r in sub.items():
+            log(f"{name}: encode {r['encode_GBps']:.1f} GB/s, decode {r['decode_GBps']:.1f} GB/s, CR "
+                f"{r['compression_ratio']:.3f}")
     if not args.no_cpu_baseline:
-        log(f"timing the oracle on {args.cpu_layers} layers on the host")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_layers)
+        threads = args.cpu_threads or host_cores()
+        log(f"timing the oracle on {args.cpu_layers} layers on the host (1 and {threads} threads)")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_layers, threads)
     print(json.dumps(result), flush=True)
 
 
