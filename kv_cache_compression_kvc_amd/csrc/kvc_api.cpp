@@ -109,10 +109,10 @@ int lossless_pipe(const uint8_t* st) {
 // Whether the fused encoders of a dense call can count a section's non-zero
 // RZE words: every wave's codes must cover whole aligned 1 KiB regions of one
 // chunk.  Per-token tiles always do; per-channel kernels count groups of 64
-// tokens of 4 or 8 bits when no group is partial.
+// tokens (2, 4 or 8 bits) when no group is partial.
 bool fused_count_ok(const TensorPol& p, int T, uint32_t chunk_bytes) {
   if (p.axis == 0) return true;
-  return p.group == 64 && p.bits >= 4 && T % 64 == 0 && chunk_bytes % (kHeadDim * 64 * p.bits / 8) == 0;
+  return p.group == 64 && T % 64 == 0 && chunk_bytes % (kHeadDim * 64 * p.bits / 8) == 0;
 }
 
 // Codes / parameter bytes of one (layer, head) slab of width `bits` (16:

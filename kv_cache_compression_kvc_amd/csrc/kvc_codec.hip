@@ -1262,6 +1262,9 @@ template <int BITS, int G, bool BF16, bool TAIL>
 __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel(CallDesc c, int which) {
   __shared__ __attribute__((aligned(16))) float zb[64 * RP];
   __shared__ __attribute__((aligned(16))) uint32_t smt[64];
+  // 2-bit groups of 64: per pass and wave, the ORs of the 8 residues of the
+  // 8-byte word index over the wave's channels (a 1 KiB region spans both waves)
+  __shared__ __attribute__((aligned(16))) uint64_t part2[(BITS == 2 && G == 64 && !TAIL) ? 2 * 2 * 8 : 1];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const TensorPol pol = which ? c.pol[1] : c.pol[0];
   const float cc = pol.c;
@@ -1466,10 +1469,46 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
             tile_gci = (which ? (int64_t)c.one.nchunks[0] : 0) + chunk_of(c, boff);
           }
         }
+        if constexpr (G == 64 && FULL && BITS == 2) {
+          if (c.nnz_pipe && c.nnz_sec[which]) {
+            // this thread's codes: the 8-byte word 2 ch + th of the group block
+            const uint64_t x = u64of(w[0], w[1]);
+            if (c.nnz_pipe == 1) {
+              // residue 2 (ch & 3) + th; the pass's 64 channels are one 1 KiB
+              // region: OR over this wave's lanes of equal (ch & 3, th), the
+              // other wave's half joins through LDS after the pass
+              const uint64_t y = or_lane_bits<2, 5>(x);
+              if ((lane & 28) == 0) part2[(2 * p + wave) * 8 + 2 * (lane & 3) + th] = y;
+            } else {
+              // the channel's aligned 16-byte unit is the words of th = 0 and 1
+              const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+              auto plo = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+              auto phi = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+              const uint64_t o = u64of(th ? plo[0] : plo[1], th ? phi[0] : phi[1]);
+              if (th == 0) tile_cnt += nz_bytes64(x | o);
+            }
+            tile_gci = (which ? (int64_t)c.one.nchunks[0] : 0) + chunk_of(c, boff);
+          }
+        }
       };
       if constexpr (TAIL) pass(std::false_type{});
       else pass(std::true_type{});
       __syncthreads();                                   // before the next pass overwrites zb
+    }
+    if constexpr (G == 64 && !TAIL && BITS == 2) {
+      if (c.nnz_pipe && c.nnz_sec[which]) {
+        if (c.nnz_pipe == 1) {
+          // both passes' regions lie in the tile's group block, hence one chunk
+          if (wave == 0) {
+            const int q = lane & 15;
+            const uint32_t cnt = (lane < 16) ? popc64(part2[(2 * (q >> 3)) * 8 + (q & 7)] |
+                                                       part2[(2 * (q >> 3) + 1) * 8 + (q & 7)]) : 0u;
+            add_chunk_nnz(c, tile_gci, cnt);
+          }
+        } else {
+          add_chunk_nnz(c, tile_gci, tile_cnt);
+        }
+      }
     }
     if constexpr (G == 64 && !TAIL && BITS >= 4) {
       if (c.nnz_pipe && c.nnz_sec[which]) {

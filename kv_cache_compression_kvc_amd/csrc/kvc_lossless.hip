@@ -127,6 +127,39 @@ __device__ __forceinline__ T block_exclusive_scan(T x, T* sh, T& total) {
   return incl - x;
 }
 
+// Inclusive prefix sum over a wavefront (all lanes active): prefix sums within
+// each 16-lane row by DPP row shifts, then the rows joined through the row
+// broadcasts of lane 15 and lane 31.
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15 into rows 1, 3
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Exclusive prefix sum over a block of NW wavefronts (blockDim.x == 64 NW):
+// wave scans by DPP, the wave totals through sh[NW]; two barriers.
+template <int NW>
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t x, uint32_t* sh, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan_u32(x);
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = sh[w];
+    before += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  total = tot;
+  __syncthreads();                                   // sh is reused by the next scan
+  return before + inc - x;
+}
+
 __device__ __forceinline__ uint64_t ld_word(const uint8_t* p, int w) {
   uint64_t v = 0;
   for (int b = 0; b < w; ++b) v |= (uint64_t)p[b] << (8 * b);
@@ -445,21 +478,23 @@ __device__ __forceinline__ uint32_t or8(uint32_t x) {
 }
 
 // Block scan of the popcounts of nd <= 1024 bitmap dwords: offs[d] = number
-// of set bits before dword d; returns the total.  256 threads.
+// of set bits before dword d; returns the total.  64 NW threads.
+template <int NW>
 __device__ __forceinline__ uint32_t scan_bitmap(const uint32_t* bm, uint32_t* offs, int nd, uint32_t* sh32) {
+  constexpr int PT = 1024 / (64 * NW);               // dwords per thread
   const int t = threadIdx.x;
-  uint32_t cnt[4], sum = 0;
+  uint32_t cnt[PT], sum = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int d = 4 * t + i;
+  for (int i = 0; i < PT; ++i) {
+    const int d = PT * t + i;
     cnt[i] = (d < nd) ? (uint32_t)__builtin_popcount(bm[d]) : 0u;
     sum += cnt[i];
   }
   uint32_t total;
-  uint32_t run = block_exclusive_scan<uint32_t>(sum, sh32, total);
+  uint32_t run = block_excl_scan_u32<NW>(sum, sh32, total);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int d = 4 * t + i;
+  for (int i = 0; i < PT; ++i) {
+    const int d = PT * t + i;
     if (d < nd) offs[d] = run;
     run += cnt[i];
   }
@@ -467,38 +502,39 @@ __device__ __forceinline__ uint32_t scan_bitmap(const uint32_t* bm, uint32_t* of
   return total;
 }
 
-
-
-// Copy nv <= 4096 16-byte lines from global memory to LDS with 256 threads:
+// Copy nv <= 4096 16-byte lines from global memory to LDS with 64 NW threads:
 // every load of a thread is issued before the first LDS store, so a block has
 // the whole chunk in flight at once.  Lines past `avail` bytes read as zero.
+template <int NW>
 __device__ __forceinline__ void stage_lines(const uint4* src, int nv, uint64_t avail, uint4* dst) {
-  uint4 x[16];
+  constexpr int NT = 64 * NW, PT = 4096 / NT;
+  uint4 x[PT];
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int k = (int)threadIdx.x + 256 * u;
+  for (int u = 0; u < PT; ++u) {
+    const int k = (int)threadIdx.x + NT * u;
     x[u] = make_uint4(0, 0, 0, 0);
     if (k < nv && (uint64_t)(16 * k + 16) <= avail) x[u] = src[k];
   }
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int k = (int)threadIdx.x + 256 * u;
+  for (int u = 0; u < PT; ++u) {
+    const int k = (int)threadIdx.x + NT * u;
     if (k < nv) dst[k] = x[u];
   }
 }
 
 // Stage a compressed chunk into LDS and check that its bitmap accounts for
 // its length.  Returns false (and flags the stream) if not.
+template <int NW>
 __device__ __forceinline__ bool load_compressed(const CallDesc& c, uint64_t pos, int stored, int n, uint4* buf,
                                                 uint32_t* offs, uint32_t* sh32, uint32_t& nnz) {
   const uint64_t avail = (c.stream_bytes > pos) ? c.stream_bytes - pos : 0;
   const int nv = (stored + 15) / 16;
   const uint4* src = (const uint4*)(c.stream + pos);
-  stage_lines(src, nv, avail, buf);
+  stage_lines<NW>(src, nv, avail, buf);
   __syncthreads();
   // bytes of the last 16-byte line past the stored length are ignored
   if (stored < n / 16) return false;
-  nnz = scan_bitmap((const uint32_t*)buf, offs, n / 64, sh32);
+  nnz = scan_bitmap<NW>((const uint32_t*)buf, offs, n / 64, sh32);
   return n / 16 + 2 * (int)nnz == stored && (uint64_t)(16 * nv) <= avail + 15;
 }
 
@@ -520,16 +556,36 @@ __device__ __forceinline__ bool wp_decode_chunk(const CallDesc& c, int64_t ch, i
   return stored < L.n && stored > 0 && pos + (uint64_t)stored <= c.stream_bytes && (pos & 15) == 0;
 }
 
-__global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
+// Waves per block of the word-parallel chunk kernels.  A chunk is one block's
+// work; more waves split its 4 KiB (or 1 KiB) pieces finer, so a chunk's
+// loads, transposes and stores run on more waves at once.  Both kernels hold
+// a 64 KiB LDS buffer, so two blocks fit a CU.  Measured on the 70B shape with
+// half of the 64-token blocks zero: placement 1.21 ms at 4 waves, 0.98 ms at
+// 8 (4 waves per SIMD, a few registers spilled), 1.33 ms at 16 (one block per
+// CU); lossless decode 0.75 ms at 4 waves, 0.93 ms at 8 (spills), 1.17 ms at 16.
+#ifndef KVC_PLACE_WAVES
+#define KVC_PLACE_WAVES 8
+#endif
+#ifndef KVC_DEC_WAVES
+#define KVC_DEC_WAVES 4
+#endif
+
+constexpr int kPlaceWaves = KVC_PLACE_WAVES;
+constexpr int kPlaceThreads = 64 * kPlaceWaves;
+constexpr int kDecWaves = KVC_DEC_WAVES;
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
+  constexpr int NT = 64 * NW;
   __shared__ __attribute__((aligned(16))) uint4 buf[4096];
   __shared__ uint32_t offs[1024];
-  __shared__ uint32_t sh32[256];
+  __shared__ uint32_t sh32[NW];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const XposeLane X = xpose_lane();
-  // this block's chunks are blockIdx.x + gridDim.x * i; 256 at a time are
+  // this block's chunks are blockIdx.x + gridDim.x * i; NT at a time are
   // checked in parallel and the block then works through those to decode
-  __shared__ uint32_t cand[256];
-  for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += 256) {
+  __shared__ uint32_t cand[NT];
+  for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += NT) {
   {
     const int64_t mine = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + threadIdx.x);
     ChunkLoc L;
@@ -538,7 +594,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t
     cand[threadIdx.x] = (mine < c.total_chunks && wp_decode_chunk(c, mine, 1, L, pos, stored)) ? 1u : 0u;
   }
   __syncthreads();
-  for (int i = 0; i < 256; ++i) {
+  for (int i = 0; i < NT; ++i) {
     if (!cand[i]) continue;
     const int64_t ch = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i);
     ChunkLoc L;
@@ -547,7 +603,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t
     wp_decode_chunk(c, ch, 1, L, pos, stored);
     const int n = (int)L.n;
     uint32_t nnz = 0;
-    const bool ok = load_compressed(c, pos, stored, n, buf, offs, sh32, nnz);
+    const bool ok = load_compressed<NW>(c, pos, stored, n, buf, offs, sh32, nnz);
     if (!ok) {
       if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
       __syncthreads();
@@ -558,7 +614,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t
     const int ngi = n / 4096, dpj = n / 512;
     const int j = lane >> 3, bb = lane & 7;
     uint32_t bad = 0;
-    for (int gi = wave; gi < ngi; gi += 4) {
+    for (int gi = wave; gi < ngi; gi += NW) {
       uint32_t w[16];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
@@ -590,15 +646,17 @@ __global__ __launch_bounds__(256) void k_ll_decode_p1(CallDesc c, const uint32_t
   }
 }
 
-__global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t* worklist) {
+template <int NW>
+__global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p2(CallDesc c, const uint32_t* worklist) {
+  constexpr int NT = 64 * NW;
   __shared__ __attribute__((aligned(16))) uint4 buf[4096];
   __shared__ uint32_t offs[1024];
-  __shared__ uint32_t sh32[256];
+  __shared__ uint32_t sh32[NW];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  // this block's chunks are blockIdx.x + gridDim.x * i; 256 at a time are
+  // this block's chunks are blockIdx.x + gridDim.x * i; NT at a time are
   // checked in parallel and the block then works through those to decode
-  __shared__ uint32_t cand[256];
-  for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += 256) {
+  __shared__ uint32_t cand[NT];
+  for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += NT) {
   {
     const int64_t mine = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + threadIdx.x);
     ChunkLoc L;
@@ -607,7 +665,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t
     cand[threadIdx.x] = (mine < c.total_chunks && wp_decode_chunk(c, mine, 2, L, pos, stored)) ? 1u : 0u;
   }
   __syncthreads();
-  for (int i = 0; i < 256; ++i) {
+  for (int i = 0; i < NT; ++i) {
     if (!cand[i]) continue;
     const int64_t ch = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i);
     ChunkLoc L;
@@ -616,7 +674,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t
     wp_decode_chunk(c, ch, 2, L, pos, stored);
     const int n = (int)L.n;
     uint32_t nnz = 0;
-    const bool ok = load_compressed(c, pos, stored, n, buf, offs, sh32, nnz);
+    const bool ok = load_compressed<NW>(c, pos, stored, n, buf, offs, sh32, nnz);
     if (!ok) {
       if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
       __syncthreads();
@@ -627,7 +685,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_p2(CallDesc c, const uint32_t
     const int nblk = n / 1024, dpj = n / 512;
     const int rr = lane & 31;
     uint32_t bad = 0;
-    for (int blk = wave; blk < nblk; blk += 4) {
+    for (int blk = wave; blk < nblk; blk += NW) {
       uint32_t v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -1047,14 +1105,16 @@ __device__ bool wait_announced(const CallDesc& c, const uint32_t* ann, const uin
 
 // PIPE: the plan's pipeline when it is one of the two encoded here (1:
 // TUPL8_1 -> BIT_8 -> RZE_2, 2: TUPL8_1 -> RZE_2), else 0; one instantiation
-// each, so none carries the other's registers.
+// each, so none carries the other's registers.  NW waves per block.
 // One chunk of the placement (dense: k at or past the first chunk with work,
 // in ticket order; paged: any order, written to the request's own stream).
-template <int PIPE, bool PAGED>
+template <int PIPE, bool PAGED, int NW>
 __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_t kf, uint32_t* ann, uint32_t* grp,
                                             const XposeLane& X, int wave, int lane, uint32_t* ob, uint32_t* bm,
                                             uint32_t* offs, uint32_t* sh32) {
   constexpr int pipe = PIPE;
+  constexpr int NS = 16 / NW;                          // 4 KiB blocks per wave (mode 2)
+  constexpr int NU = 64 / NW;                          // 1 KiB blocks per wave (mode 4)
   const int r = PAGED ? find_req_by_chunk(c, k) : 0;
   const ReqDesc rq = req_at(c, r);
   const uint64_t base = PAGED ? stream_base(c, r, true) : 0;
@@ -1070,28 +1130,29 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
                              : ((pipe == 0 || !fast_eligible(pipe, L.n)) ? 3 : (pipe == 1 ? 2 : 4));
   const int n = (int)L.n;
   const int ngi = n >> 12, nd = n >> 6, dpj = n >> 9;
-  // R: this lane's 64 bytes of the chunk.  Mode 2: R[16 s4 .. 16 s4 + 15] =
-  // bytes 64 lane .. 64 lane + 63 of 4 KiB block gi = wave + 4 s4, input
-  // word 8 lane + kk at R[16 s4 + 2 kk], transposed there in place.  Mode 4:
-  // R[4 s16 .. 4 s16 + 3] = 16-byte unit `lane` of 1 KiB block wave + 4 s16.
-  uint32_t R[64];
+  // R: this lane's 64 bytes of each of the wave's pieces of the chunk.
+  // Mode 2: R[16 s4 .. 16 s4 + 15] = bytes 64 lane .. 64 lane + 63 of 4 KiB
+  // block gi = wave + NW s4, input word 8 lane + kk at R[16 s4 + 2 kk],
+  // transposed there in place.  Mode 4: R[4 u .. 4 u + 3] = 16-byte unit
+  // `lane` of 1 KiB block wave + NW u.
+  uint32_t R[16 * NS];
   if (mode == 4) {
     // every load first, so the whole chunk is in flight at once: buffer
     // loads with one lane offset and wave-uniform block offsets (blocks past
     // the chunk read zero)
     const __amdgpu_buffer_rsrc_t rs = ll_rsrc(slot, (uint32_t)n);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint4 x = ll_load16(rs, 16u * (uint32_t)lane, 1024u * (uint32_t)(wave + 4 * u));
+    for (int u = 0; u < NU; ++u) {
+      const uint4 x = ll_load16(rs, 16u * (uint32_t)lane, 1024u * (uint32_t)(wave + NW * u));
       R[4 * u] = x.x; R[4 * u + 1] = x.y; R[4 * u + 2] = x.z; R[4 * u + 3] = x.w;
     }
   }
   if (mode == 2) {
-    // block by block (measured faster here than issuing the whole chunk first)
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int gi = wave + 4 * s4;
+    for (int s4 = 0; s4 < NS; ++s4) {
+      const int gi = wave + NW * s4;
       if (gi < ngi) {
+        // block by block (measured faster than issuing all of a wave's loads first)
         const uint4* src = (const uint4*)(slot + (int64_t)gi * 4096 + 64 * lane);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1115,8 +1176,8 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
     // and byte j make two bitmap dwords (ballot)
     const int nblk = n >> 10;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int blk = wave + 4 * u;
+    for (int u = 0; u < NU; ++u) {
+      const int blk = wave + NW * u;
       if (blk < nblk) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -1144,7 +1205,7 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
   }
   bool consistent = true;
   if (mode == 2 || mode == 4) {
-    const uint32_t nnz = scan_bitmap(bm, offs, nd, sh32);
+    const uint32_t nnz = scan_bitmap<NW>(bm, offs, nd, sh32);
     consistent = n / 16 + 2 * (int64_t)nnz == stored;    // the size the scan used
     if (!consistent && threadIdx.x == 0) set_status2(c.ctl, kStStall);
   }
@@ -1153,8 +1214,8 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
     uint16_t* ow = (uint16_t*)(ob + nd);
     const int j = lane >> 3, r4 = 4 * (lane & 7);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int gi = wave + 4 * s4;
+    for (int s4 = 0; s4 < NS; ++s4) {
+      const int gi = wave + NW * s4;
       if (gi < ngi) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
@@ -1176,8 +1237,8 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
     const int nblk = n >> 10;
     const uint32_t rr = (uint32_t)(lane & 31);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int blk = wave + 4 * u;
+    for (int u = 0; u < NU; ++u) {
+      const int blk = wave + NW * u;
       if (blk < nblk) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -1195,9 +1256,13 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
     const int64_t pad = align16(stored) - stored;
     if (threadIdx.x < pad) dst[stored + threadIdx.x] = 0;
   } else if (consistent) {
-    // chunks below kf are raw at their places: their codes are never covered
+    // the output [fin, fin + align16(stored)) covers the codes of chunks j0 .. j1
+    // (and its own); chunks below kf are raw at their places: their codes are
+    // never covered
+    const uint64_t end = fin + (uint64_t)align16(stored);
     const int64_t j0 = PAGED ? k : min(max(first_covered(c, fin), kf), k);
-    if (!wait_announced(c, ann, grp, j0, k)) {
+    const int64_t j1 = (PAGED || end == fin) ? j0 : max(j0, min(first_covered(c, end - 1) + 1, k));
+    if (!wait_announced(c, ann, grp, j0, j1)) {
       if (threadIdx.x == 0) set_status2(c.ctl, kStStall);
     } else {
       const uint4* src = (mode == 3) ? (const uint4*)(c.codes_out + L.src)
@@ -1219,11 +1284,11 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
 }
 
 template <int PIPE>
-__global__ __launch_bounds__(256) void k_place(CallDesc c) {
+__global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 2 : 4) void k_place(CallDesc c) {
   __shared__ __attribute__((aligned(16))) uint32_t ob[16384];   // output assembly / raw chunk (64 KiB)
   __shared__ uint32_t bm[1024];
   __shared__ uint32_t offs[1024];
-  __shared__ uint32_t sh32[256];
+  __shared__ uint32_t sh32[kPlaceWaves];
   __shared__ int64_t tk[1];
   const int64_t N = c.total_chunks;
   uint32_t* ann = c.place_flags;
@@ -1264,7 +1329,7 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
       __syncthreads();
       continue;
     }
-    place_chunk<PIPE, false>(c, kf + (t - nb0), kf, ann, grp, X, wave, lane, ob, bm, offs, sh32);
+    place_chunk<PIPE, false, kPlaceWaves>(c, kf + (t - nb0), kf, ann, grp, X, wave, lane, ob, bm, offs, sh32);
   }
 }
 
@@ -1272,15 +1337,15 @@ __global__ __launch_bounds__(256) void k_place(CallDesc c) {
 // stream, so chunks are placed in any order, with no announcements; the
 // compaction kernel writes the headers and parameter sections.
 template <int PIPE>
-__global__ __launch_bounds__(256) void k_place_paged(CallDesc c) {
+__global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 2 : 4) void k_place_paged(CallDesc c) {
   __shared__ __attribute__((aligned(16))) uint32_t ob[16384];
   __shared__ uint32_t bm[1024];
   __shared__ uint32_t offs[1024];
-  __shared__ uint32_t sh32[256];
+  __shared__ uint32_t sh32[kPlaceWaves];
   const XposeLane X = xpose_lane();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   for (int64_t k = blockIdx.x; k < c.total_chunks; k += gridDim.x)
-    place_chunk<PIPE, true>(c, k, 0, nullptr, nullptr, X, wave, lane, ob, bm, offs, sh32);
+    place_chunk<PIPE, true, kPlaceWaves>(c, k, 0, nullptr, nullptr, X, wave, lane, ob, bm, offs, sh32);
 }
 
 hipError_t launch_place(const CallDesc& c, hipStream_t s) {
@@ -1289,15 +1354,15 @@ hipError_t launch_place(const CallDesc& c, hipStream_t s) {
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
   if (c.place == 2) {
     if (c.total_chunks == 0) return hipSuccess;
-    if (p1) k_place_paged<1><<<grid, 256, 0, s>>>(c);
-    else if (p2) k_place_paged<2><<<grid, 256, 0, s>>>(c);
-    else k_place_paged<0><<<grid, 256, 0, s>>>(c);
+    if (p1) k_place_paged<1><<<grid, kPlaceThreads, 0, s>>>(c);
+    else if (p2) k_place_paged<2><<<grid, kPlaceThreads, 0, s>>>(c);
+    else k_place_paged<0><<<grid, kPlaceThreads, 0, s>>>(c);
   } else if (p1) {
-    k_place<1><<<grid, 256, 0, s>>>(c);
+    k_place<1><<<grid, kPlaceThreads, 0, s>>>(c);
   } else if (p2) {
-    k_place<2><<<grid, 256, 0, s>>>(c);
+    k_place<2><<<grid, kPlaceThreads, 0, s>>>(c);
   } else {
-    k_place<0><<<grid, 256, 0, s>>>(c);
+    k_place<0><<<grid, kPlaceThreads, 0, s>>>(c);
   }
   return hipGetLastError();
 }
@@ -1479,8 +1544,8 @@ hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s) {
   const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
   const int fgrid = (int)std::min<int64_t>(c.total_chunks, 512);
-  if (p1) k_ll_decode_p1<<<fgrid, 256, 0, s>>>(c, worklist);
-  else if (p2) k_ll_decode_p2<<<fgrid, 256, 0, s>>>(c, worklist);
+  if (p1) k_ll_decode_p1<kDecWaves><<<fgrid, 64 * kDecWaves, 0, s>>>(c, worklist);
+  else if (p2) k_ll_decode_p2<kDecWaves><<<fgrid, 64 * kDecWaves, 0, s>>>(c, worklist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (all_word_parallel(c)) return hipSuccess;
   k_ll_decode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
