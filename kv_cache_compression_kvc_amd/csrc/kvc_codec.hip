@@ -322,6 +322,36 @@ __device__ __forceinline__ float unpack_code(const uint32_t* w, int i) {
   else return (float)((w[i >> 2] >> (8 * (i & 3))) & 255u);
 }
 
+// Codes spread one per byte, so that each converts with one v_cvt_f32_ubyteN:
+// for a dword of packed codes, mask k holds codes k, k + K, k + 2K, k + 3K in
+// its four bytes (K = 8 / BITS masks per dword; the 8-bit codes are their own).
+template <int BITS>
+__device__ __forceinline__ void code_masks(const uint32_t* w, int ndw, uint32_t* m) {
+#pragma unroll
+  for (int d = 0; d < ndw; ++d) {
+    if constexpr (BITS == 8) {
+      m[d] = w[d];
+    } else if constexpr (BITS == 4) {
+      m[2 * d] = w[d] & 0x0F0F0F0Fu;
+      m[2 * d + 1] = (w[d] >> 4) & 0x0F0F0F0Fu;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m[4 * d + k] = (w[d] >> (2 * k)) & 0x03030303u;
+    }
+  }
+  // opaque to the compiler: otherwise it folds each byte's extraction back
+  // into a bit-field extract per code (v_bfe + v_cvt_f32_ubyte0)
+#pragma unroll
+  for (int k = 0; k < ndw * (8 / BITS); ++k) asm volatile("" : "+v"(m[k]));
+}
+// code i as binary32, from code_masks
+template <int BITS>
+__device__ __forceinline__ float code_of(const uint32_t* m, int i) {
+  constexpr int K = 8 / BITS;                         // codes per byte
+  const int d = i / (4 * K), r = i % (4 * K);
+  return (float)((m[K * d + r % K] >> (8 * (r / K))) & 255u);
+}
+
 // 16-bit pair -> two binary32 values
 template <bool BF16>
 __device__ __forceinline__ void unpack16(uint32_t u, float& lo, float& hi) {
@@ -1122,8 +1152,10 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
       mu[j] = f_from_h16(q.pw[j] >> 16);
     }
     float f[64];
+    uint32_t cm[16];                               // 2 BITS dwords of codes, 8 / BITS masks each
+    code_masks<BITS>(q.w, 2 * BITS, cm);
 #pragma unroll
-    for (int r2 = 0; r2 < 64; ++r2) f[r2] = __builtin_fmaf(unpack_code<BITS>(q.w, r2), sg[r2 / LG], mu[r2 / LG]);
+    for (int r2 = 0; r2 < 64; ++r2) f[r2] = __builtin_fmaf(code_of<BITS>(cm, r2), sg[r2 / LG], mu[r2 / LG]);
 
     fwht64_inreg(f);
     fwht_cross(f);
@@ -1225,8 +1257,10 @@ __global__ __launch_bounds__(256, 4) void k_decode_token_m(CallDesc c, int which
       mu[j] = f_from_h16(q.pw[j] >> 16);
     }
     float f[64];
+    uint32_t cm[16];                               // 2 BITS dwords of codes, 8 / BITS masks each
+    code_masks<BITS>(q.w, 2 * BITS, cm);
 #pragma unroll
-    for (int r2 = 0; r2 < 64; ++r2) f[r2] = __builtin_fmaf(unpack_code<BITS>(q.w, r2), sg[r2 / LG], mu[r2 / LG]);
+    for (int r2 = 0; r2 < 64; ++r2) f[r2] = __builtin_fmaf(code_of<BITS>(cm, r2), sg[r2 / LG], mu[r2 / LG]);
 
     fwht64_inreg(f);
     fwht_cross(f);
@@ -1723,8 +1757,10 @@ __global__ __launch_bounds__(256, 4) void k_decode_channel(CallDesc c, int which
       const float sg = f_from_h16(q.pw[p] & 0xffffu);
       const float mu = f_from_h16(q.pw[p] >> 16);
       // rows of tokens past the end hold finite filler that is never stored
+      uint32_t cm[8];                              // BITS dwords of codes, 8 / BITS masks each
+      code_masks<BITS>(q.w[p], BITS, cm);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) zw[i * RP + lane] = __builtin_fmaf(unpack_code<BITS>(q.w[p], i), sg, mu);
+      for (int i = 0; i < 32; ++i) zw[i * RP + lane] = __builtin_fmaf(code_of<BITS>(cm, i), sg, mu);
       wave_sync();
       if (hf == p) {
         const float* rrow = zw + v * RP;
