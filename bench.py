@@ -436,8 +436,9 @@ def layer_pipeline(d: Dense, steps, warmup) -> dict:
     evs = [torch.cuda.Event() for _ in range(L)]
 
     def pipe(do_enc=True, do_dec=True):
-        sa.wait_stream(s)
-        sb.wait_stream(s)
+        base = torch.cuda.current_stream()             # the capturing stream under graph capture
+        sa.wait_stream(base)
+        sb.wait_stream(base)
         for l in range(L):
             if do_enc:
                 p1.encode(d.k[l], d.v[l], T, bufs[l], wa, sync=False, stream=sa)
@@ -446,17 +447,38 @@ def layer_pipeline(d: Dense, steps, warmup) -> dict:
                 if do_enc:
                     sb.wait_event(evs[l])
                 p1.decode(bufs[l], ms1, T, d.kd[l], d.vd[l], wb, stream=sb)
-        s.wait_stream(sa)
-        s.wait_stream(sb)
+        base.wait_stream(sa)
+        base.wait_stream(sb)
 
     pipe_ms = timed(pipe, steps, warmup, s)
     enc1_ms = timed(lambda: pipe(True, False), steps, 2, s)
     dec1_ms = timed(lambda: pipe(False, True), steps, 2, s)
     assert p1.query_status(wa) == K.OK and p1.query_status(wb) == K.OK
-    del bufs, wa, wb
+    # host time to enqueue one pass (the calls return without waiting)
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    pipe()
+    host_ms = (time.perf_counter() - h0) * 1e3
+    torch.cuda.synchronize()
+    # the same pass captured once in a HIP graph (both streams and the events
+    # between them) and replayed: a serving loop's form without the host's
+    # per-call launch cost
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(s)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            pipe()
+    s.wait_stream(side)
+    torch.cuda.synchronize()
+    graph_ms = timed(g.replay, steps, 2, s)
+    assert p1.query_status(wa) == K.OK and p1.query_status(wb) == K.OK
+    del g, bufs, wa, wb
     return {"ms_per_step": round(pipe_ms, 4), "GBps": round(gbps(U, pipe_ms), 3),
             "encode_ms": round(enc1_ms, 4), "encode_GBps": round(gbps(U, enc1_ms), 3),
             "decode_ms": round(dec1_ms, 4), "decode_GBps": round(gbps(U, dec1_ms), 3),
+            "host_enqueue_ms": round(host_ms, 3),
+            "graph_replay": {"ms_per_step": round(graph_ms, 4), "GBps": round(gbps(U, graph_ms), 3)},
             "calls": f"{L} one-layer encodes on one stream, {L} one-layer decodes on another, "
                      "each decode after its layer's encode (an event)"}
 

@@ -164,7 +164,7 @@ void request_layout(const kvc_plan_s* p, int T, ReqDesc& rq) {
 
 // Workspace carving shared by all calls.
 struct WsLayout {
-  int64_t ctl, sizes, offs, worklist, flags, scan, codes, params, reqs, slabs, delta, total;
+  int64_t ctl, sizes, offs, worklist, flags, scan, counts, codes, params, reqs, slabs, delta, total;
 };
 
 // Bytes of the token-delta area of a dense encode: the transformed copy of
@@ -196,7 +196,9 @@ WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int
   w.flags = a256(w.worklist + 4 * std::max<int64_t>(nchunks, 1));
   // look-back words of the dense scan: one per 1024 chunks
   w.scan = a256(w.flags + 4 * (nchunks + (nchunks + 63) / 64 + 1));
-  w.codes = a256(w.scan + 8 * (nchunks / 1024 + 1));
+  // the fused encoders' non-zero word counters: kNnzSlots per chunk
+  w.counts = a256(w.scan + 8 * (nchunks / 1024 + 1));
+  w.codes = a256(w.counts + 4 * (int64_t)kNnzSlots * std::max<int64_t>(nchunks, 1));
   w.params = a256(w.codes + codes_area);
   w.reqs = a256(w.params + params_area);
   w.slabs = a256(w.reqs + (R > 1 ? R * (int64_t)sizeof(ReqDesc) : 0));
@@ -616,6 +618,7 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   c.codes_out = ws + w.codes;
   c.stream = (uint8_t*)d_out;
   c.chunk_sizes = (uint32_t*)(ws + w.sizes);
+  c.chunk_counts = (uint32_t*)(ws + w.counts);
   c.chunk_offs = (uint64_t*)(ws + w.offs);
   c.ctl = (Control*)(ws + w.ctl);
   c.total_chunks = c.one.nchunks[0] + c.one.nchunks[1];
@@ -624,6 +627,9 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   c.scan_state = (uint64_t*)(ws + w.scan);
   for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads, false);
   c.nnz_pipe = lossless_pipe(p->cfg.lossless);
+#ifdef KVC_NO_FUSED_COUNT
+  c.nnz_pipe = 0;
+#endif
   for (int k = 0; k < 2; ++k) c.nnz_sec[k] = (c.nnz_pipe && fused_count_ok(p->pol[k], tokens, p->cfg.chunk_bytes)) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -644,7 +650,11 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   }
   if ((e = timed(KVC_KERNEL_ENCODE_K, s, [&] { return fused_all(p, c, tb, 0, true, s); })) != hipSuccess) return hip_fail(e, "encode K");
   if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return fused_all(p, c, tb, 1, true, s); })) != hipSuccess) return hip_fail(e, "encode V");
-  if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
+  // every chunk counted by the fused kernels and encoded by the placement:
+  // the scan turns the counts into sizes itself
+  c.counts_to_sizes = (c.nnz_pipe && c.nnz_sec[0] && c.nnz_sec[1] && all_word_parallel(c)) ? 1 : 0;
+  if (!c.counts_to_sizes)
+    if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan_dense(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
   if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_place(c, s); })) != hipSuccess) return hip_fail(e, "place");
   if (h_out_bytes) {
@@ -704,8 +714,8 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
     if ((st = upload_slabs(p, tokens, ws + w.slabs, s, c, tb)) != KVC_OK) return st;
     c.direct[0] = c.direct[1] = 0;
   }
+  c.validate_in_reset = 1;                           // one launch clears the status and checks the header
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
-  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_validate(c, s); })) != hipSuccess) return hip_fail(e, "validate");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan_dense(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
   if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return fused_all(p, c, tb, 0, false, s); })) != hipSuccess) return hip_fail(e, "decode K");

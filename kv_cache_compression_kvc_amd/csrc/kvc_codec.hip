@@ -609,16 +609,22 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
   return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
          __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
+// counter slot of this wave: the waves writing one chunk's codes spread over
+// kNnzSlots addresses
+__device__ __forceinline__ uint32_t* nnz_slot(const CallDesc& c, int64_t gci) {
+  const uint32_t w = (uint32_t)blockIdx.x * (blockDim.x >> 6) + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  return c.chunk_counts + gci * kNnzSlots + (w & (kNnzSlots - 1));
+}
 __device__ __forceinline__ void add_chunk_nnz(const CallDesc& c, int64_t gci, uint32_t v) {
   const uint32_t t = wave_sum(v);
-  if (__lane_id() == 0 && t) __hip_atomic_fetch_add(&c.chunk_sizes[gci], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__lane_id() == 0 && t) __hip_atomic_fetch_add(nnz_slot(c, gci), t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // as add_chunk_nnz when only lanes L0..L3 hold non-zero counts
 template <int L0, int L1, int L2, int L3>
 __device__ __forceinline__ void add_chunk_nnz4(const CallDesc& c, int64_t gci, uint32_t v) {
   const uint32_t t = __builtin_amdgcn_readlane(v, L0) + __builtin_amdgcn_readlane(v, L1) +
                      __builtin_amdgcn_readlane(v, L2) + __builtin_amdgcn_readlane(v, L3);
-  if (__lane_id() == 0 && t) __hip_atomic_fetch_add(&c.chunk_sizes[gci], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__lane_id() == 0 && t) __hip_atomic_fetch_add(nnz_slot(c, gci), t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t u64of(uint32_t lo, uint32_t hi) { return ((uint64_t)hi << 32) | lo; }
 

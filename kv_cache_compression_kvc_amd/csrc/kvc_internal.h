@@ -13,6 +13,10 @@ constexpr int kHeadDim = 128;          // head_dim the kernels are written for
 constexpr uint32_t kMagic = 0x3143564Bu;
 constexpr int kHeaderBytes = 64;
 constexpr uint32_t kRawFlag = 0x80000000u;
+// Non-zero-word counters per chunk that the fused encoders add to (a wave
+// picks one by its index), so that the waves of one chunk spread their
+// atomics over several addresses; the scan and the size pass sum them.
+constexpr int kNnzSlots = 16;
 
 // Status word bits recorded by kernels in the workspace control block.
 enum : uint32_t {
@@ -99,6 +103,10 @@ struct CallDesc {
                              //   2 = paged, chunks placed from the workspace (k_place_paged)
   uint32_t* place_flags;     //   [total chunks] read announcements, then [ceil(total / 64)] group counts
   uint64_t* scan_state;      // dense calls: look-back words of the chunk-size scan, one per 1024 chunks
+  int counts_to_sizes;       // dense encode: every chunk is counted by the fused kernels and
+                             //   encoded by the placement, so the scan turns counts into sizes
+                             //   itself (no size pass)
+  int validate_in_reset;     // dense decode: the reset kernel also checks the header
   int nnz_pipe;              // encode: 1 or 2 when the fused kernels count the non-zero RZE
   int nnz_sec[2];            //   words of pipeline P1 / P2 per chunk (into chunk_sizes), per section
   uint8_t* params_ws;        // workspace parameter staging area (paged encode)
@@ -107,6 +115,7 @@ struct CallDesc {
   uint64_t* req_offsets_out;    // paged encode: written by the scan
   uint64_t stream_bytes;     // decode: bytes available in the input
   uint32_t* chunk_sizes;     // [total chunks] stored sizes | raw flag
+  uint32_t* chunk_counts;    // encode: [total chunks][kNnzSlots] non-zero RZE word counts of the fused encoders
   uint64_t* chunk_offs;      // [total chunks + 1] exclusive scan of align16(stored)
   Control* ctl;
   int64_t total_chunks;
@@ -135,6 +144,9 @@ hipError_t launch_compact(const CallDesc& c, hipStream_t s);
 hipError_t launch_place(const CallDesc& c, hipStream_t s);
 hipError_t launch_validate(const CallDesc& c, hipStream_t s);
 hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s);
+// Whether a one-request call's chunks all go to the word-parallel kernels (a
+// standard pipeline and every chunk size a multiple of its block).
+bool all_word_parallel(const CallDesc& c);
 // 16-bit passthrough slabs of a mixed tensor: gather into the codes section
 // (encode) or scatter back into the tensor (decode)
 hipError_t launch_slab_copy(const CallDesc& c, int which, bool encode, hipStream_t s);

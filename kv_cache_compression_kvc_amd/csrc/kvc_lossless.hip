@@ -71,12 +71,26 @@ __device__ __forceinline__ ChunkLoc locate_chunk(const CallDesc& c, const ReqDes
 
 __device__ __forceinline__ int64_t align16(int64_t x) { return (x + 15) & ~(int64_t)15; }
 
+// non-zero RZE words the fused encoders counted for chunk k (the sum of its slots)
+__device__ __forceinline__ uint32_t chunk_count(const CallDesc& c, int64_t k) {
+  const uint4* q = (const uint4*)(c.chunk_counts + k * kNnzSlots);
+  uint32_t t = 0;
+#pragma unroll
+  for (int i = 0; i < kNnzSlots / 4; ++i) {
+    const uint4 x = q[i];
+    t += x.x + x.y + x.z + x.w;
+  }
+  return t;
+}
+
 __device__ __forceinline__ uint64_t stream_base(const CallDesc& c, int r, bool encode) {
   if (c.R == 1 && c.req_offsets == nullptr && c.req_offsets_out == nullptr) return 0;
   return encode ? c.req_offsets_out[r] : c.req_offsets[r];
 }
 
 // ------------------------------------------------------------------ reset
+
+__device__ void validate_request(const CallDesc& c, int r);
 
 __global__ void k_reset(CallDesc c) {
   Control* ctl = c.ctl;
@@ -89,13 +103,18 @@ __global__ void k_reset(CallDesc c) {
     ctl->pad[2] = 0;   // tickets of the single-pass placement
     ctl->pad[3] = ~0ull;  // first chunk with placement work (a minimum)
     ctl->pad[4] = 0;   // tickets of the dense scan
+    ctl->pad[5] = 0;   // compressed chunks left to the word-parallel decode kernels
+  }
+  if (c.validate_in_reset && blockIdx.x == 0) {
+    __syncthreads();                                   // the status word is clear before any check sets it
+    if (threadIdx.x < 64) validate_request(c, 0);
   }
   if (c.scan_state && blockIdx.x == 0)
     for (int64_t i = threadIdx.x; i <= c.total_chunks / 1024; i += blockDim.x) c.scan_state[i] = 0;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, di = (int64_t)gridDim.x * blockDim.x;
   // the fused encoders accumulate per-chunk non-zero word counts here
   if (c.nnz_pipe)
-    for (int64_t i = i0; i < c.total_chunks; i += di) c.chunk_sizes[i] = 0;
+    for (int64_t i = i0; i < c.total_chunks * (kNnzSlots / 4); i += di) ((uint4*)c.chunk_counts)[i] = make_uint4(0, 0, 0, 0);
   if (c.place_flags)
     for (int64_t i = i0; i < c.total_chunks + (c.total_chunks + 63) / 64; i += di) c.place_flags[i] = 0;
 }
@@ -394,8 +413,7 @@ __global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, uint32_t* worklist
       const uint64_t* src = (const uint64_t*)(c.codes + L.src);
       uint32_t nnz;
       if (c.nnz_pipe == pipe && c.nnz_sec[L.w]) {
-        nnz = c.chunk_sizes[ch];
-        __syncthreads();                  // every thread read it before thread 0 overwrites it
+        nnz = chunk_count(c, ch);
       } else {
         nnz = (pipe == 1) ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
       }
@@ -585,6 +603,8 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
   // this block's chunks are blockIdx.x + gridDim.x * i; NT at a time are
   // checked in parallel and the block then works through those to decode
   __shared__ uint32_t cand[NT];
+  // nothing to decode (e.g. every chunk raw): leave at once
+  if (__hip_atomic_load((const uint32_t*)&c.ctl->pad[5], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
   for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += NT) {
   {
     const int64_t mine = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + threadIdx.x);
@@ -656,6 +676,8 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
   // this block's chunks are blockIdx.x + gridDim.x * i; NT at a time are
   // checked in parallel and the block then works through those to decode
   __shared__ uint32_t cand[NT];
+  // nothing to decode (e.g. every chunk raw): leave at once
+  if (__hip_atomic_load((const uint32_t*)&c.ctl->pad[5], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
   for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += NT) {
   {
     const int64_t mine = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + threadIdx.x);
@@ -716,7 +738,7 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
 // Whether every chunk of a one-request call goes to the word-parallel
 // kernels (a standard pipeline, and every chunk size a multiple of its
 // block): then the stage engine's worklist stays empty and it is not launched.
-static bool all_word_parallel(const CallDesc& c) {
+bool all_word_parallel(const CallDesc& c) {
   const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
   if (c.R != 1 || !(p1 || p2)) return false;
@@ -821,7 +843,7 @@ constexpr int kScanPer = 1024;
 constexpr uint64_t kLbAgg = 1ull << 62, kLbIncl = 2ull << 62, kLbVal = (1ull << 62) - 1;
 
 __global__ __launch_bounds__(256) void k_scan_dense(CallDesc c, int from_table) {
-  __shared__ uint64_t sh[256];
+  __shared__ uint32_t sh32[4];
   __shared__ int64_t sb[2];
   const int t = threadIdx.x;
   const int64_t N = c.total_chunks;
@@ -842,14 +864,23 @@ __global__ __launch_bounds__(256) void k_scan_dense(CallDesc c, int from_table) 
         if (pos + 4 <= c.stream_bytes && pos + 4 <= (uint64_t)rq.payload_off) e[i] = *(const uint32_t*)(c.stream + pos);
         else set_status2(c.ctl, kStCorrupt);
         c.chunk_sizes[k] = e[i];
+      } else if (c.counts_to_sizes) {
+        // a counted chunk of a standard pipeline: its encoded size, or raw
+        // when that does not shrink it (the size pass's rule)
+        const int64_t n = locate_chunk(c, rq, 0, k).n;
+        const int64_t size = n / 16 + 2 * (int64_t)chunk_count(c, k);
+        e[i] = (size >= n) ? ((uint32_t)n | kRawFlag) : (uint32_t)size;
+        c.chunk_sizes[k] = e[i];
       } else {
         e[i] = c.chunk_sizes[k];
       }
     }
     sum += (uint64_t)align16(e[i] & 0x7fffffffu);
   }
-  uint64_t agg;
-  const uint64_t ex = block_exclusive_scan<uint64_t>(sum, sh, agg);
+  // a block's 1024 chunks hold at most 64 MiB: the block-local scan fits 32 bits
+  uint32_t agg32;
+  const uint64_t ex = block_excl_scan_u32<4>((uint32_t)sum, sh32, agg32);
+  const uint64_t agg = agg32;
   if (t == 0) {
     uint64_t* st = c.scan_state;
     uint64_t prefix = 0;
@@ -1298,6 +1329,10 @@ __global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 
   const int64_t kf = (int64_t)min<uint64_t>(c.ctl->pad[3], (uint64_t)N);
   const int64_t nb0 = (kf + 63) / 64, last = nb0 + (N - kf);
   const ReqDesc& rq = c.one;
+  // there are last + 1 tickets: the blocks past them leave without taking one
+  // (one atomic counter that every block of a large grid hit was the cost of
+  // small calls whose chunks all stay in place)
+  if ((int64_t)blockIdx.x > last) return;
   const XposeLane X = xpose_lane();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   uint32_t* ticket = (uint32_t*)&c.ctl->pad[2];
@@ -1369,9 +1404,8 @@ hipError_t launch_place(const CallDesc& c, hipStream_t s) {
 
 // ------------------------------------------------------------------ decode
 
-// Check each request's header against the plan and the bytes available.
-__global__ __launch_bounds__(64) void k_validate(CallDesc c) {
-  for (int r = blockIdx.x; r < c.R; r += gridDim.x) {
+// Check request r's header against the plan and the bytes available (64 threads).
+__device__ void validate_request(const CallDesc& c, int r) {
     const ReqDesc rq = req_at(c, r);
     const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
     const int t = threadIdx.x;
@@ -1414,11 +1448,15 @@ __global__ __launch_bounds__(64) void k_validate(CallDesc c) {
       // the width map must be the plan's
       const uint8_t* h = c.stream + base;
       const int64_t mapn = 2 * (int64_t)c.layers * c.heads;
-      for (int64_t p = t; p < mapn; p += blockDim.x)
+      for (int64_t p = t; p < mapn; p += 64)
         if (h[64 + p] != c.width_map[p]) bad = kStMismatch;
     }
     if (bad) set_status2(c.ctl, bad);
-  }
+}
+
+// Check each request's header against the plan and the bytes available.
+__global__ __launch_bounds__(64) void k_validate(CallDesc c) {
+  for (int r = blockIdx.x; r < c.R; r += gridDim.x) validate_request(c, r);
 }
 
 hipError_t launch_validate(const CallDesc& c, hipStream_t s) {
@@ -1430,6 +1468,7 @@ hipError_t launch_validate(const CallDesc& c, hipStream_t s) {
 // Block 0 also checks that each stream's chunk sizes add up to its header total.
 __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* worklist) {
   __shared__ uint32_t sh32[256];
+  uint32_t wp = 0;                                   // thread 0: compressed chunks left to the word-parallel kernels
   if (blockIdx.x == 0) {
     for (int r = threadIdx.x; r < c.R; r += blockDim.x) {
       const ReqDesc rq = req_at(c, r);
@@ -1490,10 +1529,14 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
       const int64_t nv = L.n / 16;
       for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) dst[k] = src[k];
       for (int64_t p = nv * 16 + threadIdx.x; p < L.n; p += blockDim.x) c.codes[L.src + p] = c.stream[pos + p];
-    } else if (!fast_eligible(fast_pipeline(c), L.n) && threadIdx.x == 0) {
-      push_work(c, worklist, ch);                   // the stage engine; the word-parallel kernels find theirs
+    } else if (!fast_eligible(fast_pipeline(c), L.n)) {
+      if (threadIdx.x == 0) push_work(c, worklist, ch);   // the stage engine
+    } else if (threadIdx.x == 0) {
+      ++wp;                                               // the word-parallel kernels find theirs by index
     }
   }
+  if (threadIdx.x == 0 && wp)
+    __hip_atomic_fetch_add((uint32_t*)&c.ctl->pad[5], wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(256) void k_ll_decode_generic(CallDesc c, const uint32_t* worklist) {
