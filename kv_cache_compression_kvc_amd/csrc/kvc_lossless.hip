@@ -71,6 +71,20 @@ __device__ __forceinline__ ChunkLoc locate_chunk(const CallDesc& c, const ReqDes
 
 __device__ __forceinline__ int64_t align16(int64_t x) { return (x + 15) & ~(int64_t)15; }
 
+// Raw buffer access (wave-uniform base and size; out-of-range lanes read zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ll_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 ll_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef int int4v_ __attribute__((ext_vector_type(4)));
+  const int4v_ x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4((uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w);
+}
+
 // non-zero RZE words the fused encoders counted for chunk k (the sum of its slots)
 __device__ __forceinline__ uint32_t chunk_count(const CallDesc& c, int64_t k) {
   const uint4* q = (const uint4*)(c.chunk_counts + k * kNnzSlots);
@@ -580,7 +594,9 @@ __device__ __forceinline__ bool wp_decode_chunk(const CallDesc& c, int64_t ch, i
 // a 64 KiB LDS buffer, so two blocks fit a CU.  Measured on the 70B shape with
 // half of the 64-token blocks zero: placement 1.21 ms at 4 waves, 0.98 ms at
 // 8 (4 waves per SIMD, a few registers spilled), 1.33 ms at 16 (one block per
-// CU); lossless decode 0.75 ms at 4 waves, 0.93 ms at 8 (spills), 1.17 ms at 16.
+// CU); lossless decode 0.75 ms at 4 waves, 0.93 ms at 8 (spills), 1.17 ms at 16,
+// and 0.91 ms with one 8-wave block per CU holding two chunk buffers, the next
+// chunk loaded straight into LDS while the current one is expanded.
 #ifndef KVC_PLACE_WAVES
 #define KVC_PLACE_WAVES 8
 #endif
@@ -1082,20 +1098,6 @@ constexpr uint64_t kPlaceWaitTicks = 1ull << 27;
 
 __device__ __forceinline__ uint32_t ld_flag(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Raw buffer access (wave-uniform base and size; out-of-range lanes read zero).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t ll_rsrc(const void* p, uint32_t bytes) {
-  const uint64_t a = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
-                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-__device__ __forceinline__ uint4 ll_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  typedef int int4v_ __attribute__((ext_vector_type(4)));
-  const int4v_ x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
-  return make_uint4((uint32_t)x.x, (uint32_t)x.y, (uint32_t)x.z, (uint32_t)x.w);
 }
 
 // first chunk whose codes end after payload offset `fin` (dense stream)
