@@ -537,6 +537,29 @@ def paged(wl, steps, warmup) -> dict:
     return res
 
 
+def bandwidth_probes(total_bytes: int = 4 << 30, reps: int = 5) -> dict:
+    """What HBM gives a kernel that only streams, with the fused kernels'
+    16-byte accesses and store policy: read-only, write-only, copy, and the
+    read:write mixes of the fused encoders (about 4:1) and decoders (about
+    1:4).  GB/s counts bytes read plus bytes written."""
+    import torch
+    import kv_cache_compression_kvc_amd as K
+    dev = torch.device("cuda:0")
+    a = torch.empty(total_bytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(total_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.uint8, device=dev)
+    s = torch.cuda.current_stream()
+    out = {}
+    for r, w in ((1, 0), (0, 1), (1, 1), (4, 1), (1, 4)):
+        items = total_bytes // (16 * max(r, w))
+        fn = lambda: K.probe_bandwidth(a, b, items, r, w, sink, s)
+        ms = timed(fn, reps, 2, s)
+        out[f"{r}:{w}"] = {"GBps": round(items * 16 * (r + w) / (ms * 1e-3) / 1e9, 1),
+                           "frac": round(items * 16 * (r + w) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del a, b, sink
+    return out
+
+
 def free():
     import torch
     gc.collect()
@@ -598,6 +621,9 @@ def main():
     copy_gbps = 2 * args.copy_bytes * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     log(f"device copy of {args.copy_bytes} bytes: {copy_gbps:.1f} GB/s (read + write)")
     del ca, cb
+    probes = bandwidth_probes()
+    log("bandwidth reference (reads:writes of 16-byte lines): " +
+        ", ".join(f"{k_} {v_['GBps']:.0f} GB/s" for k_, v_ in probes.items()))
 
     wl = W.WORKLOADS[args.workload]
     dk, dv = (int(x) for x in args.delta.split(":"))
@@ -676,6 +702,7 @@ def main():
     result["kernel_ms_per_launch"] = {k_: round(v_, 4) for k_, v_ in kms.items()}
     result["fused_kernels"] = {k_: v_ for k_, v_ in head["kernels"].items() if "ENCODE" in k_ or "DECODE" in k_}
     result["device_copy_GBps"] = round(copy_gbps, 1)
+    result["bandwidth_reference"] = probes
     result["graph_replay"] = (None if graph_ms is None else
                               {"ms_per_step": round(graph_ms, 4), "GBps": round(gbps(U, graph_ms), 3)})
     result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,

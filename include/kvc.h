@@ -264,6 +264,17 @@ kvc_status kvc_profile_enable(int on);
 kvc_status kvc_profile_reset(void);
 kvc_status kvc_profile_query(int kind, double* total_ms, int64_t* launches);
 
+/* Bandwidth reference for the measurements (no part of the compression
+ * path): enqueue on `stream` a streaming kernel over `items` items, each
+ * reading `reads` 16-byte lines of d_src (items * reads * 16 bytes) and
+ * writing `writes` 16-byte lines of d_dst (items * writes * 16 bytes), with
+ * the buffer accesses and store cache policy of the fused kernels and no
+ * other work.  (reads, writes) is one of (1,0), (0,1), (1,1), (2,1), (4,1),
+ * (1,4); other pairs return KVC_ERR_UNSUPPORTED.  d_sink is a 4-byte device
+ * word the read-only form may write.  Time it with events on `stream`. */
+kvc_status kvc_probe_bandwidth(const void* d_src, void* d_dst, int64_t items, int reads, int writes,
+                               uint32_t* d_sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

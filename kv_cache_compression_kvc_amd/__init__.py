@@ -89,6 +89,7 @@ def lib():
             "kvc_profile_enable": [C.c_int],
             "kvc_profile_reset": [],
             "kvc_profile_query": [C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_int64)],
+            "kvc_probe_bandwidth": [P, P, I64, C.c_int, C.c_int, P, P],
             "kvc_predicted_jct": [C.POINTER(Profile), C.POINTER(RequestContext), C.POINTER(C.c_double)],
             "kvc_selector_create": [C.POINTER(Profile), I32, C.POINTER(SelectorConfig), C.POINTER(C.c_void_p)],
             "kvc_selector_destroy": [P],
@@ -264,6 +265,12 @@ def profile_query(kind) -> tuple:
     ms, n = C.c_double(0), C.c_int64(0)
     _check(lib().kvc_profile_query(k, C.byref(ms), C.byref(n)), "kvc_profile_query")
     return ms.value, n.value
+
+
+def probe_bandwidth(src, dst, items: int, reads: int, writes: int, sink, stream=None):
+    """Enqueue the bandwidth reference kernel (kvc_probe_bandwidth)."""
+    _check(lib().kvc_probe_bandwidth(_ptr(src), _ptr(dst), items, reads, writes, _ptr(sink), _stream(stream)),
+           "kvc_probe_bandwidth")
 
 
 # ---------------------------------------------------------------- selection

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvc.so")
-SOURCES = ["kvc_api.cpp", "kvc_codec.hip", "kvc_lossless.hip", "kvc_select.cpp"]
+SOURCES = ["kvc_api.cpp", "kvc_codec.hip", "kvc_lossless.hip", "kvc_probe.hip", "kvc_select.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
