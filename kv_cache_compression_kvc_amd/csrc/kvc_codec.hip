@@ -51,6 +51,27 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Element i of a table that no wave of the running launch writes (chunk
+// sizes and offsets, request descriptors, block tables: all written by earlier
+// launches or the host), for an i that is the same in every lane of the wave
+// (the index is taken from the first active lane).  It is read through the scalar
+// cache: waiting for a scalar load does not wait for the wave's outstanding
+// vector stores, as waiting for a vector load would (one counter covers both),
+// so a tile's table lookups never drain the previous tile's stores.
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* base, int64_t i) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)i);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)i >> 32));
+  const int64_t iu = (int64_t)(((uint64_t)hi << 32) | lo);
+  static_assert(sizeof(T) % 4 == 0 && alignof(T) >= 4, "tables of whole dwords");
+  typedef const __attribute__((address_space(4))) uint32_t cdword;
+  cdword* src = (cdword*)base + iu * (int64_t)(sizeof(T) / 4);
+  uint32_t w[sizeof(T) / 4];
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 4); ++k) w[k] = src[k];
+  return __builtin_bit_cast(T, w);
+}
+
 typedef int int4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
 
@@ -450,7 +471,7 @@ __device__ __forceinline__ void set_status(Control* ctl, uint32_t bit) {
 }
 
 __device__ __forceinline__ ReqDesc load_req(const CallDesc& c, int r) {
-  return (c.R == 1) ? c.one : c.reqs[r];
+  return (c.R == 1) ? c.one : uniform_load(c.reqs, r);
 }
 
 __device__ __forceinline__ int find_req_by_tile(const CallDesc& c, int which, int64_t tile) {
@@ -458,7 +479,8 @@ __device__ __forceinline__ int find_req_by_tile(const CallDesc& c, int which, in
   int lo = 0, hi = c.R - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    const int64_t b = which ? c.reqs[mid].tile_begin[1] : c.reqs[mid].tile_begin[0];
+    const ReqDesc rm = uniform_load(c.reqs, mid);
+    const int64_t b = which ? rm.tile_begin[1] : rm.tile_begin[0];
     if (b <= tile) lo = mid; else hi = mid - 1;
   }
   return lo;
@@ -471,7 +493,7 @@ __device__ __forceinline__ int64_t page_run_base(const CallDesc& c, const ReqDes
   const int64_t vpp = (int64_t)c.page_tokens * c.heads;     // vectors per page
   const int64_t page = vstart / vpp;
   const int64_t voff = vstart - page * vpp;
-  const int32_t blk = c.block_table[(int64_t)rq.row * c.max_blocks + page];
+  const int32_t blk = uniform_load(c.block_table, (int64_t)rq.row * c.max_blocks + page);
   ok = blk >= 0 && blk < c.num_blocks;
   if (!ok) return 0;
   return (((int64_t)l * c.num_blocks + blk) * c.page_tokens * c.heads + voff) * kHeadDim;
@@ -737,7 +759,7 @@ __device__ __forceinline__ TokTile enc_token_tile(const CallDesc& c, int which, 
       const int64_t tps = (T + 31) >> 5;
       const int sl = (int)(tile / tps);
       const int64_t t0 = (tile - (int64_t)sl * tps) * 32;
-      const SlabDesc sd = c.slabs[sl];
+      const SlabDesc sd = uniform_load(c.slabs, sl);
       t.vg0 = t0;
       t.nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, T - t0));
       t.src = in + (((int64_t)sd.l * T + t0) * c.heads + sd.h) * kHeadDim;
@@ -1003,7 +1025,7 @@ __device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, i
       const int64_t tps = (T + 31) >> 5;
       const int sl = (int)(tile / tps);
       const int64_t t0 = (tile - (int64_t)sl * tps) * 32;
-      const SlabDesc sd = c.slabs[sl];
+      const SlabDesc sd = uniform_load(c.slabs, sl);
       nv = (int)std::max<int64_t>(0, std::min<int64_t>(32, T - t0));
       d.nvo = nv;
       d.csrc = c.codes + pick(which, c.one.codes_off) + sd.codes_off + t0 * CB;
@@ -1025,15 +1047,15 @@ __device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, i
       // a tile never straddles chunks here; a raw chunk is read in place
       const int64_t ci = chunk_of(c, coff);
       const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
-      const uint32_t e = c.chunk_sizes[gci];
+      const uint32_t e = uniform_load(c.chunk_sizes, gci);
       if (e >> 31) {
-        const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] + (uint64_t)(coff - ci * c.chunk_bytes);
+        const uint64_t pos = (uint64_t)c.one.payload_off + uniform_load(c.chunk_offs, gci) + (uint64_t)(coff - ci * c.chunk_bytes);
         d.csrc = c.stream + pos;
         d.cbytes = (pos >= c.stream_bytes) ? 0u : (uint32_t)std::min<uint64_t>(d.cbytes, c.stream_bytes - pos);
       } else if (MIRROR && BITS == 2 && c.mirror[which]) {
         const int64_t n = std::min<int64_t>((int64_t)c.chunk_bytes, pick(which, c.one.codes_bytes) - ci * (int64_t)c.chunk_bytes);
         if ((n & 4095) == 0) {
-          const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci];
+          const uint64_t pos = (uint64_t)c.one.payload_off + uniform_load(c.chunk_offs, gci);
           const int64_t toff = coff - ci * (int64_t)c.chunk_bytes;
           d.p1 = 1;
           d.p1_n = (int)n;
@@ -1368,7 +1390,7 @@ __global__ __launch_bounds__(128, TAIL ? 4 : KVC_EC_WAVES) void k_encode_channel
     uint32_t* psec = prm;
     if (c.mixed) {
       const int sl = tile / n64;
-      const SlabDesc sd = c.slabs[sl];
+      const SlabDesc sd = uniform_load(c.slabs, sl);
       l = sd.l;
       h = sd.h;
       g64 = TAIL ? T / 64 : tile - sl * n64;
@@ -1622,7 +1644,7 @@ struct ChDecOrder {
     if (slabs) {
       const int tile = (int)(u >> 1);
       o.sl = tile / n64;
-      const SlabDesc sd = slabs[o.sl];
+      const SlabDesc sd = uniform_load(slabs, o.sl);
       o.l = sd.l; o.h = sd.h; o.g64 = tile - o.sl * n64; o.half = (int)(u & 1);
       o.k = 2 * o.h + o.half;
       return o;
@@ -1673,7 +1695,7 @@ __device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, WaveTi
   // (layer, head) within the section layout: a mixed slab is a one-layer, one-head run
   int l = wt.l, h = wt.h, Ho = H;
   if (wt.sl >= 0) {
-    const SlabDesc sd = c.slabs[wt.sl];
+    const SlabDesc sd = uniform_load(c.slabs, wt.sl);
     codes_sec += sd.codes_off;
     prm = (const uint32_t*)((const uint8_t*)prm + sd.params_off);
     l = 0; h = 0; Ho = 1;
@@ -1693,9 +1715,9 @@ __device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, WaveTi
         // a group block never straddles chunks here; a raw chunk is read in place
         const int64_t ci = chunk_of(c, boff);
         const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
-        const uint32_t e = c.chunk_sizes[gci];
+        const uint32_t e = uniform_load(c.chunk_sizes, gci);
         if (e >> 31) {
-          const uint64_t pos = (uint64_t)c.one.payload_off + c.chunk_offs[gci] +
+          const uint64_t pos = (uint64_t)c.one.payload_off + uniform_load(c.chunk_offs, gci) +
                                (uint64_t)(boff - ci * c.chunk_bytes) + (uint64_t)ch * colb;
           have = pos + (uint64_t)colb <= c.stream_bytes;
           col = c.stream + pos;
