@@ -849,6 +849,9 @@ kvc_status kvc_decode_paged(kvc_plan_t p, const void* d_in, size_t in_bytes, con
   c.total_chunks = j.chunks;
   c.tiles[0] = j.tiles[0];
   c.tiles[1] = j.tiles[1];
+  // raw chunks are read from the stream by the reconstruct kernels
+  c.direct[0] = c.direct[1] = 1;
+  c.straddle = 1;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (R > 1) {

@@ -1086,6 +1086,22 @@ __device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, i
     if (!pok) { if (__lane_id() == 0) set_status(c.ctl, kStCorrupt); nv = 0; }
     d.csrc = c.codes + pick(which, rq.codes_off) + vg0 * CB;
     d.cbytes = (uint32_t)nv * CB;
+    if (c.direct[which] && nv > 0) {
+      // the tile covers one or two chunks; when all are raw it reads the
+      // stream, where consecutive raw chunks lie back to back
+      const int64_t coff = vg0 * CB;
+      const int64_t ci0 = chunk_of(c, coff), ci1 = chunk_of(c, coff + d.cbytes - 1);
+      const int64_t g0 = rq.chunk_begin + (which ? rq.nchunks[0] : 0);
+      const uint32_t e0 = uniform_load(c.chunk_sizes, g0 + ci0);
+      const uint32_t e1 = (ci1 != ci0) ? uniform_load(c.chunk_sizes, g0 + ci1) : e0;
+      if ((e0 & e1) >> 31) {
+        const uint64_t pos = off + (uint64_t)rq.payload_off +
+                             (uniform_load(c.chunk_offs, g0 + ci0) - uniform_load(c.chunk_offs, rq.chunk_begin)) +
+                             (uint64_t)(coff - ci0 * c.chunk_bytes);
+        d.csrc = c.stream + pos;
+        d.cbytes = (pos >= c.stream_bytes) ? 0u : (uint32_t)std::min<uint64_t>(d.cbytes, c.stream_bytes - pos);
+      }
+    }
     params_base = c.stream + (pok ? off : 0) + pick(which, rq.params_off);
     bool ok;
     const int64_t base = page_run_base(c, rq, l, vstart, ok);

@@ -97,6 +97,9 @@ struct CallDesc {
   uint8_t* codes_out;        // encode: where compressed chunk bytes go (== codes: in place)
   int direct[2];             // decode: reconstruct kernels read raw chunks of K / V from the stream
   int mirror[2];             // decode: ... and decode TUPL8_1 -> BIT_8 -> RZE_2 chunks of 2-bit
+  int straddle;              // decode (paged): a reconstruct tile may cover two chunks; it reads the
+                             //   stream only if both are raw, so raw chunks next to a compressed one
+                             //   are still copied to the codes area
                              //   per-token codes themselves, from per-segment word counts that
                              //   k_ll_decode_raw leaves in the chunk's slot of the codes area
   int place;                 // encode: 1 = dense, finish the stream in one in-place pass (k_place);

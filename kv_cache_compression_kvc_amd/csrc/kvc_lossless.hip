@@ -1496,7 +1496,15 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
       if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
       continue;
     }
-    if (raw && c.direct[L.w]) {
+    bool in_place = raw && c.direct[L.w];
+    if (in_place && c.straddle) {
+      // a tile that also covers a compressed neighbour reads both from the codes area
+      const int64_t s0 = rq.chunk_begin + (L.w ? rq.nchunks[0] : 0), s1 = s0 + rq.nchunks[L.w];
+      const bool prev_c = ch > s0 && !(c.chunk_sizes[ch - 1] >> 31);
+      const bool next_c = ch + 1 < s1 && !(c.chunk_sizes[ch + 1] >> 31);
+      in_place = !(prev_c || next_c);
+    }
+    if (in_place) {
       // the reconstruct kernels read this chunk from the stream
     } else if (!raw && c.mirror[L.w] && fast_eligible(1, L.n)) {
       // the reconstruct kernels decode this chunk from the stream; they need

@@ -284,6 +284,52 @@ def test_paged_matches_oracle():
     assert np.array_equal(to_u16(kq), kqo) and np.array_equal(to_u16(vq), vqo)
 
 
+@pytest.mark.parametrize("kbits,vbits", [(4, 4), (8, 2)])
+def test_paged_mixed_raw_and_compressed_chunks(kbits, vbits):
+    """Paged pools with half of the pages zero and 4 KiB chunks: compressed and
+    raw chunks alternate, and the reconstruct tiles (32 vectors, starting at
+    layer boundaries that are not chunk-aligned) straddle pairs of chunks of
+    every kind.  A tile whose chunks are all raw reads the stream in place;
+    the others read the codes area, which must then hold the raw neighbours
+    of compressed chunks too."""
+    TP = W.TensorPolicy
+    wl = W.WORKLOADS["c4_paged_llama8b"].with_(layers=3, chunk_bytes=4096, k=TP(kbits, "token", 128),
+                                                v=TP(vbits, "token", 32))
+    batch = W.paged_layout(wl, requests=8, min_len=5, max_len=300)
+    kp, vp = W.paged_pools(wl, batch)
+    rng = np.random.default_rng(kbits)
+    for pool in (kp, vp):
+        zero = torch.from_numpy(rng.random(pool.shape[:2]) < 0.5)
+        pool[zero] = 0
+    log(f"paged mixed-chunk case K{kbits} V{vbits} lens {batch.seq_lens.tolist()}")
+    cfg = O.cfg_from_workload(wl)
+    st, ref, ref_offs = O.encode_paged(cfg, to_u16(kp), to_u16(vp), batch.num_blocks, wl.page_tokens,
+                                       batch.block_table, batch.seq_lens)
+    assert st == O.OK
+    plan = K.Plan(K.config_from_workload(wl, max_tokens=0))
+    ms, wsb = plan.sizes_paged(batch.seq_lens)
+    out = torch.full((ms,), 0xA5, dtype=torch.uint8, device=DEV)
+    ws = torch.full((wsb,), 0x5A, dtype=torch.uint8, device=DEV)
+    offs = torch.zeros(len(batch.seq_lens) + 1, dtype=torch.int64, device=DEV)
+    bt = torch.from_numpy(batch.block_table).to(DEV)
+    n = plan.encode_paged(kp.to(DEV), vp.to(DEV), batch.num_blocks, bt, batch.seq_lens, out, offs, ws)
+    assert np.array_equal(offs.cpu().numpy().astype(np.uint64), ref_offs)
+    assert np.array_equal(out[:n].cpu().numpy(), ref)
+    assert ref.size < ms, "no chunk compressed"
+    dst = W.paged_layout(wl, requests=8, min_len=5, max_len=300, stream=1)
+    kq = torch.zeros_like(kp, device=DEV)
+    vq = torch.zeros_like(vp, device=DEV)
+    s = torch.from_numpy(ref).to(DEV)
+    ws.fill_(0x5A)
+    plan.decode_paged(s, ref.size, offs, dst.seq_lens, kq, vq, dst.num_blocks,
+                      torch.from_numpy(dst.block_table).to(DEV), ws)
+    assert plan.query_status(ws) == K.OK
+    kqo = np.zeros_like(to_u16(kp)); vqo = np.zeros_like(to_u16(vp))
+    st = O.decode_paged(ref, ref_offs, kqo, vqo, dst.num_blocks, wl.page_tokens, dst.block_table, dst.seq_lens)
+    assert st == O.OK
+    assert np.array_equal(to_u16(kq), kqo) and np.array_equal(to_u16(vq), vqo)
+
+
 def test_encode_is_deterministic_and_async_size_matches():
     wl = C3
     L, T = 2, 256
