@@ -115,6 +115,22 @@ bool fused_count_ok(const TensorPol& p, int T, uint32_t chunk_bytes) {
   return p.group == 64 && T % 64 == 0 && chunk_bytes % (kHeadDim * 64 * p.bits / 8) == 0;
 }
 
+// Whether the fused encoders of a paged call can count a section's non-zero
+// RZE words.  TUPL8_1 -> RZE_2 counts per aligned 16-byte unit, which every
+// tile covers whole.  TUPL8_1 -> BIT_8 -> RZE_2 counts per aligned 1 KiB
+// region, which a tile covers whole only if every layer of every request
+// starts on a region boundary.  A tile that covers two chunks splits its
+// count between them.
+bool paged_count_ok(const TensorPol& p, int pipe, int H, const int32_t* lens, int R) {
+  if (p.axis != 0) return false;
+  if (pipe == 2) return true;
+  if (pipe != 1) return false;
+  const int64_t layer_vec_bytes = (int64_t)H * kHeadDim * p.bits / 8;
+  for (int r = 0; r < R; ++r)
+    if (((int64_t)lens[r] * layer_vec_bytes) % 1024) return false;
+  return true;
+}
+
 // Codes / parameter bytes of one (layer, head) slab of width `bits` (16:
 // the 16-bit values themselves): the sections of a one-layer, one-head
 // uniform stream of that width.
@@ -655,7 +671,7 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   c.counts_to_sizes = (c.nnz_pipe && c.nnz_sec[0] && c.nnz_sec[1] && all_word_parallel(c)) ? 1 : 0;
   if (!c.counts_to_sizes)
     if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
-  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan_dense(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
+  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
   if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_place(c, s); })) != hipSuccess) return hip_fail(e, "place");
   if (h_out_bytes) {
     Control h;
@@ -716,7 +732,7 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
   }
   c.validate_in_reset = 1;                           // one launch clears the status and checks the header
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
-  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan_dense(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
+  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
   if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return fused_all(p, c, tb, 0, false, s); })) != hipSuccess) return hip_fail(e, "decode K");
   if ((e = timed(KVC_KERNEL_DECODE_V, s, [&] { return fused_all(p, c, tb, 1, false, s); })) != hipSuccess) return hip_fail(e, "decode V");
@@ -791,6 +807,12 @@ kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_
   c.tiles[0] = j.tiles[0];
   c.tiles[1] = j.tiles[1];
   c.place = 2;                   // chunks go from the workspace straight into the request streams
+  c.scan_state = (uint64_t*)(ws + w.scan);
+  // the fused encoders count the non-zero RZE words of each chunk, so the
+  // size pass reads only counters
+  c.chunk_counts = (uint32_t*)(ws + w.counts);
+  c.nnz_pipe = lossless_pipe(p->cfg.lossless);
+  for (int k = 0; k < 2; ++k) c.nnz_sec[k] = paged_count_ok(p->pol[k], c.nnz_pipe, p->cfg.kv_heads, lens, R) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (R > 1) {
@@ -849,6 +871,7 @@ kvc_status kvc_decode_paged(kvc_plan_t p, const void* d_in, size_t in_bytes, con
   c.total_chunks = j.chunks;
   c.tiles[0] = j.tiles[0];
   c.tiles[1] = j.tiles[1];
+  c.scan_state = (uint64_t*)(ws + w.scan);
   // raw chunks are read from the stream by the reconstruct kernels
   c.direct[0] = c.direct[1] = 1;
   c.straddle = 1;

@@ -956,15 +956,23 @@ __global__ __launch_bounds__(256, 4) void k_encode_token(CallDesc c, int which) 
               cnt += nz_bytes64(u64of(wv[h][4 * u], wv[h][4 * u + 1]) | u64of(wv[h][4 * u + 2], wv[h][4 * u + 3]));
         }
       }
-      int64_t cbase;
+      const int64_t coff = t.vg0 * CB;
+      const int64_t ci = chunk_of(c, coff);
       if constexpr (PAGED) {
         const int r = find_req_by_tile(c, which, tile);
         const ReqDesc rq = load_req(c, r);
-        cbase = rq.chunk_begin + (which ? rq.nchunks[0] : 0);
+        const int64_t cbase = rq.chunk_begin + (which ? rq.nchunks[0] : 0);
+        // a tile may cover two chunks: a lane counts for the chunk of its vector
+        const int64_t vb = ((ci + 1) * (int64_t)c.chunk_bytes - coff) / CB;
+        if (vb < t.nv) {
+          add_chunk_nnz(c, cbase + ci, v < vb ? cnt : 0u);
+          add_chunk_nnz(c, cbase + ci + 1, v < vb ? 0u : cnt);
+        } else {
+          add_chunk_nnz(c, cbase + ci, cnt);
+        }
       } else {
-        cbase = which ? c.one.nchunks[0] : 0;
+        add_chunk_nnz(c, (which ? c.one.nchunks[0] : 0) + ci, cnt);
       }
-      add_chunk_nnz(c, cbase + chunk_of(c, t.vg0 * CB), cnt);
     }
     const __amdgpu_buffer_rsrc_t prs = make_rsrc(t.params_base + t.vg0 * NGV * 4, (uint32_t)t.nv * NGV * 4);
     const uint32_t prow = (uint32_t)v * NGV * 4;

@@ -142,7 +142,6 @@ hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s);
 // Token delta over a dense [layers][T][heads][128] tensor of 16-bit values:
 // forward (x -> y, out of place) or inverse (in place, x == y).
 hipError_t launch_delta(const CallDesc& c, int which, int T, bool forward, const void* x, void* y, hipStream_t s);
-hipError_t launch_scan_dense(const CallDesc& c, bool from_table, hipStream_t s);
 hipError_t launch_compact(const CallDesc& c, hipStream_t s);
 hipError_t launch_place(const CallDesc& c, hipStream_t s);
 hipError_t launch_validate(const CallDesc& c, hipStream_t s);

@@ -782,92 +782,32 @@ hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
 
 // ------------------------------------------------------------------ scan
 
-// One block: exclusive scan of align16(stored size) over all chunks.  For
+// Exclusive scan of align16(stored size) over all chunks of a call (one
+// request or many, the requests' chunks one after another), one block per
+// 1024 chunks, chained by decoupled look-back: a block publishes its sum,
+// then walks back over earlier blocks' words (sum, or running total once a
+// block has one) until it meets a running total.  Blocks take their index
+// from a ticket counter in the order they start, so a block waits only on
+// blocks already running; the wait is bounded all the same (kStStall).  For
 // decode the stored sizes come from the streams' chunk tables (bounds
-// checked) and are copied to chunk_sizes.  For a paged encode it also scans
-// the per-request stream sizes into req_offsets_out.
-__global__ __launch_bounds__(1024) void k_scan(CallDesc c, int from_table) {
-  __shared__ uint64_t sh[1024];
-  const int t = threadIdx.x, nt = blockDim.x;
-  const int64_t N = c.total_chunks;
-  const int64_t per = (N + nt - 1) / nt;
-  const int64_t i0 = min(N, (int64_t)t * per), i1 = min(N, i0 + per);
-  if (from_table) {
-    for (int64_t i = i0; i < i1; ++i) {
-      const int r = find_req_by_chunk(c, i);
-      const ReqDesc rq = req_at(c, r);
-      const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
-      const uint64_t pos = base + (uint64_t)rq.table_off + 4 * (uint64_t)(i - rq.chunk_begin);
-      uint32_t e = 0;
-      if (pos + 4 <= c.stream_bytes && pos + 4 <= base + (uint64_t)rq.payload_off) e = *(const uint32_t*)(c.stream + pos);
-      else set_status2(c.ctl, kStCorrupt);
-      c.chunk_sizes[i] = e;
-    }
-    __syncthreads();
-  }
-  uint64_t sum = 0;
-  for (int64_t i = i0; i < i1; ++i) sum += (uint64_t)align16(c.chunk_sizes[i] & 0x7fffffffu);
-  uint64_t total;
-  uint64_t acc = block_exclusive_scan<uint64_t>(sum, sh, total);
-  for (int64_t i = i0; i < i1; ++i) {
-    c.chunk_offs[i] = acc;
-    acc += (uint64_t)align16(c.chunk_sizes[i] & 0x7fffffffu);
-  }
-  if (t == 0) c.chunk_offs[N] = total;
-  __syncthreads();
-  if (from_table) return;
-  if (c.req_offsets_out == nullptr) {
-    if (t == 0) c.ctl->total = (uint64_t)c.one.payload_off + total;
-    return;
-  }
-  // per-request stream sizes -> offsets
-  const int R = c.R;
-  const int rper = (R + nt - 1) / nt;
-  const int r0 = min(R, t * rper), r1 = min(R, r0 + rper);
-  __threadfence_block();
-  uint64_t rs = 0;
-  for (int r = r0; r < r1; ++r) {
-    const ReqDesc rq = req_at(c, r);
-    const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
-    rs += (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
-  }
-  uint64_t rtotal;
-  uint64_t racc = block_exclusive_scan<uint64_t>(rs, sh, rtotal);
-  for (int r = r0; r < r1; ++r) {
-    const ReqDesc rq = req_at(c, r);
-    const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
-    c.req_offsets_out[r] = racc;
-    racc += (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
-  }
-  if (t == 0) { c.req_offsets_out[R] = rtotal; c.ctl->total = rtotal; }
-}
-
-hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s) {
-  k_scan<<<1, 1024, 0, s>>>(c, from_table ? 1 : 0);
-  return hipGetLastError();
-}
-
-// The same scan for a dense call (one request) over many blocks, one per 1024
-// chunks, chained by decoupled look-back: a block publishes its sum, then
-// walks back over earlier blocks' words (sum, or running total once a block
-// has one) until it meets a running total.  Blocks take their index from a
-// ticket counter in the order they start, so a block waits only on blocks
-// already running; the wait is bounded all the same (kStStall).  A dense
-// encode also gets the first chunk that is not raw at its all-raw place (the
-// minimum over blocks) for the placement.
+// checked) and are copied to chunk_sizes.  A dense encode also gets the first
+// chunk that is not raw at its all-raw place (the minimum over blocks) for
+// the placement.
 constexpr int kScanPer = 1024;
 constexpr uint64_t kLbAgg = 1ull << 62, kLbIncl = 2ull << 62, kLbVal = (1ull << 62) - 1;
 
-__global__ __launch_bounds__(256) void k_scan_dense(CallDesc c, int from_table) {
+__global__ __launch_bounds__(256) void k_scan_chunks(CallDesc c, int from_table) {
   __shared__ uint32_t sh32[4];
   __shared__ int64_t sb[2];
   const int t = threadIdx.x;
   const int64_t N = c.total_chunks;
-  const ReqDesc& rq = c.one;
   if (t == 0) sb[0] = (int64_t)__hip_atomic_fetch_add((uint32_t*)&c.ctl->pad[4], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int64_t vb = sb[0];
   const int64_t k0 = vb * kScanPer + 4 * t;
+  // the request of each of the thread's chunks (consecutive)
+  int r = (k0 < N) ? find_req_by_chunk(c, k0) : 0;
+  ReqDesc rq = req_at(c, r);
   uint32_t e[4];
   uint64_t sum = 0;
 #pragma unroll
@@ -875,15 +815,17 @@ __global__ __launch_bounds__(256) void k_scan_dense(CallDesc c, int from_table) 
     const int64_t k = k0 + i;
     e[i] = 0;
     if (k < N) {
+      while (r + 1 < c.R && k >= rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1]) rq = req_at(c, ++r);
       if (from_table) {
-        const uint64_t pos = (uint64_t)rq.table_off + 4 * (uint64_t)k;
-        if (pos + 4 <= c.stream_bytes && pos + 4 <= (uint64_t)rq.payload_off) e[i] = *(const uint32_t*)(c.stream + pos);
+        const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+        const uint64_t pos = base + (uint64_t)rq.table_off + 4 * (uint64_t)(k - rq.chunk_begin);
+        if (pos + 4 <= c.stream_bytes && pos + 4 <= base + (uint64_t)rq.payload_off) e[i] = *(const uint32_t*)(c.stream + pos);
         else set_status2(c.ctl, kStCorrupt);
         c.chunk_sizes[k] = e[i];
       } else if (c.counts_to_sizes) {
         // a counted chunk of a standard pipeline: its encoded size, or raw
         // when that does not shrink it (the size pass's rule)
-        const int64_t n = locate_chunk(c, rq, 0, k).n;
+        const int64_t n = locate_chunk(c, rq, r, k).n;
         const int64_t size = n / 16 + 2 * (int64_t)chunk_count(c, k);
         e[i] = (size >= n) ? ((uint32_t)n | kRawFlag) : (uint32_t)size;
         c.chunk_sizes[k] = e[i];
@@ -924,29 +866,60 @@ __global__ __launch_bounds__(256) void k_scan_dense(CallDesc c, int from_table) 
   __syncthreads();
   uint64_t acc = (uint64_t)sb[1] + ex;
   int64_t first_work = N;
+  const bool dense_place = c.place == 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t k = k0 + i;
     if (k < N) {
       c.chunk_offs[k] = acc;
-      if (c.place && first_work == N && !((e[i] >> 31) && acc == (uint64_t)locate_chunk(c, rq, 0, k).src)) first_work = k;
+      if (dense_place && first_work == N && !((e[i] >> 31) && acc == (uint64_t)locate_chunk(c, c.one, 0, k).src))
+        first_work = k;
       acc += (uint64_t)align16(e[i] & 0x7fffffffu);
     }
   }
-  if (c.place && first_work < N)
+  if (dense_place && first_work < N)
     __hip_atomic_fetch_min(&c.ctl->pad[3], (uint64_t)first_work, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (t == 0 && (vb + 1) * kScanPer >= N) {
     const uint64_t total = (uint64_t)sb[1] + agg;
     c.chunk_offs[N] = total;
-    if (!from_table) c.ctl->total = (uint64_t)rq.payload_off + total;
+    if (!from_table && c.req_offsets_out == nullptr) c.ctl->total = (uint64_t)c.one.payload_off + total;
   }
 }
 
-hipError_t launch_scan_dense(const CallDesc& c, bool from_table, hipStream_t s) {
+// Paged encode, after the chunk scan: each request's stream size (its fixed
+// sections plus its chunks' aligned sizes) scanned into req_offsets_out, and
+// the call's total.
+__global__ __launch_bounds__(1024) void k_req_offsets(CallDesc c) {
+  __shared__ uint64_t sh[1024];
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int R = c.R;
+  const int rper = (R + nt - 1) / nt;
+  const int r0 = min(R, t * rper), r1 = min(R, r0 + rper);
+  auto size_of = [&](int r) {
+    const ReqDesc rq = req_at(c, r);
+    const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
+    return (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
+  };
+  uint64_t rs = 0;
+  for (int r = r0; r < r1; ++r) rs += size_of(r);
+  uint64_t rtotal;
+  uint64_t racc = block_exclusive_scan<uint64_t>(rs, sh, rtotal);
+  for (int r = r0; r < r1; ++r) {
+    c.req_offsets_out[r] = racc;
+    racc += size_of(r);
+  }
+  if (t == 0) { c.req_offsets_out[R] = rtotal; c.ctl->total = rtotal; }
+}
+
+hipError_t launch_scan(const CallDesc& c, bool from_table, hipStream_t s) {
   const int64_t nb = std::max<int64_t>(1, (c.total_chunks + kScanPer - 1) / kScanPer);
-  k_scan_dense<<<(int)nb, 256, 0, s>>>(c, from_table ? 1 : 0);
+  k_scan_chunks<<<(int)nb, 256, 0, s>>>(c, from_table ? 1 : 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || from_table || c.req_offsets_out == nullptr) return e;
+  k_req_offsets<<<1, 1024, 0, s>>>(c);
   return hipGetLastError();
 }
+
 
 // ------------------------------------------------------------------ compaction
 

@@ -284,24 +284,31 @@ def test_paged_matches_oracle():
     assert np.array_equal(to_u16(kq), kqo) and np.array_equal(to_u16(vq), vqo)
 
 
-@pytest.mark.parametrize("kbits,vbits", [(4, 4), (8, 2)])
-def test_paged_mixed_raw_and_compressed_chunks(kbits, vbits):
+@pytest.mark.parametrize("kbits,vbits,stages,round_lens", [(4, 4, W.BYTE_SHUFFLE_RZE, 1),
+                                                            (8, 2, W.BYTE_SHUFFLE_RZE, 1),
+                                                            (4, 2, W.LLAMA_TUPL_BIT_RZE, 4),
+                                                            (4, 2, W.LLAMA_TUPL_BIT_RZE, 1)])
+def test_paged_mixed_raw_and_compressed_chunks(kbits, vbits, stages, round_lens):
     """Paged pools with half of the pages zero and 4 KiB chunks: compressed and
-    raw chunks alternate, and the reconstruct tiles (32 vectors, starting at
-    layer boundaries that are not chunk-aligned) straddle pairs of chunks of
-    every kind.  A tile whose chunks are all raw reads the stream in place;
-    the others read the codes area, which must then hold the raw neighbours
-    of compressed chunks too."""
+    raw chunks alternate, and the tiles (32 vectors, starting at layer
+    boundaries that are not chunk-aligned) straddle pairs of chunks of every
+    kind.  The encoders split a straddling tile's non-zero word count between
+    its chunks; a reconstruct tile whose chunks are all raw reads the stream
+    in place, the others read the codes area, which must then hold the raw
+    neighbours of compressed chunks too.  With TUPL8_1 -> BIT_8 -> RZE_2 the
+    encoders count only when every layer starts on a 1 KiB boundary (lengths
+    rounded to multiples of 4 here); the ragged case takes the size pass."""
     TP = W.TensorPolicy
     wl = W.WORKLOADS["c4_paged_llama8b"].with_(layers=3, chunk_bytes=4096, k=TP(kbits, "token", 128),
-                                                v=TP(vbits, "token", 32))
+                                                v=TP(vbits, "token", 32), stages=stages)
     batch = W.paged_layout(wl, requests=8, min_len=5, max_len=300)
+    batch.seq_lens[:] = np.maximum(round_lens, batch.seq_lens // round_lens * round_lens)
     kp, vp = W.paged_pools(wl, batch)
     rng = np.random.default_rng(kbits)
     for pool in (kp, vp):
         zero = torch.from_numpy(rng.random(pool.shape[:2]) < 0.5)
         pool[zero] = 0
-    log(f"paged mixed-chunk case K{kbits} V{vbits} lens {batch.seq_lens.tolist()}")
+    log(f"paged mixed-chunk case K{kbits} V{vbits} {stages} lens {batch.seq_lens.tolist()}")
     cfg = O.cfg_from_workload(wl)
     st, ref, ref_offs = O.encode_paged(cfg, to_u16(kp), to_u16(vp), batch.num_blocks, wl.page_tokens,
                                        batch.block_table, batch.seq_lens)
@@ -317,6 +324,7 @@ def test_paged_mixed_raw_and_compressed_chunks(kbits, vbits):
     assert np.array_equal(out[:n].cpu().numpy(), ref)
     assert ref.size < ms, "no chunk compressed"
     dst = W.paged_layout(wl, requests=8, min_len=5, max_len=300, stream=1)
+    dst.seq_lens[:] = batch.seq_lens
     kq = torch.zeros_like(kp, device=DEV)
     vq = torch.zeros_like(vp, device=DEV)
     s = torch.from_numpy(ref).to(DEV)
