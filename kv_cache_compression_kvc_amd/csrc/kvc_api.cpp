@@ -398,6 +398,7 @@ struct PagedJob {
 PagedJob paged_job(const kvc_plan_s* p, const int32_t* lens, int R, bool encode) {
   PagedJob j;
   j.reqs.resize(R);
+  int64_t fixed = 0;
   for (int r = 0; r < R; ++r) {
     ReqDesc& rq = j.reqs[r];
     request_layout(p, lens[r], rq);
@@ -416,8 +417,19 @@ PagedJob paged_job(const kvc_plan_s* p, const int32_t* lens, int R, bool encode)
     }
     rq.piece_begin = j.pieces;
     if (encode) j.pieces += cdiv(rq.params_bytes[0], 65536) + cdiv(rq.params_bytes[1], 65536);
+    rq.raw_base = j.max_total;
+    rq.fixed_before = fixed;
+    if (encode) {
+      // the fused encoders write the codes where the request's stream keeps
+      // them when every chunk so far is raw (positions in the output buffer)
+      rq.codes_off[0] = rq.raw_base + rq.payload_off;
+      rq.codes_off[1] = rq.codes_off[0] + a16(rq.codes_bytes[0]);
+    }
+    fixed += rq.payload_off;
     j.max_total += rq.max_stream;
   }
+  // encode: the staging area of the stage engine's chunks uses the same offsets
+  if (encode) j.codes_area = a256(j.max_total);
   return j;
 }
 
@@ -794,8 +806,9 @@ kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_
   c.max_blocks = maxb;
   c.in_kv[0] = d_k_pool;
   c.in_kv[1] = d_v_pool;
-  c.codes = ws + w.codes;
-  c.codes_out = c.codes;
+  c.codes = (uint8_t*)d_out;
+  c.codes_out = ws + w.codes;
+  c.place_flags = (uint32_t*)(ws + w.flags);
   c.params_ws = ws + w.params;
   c.stream = (uint8_t*)d_out;
   c.req_offsets_out = d_req_offsets;
@@ -806,7 +819,7 @@ kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_
   c.total_pieces = j.pieces;
   c.tiles[0] = j.tiles[0];
   c.tiles[1] = j.tiles[1];
-  c.place = 2;                   // chunks go from the workspace straight into the request streams
+  c.place = 2;                   // chunks move in place from their all-raw positions
   c.scan_state = (uint64_t*)(ws + w.scan);
   // the fused encoders count the non-zero RZE words of each chunk, so the
   // size pass reads only counters
@@ -824,8 +837,11 @@ kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_
   if ((e = timed(KVC_KERNEL_ENCODE_V, s, [&] { return launch_encode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "encode V");
   if ((e = timed(KVC_KERNEL_LOSSLESS_ENC, s, [&] { return launch_lossless_encode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, false, s); })) != hipSuccess) return hip_fail(e, "scan");
-  if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_compact(c, s); })) != hipSuccess) return hip_fail(e, "compact");
+  // the placement first: the tables, headers and parameter sections that the
+  // compaction writes at the final request offsets may cover codes of earlier
+  // requests that are still to move
   if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_place(c, s); })) != hipSuccess) return hip_fail(e, "place");
+  if ((e = timed(KVC_KERNEL_COMPACT, s, [&] { return launch_compact(c, s); })) != hipSuccess) return hip_fail(e, "compact");
   if (h_out_bytes) {
     Control h;
     if ((st = sync_and_read(c.ctl, s, h)) != KVC_OK) return st;

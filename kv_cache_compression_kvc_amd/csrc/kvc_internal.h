@@ -69,6 +69,9 @@ struct ReqDesc {
   int64_t payload_off;       // payload offset inside this request's stream
   int64_t max_stream;        // stream bytes with every chunk raw
   int64_t piece_begin;       // first parameter-copy piece (paged encode)
+  int64_t raw_base;          // paged encode: where this request's stream would start if every
+                             //   earlier request's chunks were raw (sum of their max_stream)
+  int64_t fixed_before;      // paged encode: payload_off summed over the earlier requests
 };
 
 // Where the requests live and where their data goes.

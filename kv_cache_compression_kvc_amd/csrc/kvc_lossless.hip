@@ -866,18 +866,25 @@ __global__ __launch_bounds__(256) void k_scan_chunks(CallDesc c, int from_table)
   __syncthreads();
   uint64_t acc = (uint64_t)sb[1] + ex;
   int64_t first_work = N;
-  const bool dense_place = c.place == 1;
+  // the placement's first chunk that is not raw at its all-raw place
+  // (positions relative to c.codes: dense, the payload; paged, the output)
+  const bool track = !from_table && c.place != 0;
+  r = (k0 < N) ? find_req_by_chunk(c, k0) : 0;
+  rq = req_at(c, r);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int64_t k = k0 + i;
     if (k < N) {
       c.chunk_offs[k] = acc;
-      if (dense_place && first_work == N && !((e[i] >> 31) && acc == (uint64_t)locate_chunk(c, c.one, 0, k).src))
-        first_work = k;
+      if (track && first_work == N) {
+        while (r + 1 < c.R && k >= rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1]) rq = req_at(c, ++r);
+        const uint64_t fin = (c.place == 2 ? (uint64_t)(rq.fixed_before + rq.payload_off) : 0) + acc;
+        if (!((e[i] >> 31) && fin == (uint64_t)locate_chunk(c, rq, r, k).src)) first_work = k;
+      }
       acc += (uint64_t)align16(e[i] & 0x7fffffffu);
     }
   }
-  if (dense_place && first_work < N)
+  if (track && first_work < N)
     __hip_atomic_fetch_min(&c.ctl->pad[3], (uint64_t)first_work, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (t == 0 && (vb + 1) * kScanPer >= N) {
     const uint64_t total = (uint64_t)sb[1] + agg;
@@ -977,6 +984,15 @@ __device__ __forceinline__ int find_req_by_piece(const CallDesc& c, int64_t piec
 
 __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
   const int64_t items = c.total_chunks + c.R + c.total_pieces;
+  if (c.place == 2) {
+    // the chunk tables of a paged encode, after its placement
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < c.total_chunks;
+         k += (int64_t)gridDim.x * blockDim.x) {
+      const int r = find_req_by_chunk(c, k);
+      const ReqDesc rq = req_at(c, r);
+      *(uint32_t*)(c.stream + stream_base(c, r, true) + rq.table_off + 4 * (k - rq.chunk_begin)) = c.chunk_sizes[k];
+    }
+  }
   // with the paged placement (place == 2) the chunks are placed there
   for (int64_t it = blockIdx.x + (c.place == 2 ? c.total_chunks : 0); it < items; it += gridDim.x) {
     if (it < c.total_chunks) {
@@ -1081,6 +1097,23 @@ __device__ __forceinline__ int64_t first_covered(const CallDesc& c, uint64_t fin
   return rq.nchunks[0] + (int64_t)((fin - (uint64_t)rq.codes_off[1]) / c.chunk_bytes);
 }
 
+// first chunk whose codes, at their all-raw places, end after position `pos`
+// of the output buffer (paged encode)
+__device__ __forceinline__ int64_t first_covered_paged(const CallDesc& c, uint64_t pos) {
+  int lo = 0, hi = c.R - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((uint64_t)c.reqs[mid].raw_base <= pos) lo = mid; else hi = mid - 1;
+  }
+  const ReqDesc rq = req_at(c, lo);
+  const int64_t rel = (int64_t)pos - rq.codes_off[0];       // from the request's K codes
+  if (rel < 0) return rq.chunk_begin;
+  if (rel < rq.codes_bytes[0]) return rq.chunk_begin + rel / c.chunk_bytes;
+  const int64_t v0 = rq.codes_off[1] - rq.codes_off[0];
+  if (rel < v0) return rq.chunk_begin + rq.nchunks[0];
+  return rq.chunk_begin + rq.nchunks[0] + min((rel - v0) / (int64_t)c.chunk_bytes, (int64_t)rq.nchunks[1]);
+}
+
 // Block-wide: wait until every chunk in [j0, k) has announced.  Whole groups
 // of 64 chunks are checked through their counters, the ragged ends chunk by
 // chunk.  Returns false if a wait ran out or an earlier one did (kStStall).
@@ -1123,16 +1156,17 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
   constexpr int NU = 64 / NW;                          // 1 KiB blocks per wave (mode 4)
   const int r = PAGED ? find_req_by_chunk(c, k) : 0;
   const ReqDesc rq = req_at(c, r);
-  const uint64_t base = PAGED ? stream_base(c, r, true) : 0;
   const ChunkLoc L = locate_chunk(c, rq, r, k);
   const uint32_t e = c.chunk_sizes[k];
   const int64_t stored = e & 0x7fffffffu;
-  const uint64_t fin = c.chunk_offs[k] - c.chunk_offs[rq.chunk_begin];
-  uint8_t* dst = c.stream + base + rq.payload_off + fin;
+  // final position relative to c.codes (dense: the payload; paged: the output
+  // buffer, whose request r starts at fixed_before + chunk_offs[chunk_begin])
+  const uint64_t fin = (PAGED ? (uint64_t)(rq.fixed_before + rq.payload_off) : 0) + c.chunk_offs[k];
+  uint8_t* dst = c.codes + fin;
   const uint8_t* slot = c.codes + L.src;
   // 0: raw, in place; 1: raw, moves; 2: TUPL8_1 -> BIT_8 -> RZE_2 here;
   // 3: from the staging area; 4: TUPL8_1 -> RZE_2 here
-  const int mode = (e >> 31) ? ((!PAGED && fin == (uint64_t)L.src) ? 0 : 1)
+  const int mode = (e >> 31) ? ((fin == (uint64_t)L.src) ? 0 : 1)
                              : ((pipe == 0 || !fast_eligible(pipe, L.n)) ? 3 : (pipe == 1 ? 2 : 4));
   const int n = (int)L.n;
   const int ngi = n >> 12, nd = n >> 6, dpj = n >> 9;
@@ -1198,14 +1232,13 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
         }
       }
     }
-  } else if (mode == 1 && !PAGED) {
+  } else if (mode == 1) {
     const int64_t nv = align16(stored) / 16;
     for (int64_t q = threadIdx.x; q < nv; q += blockDim.x) ((uint4*)ob)[q] = ((const uint4*)slot)[q];
   }
   __syncthreads();
-  // every load of this chunk's codes has returned: announce (a paged stream is
-  // written to a buffer of its own: no ordering)
-  if (!PAGED && threadIdx.x == 0) {
+  // every load of this chunk's codes has returned: announce
+  if (threadIdx.x == 0) {
     __hip_atomic_store(ann + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(grp + (k >> 6), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -1266,13 +1299,13 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
     // (and its own); chunks below kf are raw at their places: their codes are
     // never covered
     const uint64_t end = fin + (uint64_t)align16(stored);
-    const int64_t j0 = PAGED ? k : min(max(first_covered(c, fin), kf), k);
-    const int64_t j1 = (PAGED || end == fin) ? j0 : max(j0, min(first_covered(c, end - 1) + 1, k));
+    auto cover = [&](uint64_t x) { return PAGED ? first_covered_paged(c, x) : first_covered(c, x); };
+    const int64_t j0 = min(max(cover(fin), kf), k);
+    const int64_t j1 = (end == fin) ? j0 : max(j0, min(cover(end - 1) + 1, k));
     if (!wait_announced(c, ann, grp, j0, j1)) {
       if (threadIdx.x == 0) set_status2(c.ctl, kStStall);
     } else {
-      const uint4* src = (mode == 3) ? (const uint4*)(c.codes_out + L.src)
-                                     : (PAGED && mode == 1) ? (const uint4*)slot : (const uint4*)ob;
+      const uint4* src = (mode == 3) ? (const uint4*)(c.codes_out + L.src) : (const uint4*)ob;
       const int64_t nv = align16(stored) / 16;
       for (int64_t q = threadIdx.x; q < nv; q += blockDim.x) {
         uint4 x = src[q];
@@ -1285,11 +1318,13 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
       }
     }
   }
-  if (threadIdx.x == 0) *(uint32_t*)(c.stream + base + rq.table_off + 4 * (k - rq.chunk_begin)) = e;
+  // a paged table may cover codes of earlier requests still to move: the
+  // compaction writes those after the placement
+  if (!PAGED && threadIdx.x == 0) *(uint32_t*)(c.stream + rq.table_off + 4 * k) = e;
   __syncthreads();                                     // LDS reused by the next chunk
 }
 
-template <int PIPE>
+template <int PIPE, bool PAGED>
 __global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 2 : 4) void k_place(CallDesc c) {
   __shared__ __attribute__((aligned(16))) uint32_t ob[16384];   // output assembly / raw chunk (64 KiB)
   __shared__ uint32_t bm[1024];
@@ -1303,7 +1338,6 @@ __global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 
   // entries only), then every chunk from there on, then the header
   const int64_t kf = (int64_t)min<uint64_t>(c.ctl->pad[3], (uint64_t)N);
   const int64_t nb0 = (kf + 63) / 64, last = nb0 + (N - kf);
-  const ReqDesc& rq = c.one;
   // there are last + 1 tickets: the blocks past them leave without taking one
   // (one atomic counter that every block of a large grid hit was the cost of
   // small calls whose chunks all stay in place)
@@ -1321,41 +1355,31 @@ __global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 
     __syncthreads();
     if (t > last) break;
     if (t == last) {
-      write_header(c, rq, c.stream, c.ctl->total);
-      zero_gaps(c, rq, c.stream);
-      __syncthreads();
-      continue;
-    }
-    if (t < nb0) {
-      // raw chunks at their all-raw places: table entries and padding; nothing
-      // waits on them (no later output reaches their codes)
-      const int64_t k = 64 * t + threadIdx.x;
-      if (threadIdx.x < 64 && k < kf) {
-        const ChunkLoc L = locate_chunk(c, rq, 0, k);
-        uint8_t* dst = c.stream + rq.payload_off + L.src;
-        for (int64_t b = L.n; b < align16(L.n); ++b) dst[b] = 0;
-        *(uint32_t*)(c.stream + rq.table_off + 4 * k) = c.chunk_sizes[k];
+      // dense: the header and the gaps (paged: the compaction, afterwards)
+      if (!PAGED) {
+        write_header(c, c.one, c.stream, c.ctl->total);
+        zero_gaps(c, c.one, c.stream);
       }
       __syncthreads();
       continue;
     }
-    place_chunk<PIPE, false, kPlaceWaves>(c, kf + (t - nb0), kf, ann, grp, X, wave, lane, ob, bm, offs, sh32);
+    if (t < nb0) {
+      // raw chunks at their all-raw places: padding (and dense table
+      // entries); nothing waits on them (no later output reaches their codes)
+      const int64_t k = 64 * t + threadIdx.x;
+      if (threadIdx.x < 64 && k < kf) {
+        const int r = PAGED ? find_req_by_chunk(c, k) : 0;
+        const ReqDesc rq = req_at(c, r);
+        const ChunkLoc L = locate_chunk(c, rq, r, k);
+        uint8_t* dst = c.codes + L.src;
+        for (int64_t b = L.n; b < align16(L.n); ++b) dst[b] = 0;
+        if (!PAGED) *(uint32_t*)(c.stream + rq.table_off + 4 * k) = c.chunk_sizes[k];
+      }
+      __syncthreads();
+      continue;
+    }
+    place_chunk<PIPE, PAGED, kPlaceWaves>(c, kf + (t - nb0), kf, ann, grp, X, wave, lane, ob, bm, offs, sh32);
   }
-}
-
-// Paged encodes: the codes sit in the workspace and every request has its own
-// stream, so chunks are placed in any order, with no announcements; the
-// compaction kernel writes the headers and parameter sections.
-template <int PIPE>
-__global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 2 : 4) void k_place_paged(CallDesc c) {
-  __shared__ __attribute__((aligned(16))) uint32_t ob[16384];
-  __shared__ uint32_t bm[1024];
-  __shared__ uint32_t offs[1024];
-  __shared__ uint32_t sh32[kPlaceWaves];
-  const XposeLane X = xpose_lane();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  for (int64_t k = blockIdx.x; k < c.total_chunks; k += gridDim.x)
-    place_chunk<PIPE, true, kPlaceWaves>(c, k, 0, nullptr, nullptr, X, wave, lane, ob, bm, offs, sh32);
 }
 
 hipError_t launch_place(const CallDesc& c, hipStream_t s) {
@@ -1364,15 +1388,15 @@ hipError_t launch_place(const CallDesc& c, hipStream_t s) {
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
   if (c.place == 2) {
     if (c.total_chunks == 0) return hipSuccess;
-    if (p1) k_place_paged<1><<<grid, kPlaceThreads, 0, s>>>(c);
-    else if (p2) k_place_paged<2><<<grid, kPlaceThreads, 0, s>>>(c);
-    else k_place_paged<0><<<grid, kPlaceThreads, 0, s>>>(c);
+    if (p1) k_place<1, true><<<grid, kPlaceThreads, 0, s>>>(c);
+    else if (p2) k_place<2, true><<<grid, kPlaceThreads, 0, s>>>(c);
+    else k_place<0, true><<<grid, kPlaceThreads, 0, s>>>(c);
   } else if (p1) {
-    k_place<1><<<grid, kPlaceThreads, 0, s>>>(c);
+    k_place<1, false><<<grid, kPlaceThreads, 0, s>>>(c);
   } else if (p2) {
-    k_place<2><<<grid, kPlaceThreads, 0, s>>>(c);
+    k_place<2, false><<<grid, kPlaceThreads, 0, s>>>(c);
   } else {
-    k_place<0><<<grid, kPlaceThreads, 0, s>>>(c);
+    k_place<0, false><<<grid, kPlaceThreads, 0, s>>>(c);
   }
   return hipGetLastError();
 }
