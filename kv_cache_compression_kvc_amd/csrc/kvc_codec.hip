@@ -571,7 +571,8 @@ __device__ __forceinline__ void stage_out(const float* f, uint32_t* wl, const ui
   }
   wave_sync();
   const uint32_t* rrow = wl + (lane >> 4) * RP + (lane & 15) * 4;
-  const uint32_t voff = (uint32_t)(lane >> 4) * vstride + (uint32_t)(lane & 15) * 16;
+  uint32_t voff = (uint32_t)(lane >> 4) * vstride + (uint32_t)(lane & 15) * 16;
+  asm volatile("" : "+v"(voff));   // one offset register: the per-store offsets are added here, not kept
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     uint4 x = *(const uint4*)(rrow + k * 4 * RP);
@@ -1724,6 +1725,17 @@ __device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, WaveTi
     prm = (const uint32_t*)((const uint8_t*)prm + sd.params_off);
     l = 0; h = 0; Ho = 1;
   }
+  int colb;
+  const int64_t boff = pc_block(T, G, Ho, BITS, l, grp, h, colb);
+  // a group block never straddles chunks here: a raw chunk is read in place
+  int64_t rawpos = -1;
+  if (nvw > 0 && c.direct[which]) {
+    const int64_t ci = chunk_of(c, boff);
+    const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
+    const uint32_t e = uniform_load(c.chunk_sizes, gci);
+    if (e >> 31)
+      rawpos = (int64_t)((uint64_t)c.one.payload_off + uniform_load(c.chunk_offs, gci) + (uint64_t)(boff - ci * c.chunk_bytes));
+  }
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     const int ch = 64 * p + lane;
@@ -1731,21 +1743,12 @@ __device__ __forceinline__ void ch_dec_load(const CallDesc& c, int which, WaveTi
     for (int i = 0; i < BITS; ++i) R.w[p][i] = 0;
     R.pw[p] = 0;
     if (nvw > 0) {
-      int colb;
-      const int64_t boff = pc_block(T, G, Ho, BITS, l, grp, h, colb);
       const uint8_t* col = codes_sec + boff + (int64_t)ch * colb;
       bool have = true;
-      if (c.direct[which]) {
-        // a group block never straddles chunks here; a raw chunk is read in place
-        const int64_t ci = chunk_of(c, boff);
-        const int64_t gci = (which ? (int64_t)c.one.nchunks[0] : 0) + ci;
-        const uint32_t e = uniform_load(c.chunk_sizes, gci);
-        if (e >> 31) {
-          const uint64_t pos = (uint64_t)c.one.payload_off + uniform_load(c.chunk_offs, gci) +
-                               (uint64_t)(boff - ci * c.chunk_bytes) + (uint64_t)ch * colb;
-          have = pos + (uint64_t)colb <= c.stream_bytes;
-          col = c.stream + pos;
-        }
+      if (rawpos >= 0) {
+        const uint64_t pos = (uint64_t)rawpos + (uint64_t)ch * colb;
+        have = pos + (uint64_t)colb <= c.stream_bytes;
+        col = c.stream + pos;
       }
       const uint8_t* s = col + tok0 * BITS / 8;
       if (!have) {

@@ -69,7 +69,10 @@ __device__ __forceinline__ void xpose64_lean(uint32_t& lo, uint32_t& hi) {
     lo = p[0];
     hi = p[1];
   }
-  const uint32_t lane = (uint32_t)__lane_id();
+  // opaque: the constants below are derived at each use, not hoisted out of
+  // the caller's loop into registers
+  uint32_t lane = (uint32_t)__lane_id();
+  asm volatile("" : "+v"(lane));
   uint32_t a, b, mk, sh;
 #define KVC_XROUND(J, M, XCHG)                                            \
   mk = (lane & (J)) ? ~(uint32_t)(M) : (uint32_t)(M);                     \

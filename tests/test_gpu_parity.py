@@ -225,6 +225,20 @@ def test_value_reconstruct_decodes_compressed_chunks(dtype, g, cb):
     assert s["chunks_compressed"] >= 2, s
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("cb,heads", [(8192, 8), (65536, 8), (8192, 2)])
+def test_keys_with_raw_and_compressed_chunks(dtype, bits, cb, heads):
+    # 2- or 4-bit keys in 64-token per-channel groups with the standard
+    # pipeline: raw chunks are read in place by the reconstruct kernel,
+    # compressed ones decoded by the lossless pass; zero-rich values give
+    # both kinds in one call
+    wl = C3.with_(dtype=dtype, heads=heads, k=TP(bits, "channel", 64), chunk_bytes=cb, name="key_chunks")
+    s = run_case(wl, 2, 1024, zero_rich=True, zero_frac=0.5, seed=29)
+    assert s["identical"]
+    assert s["chunks_compressed"] >= 2 and s["chunks_raw"] >= 1, s
+
+
 @pytest.mark.parametrize("section", [0, 1])
 def test_zeroed_word_under_a_set_bitmap_bit_is_detected(section):
     # TUPL8_1 -> BIT_8 -> RZE_2 chunks whose bitmap still matches their size
