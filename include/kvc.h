@@ -156,23 +156,34 @@ kvc_status kvc_plan(const kvc_config* cfg, kvc_plan_t* out);
  * Errors as kvc_plan, and KVC_ERR_INVALID_ARG for other width values. */
 kvc_status kvc_plan_mixed(const kvc_config* cfg, const uint8_t* h_bits, kvc_plan_t* out);
 
+/* Release a plan (host memory only).  NULL is accepted.  Calls still in
+ * flight on a stream keep no reference to the plan. */
 kvc_status kvc_plan_destroy(kvc_plan_t plan);
 
 /* Exact sizes for a dense call with `tokens` tokens: the largest stream
  * kvc_encode can produce (chunks stored raw) and the workspace bytes both
- * kvc_encode and kvc_decode need.  Host only. */
+ * kvc_encode and kvc_decode need.  Host only.  FastKVComp Sec. 4.2 keeps the
+ * persistent scratch and a reusable staging buffer with the runtime; here the
+ * caller allocates both once from these sizes and reuses them across calls.
+ * KVC_ERR_INVALID_ARG if tokens is outside [0, max_tokens]. */
 kvc_status kvc_plan_sizes(kvc_plan_t plan, int64_t tokens,
                           size_t* max_stream_bytes, size_t* workspace_bytes);
 
 /* Same for a paged call: the sum of the per-request maximum stream sizes and
- * the workspace for encode_paged / decode_paged.  h_seq_lens[num_requests]. */
+ * the workspace for encode_paged / decode_paged.  h_seq_lens[num_requests]
+ * (host array).  The lengths themselves, not only their total, are needed:
+ * every request's stream is chunked on its own, so the exact sizes depend on
+ * each length.  KVC_ERR_INVALID_ARG for a negative count, a missing array or
+ * a length outside [0, 2^26]. */
 kvc_status kvc_plan_sizes_paged(kvc_plan_t plan, const int32_t* h_seq_lens, int32_t num_requests,
                                 size_t* max_total_bytes, size_t* workspace_bytes);
 
 /* Encode K and V ([layers][tokens][kv_heads][head_dim], plan dtype) into one
- * stream at d_out (capacity out_capacity >= max_stream_bytes).  d_ws is the
- * caller's workspace (>= workspace_bytes, 256-byte aligned), reused across
- * calls.  If h_out_bytes is non-NULL the call synchronizes the stream, copies
+ * stream at d_out (capacity out_capacity >= max_stream_bytes): the fused
+ * rotation + quantize + pack of FastKVComp Sec. 4.1 over every token vector,
+ * then its LC-style lossless stage per chunk (Sec. 4.2).  d_k, d_v, d_out and
+ * d_ws are device pointers the caller owns; d_ws is the workspace
+ * (>= workspace_bytes, 256-byte aligned), reused across calls.  If h_out_bytes is non-NULL the call synchronizes the stream, copies
  * back the 8-byte compressed size (the only device-to-host transfer) and
  * returns any device-detected status; with NULL the call is fully
  * asynchronous and the size is the header's total_bytes field.  With the
@@ -204,15 +215,24 @@ kvc_status kvc_encode_noalloc(kvc_plan_t plan, const void* d_k, const void* d_v,
                               void* d_out, size_t out_capacity, size_t* h_out_bytes, void* stream);
 
 /* Decode a stream of in_bytes bytes holding `tokens` tokens into d_k and d_v
- * ([layers][tokens][kv_heads][head_dim]).  The device validates the header
- * against the plan and every chunk against in_bytes; failures are recorded
- * as KVC_ERR_PLAN_MISMATCH or KVC_ERR_CORRUPT_STREAM (read them with
- * kvc_query_status), in which case the output contents are unspecified but
- * no read or write leaves the given buffers. */
+ * ([layers][tokens][kv_heads][head_dim]): lossless decode per chunk, then the
+ * fused reconstruction of FastKVComp Sec. 4.1 (dequantization, inverse
+ * Hadamard, normalization, sign restoration).  `tokens` is the length the
+ * caller sized d_k and d_v for; the header must state the same (so the
+ * launch shapes are known on the host, with no read-back of the header, and
+ * a stream of another length is reported rather than written past the
+ * buffers).  The device validates the header against the plan and every
+ * chunk against in_bytes; failures are recorded as KVC_ERR_PLAN_MISMATCH or
+ * KVC_ERR_CORRUPT_STREAM (read them with kvc_query_status), in which case the
+ * output contents are unspecified but no read or write leaves the given
+ * buffers.  Host-detected errors (NULL or misaligned pointers, tokens outside
+ * [0, max_tokens], in_bytes shorter than the fixed sections, ws_bytes too
+ * small) return before anything is enqueued. */
 kvc_status kvc_decode(kvc_plan_t plan, const void* d_in, size_t in_bytes, int32_t tokens,
                       void* d_k, void* d_v, void* d_ws, size_t ws_bytes, void* stream);
 
-/* Paged encode: request r (length h_seq_lens[r]) has token t in pool block
+/* Paged encode (FastKVComp Sec. 4.2: the runtime consumes the frontend's
+ * device buffers, here a paged pool): request r (length h_seq_lens[r]) has token t in pool block
  * d_block_table[r * max_blocks_per_req + t / page_tokens], slot
  * t % page_tokens.  Each request becomes its own stream (format above, tokens
  * = its length); request r's stream starts at d_req_offsets[r] within d_out and
@@ -228,7 +248,10 @@ kvc_status kvc_encode_paged(kvc_plan_t plan, const void* d_k_pool, const void* d
 
 /* Paged decode: the mirror image; the reconstruction kernel scatters each
  * request's tokens into the pools through d_block_table (which may differ
- * from the one used to encode). */
+ * from the one used to encode).  d_req_offsets[num_requests + 1] is the
+ * device array kvc_encode_paged wrote; each request's header is checked
+ * against the plan and its length, and its chunks against in_bytes, with
+ * errors recorded in the workspace status as for kvc_decode. */
 kvc_status kvc_decode_paged(kvc_plan_t plan, const void* d_in, size_t in_bytes,
                             const uint64_t* d_req_offsets, const int32_t* h_seq_lens, int32_t num_requests,
                             void* d_k_pool, void* d_v_pool, int64_t num_blocks,
@@ -236,10 +259,15 @@ kvc_status kvc_decode_paged(kvc_plan_t plan, const void* d_in, size_t in_bytes,
                             void* d_ws, size_t ws_bytes, void* stream);
 
 /* Synchronize `stream`, return the device status recorded in the workspace by
- * the last call that used it, and clear it. */
+ * the last call that used it, and clear it.  FastKVComp Sec. 4.2 returns only
+ * a size scalar to the host; the status word is the other value that stays
+ * on the device until asked for. */
 kvc_status kvc_query_status(kvc_plan_t plan, const void* d_ws, void* stream);
 
+/* Static name of a status code. */
 const char* kvc_status_string(kvc_status s);
+/* Detail of the calling thread's last host-detected error (thread-local,
+ * valid until that thread's next call). */
 const char* kvc_last_error(void);
 
 /* Optional per-kernel timing.  While enabled, every kernel launch of the
