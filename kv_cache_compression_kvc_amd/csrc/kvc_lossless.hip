@@ -118,6 +118,7 @@ __global__ void k_reset(CallDesc c) {
     ctl->pad[3] = ~0ull;  // first chunk with placement work (a minimum)
     ctl->pad[4] = 0;   // tickets of the dense scan
     ctl->pad[5] = 0;   // compressed chunks left to the word-parallel decode kernels
+    ctl->pad[6] = 0;   // chunks listed for a whole block (front of the worklist)
   }
   if (c.validate_in_reset && blockIdx.x == 0) {
     __syncthreads();                                   // the status word is clear before any check sets it
@@ -360,6 +361,20 @@ __device__ bool stage_inverse(int stage, const uint8_t* in, int in_n, uint8_t* o
 // kernels (entries from the front of the list); all others go to the general
 // engine (entries from the back).  The list has one entry per chunk.
 __device__ __forceinline__ uint32_t* generic_count(const CallDesc& c) { return (uint32_t*)&c.ctl->pad[1]; }
+// Chunks that need a whole block (a reduction or a copy) are listed from the
+// front of the worklist by the one-thread-per-chunk classification passes;
+// the stage engine's chunks fill it from the back.  A chunk is in at most
+// one of the two lists, so they never meet.
+__device__ __forceinline__ uint32_t* block_count(const CallDesc& c) { return (uint32_t*)&c.ctl->pad[6]; }
+__device__ __forceinline__ void push_block(const CallDesc& c, uint32_t* worklist, int64_t ch) {
+  const uint32_t k = __hip_atomic_fetch_add(block_count(c), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  worklist[k] = (uint32_t)ch;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += (uint32_t)__shfl_xor((int)x, o);
+  return x;
+}
 
 __device__ __forceinline__ int fast_pipeline(const CallDesc& c) {
   if (c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0) return 1;
@@ -411,36 +426,50 @@ __device__ uint32_t nnz_tupl8_rze2(const uint64_t* src, int n, uint32_t* sh32) {
   return total;
 }
 
-__global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, uint32_t* worklist) {
-  __shared__ uint32_t sh32[256];
+// Encode sizes, one thread per chunk: a counted chunk of a standard pipeline
+// gets its size from the fused encoders' counts (raw when that does not
+// shrink it); an uncounted one is listed for k_ll_sizes; other pipelines'
+// chunks go to the stage engine; with no lossless stage every chunk is raw.
+__global__ __launch_bounds__(256) void k_ll_classify_enc(CallDesc c, uint32_t* worklist) {
   const int pipe = fast_pipeline(c);
-  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+  for (int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ch < c.total_chunks;
+       ch += (int64_t)gridDim.x * blockDim.x) {
     const int r = find_req_by_chunk(c, ch);
     const ReqDesc rq = req_at(c, r);
     const ChunkLoc L = locate_chunk(c, rq, r, ch);
     const int n = (int)L.n;
-    bool work = true;
-    const bool fast = fast_eligible(pipe, n);
-    if (fast) {
-      // exact size without the transform; raw chunks are done here.  The
-      // fused encoders may already have counted the non-zero words.
-      const uint64_t* src = (const uint64_t*)(c.codes + L.src);
-      uint32_t nnz;
+    if (fast_eligible(pipe, n)) {
       if (c.nnz_pipe == pipe && c.nnz_sec[L.w]) {
-        nnz = chunk_count(c, ch);
+        const int64_t size = n / 16 + 2 * (int64_t)chunk_count(c, ch);
+        c.chunk_sizes[ch] = (size >= n) ? ((uint32_t)n | kRawFlag) : (uint32_t)size;
       } else {
-        nnz = (pipe == 1) ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
+        push_block(c, worklist, ch);
       }
-      // a compressible chunk is encoded by the placement, which needs only
-      // its size
-      const int64_t size = n / 16 + 2 * (int64_t)nnz;
-      if (threadIdx.x == 0) c.chunk_sizes[ch] = (size >= n) ? ((uint32_t)n | kRawFlag) : (uint32_t)size;
-      work = false;
     } else if (c.stages[0] == 0) {
-      if (threadIdx.x == 0) c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
-      work = false;
+      c.chunk_sizes[ch] = (uint32_t)n | kRawFlag;
+    } else {
+      push_work(c, worklist, ch);
     }
-    if (work && threadIdx.x == 0) push_work(c, worklist, ch);
+  }
+}
+
+// The listed chunks' sizes, one block per chunk: the exact non-zero word count
+// without the transform (a compressible chunk is encoded by the placement,
+// which needs only its size).
+__global__ __launch_bounds__(256) void k_ll_sizes(CallDesc c, const uint32_t* worklist) {
+  __shared__ uint32_t sh32[256];
+  const int pipe = fast_pipeline(c);
+  const uint32_t count = __hip_atomic_load(block_count(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+    const int64_t ch = worklist[item];
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const int n = (int)L.n;
+    const uint64_t* src = (const uint64_t*)(c.codes + L.src);
+    const uint32_t nnz = (pipe == 1) ? nnz_tupl8_bit8_rze2(src, n, sh32) : nnz_tupl8_rze2(src, n, sh32);
+    const int64_t size = n / 16 + 2 * (int64_t)nnz;
+    if (threadIdx.x == 0) c.chunk_sizes[ch] = (size >= n) ? ((uint32_t)n | kRawFlag) : (uint32_t)size;
     __syncthreads();
   }
 }
@@ -608,6 +637,42 @@ constexpr int kPlaceWaves = KVC_PLACE_WAVES;
 constexpr int kPlaceThreads = 64 * kPlaceWaves;
 constexpr int kDecWaves = KVC_DEC_WAVES;
 
+// The stored lines of a chunk, loaded into registers (PT 16-byte lines per
+// thread; lines past the stored length or the stream's end read zero), and
+// their copy into LDS.  Split so that the next chunk's loads are in flight
+// while the current chunk decodes.
+template <int NW>
+struct ChunkLines {
+  static constexpr int NT = 64 * NW, PT = 4096 / NT;
+  uint4 x[PT];
+  __device__ __forceinline__ void load(const CallDesc& c, uint64_t pos, int stored) {
+    const uint64_t avail = (c.stream_bytes > pos) ? c.stream_bytes - pos : 0;
+    const int nv = (stored + 15) / 16;
+    const uint4* src = (const uint4*)(c.stream + pos);
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int k = (int)threadIdx.x + NT * u;
+      x[u] = make_uint4(0, 0, 0, 0);
+      if (k < nv && (uint64_t)(16 * k + 16) <= avail) x[u] = src[k];
+    }
+  }
+  __device__ __forceinline__ void to_lds(int stored, uint4* dst) const {
+    const int nv = (stored + 15) / 16;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int k = (int)threadIdx.x + NT * u;
+      if (k < nv) dst[k] = x[u];
+    }
+  }
+};
+
+// first candidate at or after i (NT when none), the same in every thread
+template <int NT>
+__device__ __forceinline__ int next_cand(const uint32_t* cand, int i) {
+  while (i < NT && !cand[i]) ++i;
+  return i;
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
   constexpr int NT = 64 * NW;
@@ -617,7 +682,8 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const XposeLane X = xpose_lane();
   // this block's chunks are blockIdx.x + gridDim.x * i; NT at a time are
-  // checked in parallel and the block then works through those to decode
+  // checked in parallel and the block then works through those to decode,
+  // the next one's lines loading while the current one decodes
   __shared__ uint32_t cand[NT];
   // nothing to decode (e.g. every chunk raw): leave at once
   if (__hip_atomic_load((const uint32_t*)&c.ctl->pad[5], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
@@ -630,16 +696,35 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
     cand[threadIdx.x] = (mine < c.total_chunks && wp_decode_chunk(c, mine, 1, L, pos, stored)) ? 1u : 0u;
   }
   __syncthreads();
-  for (int i = 0; i < NT; ++i) {
-    if (!cand[i]) continue;
-    const int64_t ch = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i);
-    ChunkLoc L;
-    uint64_t pos;
-    int stored;
-    wp_decode_chunk(c, ch, 1, L, pos, stored);
+  ChunkLines<NW> lines;
+  ChunkLoc L;
+  uint64_t pos = 0;
+  int stored = 0;
+  int i = next_cand<NT>(cand, 0);
+  if (i < NT) {
+    wp_decode_chunk(c, (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i), 1, L, pos, stored);
+    lines.load(c, pos, stored);
+  }
+  while (i < NT) {
     const int n = (int)L.n;
+    const ChunkLoc Lc = L;
+    const int sc = stored;
+    const uint64_t avail = (c.stream_bytes > pos) ? c.stream_bytes - pos : 0;
+    lines.to_lds(sc, buf);
+    __syncthreads();
+    // the next chunk's loads go out now
+    i = next_cand<NT>(cand, i + 1);
+    if (i < NT) {
+      wp_decode_chunk(c, (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i), 1, L, pos, stored);
+      lines.load(c, pos, stored);
+    }
+    // bytes of the last 16-byte line past the stored length are ignored
+    bool ok = sc >= n / 16;
     uint32_t nnz = 0;
-    const bool ok = load_compressed<NW>(c, pos, stored, n, buf, offs, sh32, nnz);
+    if (ok) {
+      nnz = scan_bitmap<NW>((const uint32_t*)buf, offs, n / 64, sh32);
+      ok = n / 16 + 2 * (int)nnz == sc && (uint64_t)(16 * ((sc + 15) / 16)) <= avail + 15;
+    }
     if (!ok) {
       if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
       __syncthreads();
@@ -657,11 +742,11 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
         const int d = j * dpj + 8 * gi + kk;
         const uint32_t bits = bm[d];
         const uint32_t nib = (bits >> (4 * bb)) & 15u;
-        const uint32_t r0 = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << (4 * bb)) - 1u));
+        const uint32_t rr = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << (4 * bb)) - 1u));
         uint32_t q[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint32_t rk = r0 + (uint32_t)__builtin_popcount(nib & ((1u << u) - 1u));
+          const uint32_t rk = rr + (uint32_t)__builtin_popcount(nib & ((1u << u) - 1u));
           const uint32_t v = ((nib >> u) & 1u) ? (uint32_t)words[min(rk, nnz - 1u)] : 0u;
           bad |= ((nib >> u) & 1u) & (uint32_t)(v == 0u);
           q[u] = v;
@@ -671,17 +756,16 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
         w[2 * kk] = lo;
         w[2 * kk + 1] = hi;
       }
-      uint4* dst = (uint4*)(c.codes + L.src + (int64_t)gi * 4096 + 64 * lane);
+      uint4* dst = (uint4*)(c.codes + Lc.src + (int64_t)gi * 4096 + 64 * lane);
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
     }
-    // a set bitmap bit must mark a non-zero word
+    // a set bitmap bit must mark a non-zero word (and the block is done with buf)
     if (__syncthreads_or((int)bad) && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
   }
   __syncthreads();                                   // cand is rewritten next round
   }
 }
-
 template <int NW>
 __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p2(CallDesc c, const uint32_t* worklist) {
   constexpr int NT = 64 * NW;
@@ -771,10 +855,11 @@ bool all_word_parallel(const CallDesc& c) {
 hipError_t launch_lossless_encode(const CallDesc& c, hipStream_t s) {
   if (c.total_chunks == 0) return hipSuccess;
   uint32_t* worklist = (uint32_t*)(c.chunk_offs + c.total_chunks + 1);
-  const int grid = (int)std::min<int64_t>(c.total_chunks, 256 * 8);
-  k_ll_sizes<<<grid, 256, 0, s>>>(c, worklist);
+  k_ll_classify_enc<<<(int)std::min<int64_t>((c.total_chunks + 255) / 256, 4096), 256, 0, s>>>(c, worklist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  k_ll_sizes<<<(int)std::min<int64_t>(c.total_chunks, 256 * 8), 256, 0, s>>>(c, worklist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (all_word_parallel(c)) return hipSuccess;
   k_ll_encode_generic<<<(int)std::min<int64_t>(c.total_chunks, 512), 256, 0, s>>>(c, worklist);
   return hipGetLastError();
@@ -1463,22 +1548,28 @@ hipError_t launch_validate(const CallDesc& c, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Raw chunks are copied to their code slot; compressed chunks go to a worklist.
-// Block 0 also checks that each stream's chunk sizes add up to its header total.
-__global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* worklist) {
-  __shared__ uint32_t sh32[256];
-  uint32_t wp = 0;                                   // thread 0: compressed chunks left to the word-parallel kernels
-  if (blockIdx.x == 0) {
-    for (int r = threadIdx.x; r < c.R; r += blockDim.x) {
-      const ReqDesc rq = req_at(c, r);
-      const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
-      const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
-      const uint64_t want = (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
-      if (base + 64 > c.stream_bytes || *(const uint64_t*)(c.stream + base + 56) != want)
-        set_status2(c.ctl, kStCorrupt);
-    }
+// Decode classification, one thread per chunk (and per request: each
+// stream's chunk sizes must add up to its header's total).  A chunk whose
+// size, place or alignment is impossible marks the stream corrupt.  A raw
+// chunk the reconstruct kernels read in place needs nothing; a raw chunk they
+// cannot (paged tiles may cover it with a compressed neighbour) and a
+// compressed chunk they decode themselves are listed for k_ll_decode_raw; a
+// compressed chunk of a standard pipeline is left to the word-parallel
+// kernels (which find it by index; only the count is kept here), and any
+// other goes to the stage engine.
+__global__ __launch_bounds__(256) void k_ll_classify_dec(CallDesc c, uint32_t* worklist) {
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, dt = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t r = t0; r < c.R; r += dt) {
+    const ReqDesc rq = req_at(c, (int)r);
+    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+    const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
+    const uint64_t want = (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
+    if (base + 64 > c.stream_bytes || *(const uint64_t*)(c.stream + base + 56) != want)
+      set_status2(c.ctl, kStCorrupt);
   }
-  for (int64_t ch = blockIdx.x; ch < c.total_chunks; ch += gridDim.x) {
+  const int pipe = fast_pipeline(c);
+  uint32_t wp = 0;                                   // compressed chunks left to the word-parallel kernels
+  for (int64_t ch = t0; ch < c.total_chunks; ch += dt) {
     const int r = find_req_by_chunk(c, ch);
     const ReqDesc rq = req_at(c, r);
     const ChunkLoc L = locate_chunk(c, rq, r, ch);
@@ -1490,7 +1581,7 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
     const bool ok = (raw ? stored == L.n : (stored < L.n && stored > 0)) && pos + (uint64_t)stored <= c.stream_bytes &&
                     (pos & 15) == 0;
     if (!ok) {
-      if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+      set_status2(c.ctl, kStCorrupt);
       continue;
     }
     bool in_place = raw && c.direct[L.w];
@@ -1503,10 +1594,36 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
     }
     if (in_place) {
       // the reconstruct kernels read this chunk from the stream
-    } else if (!raw && c.mirror[L.w] && fast_eligible(1, L.n)) {
-      // the reconstruct kernels decode this chunk from the stream; they need
-      // the number of non-zero words before each bitmap dword: n / 64 words
-      // in the chunk's codes slot
+    } else if (raw || (c.mirror[L.w] && fast_eligible(1, L.n))) {
+      push_block(c, worklist, ch);
+    } else if (!fast_eligible(pipe, L.n)) {
+      push_work(c, worklist, ch);                    // the stage engine
+    } else {
+      ++wp;                                          // the word-parallel kernels find theirs by index
+    }
+  }
+  wp = wave_sum_u32(wp);
+  if ((threadIdx.x & 63) == 0 && wp)
+    __hip_atomic_fetch_add((uint32_t*)&c.ctl->pad[5], wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The listed chunks, one block each: a raw chunk is copied to its code slot;
+// for a compressed chunk the reconstruct kernel decodes itself, the number of
+// non-zero words before each bitmap dword (n / 64 words in the chunk's codes
+// slot), checked against the stored size.
+__global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, const uint32_t* worklist) {
+  __shared__ uint32_t sh32[256];
+  const uint32_t count = __hip_atomic_load(block_count(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (uint32_t item = blockIdx.x; item < count; item += gridDim.x) {
+    const int64_t ch = worklist[item];
+    const int r = find_req_by_chunk(c, ch);
+    const ReqDesc rq = req_at(c, r);
+    const ChunkLoc L = locate_chunk(c, rq, r, ch);
+    const uint32_t e = c.chunk_sizes[ch];
+    const int64_t stored = e & 0x7fffffffu;
+    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+    const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+    if (!(e >> 31)) {
       const int n = (int)L.n, nd = n / 64;
       if (stored < n / 16) {
         if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
@@ -1530,20 +1647,15 @@ __global__ __launch_bounds__(256) void k_ll_decode_raw(CallDesc c, uint32_t* wor
         run += cnt[i];
       }
       if (n / 16 + 2 * (int64_t)total != stored && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
-    } else if (raw) {
+    } else {
       const uint4* src = (const uint4*)(c.stream + pos);
       uint4* dst = (uint4*)(c.codes + L.src);
       const int64_t nv = L.n / 16;
       for (int64_t k = threadIdx.x; k < nv; k += blockDim.x) dst[k] = src[k];
       for (int64_t p = nv * 16 + threadIdx.x; p < L.n; p += blockDim.x) c.codes[L.src + p] = c.stream[pos + p];
-    } else if (!fast_eligible(fast_pipeline(c), L.n)) {
-      if (threadIdx.x == 0) push_work(c, worklist, ch);   // the stage engine
-    } else if (threadIdx.x == 0) {
-      ++wp;                                               // the word-parallel kernels find theirs by index
     }
+    __syncthreads();                                 // sh32 is reused by the next chunk
   }
-  if (threadIdx.x == 0 && wp)
-    __hip_atomic_fetch_add((uint32_t*)&c.ctl->pad[5], wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(256) void k_ll_decode_generic(CallDesc c, const uint32_t* worklist) {
@@ -1587,10 +1699,12 @@ __global__ __launch_bounds__(256) void k_ll_decode_generic(CallDesc c, const uin
 hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s) {
   if (c.total_chunks == 0) return hipSuccess;
   uint32_t* worklist = (uint32_t*)(c.chunk_offs + c.total_chunks + 1);
-  const int grid = (int)std::min<int64_t>(c.total_chunks, 256 * 8);
-  k_ll_decode_raw<<<grid, 256, 0, s>>>(c, worklist);
+  k_ll_classify_dec<<<(int)std::min<int64_t>((std::max<int64_t>(c.total_chunks, c.R) + 255) / 256, 4096), 256, 0, s>>>(
+      c, worklist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  k_ll_decode_raw<<<(int)std::min<int64_t>(c.total_chunks, 256 * 8), 256, 0, s>>>(c, worklist);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
   const int fgrid = (int)std::min<int64_t>(c.total_chunks, 512);
