@@ -655,9 +655,6 @@ kvc_status kvc_encode(kvc_plan_t p, const void* d_k, const void* d_v, int32_t to
   c.scan_state = (uint64_t*)(ws + w.scan);
   for (int k = 0; k < 2; ++k) c.tiles[k] = tiles_of(p->pol[k], c.layers, tokens, c.heads, false);
   c.nnz_pipe = lossless_pipe(p->cfg.lossless);
-#ifdef KVC_NO_FUSED_COUNT
-  c.nnz_pipe = 0;
-#endif
   for (int k = 0; k < 2; ++k) c.nnz_sec[k] = (c.nnz_pipe && fused_count_ok(p->pol[k], tokens, p->cfg.chunk_bytes)) ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
