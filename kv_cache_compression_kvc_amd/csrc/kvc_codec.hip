@@ -667,19 +667,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // One 16-byte load per lane into LDS at m0 + 16 * lane.  Issued from asm so
 // that the compiler's wait insertion does not add a wait for all outstanding
-// memory operations before every LDS read; the caller waits explicitly.
+// memory operations before every LDS read; the caller waits explicitly.  A
+// load to LDS that reads m0 needs one wait state after the scalar write of
+// m0, which the compiler cannot add inside an asm statement: hence the nop.
 #ifndef KVC_DMA_NT
 #define KVC_DMA_NT 1
 #endif
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
 #if KVC_DMA_NT
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
 #else
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
 #endif
                :
                : "v"(voff), "s"(r), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Wait until at most N vector memory operations are outstanding (they
