@@ -296,11 +296,16 @@ kvc_status kvc_profile_query(int kind, double* total_ms, int64_t* launches);
  * path): enqueue on `stream` a streaming kernel over `items` items, each
  * reading `reads` 16-byte lines of d_src (items * reads * 16 bytes) and
  * writing `writes` 16-byte lines of d_dst (items * writes * 16 bytes), with
- * the buffer accesses and store cache policy of the fused kernels and no
- * other work.  (reads, writes) is one of (1,0), (0,1), (1,1), (2,1), (4,1),
- * (1,4); other pairs return KVC_ERR_UNSUPPORTED.  d_sink is a 4-byte device
- * word the read-only form may write.  Time it with events on `stream`. */
-kvc_status kvc_probe_bandwidth(const void* d_src, void* d_dst, int64_t items, int reads, int writes,
+ * 16-byte buffer accesses, non-temporal stores and no other work.  With
+ * flags 0 it loads with the default cache policy from a capped grid of
+ * looping waves, as most fused kernels do; KVC_PROBE_NT_LOADS makes the
+ * loads non-temporal, KVC_PROBE_SHORT_WAVES launches one wave per 256 items
+ * (each wave handles its items once and exits).  (reads, writes) is one of (1,0), (0,1),
+ * (1,1), (2,1), (4,1), (1,4); other pairs return KVC_ERR_UNSUPPORTED, other
+ * flag bits KVC_ERR_INVALID_ARG.  d_sink is a 4-byte device word the
+ * read-only form may write.  Time it with events on `stream`. */
+enum { KVC_PROBE_NT_LOADS = 1, KVC_PROBE_SHORT_WAVES = 2 };
+kvc_status kvc_probe_bandwidth(const void* d_src, void* d_dst, int64_t items, int reads, int writes, int flags,
                                uint32_t* d_sink, void* stream);
 
 #ifdef __cplusplus

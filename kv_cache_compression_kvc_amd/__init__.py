@@ -89,7 +89,7 @@ def lib():
             "kvc_profile_enable": [C.c_int],
             "kvc_profile_reset": [],
             "kvc_profile_query": [C.c_int, C.POINTER(C.c_double), C.POINTER(C.c_int64)],
-            "kvc_probe_bandwidth": [P, P, I64, C.c_int, C.c_int, P, P],
+            "kvc_probe_bandwidth": [P, P, I64, C.c_int, C.c_int, C.c_int, P, P],
             "kvc_predicted_jct": [C.POINTER(Profile), C.POINTER(RequestContext), C.POINTER(C.c_double)],
             "kvc_selector_create": [C.POINTER(Profile), I32, C.POINTER(SelectorConfig), C.POINTER(C.c_void_p)],
             "kvc_selector_destroy": [P],
@@ -267,10 +267,13 @@ def profile_query(kind) -> tuple:
     return ms.value, n.value
 
 
-def probe_bandwidth(src, dst, items: int, reads: int, writes: int, sink, stream=None):
+PROBE_NT_LOADS, PROBE_SHORT_WAVES = 1, 2
+
+
+def probe_bandwidth(src, dst, items: int, reads: int, writes: int, sink, stream=None, flags: int = 0):
     """Enqueue the bandwidth reference kernel (kvc_probe_bandwidth)."""
-    _check(lib().kvc_probe_bandwidth(_ptr(src), _ptr(dst), items, reads, writes, _ptr(sink), _stream(stream)),
-           "kvc_probe_bandwidth")
+    _check(lib().kvc_probe_bandwidth(_ptr(src), _ptr(dst), items, reads, writes, flags, _ptr(sink),
+                                     _stream(stream)), "kvc_probe_bandwidth")
 
 
 # ---------------------------------------------------------------- selection

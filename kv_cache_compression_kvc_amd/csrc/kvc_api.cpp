@@ -975,15 +975,16 @@ kvc_status kvc_query_status(kvc_plan_t p, const void* d_ws, void* stream) {
   return device_status(h.status);
 }
 
-kvc_status kvc_probe_bandwidth(const void* d_src, void* d_dst, int64_t items, int reads, int writes,
+kvc_status kvc_probe_bandwidth(const void* d_src, void* d_dst, int64_t items, int reads, int writes, int flags,
                                uint32_t* d_sink, void* stream) {
   if (items < 0) return fail(KVC_ERR_INVALID_ARG, "items must be >= 0");
+  if (flags & ~(KVC_PROBE_NT_LOADS | KVC_PROBE_SHORT_WAVES)) return fail(KVC_ERR_INVALID_ARG, "unknown probe flags %d", flags);
   const int pair = (reads < 0 || reads > 4 || writes < 0 || writes > 4) ? -1 : reads * 16 + writes;
   if (pair != 0x10 && pair != 0x01 && pair != 0x11 && pair != 0x21 && pair != 0x41 && pair != 0x14)
     return fail(KVC_ERR_UNSUPPORTED, "no probe for %d reads : %d writes", reads, writes);
   if ((reads && !d_src) || (writes && !d_dst) || (!writes && !d_sink))
     return fail(KVC_ERR_INVALID_ARG, "a buffer the probe touches is NULL");
-  const hipError_t e = launch_probe(d_src, d_dst, items, reads, writes, d_sink, (hipStream_t)stream);
+  const hipError_t e = launch_probe(d_src, d_dst, items, reads, writes, flags, d_sink, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "probe");
   return KVC_OK;
 }

@@ -157,9 +157,9 @@ bool all_word_parallel(const CallDesc& c);
 hipError_t launch_slab_copy(const CallDesc& c, int which, bool encode, hipStream_t s);
 
 // Bandwidth reference kernel: `items` items, each reading `reads` and writing
-// `writes` 16-byte lines (kvc_probe.hip).
-hipError_t launch_probe(const void* src, void* dst, int64_t items, int reads, int writes, uint32_t* sink,
-                        hipStream_t s);
+// `writes` 16-byte lines (kvc_probe.hip); flags as kvc_probe_bandwidth's.
+hipError_t launch_probe(const void* src, void* dst, int64_t items, int reads, int writes, int flags,
+                        uint32_t* sink, hipStream_t s);
 
 // Per-kernel timing hooks (kvc_api.cpp).
 void prof_begin(int kind, hipStream_t s);
