@@ -691,7 +691,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 #endif
                :
                : "v"(voff), "s"(r), "s"(lds)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Wait until at most N vector memory operations are outstanding (they

@@ -673,14 +673,36 @@ __device__ __forceinline__ int next_cand(const uint32_t* cand, int i) {
   return i;
 }
 
+// RZE_2 expansion of a nibble of the bitmap (4 words): the nibble's non-zero
+// words lie consecutively in the stream; entry `nib` of this table holds the
+// v_perm_b32 selectors that place them (from the 8 bytes starting at the
+// first one) into words 0, 1 (.x) and 2, 3 (.y), zero bytes elsewhere, and
+// the words that must be non-zero, as a 1 per 16-bit half (.z, .w).
+__device__ __forceinline__ uint4 rze_nibble_entry(uint32_t nib) {
+  uint32_t sel[2] = {0, 0}, ex[2] = {0, 0}, k = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const bool present = (nib >> u) & 1u;
+    const uint32_t half = present ? ((2u * k) | ((2u * k + 1u) << 8)) : 0x0C0Cu;   // 0x0C: a zero byte
+    sel[u >> 1] |= half << (16 * (u & 1));
+    ex[u >> 1] |= (present ? 1u : 0u) << (16 * (u & 1));
+    k += present ? 1u : 0u;
+  }
+  return make_uint4(sel[0], sel[1], ex[0], ex[1]);
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
   constexpr int NT = 64 * NW;
-  __shared__ __attribute__((aligned(16))) uint4 buf[4096];
+  // one line past the chunk: a lane reads three dwords from its first word's
+  // dword, which may run past the last stored word
+  __shared__ __attribute__((aligned(16))) uint4 buf[4096 + 1];
   __shared__ uint32_t offs[1024];
   __shared__ uint32_t sh32[NW];
+  __shared__ __attribute__((aligned(16))) uint4 nibtab[16];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const XposeLane X = xpose_lane();
+  if (threadIdx.x < 16) nibtab[threadIdx.x] = rze_nibble_entry(threadIdx.x);
   // this block's chunks are blockIdx.x + gridDim.x * i; NT at a time are
   // checked in parallel and the block then works through those to decode,
   // the next one's lines loading while the current one decodes
@@ -731,9 +753,17 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
       continue;
     }
     const uint32_t* bm = (const uint32_t*)buf;
-    const uint16_t* words = (const uint16_t*)buf + n / 32;
+    const uint32_t* buf32 = (const uint32_t*)buf;
+    const uint32_t wbase = (uint32_t)(n / 64);         // first dword of the words
     const int ngi = n / 4096, dpj = n / 512;
     const int j = lane >> 3, bb = lane & 7;
+    const uint32_t below = (1u << (4 * bb)) - 1u;      // bitmap bits of the nibbles before this lane's
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    // (1, 1) kept opaque: min(word, 1) stays one packed v_pk_min_u16 per pair
+    // instead of becoming two compares and selects
+    uint32_t one2w = 0x00010001u;
+    asm volatile("" : "+v"(one2w));
+    const u16x2 one2 = __builtin_bit_cast(u16x2, one2w);
     uint32_t bad = 0;
     for (int gi = wave; gi < ngi; gi += NW) {
       uint32_t w[16];
@@ -742,16 +772,19 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
         const int d = j * dpj + 8 * gi + kk;
         const uint32_t bits = bm[d];
         const uint32_t nib = (bits >> (4 * bb)) & 15u;
-        const uint32_t rr = offs[d] + (uint32_t)__builtin_popcount(bits & ((1u << (4 * bb)) - 1u));
-        uint32_t q[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t rk = rr + (uint32_t)__builtin_popcount(nib & ((1u << u) - 1u));
-          const uint32_t v = ((nib >> u) & 1u) ? (uint32_t)words[min(rk, nnz - 1u)] : 0u;
-          bad |= ((nib >> u) & 1u) & (uint32_t)(v == 0u);
-          q[u] = v;
-        }
-        uint32_t lo = q[0] | (q[1] << 16), hi = q[2] | (q[3] << 16);
+        // index of the nibble's first non-zero word; in a chunk that passed
+        // the size check every set bit's word lies below nnz
+        const uint32_t rr = offs[d] + (uint32_t)__builtin_popcount(bits & below);
+        const uint32_t di = min(wbase + (rr >> 1), 16383u);
+        const uint32_t d0 = buf32[di], d1 = buf32[di + 1], d2 = buf32[di + 2];
+        const uint32_t sh = (rr & 1u) << 4;
+        const uint32_t p01 = __builtin_amdgcn_alignbit(d1, d0, sh), p23 = __builtin_amdgcn_alignbit(d2, d1, sh);
+        const uint4 e = nibtab[nib];
+        uint32_t lo = __builtin_amdgcn_perm(p23, p01, e.x), hi = __builtin_amdgcn_perm(p23, p01, e.y);
+        // a set bit must mark a non-zero word: min(word, 1) per half against the table
+        const uint32_t nzlo = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, lo), one2));
+        const uint32_t nzhi = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, hi), one2));
+        bad |= (nzlo ^ e.z) | (nzhi ^ e.w);
         xpose64(lo, hi, X);
         w[2 * kk] = lo;
         w[2 * kk + 1] = hi;

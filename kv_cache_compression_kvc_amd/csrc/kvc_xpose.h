@@ -9,7 +9,11 @@
 namespace kvc {
 
 __device__ __forceinline__ uint32_t rotr32(uint32_t x, uint32_t s) { return __builtin_amdgcn_alignbit(x, x, s); }
-__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
+// (m & a) | (~m & b) in one instruction: v_bitop3_b32's table is indexed by
+// (m << 2) | (a << 1) | b, and 0xCA is "m ? a : b"
+__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_bitop3_b32(m, a, b, 0xCA);
+}
 
 // Lane constants of the 64x64 bit transpose: for the rounds exchanging with
 // lane ^ 16, ^ 8, ^ 4, ^ 2, ^ 1, the bits this lane keeps and the rotation
@@ -32,12 +36,14 @@ __device__ __forceinline__ XposeLane xpose_lane() {
   return x;
 }
 // partner values: lane ^ 16 and lane ^ 4 through the swizzle unit, lane ^ 8
-// (rotate a 16-lane row by 8), lane ^ 2 and lane ^ 1 (quad permutes) by DPP
+// (rotate a 16-lane row by 8), lane ^ 2 and lane ^ 1 (quad permutes) by DPP.
+// Every source lane of these DPP patterns lies in the wave, so no old value
+// is needed (bound_ctrl: an inactive source would read 0).
 __device__ __forceinline__ uint32_t xchg16(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); }
-__device__ __forceinline__ uint32_t xchg8(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t xchg8(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true); }
 __device__ __forceinline__ uint32_t xchg4(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F); }
-__device__ __forceinline__ uint32_t xchg2(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ uint32_t xchg1(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ uint32_t xchg2(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true); }
+__device__ __forceinline__ uint32_t xchg1(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true); }
 
 // Lane i holds row i of a 64x64 bit matrix (lo: bits 0..31, hi: 32..63);
 // afterwards lane c holds column c.  Each round swaps the off-diagonal
