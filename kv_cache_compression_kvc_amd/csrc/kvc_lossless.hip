@@ -524,17 +524,30 @@ __global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uin
 // words; the decode kernels below read them back.
 
 // bits 0..3: which 16-bit quarters of (lo, hi) are non-zero
-__device__ __forceinline__ uint32_t nz_quarters(uint32_t lo, uint32_t hi) {
-  const uint32_t a = ((lo & 0xFFFFu) != 0u) | ((uint32_t)((lo >> 16) != 0u) << 1);
-  const uint32_t b = ((hi & 0xFFFFu) != 0u) | ((uint32_t)((hi >> 16) != 0u) << 1);
-  return a | (b << 2);
+// (1, 1) as two 16-bit halves, opaque to the compiler: min(x, one) on the
+// halves stays one v_pk_min_u16 instead of becoming compares and selects
+typedef unsigned short ll_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ ll_u16x2 opaque_one2() {
+  uint32_t w = 0x00010001u;
+  asm volatile("" : "+v"(w));
+  return __builtin_bit_cast(ll_u16x2, w);
+}
+// per 16-bit half of x: 1 if non-zero, else 0
+__device__ __forceinline__ uint32_t nz_halves(uint32_t x, ll_u16x2 one2) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ll_u16x2, x), one2));
+}
+// bit q: 16-bit word q of (lo, hi) is non-zero
+__device__ __forceinline__ uint32_t nz_quarters(uint32_t lo, uint32_t hi, ll_u16x2 one2) {
+  const uint32_t q = nz_halves(lo, one2) | (nz_halves(hi, one2) << 2);   // bits 0, 2, 16, 18
+  return (q | (q >> 15)) & 15u;
 }
 
-// OR over the 8 lanes of each aligned group of 8
+// OR over the 8 lanes of each aligned group of 8 (every DPP source lane
+// exists: no old value needed)
 __device__ __forceinline__ uint32_t or8(uint32_t x) {
-  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);    // lane ^ 1
-  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);    // lane ^ 2
-  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);   // mirror within 8
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);    // lane ^ 1
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);    // lane ^ 2
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true);   // mirror within 8
   return x;
 }
 
@@ -691,6 +704,22 @@ __device__ __forceinline__ uint4 rze_nibble_entry(uint32_t nib) {
   return make_uint4(sel[0], sel[1], ex[0], ex[1]);
 }
 
+// RZE_2 compaction of a nibble: the v_perm_b32 selectors that gather its
+// non-zero words (of the 8 bytes lo, hi) to the front, words 0, 1 (.x) and
+// 2, 3 (.y), in order; the rest is don't-care.
+__device__ __forceinline__ uint2 rze_compact_entry(uint32_t nib) {
+  uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu}, k = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if ((nib >> u) & 1u) {
+      const uint32_t half = (2u * u) | ((2u * u + 1u) << 8);
+      sel[k >> 1] = (sel[k >> 1] & ~(0xFFFFu << (16 * (k & 1)))) | (half << (16 * (k & 1)));
+      ++k;
+    }
+  }
+  return make_uint2(sel[0], sel[1]);
+}
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
   constexpr int NT = 64 * NW;
@@ -758,12 +787,7 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
     const int ngi = n / 4096, dpj = n / 512;
     const int j = lane >> 3, bb = lane & 7;
     const uint32_t below = (1u << (4 * bb)) - 1u;      // bitmap bits of the nibbles before this lane's
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    // (1, 1) kept opaque: min(word, 1) stays one packed v_pk_min_u16 per pair
-    // instead of becoming two compares and selects
-    uint32_t one2w = 0x00010001u;
-    asm volatile("" : "+v"(one2w));
-    const u16x2 one2 = __builtin_bit_cast(u16x2, one2w);
+    const ll_u16x2 one2 = opaque_one2();
     uint32_t bad = 0;
     for (int gi = wave; gi < ngi; gi += NW) {
       uint32_t w[16];
@@ -782,9 +806,7 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
         const uint4 e = nibtab[nib];
         uint32_t lo = __builtin_amdgcn_perm(p23, p01, e.x), hi = __builtin_amdgcn_perm(p23, p01, e.y);
         // a set bit must mark a non-zero word: min(word, 1) per half against the table
-        const uint32_t nzlo = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, lo), one2));
-        const uint32_t nzhi = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, hi), one2));
-        bad |= (nzlo ^ e.z) | (nzhi ^ e.w);
+        bad |= (nz_halves(lo, one2) ^ e.z) | (nz_halves(hi, one2) ^ e.w);
         xpose64(lo, hi, X);
         w[2 * kk] = lo;
         w[2 * kk + 1] = hi;
@@ -1268,7 +1290,7 @@ __device__ bool wait_announced(const CallDesc& c, const uint32_t* ann, const uin
 template <int PIPE, bool PAGED, int NW>
 __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_t kf, uint32_t* ann, uint32_t* grp,
                                             const XposeLane& X, int wave, int lane, uint32_t* ob, uint32_t* bm,
-                                            uint32_t* offs, uint32_t* sh32) {
+                                            uint32_t* offs, uint32_t* sh32, const uint2* cmptab) {
   constexpr int pipe = PIPE;
   constexpr int NS = 16 / NW;                          // 4 KiB blocks per wave (mode 2)
   constexpr int NU = 64 / NW;                          // 1 KiB blocks per wave (mode 4)
@@ -1306,6 +1328,7 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
     }
   }
   if (mode == 2) {
+    const ll_u16x2 one2 = opaque_one2();
 #pragma unroll
     for (int s4 = 0; s4 < NS; ++s4) {
       const int gi = wave + NW * s4;
@@ -1323,7 +1346,7 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
           xpose64(lo, hi, X);
           R[16 * s4 + 2 * kk] = lo;
           R[16 * s4 + 2 * kk + 1] = hi;
-          const uint32_t dw = or8(nz_quarters(lo, hi) << (4 * (lane & 7)));
+          const uint32_t dw = or8(nz_quarters(lo, hi, one2) << (4 * (lane & 7)));
           if ((lane & 7) == 0) bm[(lane >> 3) * dpj + 8 * gi + kk] = dw;
         }
       }
@@ -1370,6 +1393,7 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
     for (int d = threadIdx.x; d < nd; d += blockDim.x) ob[d] = bm[d];
     uint16_t* ow = (uint16_t*)(ob + nd);
     const int j = lane >> 3, r4 = 4 * (lane & 7);
+    const uint32_t below = (1u << r4) - 1u;            // bitmap bits of the nibbles before this lane's
 #pragma unroll
     for (int s4 = 0; s4 < NS; ++s4) {
       const int gi = wave + NW * s4;
@@ -1377,14 +1401,20 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           const int d = j * dpj + 8 * gi + kk;
-          const uint32_t bits = bm[d], base = offs[d];
+          const uint32_t bits = bm[d];
+          const uint32_t nib = (bits >> r4) & 15u;
+          // the nibble's non-zero words, in order, go to consecutive words
+          // from its first index
+          const uint32_t rr = offs[d] + (uint32_t)__builtin_popcount(bits & below);
           const uint32_t lo = R[16 * s4 + 2 * kk], hi = R[16 * s4 + 2 * kk + 1];
-          const uint32_t v[4] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu, hi >> 16};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t rr = (uint32_t)(r4 + q);
-            if ((bits >> rr) & 1u) ow[base + (uint32_t)__builtin_popcount(bits & ((1u << rr) - 1u))] = (uint16_t)v[q];
-          }
+          const uint2 sel = cmptab[nib];
+          const uint32_t c01 = __builtin_amdgcn_perm(hi, lo, sel.x), c23 = __builtin_amdgcn_perm(hi, lo, sel.y);
+          const uint32_t pc = (uint32_t)__builtin_popcount(nib);
+          uint16_t* p = ow + rr;
+          if (pc > 0) p[0] = (uint16_t)c01;
+          if (pc > 1) p[1] = (uint16_t)(c01 >> 16);
+          if (pc > 2) p[2] = (uint16_t)c23;
+          if (pc > 3) p[3] = (uint16_t)(c23 >> 16);
         }
       }
     }
@@ -1449,6 +1479,8 @@ __global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 
   __shared__ uint32_t offs[1024];
   __shared__ uint32_t sh32[kPlaceWaves];
   __shared__ int64_t tk[1];
+  __shared__ uint2 cmptab[16];
+  if (threadIdx.x < 16) cmptab[threadIdx.x] = rze_compact_entry(threadIdx.x);   // read after the first barrier
   const int64_t N = c.total_chunks;
   uint32_t* ann = c.place_flags;
   uint32_t* grp = c.place_flags + N;
@@ -1496,7 +1528,7 @@ __global__ __launch_bounds__(kPlaceThreads, kPlaceWaves / 2 < 4 ? kPlaceWaves / 
       __syncthreads();
       continue;
     }
-    place_chunk<PIPE, PAGED, kPlaceWaves>(c, kf + (t - nb0), kf, ann, grp, X, wave, lane, ob, bm, offs, sh32);
+    place_chunk<PIPE, PAGED, kPlaceWaves>(c, kf + (t - nb0), kf, ann, grp, X, wave, lane, ob, bm, offs, sh32, cmptab);
   }
 }
 
