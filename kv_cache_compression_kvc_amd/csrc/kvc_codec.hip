@@ -173,9 +173,6 @@ __device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff)
   const int2v x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, kLoadPol);
   return make_uint2((uint32_t)x.x, (uint32_t)x.y);
 }
-__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
-}
 
 __device__ __forceinline__ uint32_t h16_from(float f) {
   _Float16 h = (_Float16)f;                     // v_cvt_f16_f32, round to nearest even
@@ -1084,7 +1081,11 @@ __device__ __forceinline__ DecTok dec_token_tile(const CallDesc& c, int which, i
           d.p1_q = (int)((toff >> 10) & 3);
           d.p1_pref = (const uint32_t*)(c.codes + pick(which, c.one.codes_off) + ci * (int64_t)c.chunk_bytes);
           d.csrc = c.stream + pos;
-          d.cbytes = (pos >= c.stream_bytes) ? 0u : (uint32_t)std::min<uint64_t>(e & 0x7fffffffu, c.stream_bytes - pos);
+          // the chunk with its zero padding to 16 bytes: the word loads are
+          // whole dwords, and the last word may end 2 bytes short of one
+          d.cbytes = (pos >= c.stream_bytes)
+                         ? 0u
+                         : (uint32_t)std::min<uint64_t>(((e & 0x7fffffffu) + 15u) & ~15u, c.stream_bytes - pos);
         }
       }
     }
@@ -1242,26 +1243,30 @@ __global__ __launch_bounds__(256, 4) void k_decode_token(CallDesc c, int which) 
 // wave then reads its tile's codes from there.  Reads are buffer loads bounded
 // by the stored size: a set bit over a zero word marks a corrupt stream.
 // -------------------------------------------------------------------
-__device__ __forceinline__ uint32_t p1_block_to_lds(const DecTok& t, const uint32_t* seg, uint32_t* blk) {
+// The nibble's non-zero words are consecutive in the stream: three dword
+// loads from the one holding its first word cover them, and the nibble's
+// entry of `nibtab` (rze_nibble_entry) spreads them to their places.
+__device__ __forceinline__ uint32_t p1_block_to_lds(const DecTok& t, const uint32_t* seg, uint32_t* blk,
+                                                   const uint4* nibtab) {
   const int lane = __lane_id();
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(t.csrc, t.cbytes);
   const uint32_t words = (uint32_t)t.p1_n / 16u;
   const uint32_t sh = 4u * (uint32_t)(lane & 7);
+  const rze_u16x2 one2 = opaque_one2();
   uint32_t bad = 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const uint32_t kb = seg[h];                 // bitmap dword of transpose kk = 2 p1_q + h
     const uint32_t nib = (kb >> sh) & 15u;
     const uint32_t r0 = seg[2 + h] + (uint32_t)__builtin_popcount(kb & ((1u << sh) - 1u));
-    uint32_t q[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t on = (nib >> u) & 1u;
-      const uint32_t rk = r0 + (uint32_t)__builtin_popcount(nib & ((1u << u) - 1u));
-      q[u] = bload2(rs, on ? words + 2u * rk : 0x7ffffff0u);
-      bad |= on & (uint32_t)(q[u] == 0u);
-    }
-    uint32_t lo = q[0] | (q[1] << 16), hi = q[2] | (q[3] << 16);
+    // bytes past the stored size read zero (a set bit there is a corrupt stream)
+    const uint32_t off = words + 2u * (r0 & ~1u);
+    const uint32_t d0 = bload4(rs, off, 0), d1 = bload4(rs, off + 4u, 0), d2 = bload4(rs, off + 8u, 0);
+    const uint32_t s16 = (r0 & 1u) << 4;
+    const uint32_t p01 = __builtin_amdgcn_alignbit(d1, d0, s16), p23 = __builtin_amdgcn_alignbit(d2, d1, s16);
+    const uint4 e = nibtab[nib];
+    uint32_t lo = __builtin_amdgcn_perm(p23, p01, e.x), hi = __builtin_amdgcn_perm(p23, p01, e.y);
+    bad |= (nz_halves(lo, one2) ^ e.z) | (nz_halves(hi, one2) ^ e.w);
     xpose64_lean(lo, hi);
     *(uint2*)(blk + 2 * (8 * lane + 2 * t.p1_q + h)) = make_uint2(lo, hi);
   }
@@ -1273,7 +1278,9 @@ __global__ __launch_bounds__(256, 4) void k_decode_token_m(CallDesc c, int which
   constexpr int BITS = 2;
   __shared__ __attribute__((aligned(16))) uint32_t lds[4 * kWaveLds];
   __shared__ __attribute__((aligned(16))) uint32_t blk[1024];      // one decoded 4 KiB block
+  __shared__ __attribute__((aligned(16))) uint4 nibtab[16];         // RZE_2 nibble expansion
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (threadIdx.x < 16) nibtab[threadIdx.x] = rze_nibble_entry(threadIdx.x);   // read after a barrier
   uint32_t* wl = lds + wave * kWaveLds;
   const TensorPol pol = which ? c.pol[1] : c.pol[0];
   const float cc = pol.c;
@@ -1309,7 +1316,7 @@ __global__ __launch_bounds__(256, 4) void k_decode_token_m(CallDesc c, int which
     }
     if (t.p1) {                                  // the same for the block's four tiles
       __syncthreads();                           // the previous block's readers are done
-      const uint32_t bad = p1_block_to_lds(t, q.w, blk);
+      const uint32_t bad = p1_block_to_lds(t, q.w, blk, nibtab);
       if (bad) set_status(c.ctl, kStCorrupt);
       __syncthreads();
       const uint4 x = *(const uint4*)(blk + 256 * t.p1_q + 8 * v + 4 * hf);

@@ -524,24 +524,6 @@ __global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uin
 // words; the decode kernels below read them back.
 
 // bits 0..3: which 16-bit quarters of (lo, hi) are non-zero
-// (1, 1) as two 16-bit halves, opaque to the compiler: min(x, one) on the
-// halves stays one v_pk_min_u16 instead of becoming compares and selects
-typedef unsigned short ll_u16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ ll_u16x2 opaque_one2() {
-  uint32_t w = 0x00010001u;
-  asm volatile("" : "+v"(w));
-  return __builtin_bit_cast(ll_u16x2, w);
-}
-// per 16-bit half of x: 1 if non-zero, else 0
-__device__ __forceinline__ uint32_t nz_halves(uint32_t x, ll_u16x2 one2) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(ll_u16x2, x), one2));
-}
-// bit q: 16-bit word q of (lo, hi) is non-zero
-__device__ __forceinline__ uint32_t nz_quarters(uint32_t lo, uint32_t hi, ll_u16x2 one2) {
-  const uint32_t q = nz_halves(lo, one2) | (nz_halves(hi, one2) << 2);   // bits 0, 2, 16, 18
-  return (q | (q >> 15)) & 15u;
-}
-
 // OR over the 8 lanes of each aligned group of 8 (every DPP source lane
 // exists: no old value needed)
 __device__ __forceinline__ uint32_t or8(uint32_t x) {
@@ -686,40 +668,6 @@ __device__ __forceinline__ int next_cand(const uint32_t* cand, int i) {
   return i;
 }
 
-// RZE_2 expansion of a nibble of the bitmap (4 words): the nibble's non-zero
-// words lie consecutively in the stream; entry `nib` of this table holds the
-// v_perm_b32 selectors that place them (from the 8 bytes starting at the
-// first one) into words 0, 1 (.x) and 2, 3 (.y), zero bytes elsewhere, and
-// the words that must be non-zero, as a 1 per 16-bit half (.z, .w).
-__device__ __forceinline__ uint4 rze_nibble_entry(uint32_t nib) {
-  uint32_t sel[2] = {0, 0}, ex[2] = {0, 0}, k = 0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const bool present = (nib >> u) & 1u;
-    const uint32_t half = present ? ((2u * k) | ((2u * k + 1u) << 8)) : 0x0C0Cu;   // 0x0C: a zero byte
-    sel[u >> 1] |= half << (16 * (u & 1));
-    ex[u >> 1] |= (present ? 1u : 0u) << (16 * (u & 1));
-    k += present ? 1u : 0u;
-  }
-  return make_uint4(sel[0], sel[1], ex[0], ex[1]);
-}
-
-// RZE_2 compaction of a nibble: the v_perm_b32 selectors that gather its
-// non-zero words (of the 8 bytes lo, hi) to the front, words 0, 1 (.x) and
-// 2, 3 (.y), in order; the rest is don't-care.
-__device__ __forceinline__ uint2 rze_compact_entry(uint32_t nib) {
-  uint32_t sel[2] = {0x0C0C0C0Cu, 0x0C0C0C0Cu}, k = 0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    if ((nib >> u) & 1u) {
-      const uint32_t half = (2u * u) | ((2u * u + 1u) << 8);
-      sel[k >> 1] = (sel[k >> 1] & ~(0xFFFFu << (16 * (k & 1)))) | (half << (16 * (k & 1)));
-      ++k;
-    }
-  }
-  return make_uint2(sel[0], sel[1]);
-}
-
 template <int NW>
 __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
   constexpr int NT = 64 * NW;
@@ -787,7 +735,7 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
     const int ngi = n / 4096, dpj = n / 512;
     const int j = lane >> 3, bb = lane & 7;
     const uint32_t below = (1u << (4 * bb)) - 1u;      // bitmap bits of the nibbles before this lane's
-    const ll_u16x2 one2 = opaque_one2();
+    const rze_u16x2 one2 = opaque_one2();
     uint32_t bad = 0;
     for (int gi = wave; gi < ngi; gi += NW) {
       uint32_t w[16];
@@ -1328,7 +1276,7 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
     }
   }
   if (mode == 2) {
-    const ll_u16x2 one2 = opaque_one2();
+    const rze_u16x2 one2 = opaque_one2();
 #pragma unroll
     for (int s4 = 0; s4 < NS; ++s4) {
       const int gi = wave + NW * s4;
