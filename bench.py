@@ -276,8 +276,32 @@ def timed(fn, steps, warmup, stream):
     return a.elapsed_time(b) / steps
 
 
+def timed_steps(fn, steps, stream):
+    """(ms per call over all `steps` calls, [ms of each call]): one event
+    before the first call, one after each call, all on `stream`, so the total
+    is the same bracket as timed()'s."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    each = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, each
+
+
+def spread(each) -> dict:
+    """min, median and max of per-step times (ms)."""
+    xs = sorted(each)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"min": round(xs[0], 4), "median": round(med, 4), "max": round(xs[-1], 4)}
+
+
 def profiled(fn, steps, warmup, stream):
-    """(ms per call of fn, {kernel kind: ms per launch}) over `steps` timed calls."""
+    """(ms per call of fn, {kernel kind: ms per launch}, [ms of each call])
+    over `steps` timed calls."""
     import torch
     import kv_cache_compression_kvc_amd as K
     for _ in range(warmup):
@@ -285,10 +309,10 @@ def profiled(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     K.profile_reset()
     K.profile_enable(True)
-    ms = timed(fn, steps, 0, stream)
+    ms, each = timed_steps(fn, steps, stream)
     K.profile_enable(False)
     prof = {name: K.profile_query(name) for name in K.KERNELS}
-    return ms, {k: t / c for k, (t, c) in prof.items() if c}
+    return ms, {k: t / c for k, (t, c) in prof.items() if c}, each
 
 
 class Dense:
@@ -356,7 +380,7 @@ class Dense:
         """Step, encode-only and decode-only times and per-kernel figures."""
         import torch
         s = torch.cuda.current_stream()
-        step_ms, kms = profiled(self.step, steps, warmup, s)
+        step_ms, kms, each = profiled(self.step, steps, warmup, s)
         enc_ms = timed(self.encode, steps, 2, s)
         dec_ms = timed(self.decode, steps, 2, s)
         import kv_cache_compression_kvc_amd as K
@@ -373,7 +397,8 @@ class Dense:
                 kernels[name] = kern(kms[a_] + kms[b_], fb[a_] + fb[b_])
         s_enc, s_dec = gbps(U, enc_ms), gbps(U, dec_ms)
         s_p = s_enc * s_dec / (s_enc + s_dec)
-        return {"uncompressed_bytes": U, "ms_per_step": round(step_ms, 4), "GBps": round(gbps(U, step_ms), 3),
+        return {"uncompressed_bytes": U, "ms_per_step": round(step_ms, 4), "step_ms_spread": spread(each),
+                "GBps": round(gbps(U, step_ms), 3),
                 "encode_ms": round(enc_ms, 4), "encode_GBps": round(s_enc, 3),
                 "encode_frac_hbm_peak": round(s_enc / HBM_PEAK_GBPS, 4),
                 "decode_ms": round(dec_ms, 4), "decode_GBps": round(s_dec, 3),
@@ -516,8 +541,8 @@ def paged(wl, steps, warmup) -> dict:
         plan.decode_paged(out, n, offs, dst.seq_lens, kq, vq, dst.num_blocks, btd, ws)
 
     s = torch.cuda.current_stream()
-    enc_ms, ke = profiled(enc, steps, warmup, s)
-    dec_ms, kd = profiled(dec, steps, warmup, s)
+    enc_ms, ke, _ = profiled(enc, steps, warmup, s)
+    dec_ms, kd, _ = profiled(dec, steps, warmup, s)
     st = plan.query_status(ws)
     assert st == K.OK, K.status_string(st)
     fb = {"ENCODE_K": elems * fused_bytes_per_elem(wl.k), "ENCODE_V": elems * fused_bytes_per_elem(wl.v),
@@ -685,6 +710,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": head["ms_per_step"],
+        "step_ms_spread": head["step_ms_spread"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
