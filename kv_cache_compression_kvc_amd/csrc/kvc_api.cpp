@@ -200,6 +200,11 @@ int64_t slab_area(const kvc_plan_s* p) {
   return a256(n * (int64_t)sizeof(SlabDesc)) + a256(n);
 }
 
+// Request area of a paged call (R > 1): the descriptors, then the two tile ->
+// request tables (kReqTableMax + 1 entries each).
+int64_t req_table_off(int64_t R) { return a256(R * (int64_t)sizeof(ReqDesc)); }
+int64_t req_area(int64_t R) { return req_table_off(R) + 2 * 4 * (int64_t)(kReqTableMax + 1); }
+
 WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int64_t R, int64_t slabs = 0,
                    int64_t delta = 0) {
   WsLayout w;
@@ -217,7 +222,7 @@ WsLayout ws_layout(int64_t nchunks, int64_t codes_area, int64_t params_area, int
   w.codes = a256(w.counts + 4 * (int64_t)kNnzSlots * std::max<int64_t>(nchunks, 1));
   w.params = a256(w.codes + codes_area);
   w.reqs = a256(w.params + params_area);
-  w.slabs = a256(w.reqs + (R > 1 ? R * (int64_t)sizeof(ReqDesc) : 0));
+  w.slabs = a256(w.reqs + (R > 1 ? req_area(R) : 0));
   w.delta = a256(w.slabs + slabs);
   w.total = a256(w.delta + delta);
   return w;
@@ -394,6 +399,30 @@ struct PagedJob {
   int64_t chunks = 0, pieces = 0, codes_area = 0, params_area = 0, max_total = 0;
   int64_t tiles[2] = {0, 0};
 };
+
+// The request area's bytes (descriptors and tile -> request tables) of a
+// paged call with R > 1, uploaded in one copy; sets the call's table
+// pointers (into the workspace at `d_area`) and shifts.
+std::vector<uint8_t> request_area(const PagedJob& j, uint8_t* d_area, CallDesc& c) {
+  const int64_t R = (int64_t)j.reqs.size();
+  std::vector<uint8_t> bytes((size_t)req_area(R), 0);
+  std::memcpy(bytes.data(), j.reqs.data(), (size_t)R * sizeof(ReqDesc));
+  for (int w = 0; w < 2; ++w) {
+    int sh = 0;
+    while (((j.tiles[w] + (int64_t(1) << sh) - 1) >> sh) > kReqTableMax) ++sh;
+    const int64_t n = (j.tiles[w] + (int64_t(1) << sh) - 1) >> sh;      // entries 0..n
+    int32_t* tab = (int32_t*)(bytes.data() + req_table_off(R)) + w * (kReqTableMax + 1);
+    int64_t r = 0;
+    for (int64_t i = 0; i <= n; ++i) {
+      const int64_t t = i << sh;
+      while (r + 1 < R && j.reqs[(size_t)r + 1].tile_begin[w] <= t) ++r;
+      tab[i] = (int32_t)r;
+    }
+    c.req_tab[w] = (const int32_t*)(d_area + req_table_off(R)) + w * (kReqTableMax + 1);
+    c.req_shift[w] = sh;
+  }
+  return bytes;
+}
 
 PagedJob paged_job(const kvc_plan_s* p, const int32_t* lens, int R, bool encode) {
   PagedJob j;
@@ -826,7 +855,9 @@ kvc_status kvc_encode_paged(kvc_plan_t p, const void* d_k_pool, const void* d_v_
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (R > 1) {
-    e = hipMemcpyAsync(ws + w.reqs, j.reqs.data(), R * sizeof(ReqDesc), hipMemcpyHostToDevice, s);
+    // pageable source: the copy has taken the bytes when it returns
+    const std::vector<uint8_t> area = request_area(j, ws + w.reqs, c);
+    e = hipMemcpyAsync(ws + w.reqs, area.data(), area.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(requests)");
   }
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
@@ -891,7 +922,8 @@ kvc_status kvc_decode_paged(kvc_plan_t p, const void* d_in, size_t in_bytes, con
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (R > 1) {
-    e = hipMemcpyAsync(ws + w.reqs, j.reqs.data(), R * sizeof(ReqDesc), hipMemcpyHostToDevice, s);
+    const std::vector<uint8_t> area = request_area(j, ws + w.reqs, c);
+    e = hipMemcpyAsync(ws + w.reqs, area.data(), area.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(requests)");
   }
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");

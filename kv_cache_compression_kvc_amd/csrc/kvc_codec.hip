@@ -483,7 +483,10 @@ __device__ __forceinline__ ReqDesc load_req(const CallDesc& c, int r) {
 
 __device__ __forceinline__ int find_req_by_tile(const CallDesc& c, int which, int64_t tile) {
   if (c.R == 1) return 0;
-  int lo = 0, hi = c.R - 1;
+  // the table brackets the request; the search is usually over one or two
+  const int64_t q = tile >> c.req_shift[which];
+  const int32_t* tab = which ? c.req_tab[1] : c.req_tab[0];
+  int lo = uniform_load(tab, q), hi = uniform_load(tab, q + 1);
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     const ReqDesc rm = uniform_load(c.reqs, mid);

@@ -75,10 +75,18 @@ struct ReqDesc {
 };
 
 // Where the requests live and where their data goes.
+// Entries of a paged call's tile -> request table, per tensor (R > 1).
+constexpr int kReqTableMax = 4096;
+
 struct CallDesc {
   int R;                     // requests
   const ReqDesc* reqs;       // device array [R] (R > 1)
   ReqDesc one;               // the request when R == 1
+  // R > 1: req_tab[w][i] = the last request whose first tile of tensor w is at
+  // or before tile i << req_shift[w] (i up to tiles >> req_shift, inclusive),
+  // which brackets the request of any tile to [req_tab[i], req_tab[i + 1]]
+  const int32_t* req_tab[2];
+  int req_shift[2];
   int layers, heads;
   int dtype;                 // 0 fp16, 1 bf16
   TensorPol pol[2];
