@@ -298,6 +298,58 @@ def test_paged_matches_oracle():
     assert np.array_equal(to_u16(kq), kqo) and np.array_equal(to_u16(vq), vqo)
 
 
+def _paged_batch_with_lens(wl, lens, seed):
+    """A PagedBatch of the given request lengths over a pool of exactly the
+    pages they need, permuted by `seed`."""
+    P = wl.page_tokens
+    pages = (lens + P - 1) // P
+    nb = int(pages.sum())
+    maxb = max(1, int(pages.max()))
+    perm = np.random.default_rng([seed, 13]).permutation(nb).astype(np.int32)
+    bt = np.full((len(lens), maxb), -1, dtype=np.int32)
+    pos = 0
+    for r in range(len(lens)):
+        bt[r, :pages[r]] = perm[pos:pos + pages[r]]
+        pos += pages[r]
+    return W.PagedBatch(seq_lens=lens.astype(np.int32), block_table=bt, num_blocks=nb, max_blocks=maxb)
+
+
+def test_paged_many_requests_with_empty_ones():
+    # 40 requests, six of them empty (first, last, two adjacent): empty
+    # requests share their first tile with the next request, and the tile ->
+    # request table of this call (about 9150 tiles per tensor) needs a shift of
+    # 2, so the lookups go through table brackets of several requests; every
+    # stream, offset and reconstructed value must equal the oracle's
+    wl = W.WORKLOADS["c4_paged_llama8b"].with_(layers=2, chunk_bytes=8192)
+    lens = W.paged_layout(wl, requests=40, min_len=1, max_len=900).seq_lens.copy()
+    lens[[0, 7, 13, 14, 26, 39]] = 0
+    batch = _paged_batch_with_lens(wl, lens, seed=5)
+    log(f"paged lens {batch.seq_lens.tolist()} blocks {batch.num_blocks}")
+    kp, vp = W.paged_pools(wl, batch)
+    st, ref, ref_offs = O.encode_paged(O.cfg_from_workload(wl), to_u16(kp), to_u16(vp), batch.num_blocks,
+                                       wl.page_tokens, batch.block_table, batch.seq_lens)
+    assert st == O.OK
+    plan = K.Plan(K.config_from_workload(wl, max_tokens=0))
+    ms, wsb = plan.sizes_paged(batch.seq_lens)
+    out = torch.full((ms,), 0xA5, dtype=torch.uint8, device=DEV)
+    ws = torch.full((wsb,), 0x5A, dtype=torch.uint8, device=DEV)
+    offs = torch.zeros(len(lens) + 1, dtype=torch.int64, device=DEV)
+    bt = torch.from_numpy(batch.block_table).to(DEV)
+    n = plan.encode_paged(kp.to(DEV), vp.to(DEV), batch.num_blocks, bt, batch.seq_lens, out, offs, ws)
+    assert np.array_equal(offs.cpu().numpy().astype(np.uint64), ref_offs)
+    assert np.array_equal(out[:n].cpu().numpy(), ref)
+    dst = _paged_batch_with_lens(wl, lens, seed=6)
+    kq = torch.zeros_like(kp, device=DEV)
+    vq = torch.zeros_like(vp, device=DEV)
+    plan.decode_paged(torch.from_numpy(ref).to(DEV), ref.size, offs, dst.seq_lens, kq, vq, dst.num_blocks,
+                      torch.from_numpy(dst.block_table).to(DEV), ws)
+    assert plan.query_status(ws) == K.OK
+    kqo = np.zeros_like(to_u16(kp)); vqo = np.zeros_like(to_u16(vp))
+    st = O.decode_paged(ref, ref_offs, kqo, vqo, dst.num_blocks, wl.page_tokens, dst.block_table, dst.seq_lens)
+    assert st == O.OK
+    assert np.array_equal(to_u16(kq), kqo) and np.array_equal(to_u16(vq), vqo)
+
+
 @pytest.mark.parametrize("kbits,vbits,stages,round_lens", [(4, 4, W.BYTE_SHUFFLE_RZE, 1),
                                                             (8, 2, W.BYTE_SHUFFLE_RZE, 1),
                                                             (4, 2, W.LLAMA_TUPL_BIT_RZE, 4),
