@@ -146,3 +146,9 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert lib.kvc_decode(p.handle, 16, 10, 64, 16, 16, 256, wsb, None) == K.ERR_CORRUPT_STREAM
     assert lib.kvc_encode_paged(p.handle, 16, 16, 4, 16, 1, None, 0, 16, 1, 16, 256, 1, None, None) \
         == K.ERR_INVALID_ARG   # plan built without page_tokens
+    # the bandwidth probe: unknown flag bits, unsupported read:write pairs and
+    # missing buffers are host errors
+    assert lib.kvc_probe_bandwidth(16, 16, 1024, 1, 1, 4, 16, None) == K.ERR_INVALID_ARG
+    assert lib.kvc_probe_bandwidth(16, 16, 1024, 3, 1, 0, 16, None) == K.ERR_UNSUPPORTED
+    assert lib.kvc_probe_bandwidth(None, 16, 1024, 1, 1, K.PROBE_NT_LOADS, 16, None) == K.ERR_INVALID_ARG
+    assert lib.kvc_probe_bandwidth(16, 16, -1, 1, 0, K.PROBE_SHORT_WAVES, 16, None) == K.ERR_INVALID_ARG
