@@ -1136,9 +1136,13 @@ __global__ __launch_bounds__(256) void k_compact(CallDesc c) {
       if (w == 1) k -= p0;
       const int64_t off = k * 65536;
       const int64_t len = min<int64_t>(65536, rq.params_bytes[w] - off);
+      // both ends are 16-byte aligned (256-byte staging offsets, 16-byte
+      // sections and streams): 16-byte lines, then the last dwords
       const uint32_t* src = (const uint32_t*)(c.params_ws + rq.params_ws_off[w] + off);
       uint32_t* dst = (uint32_t*)(c.stream + stream_base(c, r, true) + rq.params_off[w] + off);
-      for (int64_t i = threadIdx.x; i < len / 4; i += blockDim.x) dst[i] = src[i];
+      const int64_t n16 = len / 16;
+      for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) ((uint4*)dst)[i] = ((const uint4*)src)[i];
+      for (int64_t i = 4 * n16 + threadIdx.x; i < len / 4; i += blockDim.x) dst[i] = src[i];
     }
   }
 }
