@@ -23,6 +23,7 @@ import argparse
 import gc
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -592,6 +593,30 @@ def bandwidth_probes(total_bytes: int = 4 << 30, reps: int = 5) -> dict:
     return out
 
 
+SUB_RESULTS = ("llama70b_32k_zero_rich", "llama70b_128k", "llama8b_paged_64_requests")
+
+
+def sub_result(name: str, ss: int, sw: int) -> dict:
+    """One sub-result of the default run, measured in this process."""
+    import kvc_workloads as W
+    if name == "llama70b_32k_zero_rich":
+        # the headline shape on zero-rich KV: the lossless stage compresses
+        dz = Dense(W.WORKLOADS["c3_llama70b_32k"], "zero_rich", 0.5)
+        r, kz = dz.measure(ss, sw)
+        r["values"] = "half of the 64-token blocks of each (layer, head) zero"
+        r["lossless_kernels"] = dz.lossless_kernels(kz)
+        return r
+    if name == "llama70b_128k":
+        # the 131072-token 70B shape (fp16, int2 K and V): one call, then a layer pipeline
+        d5 = Dense(W.WORKLOADS["c5_llama70b_128k"], "gaussian")
+        r, _ = d5.measure(ss, sw)
+        r["layer_pipeline"] = layer_pipeline(d5, max(2, ss // 2), 1)
+        return r
+    if name == "llama8b_paged_64_requests":
+        return paged(W.WORKLOADS["c4_paged_llama8b"], max(2, ss // 2), 1)
+    raise SystemExit(f"unknown sub-result {name}")
+
+
 def free():
     import torch
     gc.collect()
@@ -610,6 +635,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sub", action="store_true", help="measure the headline workload only")
     ap.add_argument("--sub-steps", type=int, default=0, help="timed steps of each sub-result (0: min(steps, 10))")
+    ap.add_argument("--sub-in-process", action="store_true",
+                    help="measure the sub-results in this process, one after another (for a single-process "
+                         "profiler trace of the whole run)")
+    ap.add_argument("--sub-only", choices=["llama70b_32k_zero_rich", "llama70b_128k", "llama8b_paged_64_requests"],
+                    default=None, help="measure one sub-result and print it as one JSON line (the default run "
+                                       "runs each sub-result this way, in a child process)")
     ap.add_argument("--values", choices=["gaussian", "zero_rich", "correlated"], default="gaussian",
                     help="value model: the workload's Gaussian KV (headline), KV whose 64-token blocks "
                          "are zero with probability --zero-frac, or KV correlated along tokens (AR(1), "
@@ -637,6 +668,14 @@ def main():
 
     import torch
     import kvc_workloads as W
+
+    if args.sub_only:
+        # one sub-result, printed for the parent run to collect
+        r = sub_result(args.sub_only, args.sub_steps or min(args.steps, 10), min(args.warmup, 3))
+        log(f"{args.sub_only}: encode {r['encode_GBps']:.1f} GB/s, decode {r['decode_GBps']:.1f} GB/s, CR "
+            f"{r['compression_ratio']:.3f}")
+        print(json.dumps(r), flush=True)
+        return
 
     # plain device copy of known size: practical bandwidth reference, and the
     # kernel whose counters scale the HBM byte counts of the profile runs
@@ -753,30 +792,23 @@ def main():
     free()
 
     if not args.no_sub and headline:
+        # each sub-result in a child process of its own: device memory that a
+        # previous workload of tens of GB allocated and freed slows the next
+        # one's kernels (the paged batch by 9 % after the 128K workload)
         sub = {}
         ss = args.sub_steps or min(args.steps, 10)
         sw = min(args.warmup, 3)
-        # the headline shape on zero-rich KV: the lossless stage compresses
-        dz = Dense(wl, "zero_rich", 0.5)
-        r, kz = dz.measure(ss, sw)
-        r["values"] = "half of the 64-token blocks of each (layer, head) zero"
-        r["lossless_kernels"] = dz.lossless_kernels(kz)
-        sub["llama70b_32k_zero_rich"] = r
-        dz.release()
-        del dz
-        free()
-        # the 131072-token 70B shape (fp16, int2 K and V): one call, then a layer pipeline
-        w5 = W.WORKLOADS["c5_llama70b_128k"]
-        d5 = Dense(w5, "gaussian")
-        r, _ = d5.measure(ss, sw)
-        r["layer_pipeline"] = layer_pipeline(d5, max(2, ss // 2), 1)
-        sub["llama70b_128k"] = r
-        d5.release()
-        del d5
-        free()
-        # the paged 64-request batch
-        sub["llama8b_paged_64_requests"] = paged(W.WORKLOADS["c4_paged_llama8b"], max(2, ss // 2), 1)
-        free()
+        for name in SUB_RESULTS:
+            if args.sub_in_process:
+                sub[name] = sub_result(name, ss, sw)
+                free()
+                continue
+            cmd = [sys.executable, "-u", os.path.abspath(__file__), "--sub-only", name,
+                   "--sub-steps", str(ss), "--warmup", str(sw)]
+            pr = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+            if pr.returncode != 0:
+                raise SystemExit(f"sub-result {name} failed (exit status {pr.returncode})")
+            sub[name] = json.loads(pr.stdout.strip().splitlines()[-1])
         result["sub_results"] = sub
         for name, r in sub.items():
             log(f"{name}: encode {r['encode_GBps']:.1f} GB/s, decode {r['decode_GBps']:.1f} GB/s, CR "
