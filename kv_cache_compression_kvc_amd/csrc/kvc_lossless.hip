@@ -747,7 +747,7 @@ __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_
         // index of the nibble's first non-zero word; in a chunk that passed
         // the size check every set bit's word lies below nnz
         const uint32_t rr = offs[d] + (uint32_t)__builtin_popcount(bits & below);
-        const uint32_t di = min(wbase + (rr >> 1), 16383u);
+        const uint32_t di = min(wbase + (rr >> 1), 4u * 4096u - 1u);   // at most the chunk's last dword
         const uint32_t d0 = buf32[di], d1 = buf32[di + 1], d2 = buf32[di + 2];
         const uint32_t sh = (rr & 1u) << 4;
         const uint32_t p01 = __builtin_amdgcn_alignbit(d1, d0, sh), p23 = __builtin_amdgcn_alignbit(d2, d1, sh);
