@@ -612,15 +612,13 @@ __device__ __forceinline__ bool wp_decode_chunk(const CallDesc& c, int64_t ch, i
   return stored < L.n && stored > 0 && pos + (uint64_t)stored <= c.stream_bytes && (pos & 15) == 0;
 }
 
-// Waves per block of the word-parallel chunk kernels.  A chunk is one block's
-// work; more waves split its 4 KiB (or 1 KiB) pieces finer, so a chunk's
-// loads, transposes and stores run on more waves at once.  Both kernels hold
-// a 64 KiB LDS buffer, so two blocks fit a CU.  Measured on the 70B shape with
-// half of the 64-token blocks zero: placement 1.21 ms at 4 waves, 0.98 ms at
-// 8 (4 waves per SIMD, a few registers spilled), 1.33 ms at 16 (one block per
-// CU); lossless decode 0.75 ms at 4 waves, 0.93 ms at 8 (spills), 1.17 ms at 16,
-// and 0.91 ms with one 8-wave block per CU holding two chunk buffers, the next
-// chunk loaded straight into LDS while the current one is expanded.
+// Waves per block of the placement and of the TUPL8_1 -> RZE_2 decode.  A
+// chunk is one block's work; more waves split its 4 KiB (or 1 KiB) pieces
+// finer, so a chunk's loads, transposes and stores run on more waves at once.
+// Both hold a 64 KiB LDS buffer, so two blocks fit a CU.  Measured on the 70B
+// shape with half of the 64-token blocks zero: placement 1.21 ms at 4 waves,
+// 0.98 ms at 8 (4 waves per SIMD, a few registers spilled), 1.33 ms at 16 (one
+// block per CU).
 #ifndef KVC_PLACE_WAVES
 #define KVC_PLACE_WAVES 8
 #endif
@@ -632,35 +630,6 @@ constexpr int kPlaceWaves = KVC_PLACE_WAVES;
 constexpr int kPlaceThreads = 64 * kPlaceWaves;
 constexpr int kDecWaves = KVC_DEC_WAVES;
 
-// The stored lines of a chunk, loaded into registers (PT 16-byte lines per
-// thread; lines past the stored length or the stream's end read zero), and
-// their copy into LDS.  Split so that the next chunk's loads are in flight
-// while the current chunk decodes.
-template <int NW>
-struct ChunkLines {
-  static constexpr int NT = 64 * NW, PT = 4096 / NT;
-  uint4 x[PT];
-  __device__ __forceinline__ void load(const CallDesc& c, uint64_t pos, int stored) {
-    const uint64_t avail = (c.stream_bytes > pos) ? c.stream_bytes - pos : 0;
-    const int nv = (stored + 15) / 16;
-    const uint4* src = (const uint4*)(c.stream + pos);
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int k = (int)threadIdx.x + NT * u;
-      x[u] = make_uint4(0, 0, 0, 0);
-      if (k < nv && (uint64_t)(16 * k + 16) <= avail) x[u] = src[k];
-    }
-  }
-  __device__ __forceinline__ void to_lds(int stored, uint4* dst) const {
-    const int nv = (stored + 15) / 16;
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int k = (int)threadIdx.x + NT * u;
-      if (k < nv) dst[k] = x[u];
-    }
-  }
-};
-
 // first candidate at or after i (NT when none), the same in every thread
 template <int NT>
 __device__ __forceinline__ int next_cand(const uint32_t* cand, int i) {
@@ -668,107 +637,251 @@ __device__ __forceinline__ int next_cand(const uint32_t* cand, int i) {
   return i;
 }
 
+// P1 decode staged in phases.  Output group gi (4 KiB) reads, in every bit
+// plane j, the words of bitmap dwords [j dpj + 8 gi, j dpj + 8 gi + 8), so
+// the groups [g0, g1) of a phase read one contiguous run of stored words per
+// plane.  Only those eight runs are staged (the 16-byte lines that cover
+// them, run after run), a phase at a time: a block holds 1/PH of a chunk and
+// more blocks fit a CU than with whole chunks, and the next phase's lines
+// load while the current one decodes.  A wave's decoded group goes out
+// through LDS so that every store instruction writes 1 KiB of whole lines:
+// straight from the transposes, each store would cover a quarter of 32
+// lines, which measured 13 % slower with default stores and four times
+// slower with non-temporal ones.
+#ifndef KVC_P1_PHASES
+#define KVC_P1_PHASES 4
+#endif
+constexpr int kP1Phases = KVC_P1_PHASES;
+constexpr int kP1Gpp = 16 / kP1Phases;               // groups per phase of a 64 KiB chunk
+// a phase's lines for any bitmap: 256 words per group and plane, two lines of
+// slack per run for its unaligned ends
+constexpr int kP1SegLines = 32 * kP1Gpp + 2;
+constexpr int kP1CapLines = 8 * kP1SegLines;
+// LDS per block: the phase's lines, the bitmap and its offsets, and a 4 KiB
+// output staging area per wave: 56 KB (two blocks per CU) at two phases,
+// 39 KB (four) at four
+constexpr int kP1BlocksPerCu = kP1Phases == 2 ? 2 : 4;
+static_assert(kP1Phases == 2 || kP1Phases == 4, "two or four phases");
+
+// bitmap popcount scan into 16-bit offsets (a chunk has at most 32768 words);
+// offs[nd] = total
 template <int NW>
-__global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
-  constexpr int NT = 64 * NW;
-  // one line past the chunk: a lane reads three dwords from its first word's
-  // dword, which may run past the last stored word
-  __shared__ __attribute__((aligned(16))) uint4 buf[4096 + 1];
-  __shared__ uint32_t offs[1024];
+__device__ __forceinline__ uint32_t scan_bitmap16(const uint32_t* bm, uint16_t* offs, int nd, uint32_t* sh32) {
+  constexpr int PT = 1024 / (64 * NW);
+  const int t = threadIdx.x;
+  uint32_t cnt[PT], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int d = PT * t + i;
+    cnt[i] = (d < nd) ? (uint32_t)__builtin_popcount(bm[d]) : 0u;
+    sum += cnt[i];
+  }
+  uint32_t total;
+  uint32_t run = block_excl_scan_u32<NW>(sum, sh32, total);
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int d = PT * t + i;
+    if (d < nd) offs[d] = (uint16_t)run;
+    run += cnt[i];
+  }
+  if (t == 0) offs[nd] = (uint16_t)total;
+  __syncthreads();
+  return total;
+}
+
+// orders a wave's LDS writes before its lanes read each other's (and those
+// reads before the next writes)
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// first set flag at or after i in the 64 NW-bit mask m (64 NW when none)
+template <int NW>
+__device__ __forceinline__ int next_flag(const uint64_t* m, int i) {
+  while (i < 64 * NW) {
+    const uint64_t x = m[i >> 6] >> (i & 63);
+    if (x) return i + (int)__builtin_ctzll(x);
+    i = (i | 63) + 1;
+  }
+  return 64 * NW;
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDesc c, const uint32_t* worklist) {
+  constexpr int NT = 64 * NW, PH = kP1Phases;
+  static_assert(NT == 256, "one bitmap line per thread");
+  constexpr int SPT = NT / 8;                          // loader threads per run
+  __shared__ __attribute__((aligned(16))) uint4 buf[kP1CapLines + 1];   // a lane reads 3 dwords from its first word's
+  __shared__ __attribute__((aligned(16))) uint32_t bm[1024];
+  __shared__ uint16_t offs[1024 + 1];
+  __shared__ __attribute__((aligned(16))) uint4 seg[PH * 8];   // per (phase, plane): first LDS line, first stored line, lines, word shift
   __shared__ uint32_t sh32[NW];
   __shared__ __attribute__((aligned(16))) uint4 nibtab[16];
+  __shared__ uint64_t candm[NW];
+  // a wave's decoded 4 KiB group, so that its stores cover whole lines: lane i
+  // decodes bytes [64 i, 64 i + 64) of the group; store q of lane L writes
+  // bytes 1024 q + 16 L.  16-byte slot s of lane i sits at slot s ^ ((i >> 1) & 3)
+  // of its 64 bytes, which spreads both access patterns over all banks.
+  __shared__ __attribute__((aligned(16))) uint4 ostage[NW * 256];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const XposeLane X = xpose_lane();
   if (threadIdx.x < 16) nibtab[threadIdx.x] = rze_nibble_entry(threadIdx.x);
-  // this block's chunks are blockIdx.x + gridDim.x * i; NT at a time are
-  // checked in parallel and the block then works through those to decode,
-  // the next one's lines loading while the current one decodes
-  __shared__ uint32_t cand[NT];
-  // nothing to decode (e.g. every chunk raw): leave at once
   if (__hip_atomic_load((const uint32_t*)&c.ctl->pad[5], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) return;
   for (int64_t r0 = 0; (int64_t)blockIdx.x + (int64_t)gridDim.x * r0 < c.total_chunks; r0 += NT) {
-  {
-    const int64_t mine = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + threadIdx.x);
-    ChunkLoc L;
-    uint64_t pos;
-    int stored;
-    cand[threadIdx.x] = (mine < c.total_chunks && wp_decode_chunk(c, mine, 1, L, pos, stored)) ? 1u : 0u;
-  }
-  __syncthreads();
-  ChunkLines<NW> lines;
-  ChunkLoc L;
-  uint64_t pos = 0;
-  int stored = 0;
-  int i = next_cand<NT>(cand, 0);
-  if (i < NT) {
-    wp_decode_chunk(c, (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i), 1, L, pos, stored);
-    lines.load(c, pos, stored);
-  }
-  while (i < NT) {
-    const int n = (int)L.n;
-    const ChunkLoc Lc = L;
-    const int sc = stored;
-    const uint64_t avail = (c.stream_bytes > pos) ? c.stream_bytes - pos : 0;
-    lines.to_lds(sc, buf);
+    {
+      const int64_t mine = (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + threadIdx.x);
+      ChunkLoc L;
+      uint64_t pos;
+      int stored;
+      const bool f = mine < c.total_chunks && wp_decode_chunk(c, mine, 1, L, pos, stored);
+      const uint64_t b = __ballot(f);
+      if (lane == 0) candm[wave] = b;
+    }
     __syncthreads();
-    // the next chunk's loads go out now
-    i = next_cand<NT>(cand, i + 1);
+    ChunkLoc L;
+    uint64_t pos = 0;
+    int stored = 0;
+    // x: the lines of a phase in flight, or (x[0]) line threadIdx.x of the next chunk's bitmap
+    constexpr int PTL = (kP1SegLines + SPT - 1) / SPT;   // lines per loader thread, at most
+    uint4 x[PTL];
+    auto load_bitmap = [&]() {
+      const uint64_t avail = (c.stream_bytes > pos) ? c.stream_bytes - pos : 0;
+      const int t = threadIdx.x;
+      x[0] = make_uint4(0, 0, 0, 0);
+      if (t < (int)(L.n / 256) && (uint64_t)(16 * t + 16) <= avail) x[0] = ((const uint4*)(c.stream + pos))[t];
+    };
+    int i = next_flag<NW>(candm, 0);
     if (i < NT) {
       wp_decode_chunk(c, (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i), 1, L, pos, stored);
-      lines.load(c, pos, stored);
+      load_bitmap();
     }
-    // bytes of the last 16-byte line past the stored length are ignored
-    bool ok = sc >= n / 16;
-    uint32_t nnz = 0;
-    if (ok) {
-      nnz = scan_bitmap<NW>((const uint32_t*)buf, offs, n / 64, sh32);
-      ok = n / 16 + 2 * (int)nnz == sc && (uint64_t)(16 * ((sc + 15) / 16)) <= avail + 15;
-    }
-    if (!ok) {
-      if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+    while (i < NT) {
+      const int n = (int)L.n;
+      const int64_t dst0 = L.src;
+      const int sc = stored;
+      const uint64_t cpos = pos;
+      const uint64_t avail = (c.stream_bytes > cpos) ? c.stream_bytes - cpos : 0;
+      if ((int)threadIdx.x < n / 256) *(uint4*)(bm + 4 * threadIdx.x) = x[0];
       __syncthreads();
-      continue;
-    }
-    const uint32_t* bm = (const uint32_t*)buf;
-    const uint32_t* buf32 = (const uint32_t*)buf;
-    const uint32_t wbase = (uint32_t)(n / 64);         // first dword of the words
-    const int ngi = n / 4096, dpj = n / 512;
-    const int j = lane >> 3, bb = lane & 7;
-    const uint32_t below = (1u << (4 * bb)) - 1u;      // bitmap bits of the nibbles before this lane's
-    const rze_u16x2 one2 = opaque_one2();
-    uint32_t bad = 0;
-    for (int gi = wave; gi < ngi; gi += NW) {
-      uint32_t w[16];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int d = j * dpj + 8 * gi + kk;
-        const uint32_t bits = bm[d];
-        const uint32_t nib = (bits >> (4 * bb)) & 15u;
-        // index of the nibble's first non-zero word; in a chunk that passed
-        // the size check every set bit's word lies below nnz
-        const uint32_t rr = offs[d] + (uint32_t)__builtin_popcount(bits & below);
-        const uint32_t di = min(wbase + (rr >> 1), 4u * 4096u - 1u);   // at most the chunk's last dword
-        const uint32_t d0 = buf32[di], d1 = buf32[di + 1], d2 = buf32[di + 2];
-        const uint32_t sh = (rr & 1u) << 4;
-        const uint32_t p01 = __builtin_amdgcn_alignbit(d1, d0, sh), p23 = __builtin_amdgcn_alignbit(d2, d1, sh);
-        const uint4 e = nibtab[nib];
-        uint32_t lo = __builtin_amdgcn_perm(p23, p01, e.x), hi = __builtin_amdgcn_perm(p23, p01, e.y);
-        // a set bit must mark a non-zero word: min(word, 1) per half against the table
-        bad |= (nz_halves(lo, one2) ^ e.z) | (nz_halves(hi, one2) ^ e.w);
-        xpose64(lo, hi, X);
-        w[2 * kk] = lo;
-        w[2 * kk + 1] = hi;
+      i = next_flag<NW>(candm, i + 1);
+      if (i < NT) wp_decode_chunk(c, (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i), 1, L, pos, stored);
+      // bytes of the last 16-byte line past the stored length are ignored
+      bool ok = sc >= n / 16;
+      const int nd = n / 64;
+      uint32_t nnz = 0;
+      if (ok) {
+        nnz = scan_bitmap16<NW>(bm, offs, nd, sh32);
+        ok = n / 16 + 2 * (int)nnz == sc && (uint64_t)(16 * ((sc + 15) / 16)) <= avail + 15;
       }
-      uint4* dst = (uint4*)(c.codes + Lc.src + (int64_t)gi * 4096 + 64 * lane);
+      if (!ok) {
+        if (threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
+        __syncthreads();
+        if (i < NT) load_bitmap();
+        continue;
+      }
+      const int ngi = n / 4096, dpj = n / 512;
+      const int gpp = (ngi + PH - 1) / PH;
+      if (wave == 0) {
+        // run of plane j in phase h (lane 8 h + j): words [A, B), lines A / 8 .. (B + 7) / 8
+        const int h = lane >> 3, j = lane & 7;
+        const int g0 = min(ngi, h * gpp), g1 = min(ngi, g0 + gpp);
+        uint32_t A = 0, B = 0;
+        if (h < PH) { A = offs[j * dpj + 8 * g0]; B = offs[j * dpj + 8 * g1]; }
+        const uint32_t cnt = (B > A) ? ((B + 7) >> 3) - (A >> 3) : 0u;
+        uint32_t s = cnt;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) dst[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+        for (int o = 1; o < 8; o <<= 1) {
+          const uint32_t y = (uint32_t)__shfl_up((int)s, o, 8);
+          if (j >= o) s += y;
+        }
+        const uint32_t lb = s - cnt;
+        if (h < PH) seg[lane] = make_uint4(lb, A >> 3, cnt, 8u * lb - 8u * (A >> 3));
+      }
+      __syncthreads();
+      const uint4* src = (const uint4*)(c.stream + cpos);
+      const uint32_t wline = (uint32_t)(n / 256);        // first line of the words
+      auto load_phase = [&](int h) {
+        const uint4 sg = seg[8 * h + (int)threadIdx.x / SPT];
+        const int k0 = (int)threadIdx.x % SPT;
+#pragma unroll
+        for (int u = 0; u < PTL; ++u) {
+          const int k = k0 + SPT * u;
+          const uint32_t l = wline + sg.y + (uint32_t)k;
+          x[u] = make_uint4(0, 0, 0, 0);
+          if (k < (int)sg.z && (uint64_t)(16 * l + 16) <= avail) x[u] = src[l];
+        }
+      };
+      auto store_phase = [&](int h) {
+        const uint4 sg = seg[8 * h + (int)threadIdx.x / SPT];
+        const int k0 = (int)threadIdx.x % SPT;
+#pragma unroll
+        for (int u = 0; u < PTL; ++u) {
+          const int k = k0 + SPT * u;
+          if (k < (int)sg.z) buf[sg.x + k] = x[u];
+        }
+      };
+      const uint32_t* buf32 = (const uint32_t*)buf;
+      const int j = lane >> 3, bb = lane & 7;
+      const uint32_t below = (1u << (4 * bb)) - 1u;     // bitmap bits of the nibbles before this lane's
+      const rze_u16x2 one2 = opaque_one2();
+      uint32_t bad = 0;
+      load_phase(0);
+#pragma unroll 1
+      for (int h = 0; h < PH; ++h) {
+        store_phase(h);
+        __syncthreads();
+        if (h + 1 < PH) load_phase(h + 1);
+        else if (i < NT) load_bitmap();                   // the next chunk's bitmap goes out now
+        const uint32_t shift = seg[8 * h + j].w;         // stored word index -> LDS word index
+        const int g1 = min(ngi, h * gpp + gpp);
+        for (int gi = h * gpp + wave; gi < g1; gi += NW) {
+          uint4* os = ostage + 256 * wave;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+          uint32_t w[4];
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const int kk = 2 * q + k2;
+            const int d = j * dpj + 8 * gi + kk;
+            const uint32_t bits = bm[d];
+            const uint32_t nib = (bits >> (4 * bb)) & 15u;
+            // index of the nibble's first non-zero word; every word this
+            // nibble can mark lies in the phase's run of plane j
+            const uint32_t rr = (uint32_t)offs[d] + (uint32_t)__builtin_popcount(bits & below);
+            const uint32_t di = min((rr + shift) >> 1, 4u * (uint32_t)kP1CapLines + 1u);
+            const uint32_t d0 = buf32[di], d1 = buf32[di + 1], d2 = buf32[di + 2];
+            const uint32_t sh = (rr & 1u) << 4;
+            const uint32_t p01 = __builtin_amdgcn_alignbit(d1, d0, sh), p23 = __builtin_amdgcn_alignbit(d2, d1, sh);
+            const uint4 e = nibtab[nib];
+            uint32_t lo = __builtin_amdgcn_perm(p23, p01, e.x), hi = __builtin_amdgcn_perm(p23, p01, e.y);
+            // a set bit must mark a non-zero word: min(word, 1) per half against the table
+            bad |= (nz_halves(lo, one2) ^ e.z) | (nz_halves(hi, one2) ^ e.w);
+            xpose64(lo, hi, X);
+            w[2 * k2] = lo;
+            w[2 * k2 + 1] = hi;
+          }
+          os[4 * lane + (q ^ ((lane >> 1) & 3))] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+          wave_lds_sync();
+          uint4* dst = (uint4*)(c.codes + dst0 + (int64_t)gi * 4096);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i2 = 16 * q + (lane >> 2), s2 = lane & 3;
+            dst[64 * q + lane] = os[4 * i2 + (s2 ^ ((i2 >> 1) & 3))];
+          }
+          wave_lds_sync();                                 // the next group's writes follow these reads
+        }
+        if (h + 1 < PH) __syncthreads();                 // the block is done with this phase's lines
+      }
+      // a set bitmap bit must mark a non-zero word (and the block is done with buf, bm, offs)
+      if (__syncthreads_or((int)bad) && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
     }
-    // a set bitmap bit must mark a non-zero word (and the block is done with buf)
-    if (__syncthreads_or((int)bad) && threadIdx.x == 0) set_status2(c.ctl, kStCorrupt);
-  }
-  __syncthreads();                                   // cand is rewritten next round
+    __syncthreads();                                   // candm is rewritten next round
   }
 }
+
 template <int NW>
 __global__ __launch_bounds__(64 * NW, NW / 2 < 4 ? NW / 2 : 4) void k_ll_decode_p2(CallDesc c, const uint32_t* worklist) {
   constexpr int NT = 64 * NW;
@@ -1725,7 +1838,7 @@ hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s) {
   const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
   const bool p2 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_RZE_2 && c.stages[2] == 0;
   const int fgrid = (int)std::min<int64_t>(c.total_chunks, 512);
-  if (p1) k_ll_decode_p1<kDecWaves><<<fgrid, 64 * kDecWaves, 0, s>>>(c, worklist);
+  if (p1) k_ll_decode_p1<4><<<(int)std::min<int64_t>(c.total_chunks, 256 * kP1BlocksPerCu), 256, 0, s>>>(c, worklist);
   else if (p2) k_ll_decode_p2<kDecWaves><<<fgrid, 64 * kDecWaves, 0, s>>>(c, worklist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (all_word_parallel(c)) return hipSuccess;

@@ -16,20 +16,30 @@ __device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) {
   return __builtin_amdgcn_bitop3_b32(m, a, b, 0xCA);
 }
 
-// Lane constants of the 64x64 bit transpose: for the rounds exchanging with
-// lane ^ 16, ^ 8, ^ 4, ^ 2, ^ 1, the bits this lane keeps and the rotation
-// that aligns the partner's bits.
+// Lane constants of the 64x64 bit transpose.  The rounds exchanging with
+// lane ^ 16 and lane ^ 8 move whole bytes, so each is one v_perm_b32 of the
+// lane's word and its partner's (sel16, sel8); the rounds with lane ^ 4, ^ 2
+// and ^ 1 keep the bits mk[r] and rotate the partner's by sh[r].
 struct XposeLane {
-  uint32_t mk[5];
-  uint32_t sh[5];
+  uint32_t sel16, sel8;
+  uint32_t mk[3];
+  uint32_t sh[3];
 };
+// v_perm_b32 selectors of a byte-moving round, the partner's word being the
+// high operand (bytes 4..7): lane ^ 16 (lower lanes keep their two low bytes
+// and take the partner's two low ones above them; upper lanes the mirror
+// image) and lane ^ 8 (the same with bytes 0, 2 and 1, 3)
+__device__ __forceinline__ uint32_t xpose_sel16(int lane) { return (lane & 16) ? 0x03020706u : 0x05040100u; }
+__device__ __forceinline__ uint32_t xpose_sel8(int lane) { return (lane & 8) ? 0x03070105u : 0x06020400u; }
 __device__ __forceinline__ XposeLane xpose_lane() {
   XposeLane x;
   const int lane = __lane_id();
-  const uint32_t m[5] = {0x0000FFFFu, 0x00FF00FFu, 0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
+  x.sel16 = xpose_sel16(lane);
+  x.sel8 = xpose_sel8(lane);
+  const uint32_t m[3] = {0x0F0F0F0Fu, 0x33333333u, 0x55555555u};
 #pragma unroll
-  for (int r = 0; r < 5; ++r) {
-    const int j = 16 >> r;
+  for (int r = 0; r < 3; ++r) {
+    const int j = 4 >> r;
     const bool lower = (lane & j) == 0;
     x.mk[r] = lower ? m[r] : ~m[r];
     x.sh[r] = lower ? (uint32_t)(32 - j) : (uint32_t)j;
@@ -57,15 +67,15 @@ __device__ __forceinline__ void xpose64(uint32_t& lo, uint32_t& hi, const XposeL
   }
   uint32_t a, b;
   a = xchg16(lo); b = xchg16(hi);
-  lo = bfi32(X.mk[0], lo, rotr32(a, X.sh[0])); hi = bfi32(X.mk[0], hi, rotr32(b, X.sh[0]));
+  lo = __builtin_amdgcn_perm(a, lo, X.sel16); hi = __builtin_amdgcn_perm(b, hi, X.sel16);
   a = xchg8(lo); b = xchg8(hi);
-  lo = bfi32(X.mk[1], lo, rotr32(a, X.sh[1])); hi = bfi32(X.mk[1], hi, rotr32(b, X.sh[1]));
+  lo = __builtin_amdgcn_perm(a, lo, X.sel8); hi = __builtin_amdgcn_perm(b, hi, X.sel8);
   a = xchg4(lo); b = xchg4(hi);
-  lo = bfi32(X.mk[2], lo, rotr32(a, X.sh[2])); hi = bfi32(X.mk[2], hi, rotr32(b, X.sh[2]));
+  lo = bfi32(X.mk[0], lo, rotr32(a, X.sh[0])); hi = bfi32(X.mk[0], hi, rotr32(b, X.sh[0]));
   a = xchg2(lo); b = xchg2(hi);
-  lo = bfi32(X.mk[3], lo, rotr32(a, X.sh[3])); hi = bfi32(X.mk[3], hi, rotr32(b, X.sh[3]));
+  lo = bfi32(X.mk[1], lo, rotr32(a, X.sh[1])); hi = bfi32(X.mk[1], hi, rotr32(b, X.sh[1]));
   a = xchg1(lo); b = xchg1(hi);
-  lo = bfi32(X.mk[4], lo, rotr32(a, X.sh[4])); hi = bfi32(X.mk[4], hi, rotr32(b, X.sh[4]));
+  lo = bfi32(X.mk[2], lo, rotr32(a, X.sh[2])); hi = bfi32(X.mk[2], hi, rotr32(b, X.sh[2]));
 }
 
 // xpose64 with the lane constants derived in place (for kernels with no
@@ -80,14 +90,18 @@ __device__ __forceinline__ void xpose64_lean(uint32_t& lo, uint32_t& hi) {
   // the caller's loop into registers
   uint32_t lane = (uint32_t)__lane_id();
   asm volatile("" : "+v"(lane));
-  uint32_t a, b, mk, sh;
+  uint32_t a, b, mk, sh, sel;
+  sel = xpose_sel16((int)lane);
+  a = xchg16(lo); b = xchg16(hi);
+  lo = __builtin_amdgcn_perm(a, lo, sel); hi = __builtin_amdgcn_perm(b, hi, sel);
+  sel = xpose_sel8((int)lane);
+  a = xchg8(lo); b = xchg8(hi);
+  lo = __builtin_amdgcn_perm(a, lo, sel); hi = __builtin_amdgcn_perm(b, hi, sel);
 #define KVC_XROUND(J, M, XCHG)                                            \
   mk = (lane & (J)) ? ~(uint32_t)(M) : (uint32_t)(M);                     \
   sh = (lane & (J)) ? (uint32_t)(J) : (uint32_t)(32 - (J));               \
   a = XCHG(lo); b = XCHG(hi);                                             \
   lo = bfi32(mk, lo, rotr32(a, sh)); hi = bfi32(mk, hi, rotr32(b, sh));
-  KVC_XROUND(16, 0x0000FFFFu, xchg16)
-  KVC_XROUND(8, 0x00FF00FFu, xchg8)
   KVC_XROUND(4, 0x0F0F0F0Fu, xchg4)
   KVC_XROUND(2, 0x33333333u, xchg2)
   KVC_XROUND(1, 0x55555555u, xchg1)
