@@ -331,15 +331,13 @@ __device__ __forceinline__ uint32_t pack_dword(const uint32_t* q) {
                                              __builtin_amdgcn_perm(q[3], q[1], 0x0c0c0400u), 0x05040100u);
     return (o << 4) | e;
   } else {
-    uint32_t by[4];
+    // code pairs as 4-bit values in the low byte (bits 8..23 still zero),
+    // packed as 4-bit codes; the byte selections keep the compiler from
+    // re-associating the whole merge into one shift per code
+    uint32_t t[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t p0 = (q[4 * k + 1] << 2) | q[4 * k];
-      const uint32_t p1 = (q[4 * k + 3] << 2) | q[4 * k + 2];
-      by[k] = (p1 << 4) | p0;
-    }
-    const uint32_t a = (by[1] << 8) | by[0], b = (by[3] << 8) | by[2];
-    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+    for (int k = 0; k < 8; ++k) t[k] = (q[2 * k + 1] << 2) | q[2 * k];
+    return pack_dword<4>(t);
   }
 }
 
