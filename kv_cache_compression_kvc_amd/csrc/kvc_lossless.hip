@@ -523,14 +523,17 @@ __global__ __launch_bounds__(256) void k_ll_encode_generic(CallDesc c, const uin
 // builds the bitmap, scans its popcounts for the word offsets and writes the
 // words; the decode kernels below read them back.
 
-// bits 0..3: which 16-bit quarters of (lo, hi) are non-zero
-// OR over the 8 lanes of each aligned group of 8 (every DPP source lane
-// exists: no old value needed)
-__device__ __forceinline__ uint32_t or8(uint32_t x) {
-  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);    // lane ^ 1
-  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);    // lane ^ 2
-  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true);   // mirror within 8
-  return x;
+// 8x8 transpose of nibbles over each aligned group of 8 lanes: nibble c of
+// lane 8 g + r becomes nibble r of lane 8 g + c.  Three rounds swap the
+// off-diagonal blocks: 16-bit halves with lane ^ 4, bytes with lane ^ 2
+// (one v_perm_b32 each), nibbles with lane ^ 1.
+__device__ __forceinline__ uint32_t nibble_xpose8(uint32_t x, int lane) {
+  uint32_t p = xchg4(x);
+  x = __builtin_amdgcn_perm(p, x, (lane & 4) ? 0x03020706u : 0x05040100u);
+  p = xchg2(x);
+  x = __builtin_amdgcn_perm(p, x, (lane & 2) ? 0x03070105u : 0x06020400u);
+  p = xchg1(x);
+  return bfi32((lane & 1) ? 0xF0F0F0F0u : 0x0F0F0F0Fu, x, rotr32(p, (lane & 1) ? 4u : 28u));
 }
 
 // Block scan of the popcounts of nd <= 1024 bitmap dwords: offs[d] = number
@@ -840,7 +843,7 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
           uint4* os = ostage + 256 * wave;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-          uint32_t w[4];
+          uint32_t w[4], wl[2], wh[2];
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
             const int kk = 2 * q + k2;
@@ -858,10 +861,11 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
             uint32_t lo = __builtin_amdgcn_perm(p23, p01, e.x), hi = __builtin_amdgcn_perm(p23, p01, e.y);
             // a set bit must mark a non-zero word: min(word, 1) per half against the table
             bad |= (nz_halves(lo, one2) ^ e.z) | (nz_halves(hi, one2) ^ e.w);
-            xpose64(lo, hi, X);
-            w[2 * k2] = lo;
-            w[2 * k2 + 1] = hi;
+            wl[k2] = lo;
+            wh[k2] = hi;
           }
+          xpose64_n<2>(wl, wh, X);
+          w[0] = wl[0]; w[1] = wh[0]; w[2] = wl[1]; w[3] = wh[1];
           os[4 * lane + (q ^ ((lane >> 1) & 3))] = make_uint4(w[0], w[1], w[2], w[3]);
           }
           wave_lds_sync();
@@ -1405,15 +1409,23 @@ __device__ __forceinline__ void place_chunk(const CallDesc& c, int64_t k, int64_
           const uint4 x = src[q];
           R[16 * s4 + 4 * q] = x.x; R[16 * s4 + 4 * q + 1] = x.y; R[16 * s4 + 4 * q + 2] = x.z; R[16 * s4 + 4 * q + 3] = x.w;
         }
+        uint32_t qs = 0;                                 // nibble kk: non-zero words of this lane's row kk
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          uint32_t lo = R[16 * s4 + 2 * kk], hi = R[16 * s4 + 2 * kk + 1];
-          xpose64(lo, hi, X);
-          R[16 * s4 + 2 * kk] = lo;
-          R[16 * s4 + 2 * kk + 1] = hi;
-          const uint32_t dw = or8(nz_quarters(lo, hi, one2) << (4 * (lane & 7)));
-          if ((lane & 7) == 0) bm[(lane >> 3) * dpj + 8 * gi + kk] = dw;
+        for (int k2 = 0; k2 < 8; k2 += 2) {
+          uint32_t lo[2] = {R[16 * s4 + 2 * k2], R[16 * s4 + 2 * k2 + 2]};
+          uint32_t hi[2] = {R[16 * s4 + 2 * k2 + 1], R[16 * s4 + 2 * k2 + 3]};
+          xpose64_n<2>(lo, hi, X);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int kk = k2 + u;
+            R[16 * s4 + 2 * kk] = lo[u];
+            R[16 * s4 + 2 * kk + 1] = hi[u];
+            qs |= nz_quarters(lo[u], hi[u], one2) << (4 * kk);
+          }
         }
+        // bitmap dword (j, kk) is nibble kk of lanes 8 j + bb, bb = 0..7, placed
+        // at nibble bb: after the transpose lane 8 j + kk holds it
+        bm[(lane >> 3) * dpj + 8 * gi + (lane & 7)] = nibble_xpose8(qs, lane);
       }
     }
   } else if (mode == 4) {

@@ -78,6 +78,43 @@ __device__ __forceinline__ void xpose64(uint32_t& lo, uint32_t& hi, const XposeL
   lo = bfi32(X.mk[2], lo, rotr32(a, X.sh[2])); hi = bfi32(X.mk[2], hi, rotr32(b, X.sh[2]));
 }
 
+// N transposes at once, round by round, so that each round's exchanges
+// (swizzles with their LDS latency, DPP moves with their wait states) are
+// issued together
+template <int N>
+__device__ __forceinline__ void xpose64_n(uint32_t* lo, uint32_t* hi, const XposeLane& X) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    auto p = __builtin_amdgcn_permlane32_swap(lo[i], hi[i], false, false);
+    lo[i] = p[0];
+    hi[i] = p[1];
+  }
+  uint32_t a[N], b[N];
+#define KVC_XN_EXCHANGE(XCHG)                                                   \
+  _Pragma("unroll") for (int i = 0; i < N; ++i) { a[i] = XCHG(lo[i]); b[i] = XCHG(hi[i]); }
+  KVC_XN_EXCHANGE(xchg16)
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    lo[i] = __builtin_amdgcn_perm(a[i], lo[i], X.sel16); hi[i] = __builtin_amdgcn_perm(b[i], hi[i], X.sel16);
+  }
+  KVC_XN_EXCHANGE(xchg8)
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    lo[i] = __builtin_amdgcn_perm(a[i], lo[i], X.sel8); hi[i] = __builtin_amdgcn_perm(b[i], hi[i], X.sel8);
+  }
+#define KVC_XN_BITS(XCHG, R)                                                     \
+  KVC_XN_EXCHANGE(XCHG)                                                          \
+  _Pragma("unroll") for (int i = 0; i < N; ++i) {                                \
+    lo[i] = bfi32(X.mk[R], lo[i], rotr32(a[i], X.sh[R]));                        \
+    hi[i] = bfi32(X.mk[R], hi[i], rotr32(b[i], X.sh[R]));                        \
+  }
+  KVC_XN_BITS(xchg4, 0)
+  KVC_XN_BITS(xchg2, 1)
+  KVC_XN_BITS(xchg1, 2)
+#undef KVC_XN_BITS
+#undef KVC_XN_EXCHANGE
+}
+
 // xpose64 with the lane constants derived in place (for kernels with no
 // registers to spare for XposeLane)
 __device__ __forceinline__ void xpose64_lean(uint32_t& lo, uint32_t& hi) {
