@@ -771,10 +771,16 @@ kvc_status kvc_decode(kvc_plan_t p, const void* d_in, size_t in_bytes, int32_t t
     if ((st = upload_slabs(p, tokens, ws + w.slabs, s, c, tb)) != KVC_OK) return st;
     c.direct[0] = c.direct[1] = 0;
   }
-  c.validate_in_reset = 1;                           // one launch clears the status and checks the header
-  if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
-  if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
-  if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
+  // small calls (a layer at a time, say): one launch for the whole front
+  const bool small = c.total_chunks > 0 && c.total_chunks <= kFrontChunks;
+  if (small) {
+    if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_dec_front_small(c, s); })) != hipSuccess) return hip_fail(e, "front");
+  } else {
+    c.validate_in_reset = 1;                         // one launch clears the status and checks the header
+    if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
+    if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
+  }
+  if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, small, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return fused_all(p, c, tb, 0, false, s); })) != hipSuccess) return hip_fail(e, "decode K");
   if ((e = timed(KVC_KERNEL_DECODE_V, s, [&] { return fused_all(p, c, tb, 1, false, s); })) != hipSuccess) return hip_fail(e, "decode V");
   for (int k = 0; k < 2; ++k) {
@@ -932,7 +938,7 @@ kvc_status kvc_decode_paged(kvc_plan_t p, const void* d_in, size_t in_bytes, con
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_reset(c, s); })) != hipSuccess) return hip_fail(e, "reset");
   if ((e = timed(KVC_KERNEL_AUX, s, [&] { return launch_validate(c, s); })) != hipSuccess) return hip_fail(e, "validate");
   if ((e = timed(KVC_KERNEL_SCAN, s, [&] { return launch_scan(c, true, s); })) != hipSuccess) return hip_fail(e, "scan");
-  if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, s); })) != hipSuccess) return hip_fail(e, "lossless");
+  if ((e = timed(KVC_KERNEL_LOSSLESS_DEC, s, [&] { return launch_lossless_decode(c, false, s); })) != hipSuccess) return hip_fail(e, "lossless");
   if ((e = timed(KVC_KERNEL_DECODE_K, s, [&] { return launch_decode_fused(c, 0, s); })) != hipSuccess) return hip_fail(e, "decode K");
   if ((e = timed(KVC_KERNEL_DECODE_V, s, [&] { return launch_decode_fused(c, 1, s); })) != hipSuccess) return hip_fail(e, "decode V");
   return KVC_OK;

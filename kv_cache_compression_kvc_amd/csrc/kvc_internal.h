@@ -156,7 +156,13 @@ hipError_t launch_delta(const CallDesc& c, int which, int T, bool forward, const
 hipError_t launch_compact(const CallDesc& c, hipStream_t s);
 hipError_t launch_place(const CallDesc& c, hipStream_t s);
 hipError_t launch_validate(const CallDesc& c, hipStream_t s);
-hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s);
+// classified: the chunks were classified by launch_dec_front_small
+hipError_t launch_lossless_decode(const CallDesc& c, bool classified, hipStream_t s);
+// One-request decodes of at most kFrontChunks chunks: reset, header check,
+// chunk-offset scan and classification in one single-block launch (in place
+// of launch_reset, launch_scan and the classification).
+constexpr int kFrontChunks = 1024;
+hipError_t launch_dec_front_small(const CallDesc& c, hipStream_t s);
 // Whether a one-request call's chunks all go to the word-parallel kernels (a
 // standard pipeline and every chunk size a multiple of its block).
 bool all_word_parallel(const CallDesc& c);

@@ -1699,54 +1699,107 @@ hipError_t launch_validate(const CallDesc& c, hipStream_t s) {
 // compressed chunk of a standard pipeline is left to the word-parallel
 // kernels (which find it by index; only the count is kept here), and any
 // other goes to the stage engine.
-__global__ __launch_bounds__(256) void k_ll_classify_dec(CallDesc c, uint32_t* worklist) {
-  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, dt = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t r = t0; r < c.R; r += dt) {
-    const ReqDesc rq = req_at(c, (int)r);
-    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
-    const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
-    const uint64_t want = (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
-    if (base + 64 > c.stream_bytes || *(const uint64_t*)(c.stream + base + 56) != want)
-      set_status2(c.ctl, kStCorrupt);
+// request r's chunk sizes must add up to its header's total
+__device__ __forceinline__ void check_request_total(const CallDesc& c, int64_t r) {
+  const ReqDesc rq = req_at(c, (int)r);
+  const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+  const int64_t cend = rq.chunk_begin + rq.nchunks[0] + rq.nchunks[1];
+  const uint64_t want = (uint64_t)rq.payload_off + (c.chunk_offs[cend] - c.chunk_offs[rq.chunk_begin]);
+  if (base + 64 > c.stream_bytes || *(const uint64_t*)(c.stream + base + 56) != want)
+    set_status2(c.ctl, kStCorrupt);
+}
+// classify chunk ch; returns 1 for a chunk left to the word-parallel kernels
+__device__ __forceinline__ uint32_t classify_dec_chunk(const CallDesc& c, uint32_t* worklist, int pipe, int64_t ch) {
+  const int r = find_req_by_chunk(c, ch);
+  const ReqDesc rq = req_at(c, r);
+  const ChunkLoc L = locate_chunk(c, rq, r, ch);
+  const uint32_t e = c.chunk_sizes[ch];
+  const int64_t stored = e & 0x7fffffffu;
+  const bool raw = (e >> 31) != 0;
+  const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
+  const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
+  const bool ok = (raw ? stored == L.n : (stored < L.n && stored > 0)) && pos + (uint64_t)stored <= c.stream_bytes &&
+                  (pos & 15) == 0;
+  if (!ok) {
+    set_status2(c.ctl, kStCorrupt);
+    return 0;
   }
-  const int pipe = fast_pipeline(c);
-  uint32_t wp = 0;                                   // compressed chunks left to the word-parallel kernels
-  for (int64_t ch = t0; ch < c.total_chunks; ch += dt) {
-    const int r = find_req_by_chunk(c, ch);
-    const ReqDesc rq = req_at(c, r);
-    const ChunkLoc L = locate_chunk(c, rq, r, ch);
-    const uint32_t e = c.chunk_sizes[ch];
-    const int64_t stored = e & 0x7fffffffu;
-    const bool raw = (e >> 31) != 0;
-    const uint64_t base = c.req_offsets ? c.req_offsets[r] : 0;
-    const uint64_t pos = base + (uint64_t)rq.payload_off + (c.chunk_offs[ch] - c.chunk_offs[rq.chunk_begin]);
-    const bool ok = (raw ? stored == L.n : (stored < L.n && stored > 0)) && pos + (uint64_t)stored <= c.stream_bytes &&
-                    (pos & 15) == 0;
-    if (!ok) {
-      set_status2(c.ctl, kStCorrupt);
-      continue;
-    }
-    bool in_place = raw && c.direct[L.w];
-    if (in_place && c.straddle) {
-      // a tile that also covers a compressed neighbour reads both from the codes area
-      const int64_t s0 = rq.chunk_begin + (L.w ? rq.nchunks[0] : 0), s1 = s0 + rq.nchunks[L.w];
-      const bool prev_c = ch > s0 && !(c.chunk_sizes[ch - 1] >> 31);
-      const bool next_c = ch + 1 < s1 && !(c.chunk_sizes[ch + 1] >> 31);
-      in_place = !(prev_c || next_c);
-    }
-    if (in_place) {
-      // the reconstruct kernels read this chunk from the stream
-    } else if (raw || (c.mirror[L.w] && fast_eligible(1, L.n))) {
-      push_block(c, worklist, ch);
-    } else if (!fast_eligible(pipe, L.n)) {
-      push_work(c, worklist, ch);                    // the stage engine
-    } else {
-      ++wp;                                          // the word-parallel kernels find theirs by index
-    }
+  bool in_place = raw && c.direct[L.w];
+  if (in_place && c.straddle) {
+    // a tile that also covers a compressed neighbour reads both from the codes area
+    const int64_t s0 = rq.chunk_begin + (L.w ? rq.nchunks[0] : 0), s1 = s0 + rq.nchunks[L.w];
+    const bool prev_c = ch > s0 && !(c.chunk_sizes[ch - 1] >> 31);
+    const bool next_c = ch + 1 < s1 && !(c.chunk_sizes[ch + 1] >> 31);
+    in_place = !(prev_c || next_c);
   }
+  if (in_place) {
+    // the reconstruct kernels read this chunk from the stream
+  } else if (raw || (c.mirror[L.w] && fast_eligible(1, L.n))) {
+    push_block(c, worklist, ch);
+  } else if (!fast_eligible(pipe, L.n)) {
+    push_work(c, worklist, ch);                      // the stage engine
+  } else {
+    return 1;                                        // the word-parallel kernels find theirs by index
+  }
+  return 0;
+}
+__device__ __forceinline__ void count_word_parallel(const CallDesc& c, uint32_t wp) {
   wp = wave_sum_u32(wp);
   if ((threadIdx.x & 63) == 0 && wp)
     __hip_atomic_fetch_add((uint32_t*)&c.ctl->pad[5], wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void k_ll_classify_dec(CallDesc c, uint32_t* worklist) {
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, dt = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t r = t0; r < c.R; r += dt) check_request_total(c, r);
+  const int pipe = fast_pipeline(c);
+  uint32_t wp = 0;                                   // compressed chunks left to the word-parallel kernels
+  for (int64_t ch = t0; ch < c.total_chunks; ch += dt) wp += classify_dec_chunk(c, worklist, pipe, ch);
+  count_word_parallel(c, wp);
+}
+
+// Small one-request decodes (at most kFrontChunks chunks, one per thread):
+// the reset, the header check, the chunk-offset scan over the stream's table
+// and the classification in one launch instead of three, which a layer-by-
+// layer pipeline pays once per layer.
+__global__ __launch_bounds__(kFrontChunks) void k_dec_front_small(CallDesc c, uint32_t* worklist) {
+  __shared__ uint32_t sh32[kFrontChunks / 64];
+  const int t = threadIdx.x;
+  Control* ctl = c.ctl;
+  if (t == 0) {
+    ctl->status = 0;
+    ctl->pad0 = 0;
+    ctl->total = 0;
+    for (int i = 0; i < 7; ++i) ctl->pad[i] = 0;
+    ctl->pad[3] = ~0ull;
+    __threadfence();
+  }
+  __syncthreads();                                   // the status word is clear before any check sets it
+  if (t < 64) validate_request(c, 0);
+  const int64_t N = c.total_chunks;
+  const ReqDesc& rq = c.one;
+  uint32_t e = 0;
+  if (t < N) {
+    const uint64_t pos = (uint64_t)rq.table_off + 4 * (uint64_t)t;
+    if (pos + 4 <= c.stream_bytes && pos + 4 <= (uint64_t)rq.payload_off) e = *(const uint32_t*)(c.stream + pos);
+    else set_status2(ctl, kStCorrupt);
+    c.chunk_sizes[t] = e;
+  }
+  // kFrontChunks chunks hold at most 64 MiB of stored bytes: the scan fits 32 bits
+  uint32_t total;
+  const uint32_t ex = block_excl_scan_u32<kFrontChunks / 64>((uint32_t)align16(e & 0x7fffffffu), sh32, total);
+  if (t < N) c.chunk_offs[t] = ex;
+  if (t == 0) c.chunk_offs[N] = total;
+  __threadfence_block();
+  __syncthreads();                                   // every size and offset is written
+  if (t == 0) check_request_total(c, 0);
+  count_word_parallel(c, (t < N) ? classify_dec_chunk(c, worklist, fast_pipeline(c), t) : 0u);
+}
+
+hipError_t launch_dec_front_small(const CallDesc& c, hipStream_t s) {
+  uint32_t* worklist = (uint32_t*)(c.chunk_offs + c.total_chunks + 1);
+  k_dec_front_small<<<1, kFrontChunks, 0, s>>>(c, worklist);
+  return hipGetLastError();
 }
 
 // The listed chunks, one block each: a raw chunk is copied to its code slot;
@@ -1838,13 +1891,15 @@ __global__ __launch_bounds__(256) void k_ll_decode_generic(CallDesc c, const uin
   }
 }
 
-hipError_t launch_lossless_decode(const CallDesc& c, hipStream_t s) {
+hipError_t launch_lossless_decode(const CallDesc& c, bool classified, hipStream_t s) {
   if (c.total_chunks == 0) return hipSuccess;
   uint32_t* worklist = (uint32_t*)(c.chunk_offs + c.total_chunks + 1);
-  k_ll_classify_dec<<<(int)std::min<int64_t>((std::max<int64_t>(c.total_chunks, c.R) + 255) / 256, 4096), 256, 0, s>>>(
-      c, worklist);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!classified) {
+    k_ll_classify_dec<<<(int)std::min<int64_t>((std::max<int64_t>(c.total_chunks, c.R) + 255) / 256, 4096), 256, 0, s>>>(
+        c, worklist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   k_ll_decode_raw<<<(int)std::min<int64_t>(c.total_chunks, 256 * 8), 256, 0, s>>>(c, worklist);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const bool p1 = c.stages[0] == KVC_TUPL8_1 && c.stages[1] == KVC_BIT_8 && c.stages[2] == KVC_RZE_2 && c.stages[3] == 0;
