@@ -123,6 +123,18 @@ def test_zero_rich_inputs_compress(stages):
     assert s["identical"]
 
 
+@pytest.mark.parametrize("T", [4096, 4097])
+def test_decode_front_at_the_small_call_limit(T):
+    # one layer of 4-bit per-token keys and values in 4 KiB chunks: 2 ceil(T / 8)
+    # chunks, 1024 at T = 4096 (a decode whose reset, table scan and
+    # classification are one launch) and 1026 at T = 4097 (the multi-kernel
+    # front); half-zero input, so that raw and compressed chunks are classified
+    wl = C1.with_(chunk_bytes=4096, name="front_limit")
+    s = run_case(wl, 1, T, zero_rich=True, zero_frac=0.5, seed=31)
+    assert s["identical"]
+    assert s["chunks_compressed"] >= 1 and s["chunks_raw"] >= 1, s
+
+
 @pytest.mark.parametrize("stages", [("TUPL8_1", "BIT_8", "RZE_2"), ("TUPL8_1", "RZE_2")])
 @pytest.mark.parametrize("T", [528, 516])
 def test_word_parallel_lossless_full_chunks(stages, T):
