@@ -666,17 +666,25 @@ constexpr int kP1CapLines = 8 * kP1SegLines;
 constexpr int kP1BlocksPerCu = kP1Phases == 2 ? 2 : 4;
 static_assert(kP1Phases == 2 || kP1Phases == 4, "two or four phases");
 
-// bitmap popcount scan into 16-bit offsets (a chunk has at most 32768 words);
-// offs[nd] = total
+// The decode reads bitmap dwords j dpj + c and their offsets for the eight
+// bit planes j at once; padded by 4 dwords (bitmap) and 8 halfwords (offsets)
+// per plane, the eight reads fall on eight different banks.  dpj is a
+// multiple of 8, so (dpj + 4) mod 32 is an odd multiple of 4.
+__device__ __forceinline__ int bm_pad(int d, int dpj) { return d + 4 * (d / dpj); }
+__device__ __forceinline__ int offs_pad(int d, int dpj) { return d + 8 * (d / dpj); }
+
+// bitmap popcount scan into 16-bit offsets (a chunk has at most 32768 words),
+// both arrays padded per plane; offs at offs_pad(nd) = total
 template <int NW>
-__device__ __forceinline__ uint32_t scan_bitmap16(const uint32_t* bm, uint16_t* offs, int nd, uint32_t* sh32) {
+__device__ __forceinline__ uint32_t scan_bitmap16(const uint32_t* bm, uint16_t* offs, int nd, int dpj, uint32_t* sh32) {
   constexpr int PT = 1024 / (64 * NW);
   const int t = threadIdx.x;
+  const int pj = (PT * t) / dpj;                     // a thread's PT dwords lie in one plane (dpj % PT == 0)
   uint32_t cnt[PT], sum = 0;
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int d = PT * t + i;
-    cnt[i] = (d < nd) ? (uint32_t)__builtin_popcount(bm[d]) : 0u;
+    cnt[i] = (d < nd) ? (uint32_t)__builtin_popcount(bm[d + 4 * pj]) : 0u;
     sum += cnt[i];
   }
   uint32_t total;
@@ -684,10 +692,10 @@ __device__ __forceinline__ uint32_t scan_bitmap16(const uint32_t* bm, uint16_t* 
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int d = PT * t + i;
-    if (d < nd) offs[d] = (uint16_t)run;
+    if (d < nd) offs[d + 8 * pj] = (uint16_t)run;
     run += cnt[i];
   }
-  if (t == 0) offs[nd] = (uint16_t)total;
+  if (t == 0) offs[offs_pad(nd, dpj)] = (uint16_t)total;
   __syncthreads();
   return total;
 }
@@ -717,8 +725,8 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
   static_assert(NT == 256, "one bitmap line per thread");
   constexpr int SPT = NT / 8;                          // loader threads per run
   __shared__ __attribute__((aligned(16))) uint4 buf[kP1CapLines + 1];   // a lane reads 3 dwords from its first word's
-  __shared__ __attribute__((aligned(16))) uint32_t bm[1024];
-  __shared__ uint16_t offs[1024 + 1];
+  __shared__ __attribute__((aligned(16))) uint32_t bm[1024 + 32];   // padded per plane (bm_pad)
+  __shared__ uint16_t offs[1024 + 64 + 1];                             // (offs_pad)
   __shared__ __attribute__((aligned(16))) uint4 seg[PH * 8];   // per (phase, plane): first LDS line, first stored line, lines, word shift
   __shared__ uint32_t sh32[NW];
   __shared__ __attribute__((aligned(16))) uint4 nibtab[16];
@@ -766,7 +774,8 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
       const int sc = stored;
       const uint64_t cpos = pos;
       const uint64_t avail = (c.stream_bytes > cpos) ? c.stream_bytes - cpos : 0;
-      if ((int)threadIdx.x < n / 256) *(uint4*)(bm + 4 * threadIdx.x) = x[0];
+      const int dpj = n / 512;                          // bitmap dwords per bit plane
+      if ((int)threadIdx.x < n / 256) *(uint4*)(bm + bm_pad(4 * threadIdx.x, dpj)) = x[0];
       __syncthreads();
       i = next_flag<NW>(candm, i + 1);
       if (i < NT) wp_decode_chunk(c, (int64_t)blockIdx.x + (int64_t)gridDim.x * (r0 + i), 1, L, pos, stored);
@@ -775,7 +784,7 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
       const int nd = n / 64;
       uint32_t nnz = 0;
       if (ok) {
-        nnz = scan_bitmap16<NW>(bm, offs, nd, sh32);
+        nnz = scan_bitmap16<NW>(bm, offs, nd, dpj, sh32);
         ok = n / 16 + 2 * (int)nnz == sc && (uint64_t)(16 * ((sc + 15) / 16)) <= avail + 15;
       }
       if (!ok) {
@@ -784,14 +793,14 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
         if (i < NT) load_bitmap();
         continue;
       }
-      const int ngi = n / 4096, dpj = n / 512;
+      const int ngi = n / 4096;
       const int gpp = (ngi + PH - 1) / PH;
       if (wave == 0) {
         // run of plane j in phase h (lane 8 h + j): words [A, B), lines A / 8 .. (B + 7) / 8
         const int h = lane >> 3, j = lane & 7;
         const int g0 = min(ngi, h * gpp), g1 = min(ngi, g0 + gpp);
         uint32_t A = 0, B = 0;
-        if (h < PH) { A = offs[j * dpj + 8 * g0]; B = offs[j * dpj + 8 * g1]; }
+        if (h < PH) { A = offs[offs_pad(j * dpj + 8 * g0, dpj)]; B = offs[offs_pad(j * dpj + 8 * g1, dpj)]; }
         const uint32_t cnt = (B > A) ? ((B + 7) >> 3) - (A >> 3) : 0u;
         uint32_t s = cnt;
 #pragma unroll
@@ -847,12 +856,12 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
 #pragma unroll
           for (int k2 = 0; k2 < 2; ++k2) {
             const int kk = 2 * q + k2;
-            const int d = j * dpj + 8 * gi + kk;
-            const uint32_t bits = bm[d];
+            const int d = 8 * gi + kk;                      // within plane j
+            const uint32_t bits = bm[j * (dpj + 4) + d];
             const uint32_t nib = (bits >> (4 * bb)) & 15u;
             // index of the nibble's first non-zero word; every word this
             // nibble can mark lies in the phase's run of plane j
-            const uint32_t rr = (uint32_t)offs[d] + (uint32_t)__builtin_popcount(bits & below);
+            const uint32_t rr = (uint32_t)offs[j * (dpj + 8) + d] + (uint32_t)__builtin_popcount(bits & below);
             const uint32_t di = min((rr + shift) >> 1, 4u * (uint32_t)kP1CapLines + 1u);
             const uint32_t d0 = buf32[di], d1 = buf32[di + 1], d2 = buf32[di + 2];
             const uint32_t sh = (rr & 1u) << 4;
