@@ -649,8 +649,8 @@ __device__ __forceinline__ int next_cand(const uint32_t* cand, int i) {
 // load while the current one decodes.  A wave's decoded group goes out
 // through LDS so that every store instruction writes 1 KiB of whole lines:
 // straight from the transposes, each store would cover a quarter of 32
-// lines, which measured 13 % slower with default stores and four times
-// slower with non-temporal ones.
+// lines, which measured about 18 % slower with default stores and five
+// times slower with non-temporal ones.
 #ifndef KVC_P1_PHASES
 #define KVC_P1_PHASES 4
 #endif
@@ -661,8 +661,8 @@ constexpr int kP1Gpp = 16 / kP1Phases;               // groups per phase of a 64
 constexpr int kP1SegLines = 32 * kP1Gpp + 2;
 constexpr int kP1CapLines = 8 * kP1SegLines;
 // LDS per block: the phase's lines, the bitmap and its offsets, and a 4 KiB
-// output staging area per wave: 56 KB (two blocks per CU) at two phases,
-// 39 KB (four) at four
+// output staging area per wave: about 57 KB (two blocks per CU) at two
+// phases, 40 KB (four) at four
 constexpr int kP1BlocksPerCu = kP1Phases == 2 ? 2 : 4;
 static_assert(kP1Phases == 2 || kP1Phases == 4, "two or four phases");
 
