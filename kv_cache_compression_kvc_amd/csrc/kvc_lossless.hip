@@ -825,20 +825,38 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
           if (k < (int)sg.z && (uint64_t)(16 * l + 16) <= avail) x[u] = src[l];
         }
       };
+      // A set bitmap bit must mark a non-zero word.  The size check has
+      // matched the set bits one to one with the stored words, so that holds
+      // when every stored word is non-zero: checked on the staged lines
+      // (each line of a run once; words past the last stored one excluded).
+      const rze_u16x2 one2 = opaque_one2();
+      uint32_t bad = 0;
       auto store_phase = [&](int h) {
         const uint4 sg = seg[8 * h + (int)threadIdx.x / SPT];
         const int k0 = (int)threadIdx.x % SPT;
 #pragma unroll
         for (int u = 0; u < PTL; ++u) {
           const int k = k0 + SPT * u;
-          if (k < (int)sg.z) buf[sg.x + k] = x[u];
+          if (k < (int)sg.z) {
+            buf[sg.x + k] = x[u];
+            uint4 y = x[u];
+            const int past = 8 * (int)(sg.y + (uint32_t)k) + 8 - (int)nnz;   // words of the line past the end
+            if (past > 0) {
+              // the chunk's last line: its words from 8 - past on are not stored words
+              const uint32_t keep = 8 - past;
+              y.x |= keep < 1 ? 0xFFFFu : 0u; y.x |= keep < 2 ? 0xFFFF0000u : 0u;
+              y.y |= keep < 3 ? 0xFFFFu : 0u; y.y |= keep < 4 ? 0xFFFF0000u : 0u;
+              y.z |= keep < 5 ? 0xFFFFu : 0u; y.z |= keep < 6 ? 0xFFFF0000u : 0u;
+              y.w |= keep < 7 ? 0xFFFFu : 0u; y.w |= 0xFFFF0000u;
+            }
+            bad |= (nz_halves(y.x, one2) & nz_halves(y.y, one2) & nz_halves(y.z, one2) & nz_halves(y.w, one2)) ^
+                   0x00010001u;
+          }
         }
       };
       const uint32_t* buf32 = (const uint32_t*)buf;
       const int j = lane >> 3, bb = lane & 7;
       const uint32_t below = (1u << (4 * bb)) - 1u;     // bitmap bits of the nibbles before this lane's
-      const rze_u16x2 one2 = opaque_one2();
-      uint32_t bad = 0;
       load_phase(0);
 #pragma unroll 1
       for (int h = 0; h < PH; ++h) {
@@ -868,8 +886,6 @@ __global__ __launch_bounds__(64 * NW, kP1BlocksPerCu) void k_ll_decode_p1(CallDe
             const uint32_t p01 = __builtin_amdgcn_alignbit(d1, d0, sh), p23 = __builtin_amdgcn_alignbit(d2, d1, sh);
             const uint4 e = nibtab[nib];
             uint32_t lo = __builtin_amdgcn_perm(p23, p01, e.x), hi = __builtin_amdgcn_perm(p23, p01, e.y);
-            // a set bit must mark a non-zero word: min(word, 1) per half against the table
-            bad |= (nz_halves(lo, one2) ^ e.z) | (nz_halves(hi, one2) ^ e.w);
             wl[k2] = lo;
             wh[k2] = hi;
           }
