@@ -267,15 +267,45 @@ def test_zeroed_word_under_a_set_bitmap_bit_is_detected(section):
     comp = [c for c in chunk_layout(ref, wl, L, T) if c[0] == section and not c[5] and c[4] > c[2] // 16]
     assert len(comp) >= 2, comp
     rng = np.random.default_rng(section)
-    for w, i, n, pos, stored, raw in [comp[0], comp[-1], comp[int(rng.integers(0, len(comp)))]]:
+    # random words, and the first and the last stored word of a chunk (the
+    # last one shares its 16-byte line with bytes past the chunk's words)
+    picks = [(c, None) for c in (comp[0], comp[-1], comp[int(rng.integers(0, len(comp)))])]
+    picks += [(comp[0], "first"), (comp[0], "last"), (comp[-1], "last")]
+    for (w, i, n, pos, stored, raw), which in picks:
         words = np.frombuffer(ref[pos + n // 16:pos + stored].tobytes(), np.uint16)
         assert (words != 0).all()
         bad = ref.copy()
-        at = pos + n // 16 + 2 * int(rng.integers(0, words.size))
+        k = {None: int(rng.integers(0, words.size)), "first": 0, "last": words.size - 1}[which]
+        at = pos + n // 16 + 2 * k
         bad[at:at + 2] = 0
         log(f"  section {w} chunk {i}: zeroed the word at byte {at - pos} of {stored}")
         assert gpu_decode(plan, bad, wl, T, L)[0] == K.ERR_CORRUPT_STREAM
 
+
+
+def test_zeroed_last_word_before_a_line_end_is_detected():
+    # 4-bit per-token keys in 4 KiB chunks: compressed chunks whose stored
+    # words end inside a 16-byte line; zeroing the last word (the lossless
+    # decode checks stored words per line, masking the bytes past them) or a
+    # word of that line must still mark the stream corrupt
+    wl = C1.with_(chunk_bytes=4096, name="partial_line")
+    L, T = 1, 1024
+    k, v = W.zero_rich_kv(wl, L, T, seed=31, zero_frac=0.5)
+    st, ref = oracle_encode(wl, to_u16(k), to_u16(v), T, L)
+    assert st == O.OK
+    plan = K.Plan(K.config_from_workload(wl, max_tokens=T, layers=L))
+    assert gpu_decode(plan, ref, wl, T, L)[0] == K.OK
+    odd = [c for c in chunk_layout(ref, wl, L, T)
+           if c[0] == 0 and not c[5] and c[4] > c[2] // 16 and (c[4] - c[2] // 16) % 16 != 0]
+    assert len(odd) >= 2, odd
+    for w, i, n, pos, stored, raw in odd[:3]:
+        nw = (stored - n // 16) // 2
+        for k_ in (nw - 1, (nw - 1) & ~7):                  # the last word, the first word of its line
+            bad = ref.copy()
+            at = pos + n // 16 + 2 * k_
+            bad[at:at + 2] = 0
+            log(f"  chunk {i}: zeroed word {k_} of {nw}")
+            assert gpu_decode(plan, bad, wl, T, L)[0] == K.ERR_CORRUPT_STREAM
 
 def test_paged_matches_oracle():
     wl = W.WORKLOADS["c4_paged_llama8b"].with_(layers=2, chunk_bytes=8192)
